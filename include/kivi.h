@@ -1,0 +1,166 @@
+/*
+ * kivi.h -- C ABI of libkivi: KIVI KV-cache quantization and decode attention
+ * over the packed cache, hand-written for AMD CDNA4 (gfx950).
+ *
+ * What is computed (pages cited by title and section):
+ *  - "KIVI - 2-bit KV cache quantisation" (LLM systems cookbook notebook),
+ *    "Asymmetric 2-bit quantiser" and "K (per-channel) and V (per-token)
+ *    quantisation": per group, zero = min, scale = (max - min) / (2^b - 1)
+ *    (scale 1 for a constant group), code = round((x - zero) / scale).
+ *  - "KIVI" (VeloxQuant-MLX docs), "How it works": keys are grouped along the
+ *    token axis (one group = G tokens of one channel), values along the
+ *    channel axis (one group = G channels of one token); the newest R tokens
+ *    stay in full precision and older tokens are quantized only in whole
+ *    multiples of G, so one-shot prefill and token-by-token decode give the
+ *    same cache bit for bit.
+ *  - "[Paper review] KIVI ... (ICML'24)", 1.3 (decoding: append the new K/V,
+ *    then A = softmax(q K^T), o = A V) and 3.2 system-level implementation
+ *    (dequantization fused into the matrix products).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" are HIP device addresses; the library never
+ *    allocates, frees or synchronizes; all work is enqueued on the caller's
+ *    stream in call order.  Host handles are not thread-safe.
+ *  - Arguments are validated before anything is enqueued: a call that returns
+ *    an error has had no effect on the cache.  Asynchronous kernel faults
+ *    surface at the caller's next synchronization.
+ *  - Inputs must be finite (NaN / Inf are a precondition violation and are
+ *    not checked).
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KIVI_OK = 0,
+    KIVI_ERR_INVALID_ARG = 1,      /* bad config, null pointer, bad flag    */
+    KIVI_ERR_UNSUPPORTED = 2,      /* valid KIVI, but not a shape built here */
+    KIVI_ERR_CAPACITY = 3,         /* n + n_new > max_tokens                 */
+    KIVI_ERR_BUFFER_TOO_SMALL = 4, /* device buffer or workspace too small  */
+    KIVI_ERR_STATE = 5,            /* e.g. decode on an empty cache          */
+    KIVI_ERR_HIP = 6               /* a kernel launch failed                 */
+} kivi_status;
+
+typedef enum { KIVI_F16 = 0, KIVI_F32 = 1 } kivi_dtype;
+
+/* Flush policy.  KIVI_FLUSH_WINDOW: the quantized prefix of an n-token
+   stream is Q(n) = G * floor(max(0, n - R) / G) for keys and values alike
+   ("KIVI" VeloxQuant-MLX docs, "How it works" items 3-4). */
+typedef enum { KIVI_FLUSH_WINDOW = 0 } kivi_flush_policy;
+
+typedef struct {
+    int32_t batch;        /* B  >= 1                                          */
+    int32_t n_kv_heads;   /* H  >= 1                                          */
+    int32_t n_q_heads;    /* Hq: a multiple of H; Hq / H in {1, 2, 4}         */
+    int32_t head_dim;     /* D: 128                                           */
+    int32_t bits;         /* b: 2 or 4                                        */
+    int32_t group;        /* G: 32                                            */
+    int32_t residual;     /* R >= 0, a multiple of G                          */
+    int32_t kv_dtype;     /* kivi_dtype of the K/V rows handed to append      */
+    int32_t policy;       /* kivi_flush_policy                                */
+    int32_t reserved;     /* must be 0                                        */
+    int64_t max_tokens;   /* capacity per stream, >= 1                        */
+} kivi_config;
+
+typedef struct kivi_cache kivi_cache;   /* opaque host-side handle */
+
+/* Where everything sits inside the caller's device buffer (byte offsets from
+   its start).  Packed blocks: [B*H][max_groups][block_bytes], block j of a
+   stream holding tokens [jG, jG+G).  Inside a block (offsets below are from
+   the block start): K codes, V codes (code_bytes = b*G*D/8 each), then fp16
+   K scale[D], K zero[D], V scale[D/G][G], V zero[D/G][G].  The bit order of
+   the codes is described in the kernel source (it follows the matrix-core
+   operand layout).  Ring: [B*H][ring_capacity][D] in kv_dtype for K and for
+   V; token t of a stream lives in slot t mod ring_capacity while it is in
+   the full-precision residual [n_quantized, n_tokens). */
+typedef struct {
+    size_t blocks, ring_k, ring_v;      /* region offsets                     */
+    size_t block_bytes, code_bytes;
+    size_t off_kcode, off_vcode, off_kscale, off_kzero, off_vscale, off_vzero;
+    int64_t max_groups;
+    int64_t ring_capacity;              /* R + G                              */
+    int64_t n_tokens;                   /* n                                  */
+    int64_t n_quantized;                /* Q(n), a multiple of G              */
+} kivi_layout;
+
+/* What an append of n_new tokens will do (pure host computation). */
+typedef struct {
+    int64_t n_old, n_new_total;         /* n before / after                   */
+    int64_t q_old, q_new;               /* quantized prefix before / after    */
+    int64_t flush_token_begin;          /* tokens [q_old, q_new) are quantized */
+    int64_t flush_token_end;            /*   (token t < n_old read from ring)  */
+    int64_t ring_token_begin;           /* tokens [max(q_new, n_old), n) are   */
+    int64_t ring_token_end;             /*   copied into the ring              */
+} kivi_append_plan;
+
+/* Bytes of device memory a cache with this config needs (0 if the config is
+   invalid or unsupported). */
+size_t kivi_cache_bytes(const kivi_config *cfg);
+
+/* Validate cfg and bind a host handle to the caller's device buffer
+   (dev_mem, dev_bytes >= kivi_cache_bytes(cfg), 256-byte aligned).  The
+   cache starts empty; the buffer's contents need no initialization.  The
+   buffer must outlive the handle.  *out is set only on KIVI_OK. */
+kivi_status kivi_cache_create(const kivi_config *cfg, void *dev_mem,
+                              size_t dev_bytes, kivi_cache **out);
+
+/* Release the host handle (the device buffer is the caller's). NULL is ok. */
+kivi_status kivi_cache_destroy(kivi_cache *c);
+
+/* Append n_new >= 0 tokens to every stream.  k, v: device, contiguous
+   [B][H][n_new][D] in kv_dtype (may be NULL when n_new == 0); they are read
+   by kernels enqueued on `stream` and must stay valid until those finish.
+   Enqueues, in this order: quantization of tokens [q_old, q_new) (K per
+   channel, V per token; token t < n_old is read from the ring, later tokens
+   from k/v), then the copy of tokens [max(q_new, n_old), n) into the ring.
+   flags must be 0.  Errors: INVALID_ARG (null handle, null k/v with
+   n_new > 0, n_new < 0, flags), CAPACITY (n + n_new > max_tokens), HIP. */
+kivi_status kivi_append(kivi_cache *c, const void *k, const void *v,
+                        int64_t n_new, uint32_t flags, hipStream_t stream);
+
+/* Make the cache canonical.  Under the window policy every append already
+   leaves it canonical, so this only validates the handle. */
+kivi_status kivi_flush(kivi_cache *c, hipStream_t stream);
+
+/* Host-only: what kivi_append(c, ..., n_new, ...) would enqueue. */
+kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new,
+                             kivi_append_plan *out);
+
+/* Workspace bytes kivi_decode_attn needs for any n <= max_tokens. */
+size_t kivi_decode_workspace_bytes(const kivi_cache *c);
+
+/* How decode splits the quantized prefix at the current n: *splits work
+   items per stream over whole groups, *groups_per_split groups each (plus
+   one item per stream for the full-precision residual). Host-only. */
+kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits,
+                             int32_t *groups_per_split);
+
+/* One decode-attention step over all n cached tokens of every stream:
+   out[b][hq][:] = softmax(scale * q[b][hq] . K_hat^T) V_hat, where K_hat and
+   V_hat are the dequantized groups (code * scale + zero) followed by the
+   full-precision residual, and query head hq reads KV head hq / (Hq / H).
+   q: device [B][Hq][D] in q_dtype; out: device float32 [B][Hq][D];
+   softmax_scale <= 0 selects 1/sqrt(D); workspace: device, ws_bytes >=
+   kivi_decode_workspace_bytes(c).  Errors: INVALID_ARG (null pointers, bad
+   q_dtype), STATE (n == 0), BUFFER_TOO_SMALL, HIP. */
+kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype,
+                             float softmax_scale, float *out, void *workspace,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Offsets, sizes and the current n / Q(n) (host-only). */
+kivi_status kivi_get_layout(const kivi_cache *c, kivi_layout *out);
+
+/* Static string for a status code. */
+const char *kivi_status_string(kivi_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIVI_H */

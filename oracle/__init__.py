@@ -1,0 +1,228 @@
+"""Python access to the CPU oracle (``kivi_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` import this package.  The product library
+(``kv_cache_quantization_amd``) never imports it, and this package imports
+nothing from the product library.
+
+The arithmetic lives in plain C (``kivi_oracle.c``, built with
+``-O2 -fno-fast-math -ffp-contract=off``); this module only marshals numpy
+arrays.  See the C file's header for the pages and sections each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kivi_oracle.c")
+_LIB = os.path.join(_HERE, "libkivi_oracle.so")
+
+POLICY_WINDOW = 0
+POLICY_PAPER = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call([
+            "gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+            "-shared", "-std=c99", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if (not os.path.exists(_LIB)
+                or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.oracle_f16_to_f32.restype = ctypes.c_float
+        L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_f32_to_f16.restype = ctypes.c_uint16
+        L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        L.oracle_group_quant.argtypes = [P, i32, i32, P, P, P, P, P]
+        L.oracle_dequant_one.restype = ctypes.c_float
+        L.oracle_dequant_one.argtypes = [ctypes.c_uint8, ctypes.c_uint16, ctypes.c_uint16]
+        L.oracle_quantized_prefix.argtypes = [i64, i32, i32, i32, P, P]
+        L.oracle_build_cache.argtypes = [P, P, i32, i32, i32, i64, i32, i32, i32,
+                                         i64, i64, P, P, P, P, P, P]
+        L.oracle_dequant_cache.argtypes = [P, P, i32, i32, i32, i64, i32, i32,
+                                           i64, i64, P, P, P, P, P, P, P, P]
+        L.oracle_decode_attn.argtypes = [P, P, P, i32, i32, i32, i64, i32, f64, P]
+        L.oracle_block_bytes.restype = i64
+        L.oracle_block_bytes.argtypes = [i32]
+        L.oracle_pack_blocks.argtypes = [i32, i32, i64, i32, i64, P, P, P, P, P, P, P]
+        L.oracle_code_position.argtypes = [i32, i32, i32, i32, P, P]
+        L.oracle_fake_quant_2d.argtypes = [P, i32, i32, i32, i32, i32, i32, P]
+        L.oracle_f16_to_f32_array.argtypes = [P, P, i64]
+        L.oracle_f32_to_f16_array.argtypes = [P, P, i64]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _kv(x):
+    """Return (contiguous array, dtype code): 0 = fp16 bits, 1 = float32."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        return x.view(np.uint16), 0
+    if x.dtype == np.float32:
+        return x, 1
+    raise TypeError("K/V must be float16 or float32, got %s" % x.dtype)
+
+
+# --------------------------------------------------------------------------
+# scalar building blocks
+# --------------------------------------------------------------------------
+def f16_to_f32(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().oracle_f16_to_f32_array(_p(h), _p(out), h.size)
+    return out
+
+
+def f32_to_f16(f: np.ndarray) -> np.ndarray:
+    """Round float32 values to fp16 bit patterns (uint16)."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, np.uint16)
+    lib().oracle_f32_to_f16_array(_p(f), _p(out), f.size)
+    return out
+
+
+def group_quant(g, bits: int):
+    """GroupQuant of one group: returns (codes u8, mn f32, s f32, zero16, scale16)."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    codes = np.empty(g.size, np.uint8)
+    mn = np.zeros(1, np.float32)
+    s = np.zeros(1, np.float32)
+    z = np.zeros(1, np.uint16)
+    sc = np.zeros(1, np.uint16)
+    lib().oracle_group_quant(_p(g), g.size, bits, _p(codes), _p(mn), _p(s), _p(z), _p(sc))
+    return codes, float(mn[0]), float(s[0]), int(z[0]), int(sc[0])
+
+
+def dequant_one(code: int, zero16: int, scale16: int) -> float:
+    return float(lib().oracle_dequant_one(code, zero16, scale16))
+
+
+def quantized_prefix(n: int, group: int, residual: int, policy: int = POLICY_WINDOW):
+    qk = ctypes.c_int64()
+    qv = ctypes.c_int64()
+    lib().oracle_quantized_prefix(n, group, residual, policy,
+                                  ctypes.byref(qk), ctypes.byref(qv))
+    return qk.value, qv.value
+
+
+# --------------------------------------------------------------------------
+# whole-cache views
+# --------------------------------------------------------------------------
+def build_cache(k, v, bits: int, group: int, residual: int,
+                policy: int = POLICY_WINDOW) -> dict:
+    """Logical KIVI cache of K, V ([B, H, n, D], float16 or float32)."""
+    kk, dt = _kv(k)
+    vv, dt2 = _kv(v)
+    assert dt == dt2 and kk.shape == vv.shape
+    B, H, n, D = kk.shape
+    qk, qv = quantized_prefix(n, group, residual, policy)
+    c = dict(
+        B=B, H=H, n=n, D=D, G=group, bits=bits, R=residual, policy=policy,
+        qk=qk, qv=qv,
+        kcodes=np.zeros((B, H, qk, D), np.uint8),
+        kzero16=np.zeros((B, H, qk // group, D), np.uint16),
+        kscale16=np.zeros((B, H, qk // group, D), np.uint16),
+        vcodes=np.zeros((B, H, qv, D), np.uint8),
+        vzero16=np.zeros((B, H, qv, D // group), np.uint16),
+        vscale16=np.zeros((B, H, qv, D // group), np.uint16),
+    )
+    lib().oracle_build_cache(_p(kk), _p(vv), dt, B, H, n, D, group, bits, qk, qv,
+                             _p(c["kcodes"]), _p(c["kzero16"]), _p(c["kscale16"]),
+                             _p(c["vcodes"]), _p(c["vzero16"]), _p(c["vscale16"]))
+    # the full-precision residual, verbatim in the input dtype
+    c["k_resid"] = np.ascontiguousarray(np.asarray(k)[:, :, qk:, :])
+    c["v_resid"] = np.ascontiguousarray(np.asarray(v)[:, :, qv:, :])
+    return c
+
+
+def dequant_cache(k, v, cache: dict):
+    """Float32 K_hat, V_hat [B, H, n, D] of the cache built from k, v."""
+    kk, dt = _kv(k)
+    vv, _ = _kv(v)
+    B, H, n, D = kk.shape
+    khat = np.empty((B, H, n, D), np.float32)
+    vhat = np.empty((B, H, n, D), np.float32)
+    lib().oracle_dequant_cache(
+        _p(kk), _p(vv), dt, B, H, n, D, cache["G"], cache["qk"], cache["qv"],
+        _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
+        _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
+        _p(khat), _p(vhat))
+    return khat, vhat
+
+
+def decode_attn(q, khat, vhat, sm_scale: float | None = None) -> np.ndarray:
+    """softmax(q K_hat^T * sm_scale) V_hat per query head, fp64 accumulation.
+
+    q: [B, Hq, D] (any float dtype, converted to float32); khat, vhat:
+    [B, H, n, D] float32.  Query head hq reads KV head hq // (Hq // H)."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float32))
+    khat = np.ascontiguousarray(khat, dtype=np.float32)
+    vhat = np.ascontiguousarray(vhat, dtype=np.float32)
+    B, Hq, D = q.shape
+    _, H, n, _ = khat.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, D), np.float32)
+    lib().oracle_decode_attn(_p(q), _p(khat), _p(vhat), B, H, Hq, n, D,
+                             float(sm_scale), _p(out))
+    return out
+
+
+def block_bytes(bits: int) -> int:
+    return int(lib().oracle_block_bytes(bits))
+
+
+def pack_blocks(cache: dict, max_groups: int | None = None) -> np.ndarray:
+    """Packed blocks [B*H, max_groups, block_bytes] (u8) of the quantized prefix."""
+    assert cache["qk"] == cache["qv"], "packing needs equal K/V prefixes"
+    assert cache["D"] == 128 and cache["G"] == 32
+    B, H, nq, bits = cache["B"], cache["H"], cache["qk"], cache["bits"]
+    if max_groups is None:
+        max_groups = nq // 32
+    out = np.zeros((B * H, max_groups, block_bytes(bits)), np.uint8)
+    lib().oracle_pack_blocks(B, H, nq, bits, max_groups,
+                             _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
+                             _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
+                             _p(out))
+    return out
+
+
+def code_position(bits: int, is_v: bool, token: int, channel: int):
+    d = ctypes.c_int64()
+    b = ctypes.c_int()
+    lib().oracle_code_position(bits, int(is_v), token, channel,
+                               ctypes.byref(d), ctypes.byref(b))
+    return d.value, b.value
+
+
+def fake_quant_2d(x, axis: int, bits: int, group: int, mode: int = 0) -> np.ndarray:
+    """Notebook-style reconstruction of a 2-D float32 array (see the C file)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    assert (rows if axis == 0 else cols) % group == 0
+    out = np.empty_like(x)
+    lib().oracle_fake_quant_2d(_p(x), rows, cols, axis, bits, group, mode, _p(out))
+    return out

@@ -1,0 +1,474 @@
+/*
+ * kivi_oracle.c -- plain, slow, scalar CPU reference for KIVI KV-cache
+ * quantization and decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this file: only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark do.  It shares no code, header, table or constant with the
+ * HIP library; it is written from the pages' definitions, one step at a time,
+ * in the pages' order, so that a reader can check it by eye.
+ *
+ * Sources (cited by page title and section):
+ *  [NB]  "KIVI - 2-bit KV cache quantisation" (LLM systems cookbook, serving
+ *        notebook 04): sections "Asymmetric 2-bit quantiser", "K
+ *        (per-channel) and V (per-token) quantisation", "Attention output:
+ *        quantised vs fp16", storage cell.
+ *  [VQ]  "KIVI" (VeloxQuant-MLX algorithm docs): "How it works" items 1-4 and
+ *        the zero/scale/q/recon formulas; "Re-measured after #162".
+ *  [RV]  "[Paper review] KIVI: A Tuning-Free Asymmetric 2bit Quantization for
+ *        KV Cache (ICML'24)" (chooblog): 1.1 quantization definition and its
+ *        worked example; 1.3 inference workflow; 3.2.2 grouped + residual
+ *        split; 3.2.3 Algorithm 1 (prefill / decoding) and its example.
+ *  [CQ]  "KV Cache Compression > Cache Quantization" (Language AI Handbook):
+ *        uniform quantization, the half-step error bound, QuantizedCache.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fPIC -shared
+ * (x86-64 SSE arithmetic: every float operation below is one IEEE-754
+ * binary32 operation rounded to nearest even; no FMA contraction.)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* IEEE-754 binary16 <-> binary32, written from the format definition.       */
+/* The cache stores zero and scale as fp16 ([NB] storage cell: "2 fp16 per   */
+/* group").  Rounding is to nearest, ties to even; subnormals are kept;      */
+/* magnitudes that round past 65504 become infinity.                         */
+/* ------------------------------------------------------------------------ */
+
+float oracle_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t e = (uint32_t)(h >> 10) & 0x1Fu;
+    uint32_t m = (uint32_t)h & 0x3FFu;
+    double v;
+    if (e == 0x1F) {
+        if (m != 0) return NAN;
+        v = INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)m, -24);                 /* subnormal: m * 2^-24 */
+    } else {
+        v = ldexp((double)(m | 0x400u), (int)e - 25);   /* (1024+m) * 2^(e-25) */
+    }
+    return (float)(sign ? -v : v);                 /* exact: fits binary32 */
+}
+
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+    uint32_t be = (x >> 23) & 0xFFu;
+    uint32_t man = x & 0x7FFFFFu;
+    if (be == 0xFF) return (uint16_t)(sign | 0x7C00u | (man ? 0x200u : 0u));
+    if (be == 0) return sign;      /* |f| < 2^-126: far below half of 2^-24 */
+    /* |f| = m24 * 2^(be-150) with m24 in [2^23, 2^24). */
+    uint32_t m24 = man | 0x800000u;
+    int E = (int)be - 127;                          /* unbiased exponent */
+    int qe = (E > -14 ? E : -14) - 10;              /* fp16 quantum 2^qe */
+    int sh = qe - ((int)be - 150);                  /* >= 13 */
+    uint32_t r;
+    if (sh >= 25) {
+        r = 0;                                      /* below half a quantum */
+    } else {
+        uint32_t keep = m24 >> sh;
+        uint32_t rem = m24 & ((1u << sh) - 1u);
+        uint32_t half = 1u << (sh - 1);
+        r = keep;
+        if (rem > half || (rem == half && (keep & 1u))) r++;
+    }
+    /* value = r * 2^qe; encode. For E <= -14 the bits are r itself
+       (r == 1024 is the smallest normal); above, the exponent field
+       follows E and a carry to r == 2048 rolls into the next binade. */
+    uint32_t bits = (E > -14) ? ((uint32_t)(E + 14) << 10) + r : r;
+    if (bits >= 0x7C00u) bits = 0x7C00u;
+    return (uint16_t)(sign | bits);
+}
+
+/* Round half to even ([NB] uses torch.round, which rounds ties to even). */
+static float round_half_even(float t)
+{
+    float f = floorf(t);
+    float r = t - f;                /* exact for |t| < 2^23 */
+    if (r > 0.5f) return f + 1.0f;
+    if (r < 0.5f) return f;
+    return (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* GroupQuant: asymmetric min/max quantization of one group.                 */
+/* [NB] "Asymmetric 2-bit quantiser"; [VQ] "How it works" formulas;          */
+/* [RV] 1.1:  z = min X,  s = (max X - min X) / (2^B - 1),                   */
+/*            Q(X) = round((X - z) / s),  X' = Q(X) * s + z.                 */
+/* Guard for a constant group: s == 0 -> s = 1 ([NB] quantiser, [CQ]).       */
+/* Codes are computed from the float32 (z, s); the stored pair is            */
+/* (fp16(z), fp16(s)).                                                       */
+/* ------------------------------------------------------------------------ */
+void oracle_group_quant(const float *g, int n, int bits, uint8_t *codes,
+                        float *mn_out, float *s_out,
+                        uint16_t *zero16, uint16_t *scale16)
+{
+    const float L = (float)((1 << bits) - 1);
+    float mn = g[0], mx = g[0];
+    for (int i = 1; i < n; i++) {
+        if (g[i] < mn) mn = g[i];
+        if (g[i] > mx) mx = g[i];
+    }
+    if (mn == 0.0f) mn = 0.0f;          /* a zero minimum is stored as +0 */
+    float rng = mx - mn;
+    float s = rng / L;
+    if (s == 0.0f) s = 1.0f;
+    for (int i = 0; i < n; i++) {
+        float d = g[i] - mn;
+        float t = d / s;
+        float c = round_half_even(t);
+        if (c < 0.0f) c = 0.0f;
+        if (c > L) c = L;
+        codes[i] = (uint8_t)c;
+    }
+    if (mn_out) *mn_out = mn;
+    if (s_out) *s_out = s;
+    if (zero16) *zero16 = oracle_f32_to_f16(mn);
+    if (scale16) *scale16 = oracle_f32_to_f16(s);
+}
+
+/* Dequantization of one code with the stored fp16 pair:
+   x_hat = code * scale + zero, two float32 roundings ([VQ] recon formula). */
+float oracle_dequant_one(uint8_t code, uint16_t zero16, uint16_t scale16)
+{
+    float p = (float)code * oracle_f16_to_f32(scale16);
+    return p + oracle_f16_to_f32(zero16);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Flush policies: how many tokens of an n-token stream are quantized.       */
+/* Window policy ([VQ] items 3-4): the newest R tokens stay fp16 and aged    */
+/* tokens are quantized only in whole multiples of G, for K and V alike:     */
+/*        Q(n) = G * floor(max(0, n - R) / G).                               */
+/* Paper policy ([RV] 3.2.2 / 3.2.3 Algorithm 1): keys keep r = n mod R      */
+/* tokens in full precision (Q_K = n - r); values keep the newest R          */
+/* (Q_V = max(0, n - R)).                                                    */
+/* ------------------------------------------------------------------------ */
+enum { ORACLE_POLICY_WINDOW = 0, ORACLE_POLICY_PAPER = 1 };
+
+void oracle_quantized_prefix(int64_t n, int group, int residual, int policy,
+                             int64_t *qk, int64_t *qv)
+{
+    if (policy == ORACLE_POLICY_PAPER) {
+        /* R > 0 required by the paper's definition r = l mod R. */
+        *qk = n - (n % residual);
+        *qv = n > residual ? n - residual : 0;
+    } else {
+        int64_t aged = n > residual ? n - residual : 0;
+        *qk = *qv = (aged / group) * group;
+    }
+}
+
+static float load_elem(const void *x, int dtype, int64_t idx)
+{
+    if (dtype == 0) return oracle_f16_to_f32(((const uint16_t *)x)[idx]);
+    return ((const float *)x)[idx];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Build the logical cache of one layer from n tokens.                       */
+/* Inputs k, v: [B][H][n][D] in dtype (0 = fp16 bits, 1 = float32).          */
+/* Keys per channel: group (b,h,j,c) = K[b,h, jG..jG+G-1, c]  ([NB] K along  */
+/* dim 0, [VQ] item 1, [RV] 3.2.3 step D).                                   */
+/* Values per token: group (b,h,t,j) = V[b,h,t, jG..jG+G-1]  ([NB] V along   */
+/* dim 1, [VQ] item 2, [RV] 3.2.3 step C).                                   */
+/* Outputs (logical, unpacked):                                              */
+/*   kcodes [B][H][qk][D] u8,  kzero16/kscale16 [B][H][qk/G][D]              */
+/*   vcodes [B][H][qv][D] u8,  vzero16/vscale16 [B][H][qv][D/G]              */
+/* where qk, qv come from oracle_quantized_prefix (caller passes them).      */
+/* ------------------------------------------------------------------------ */
+void oracle_build_cache(const void *k, const void *v, int dtype,
+                        int B, int H, int64_t n, int D, int G, int bits,
+                        int64_t qk, int64_t qv,
+                        uint8_t *kcodes, uint16_t *kzero16, uint16_t *kscale16,
+                        uint8_t *vcodes, uint16_t *vzero16, uint16_t *vscale16)
+{
+    float *grp = (float *)malloc(sizeof(float) * (size_t)G);
+    uint8_t *cg = (uint8_t *)malloc((size_t)G);
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++) {
+            int64_t base = ((int64_t)b * H + h) * n * D;
+            /* keys: per channel, G consecutive tokens */
+            for (int64_t j = 0; j < qk / G; j++)
+                for (int c = 0; c < D; c++) {
+                    for (int i = 0; i < G; i++)
+                        grp[i] = load_elem(k, dtype, base + (j * G + i) * D + c);
+                    int64_t pidx = (((int64_t)b * H + h) * (qk / G) + j) * D + c;
+                    oracle_group_quant(grp, G, bits, cg, NULL, NULL,
+                                       &kzero16[pidx], &kscale16[pidx]);
+                    for (int i = 0; i < G; i++)
+                        kcodes[(((int64_t)b * H + h) * qk + j * G + i) * D + c] = cg[i];
+                }
+            /* values: per token, G consecutive channels */
+            for (int64_t t = 0; t < qv; t++)
+                for (int j = 0; j < D / G; j++) {
+                    for (int i = 0; i < G; i++)
+                        grp[i] = load_elem(v, dtype, base + t * D + j * G + i);
+                    int64_t pidx = (((int64_t)b * H + h) * qv + t) * (D / G) + j;
+                    oracle_group_quant(grp, G, bits, cg, NULL, NULL,
+                                       &vzero16[pidx], &vscale16[pidx]);
+                    for (int i = 0; i < G; i++)
+                        vcodes[(((int64_t)b * H + h) * qv + t) * D + j * G + i] = cg[i];
+                }
+        }
+    free(grp);
+    free(cg);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantized view of the whole cache ([RV] 1.1 X' = Q(X) s + z; tokens in  */
+/* the full-precision residual are taken as they are, converted to float).   */
+/* khat, vhat: [B][H][n][D] float32.                                         */
+/* ------------------------------------------------------------------------ */
+void oracle_dequant_cache(const void *k, const void *v, int dtype,
+                          int B, int H, int64_t n, int D, int G,
+                          int64_t qk, int64_t qv,
+                          const uint8_t *kcodes, const uint16_t *kzero16,
+                          const uint16_t *kscale16,
+                          const uint8_t *vcodes, const uint16_t *vzero16,
+                          const uint16_t *vscale16,
+                          float *khat, float *vhat)
+{
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++) {
+            int64_t s = (int64_t)b * H + h;
+            for (int64_t t = 0; t < n; t++)
+                for (int c = 0; c < D; c++) {
+                    int64_t o = (s * n + t) * D + c;
+                    if (t < qk) {
+                        int64_t p = (s * (qk / G) + t / G) * D + c;
+                        khat[o] = oracle_dequant_one(kcodes[(s * qk + t) * D + c],
+                                                     kzero16[p], kscale16[p]);
+                    } else {
+                        khat[o] = load_elem(k, dtype, o);
+                    }
+                    if (t < qv) {
+                        int64_t p = (s * qv + t) * (D / G) + c / G;
+                        vhat[o] = oracle_dequant_one(vcodes[(s * qv + t) * D + c],
+                                                     vzero16[p], vscale16[p]);
+                    } else {
+                        vhat[o] = load_elem(v, dtype, o);
+                    }
+                }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over a (dequantized) cache, fp64 accumulation.           */
+/* [NB] attn: softmax(Q K^T / sqrt(D)) V ; [RV] 1.3 decoding step:           */
+/* A = Softmax(t_Q X_K^T), t_O = A X_V.  Grouped-query attention: query      */
+/* head hq reads KV head hq / (Hq / H).                                      */
+/* q: [B][Hq][D] float32; khat, vhat: [B][H][n][D]; out: [B][Hq][D].         */
+/* ------------------------------------------------------------------------ */
+void oracle_decode_attn(const float *q, const float *khat, const float *vhat,
+                        int B, int H, int Hq, int64_t n, int D, double sm_scale,
+                        float *out)
+{
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    int ratio = Hq / H;
+    for (int b = 0; b < B; b++)
+        for (int hq = 0; hq < Hq; hq++) {
+            int h = hq / ratio;
+            const float *qq = q + ((int64_t)b * Hq + hq) * D;
+            const float *kk = khat + ((int64_t)b * H + h) * n * D;
+            const float *vv = vhat + ((int64_t)b * H + h) * n * D;
+            double m = -INFINITY;
+            for (int64_t t = 0; t < n; t++) {
+                double s = 0.0;
+                for (int c = 0; c < D; c++) s += (double)qq[c] * (double)kk[t * D + c];
+                sc[t] = s * sm_scale;
+                if (sc[t] > m) m = sc[t];
+            }
+            double l = 0.0;
+            for (int c = 0; c < D; c++) acc[c] = 0.0;
+            for (int64_t t = 0; t < n; t++) {
+                double p = exp(sc[t] - m);
+                l += p;
+                for (int c = 0; c < D; c++) acc[c] += p * (double)vv[t * D + c];
+            }
+            float *o = out + ((int64_t)b * Hq + hq) * D;
+            for (int c = 0; c < D; c++) o[c] = (float)(acc[c] / l);
+        }
+    free(sc);
+    free(acc);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packed storage of one token group of one (batch, KV-head) stream.         */
+/*                                                                           */
+/* The pages fix the storage cost (b bits per code, two fp16 per group,      */
+/* [NB] storage cell) but not the bit order.  This library's order puts,     */
+/* for each 32-token x 128-channel tile, the codes one 64-lane wavefront     */
+/* needs for a matrix-core operand into that lane's own 16 bytes:            */
+/*                                                                           */
+/*   block = [K codes | V codes | K scale[D] | K zero[D] |                   */
+/*            V scale[D/G][G] | V zero[D/G][G]]    (codes: b*G*D/8 bytes)    */
+/*                                                                           */
+/* Code dword index (within one code area) for lane l (0..63), lane dword w  */
+/* (0..2b-1): (w/4)*256 + 4*l + (w%4).  Inside a dword, the code of slot i   */
+/* (0 <= i < 16/b) in half h (0,1) sits at bit 16*h + b*i and belongs to     */
+/*   operand o = w*(4/b) + i/4,  kk = 2*(i%4) + h.                           */
+/* Keys:   token = 16*(o/4) + l%16,      channel = 32*(o%4) + 8*(l/16) + kk  */
+/* Values: channel = 16*o + l%16,        token = 4*(l/16) + kk%4 + 16*(kk/4) */
+/* Only D = 128, G = 32 is laid out this way.                                */
+/* ------------------------------------------------------------------------ */
+static void code_position(int bits, int is_v, int token, int channel,
+                          int64_t *dword, int *bit)
+{
+    /* Invert the mapping above by search: plain and obviously bijective. */
+    int dpl = 2 * bits;
+    for (int l = 0; l < 64; l++)
+        for (int w = 0; w < dpl; w++)
+            for (int h = 0; h < 2; h++)
+                for (int i = 0; i < 16 / bits; i++) {
+                    int o = w * (4 / bits) + i / 4;
+                    int kk = 2 * (i % 4) + h;
+                    int t, c;
+                    if (!is_v) {
+                        t = 16 * (o / 4) + l % 16;
+                        c = 32 * (o % 4) + 8 * (l / 16) + kk;
+                    } else {
+                        c = 16 * o + l % 16;
+                        t = 4 * (l / 16) + kk % 4 + 16 * (kk / 4);
+                    }
+                    if (t == token && c == channel) {
+                        *dword = (int64_t)(w / 4) * 256 + 4 * l + (w % 4);
+                        *bit = 16 * h + bits * i;
+                        return;
+                    }
+                }
+    *dword = -1;
+    *bit = -1;
+}
+
+int64_t oracle_block_bytes(int bits)
+{
+    const int D = 128, G = 32;
+    return 2 * (int64_t)(bits * G * D / 8) + 4 * (int64_t)D * 2;
+}
+
+/* Pack the first nq tokens of each stream (nq a multiple of G, and the K and
+   V prefixes equal, as under the window policy) into blocks:
+   out [B*H][max_groups][block_bytes].  Uses the logical arrays of
+   oracle_build_cache for the same nq. */
+void oracle_pack_blocks(int B, int H, int64_t nq, int bits, int64_t max_groups,
+                        const uint8_t *kcodes, const uint16_t *kzero16,
+                        const uint16_t *kscale16,
+                        const uint8_t *vcodes, const uint16_t *vzero16,
+                        const uint16_t *vscale16, uint8_t *out)
+{
+    const int D = 128, G = 32;
+    const int64_t cbytes = bits * G * D / 8;
+    const int64_t bb = oracle_block_bytes(bits);
+    /* position tables for one tile, computed by the search above */
+    int64_t *kd = (int64_t *)malloc(sizeof(int64_t) * G * D);
+    int64_t *vd = (int64_t *)malloc(sizeof(int64_t) * G * D);
+    int *kb = (int *)malloc(sizeof(int) * G * D);
+    int *vb = (int *)malloc(sizeof(int) * G * D);
+    for (int t = 0; t < G; t++)
+        for (int c = 0; c < D; c++) {
+            code_position(bits, 0, t, c, &kd[t * D + c], &kb[t * D + c]);
+            code_position(bits, 1, t, c, &vd[t * D + c], &vb[t * D + c]);
+        }
+    int64_t ng = nq / G;
+    for (int64_t s = 0; s < (int64_t)B * H; s++)
+        for (int64_t j = 0; j < ng; j++) {
+            uint8_t *blk = out + (s * max_groups + j) * bb;
+            uint32_t *kc = (uint32_t *)blk;
+            uint32_t *vc = (uint32_t *)(blk + cbytes);
+            uint16_t *ks = (uint16_t *)(blk + 2 * cbytes);
+            uint16_t *kz = ks + D;
+            uint16_t *vs = kz + D;
+            uint16_t *vz = vs + D;
+            memset(blk, 0, (size_t)(2 * cbytes));
+            for (int t = 0; t < G; t++)
+                for (int c = 0; c < D; c++) {
+                    int64_t tok = j * G + t;
+                    uint32_t ck = kcodes[(s * nq + tok) * D + c];
+                    uint32_t cv = vcodes[(s * nq + tok) * D + c];
+                    kc[kd[t * D + c]] |= ck << kb[t * D + c];
+                    vc[vd[t * D + c]] |= cv << vb[t * D + c];
+                }
+            for (int c = 0; c < D; c++) {
+                ks[c] = kscale16[(s * ng + j) * D + c];
+                kz[c] = kzero16[(s * ng + j) * D + c];
+            }
+            for (int cg = 0; cg < D / G; cg++)
+                for (int t = 0; t < G; t++) {
+                    vs[cg * G + t] = vscale16[(s * nq + j * G + t) * (D / G) + cg];
+                    vz[cg * G + t] = vzero16[(s * nq + j * G + t) * (D / G) + cg];
+                }
+        }
+    free(kd);
+    free(vd);
+    free(kb);
+    free(vb);
+}
+
+/* Position of one code in the packed area (exported for the layout tests). */
+void oracle_code_position(int bits, int is_v, int token, int channel,
+                          int64_t *dword, int *bit)
+{
+    code_position(bits, is_v, token, channel, dword, bit);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Notebook-style fake quantization of a 2-D float32 array ([NB]             */
+/* quantize_grouped): groups of `group` consecutive elements along `axis`    */
+/* (0: down a column, as for keys; 1: along a row, as for values); the       */
+/* length along `axis` must be a multiple of `group` (no partial groups).    */
+/* mode 0: reconstruct with the stored fp16 pair (this cache's view);        */
+/* mode 1: reconstruct with the float32 pair, x_min + q * scale ([NB]).      */
+/* ------------------------------------------------------------------------ */
+void oracle_fake_quant_2d(const float *x, int rows, int cols, int axis,
+                          int bits, int group, int mode, float *out)
+{
+    float *g = (float *)malloc(sizeof(float) * (size_t)group);
+    uint8_t *c = (uint8_t *)malloc((size_t)group);
+    int len = axis == 0 ? rows : cols;      /* along the group axis */
+    int other = axis == 0 ? cols : rows;
+    for (int o = 0; o < other; o++)
+        for (int j = 0; j < len / group; j++) {
+            for (int i = 0; i < group; i++) {
+                int r = axis == 0 ? j * group + i : o;
+                int cc = axis == 0 ? o : j * group + i;
+                g[i] = x[(int64_t)r * cols + cc];
+            }
+            float mn, s;
+            uint16_t z16, s16;
+            oracle_group_quant(g, group, bits, c, &mn, &s, &z16, &s16);
+            for (int i = 0; i < group; i++) {
+                int r = axis == 0 ? j * group + i : o;
+                int cc = axis == 0 ? o : j * group + i;
+                float xh;
+                if (mode == 0) {
+                    xh = oracle_dequant_one(c[i], z16, s16);
+                } else {
+                    float p = (float)c[i] * s;
+                    xh = mn + p;
+                }
+                out[(int64_t)r * cols + cc] = xh;
+            }
+        }
+    free(g);
+    free(c);
+}
+
+/* Array forms of the fp16 conversions (for the tests). */
+void oracle_f16_to_f32_array(const uint16_t *h, float *f, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) f[i] = oracle_f16_to_f32(h[i]);
+}
+
+void oracle_f32_to_f16_array(const float *f, uint16_t *h, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) h[i] = oracle_f32_to_f16(f[i]);
+}
