@@ -1,0 +1,302 @@
+// kivi_api.cpp -- the C ABI of libkivi (declared in include/kivi.h): config
+// validation, the device-buffer layout, the n / Q(n) bookkeeping of the
+// window flush policy, and stream-ordered kernel launches.
+//
+// Flush schedule ("KIVI", VeloxQuant-MLX docs, "How it works" items 3-4):
+// the newest R tokens stay in full precision and aged tokens are quantized
+// only in whole groups of G, so the quantized prefix of an n-token stream is
+// Q(n) = G * floor(max(0, n - R) / G).  An append from n_old to n therefore
+// quantizes tokens [Q(n_old), Q(n)) and keeps [max(Q(n), n_old), n) in the
+// ring; the ring (capacity R + G) never holds more than n - Q(n) < R + G
+// tokens.
+#include <math.h>
+#include <new>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/kivi.h"
+#include "kivi_internal.h"
+
+using namespace kivi;
+
+struct kivi_cache {
+    kivi_config cfg;
+    uint8_t *base;
+    size_t bytes;
+    size_t off_blocks, off_ring_k, off_ring_v;
+    int64_t max_groups;
+    int64_t block_bytes, code_bytes;
+    int64_t ring_cap;
+    int esize;
+    int64_t n;      // tokens cached per stream
+    int64_t q;      // tokens quantized per stream, Q(n)
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetWaves = 4096;   // decode work items aimed for per launch
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+kivi_status validate(const kivi_config *c) {
+    if (!c) return KIVI_ERR_INVALID_ARG;
+    if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_tokens < 1)
+        return KIVI_ERR_INVALID_ARG;
+    if (c->bits != 2 && c->bits != 4) return KIVI_ERR_INVALID_ARG;
+    if (c->group < 1 || c->head_dim < 1 || c->head_dim % c->group != 0) return KIVI_ERR_INVALID_ARG;
+    if (c->residual < 0 || c->residual % c->group != 0) return KIVI_ERR_INVALID_ARG;
+    if ((int64_t)c->group * c->bits % 64 != 0) return KIVI_ERR_INVALID_ARG;
+    if (c->n_q_heads % c->n_kv_heads != 0) return KIVI_ERR_INVALID_ARG;
+    if (c->kv_dtype != KIVI_F16 && c->kv_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
+    if (c->policy != KIVI_FLUSH_WINDOW) return KIVI_ERR_INVALID_ARG;
+    if (c->reserved != 0) return KIVI_ERR_INVALID_ARG;
+    // Shapes the kernels are built for.
+    if (c->head_dim != kHeadDim || c->group != kGroup) return KIVI_ERR_UNSUPPORTED;
+    const int gq = c->n_q_heads / c->n_kv_heads;
+    if (gq != 1 && gq != 2 && gq != 4) return KIVI_ERR_UNSUPPORTED;
+    if ((int64_t)c->batch * c->n_kv_heads > (1LL << 24)) return KIVI_ERR_UNSUPPORTED;
+    return KIVI_OK;
+}
+
+struct Sizes {
+    int64_t max_groups, block_bytes, code_bytes, ring_cap;
+    int esize;
+    size_t off_blocks, off_ring_k, off_ring_v, total;
+};
+
+Sizes sizes_of(const kivi_config *c) {
+    Sizes s;
+    const int64_t streams = (int64_t)c->batch * c->n_kv_heads;
+    s.max_groups = c->max_tokens / c->group;
+    s.code_bytes = (int64_t)c->bits * c->group * c->head_dim / 8;
+    s.block_bytes = 2 * s.code_bytes + 4 * (int64_t)c->head_dim * 2;
+    s.ring_cap = (int64_t)c->residual + c->group;
+    s.esize = c->kv_dtype == KIVI_F32 ? 4 : 2;
+    s.off_blocks = 0;
+    s.off_ring_k = align_up((size_t)(streams * s.max_groups * s.block_bytes));
+    const size_t ring_bytes = align_up((size_t)(streams * s.ring_cap * c->head_dim * s.esize));
+    s.off_ring_v = s.off_ring_k + ring_bytes;
+    s.total = s.off_ring_v + ring_bytes;
+    return s;
+}
+
+int64_t quantized_prefix(const kivi_config &c, int64_t n) {
+    const int64_t aged = n > c.residual ? n - c.residual : 0;
+    return aged / c.group * c.group;
+}
+
+void decode_split_plan(const kivi_cache *c, int64_t q, int32_t *splits, int32_t *gps) {
+    const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
+    const int64_t ng = q / c->cfg.group;
+    if (ng == 0) {
+        *splits = 0;
+        *gps = 1;
+        return;
+    }
+    int64_t want = (kTargetWaves + streams - 1) / streams;
+    if (want < 1) want = 1;
+    if (want > ng) want = ng;
+    const int64_t g = (ng + want - 1) / want;
+    *gps = (int32_t)g;
+    *splits = (int32_t)((ng + g - 1) / g);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kivi_status_string(kivi_status s) {
+    switch (s) {
+    case KIVI_OK: return "ok";
+    case KIVI_ERR_INVALID_ARG: return "invalid argument";
+    case KIVI_ERR_UNSUPPORTED: return "unsupported shape";
+    case KIVI_ERR_CAPACITY: return "capacity exceeded";
+    case KIVI_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case KIVI_ERR_STATE: return "invalid state";
+    case KIVI_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t kivi_cache_bytes(const kivi_config *cfg) {
+    if (validate(cfg) != KIVI_OK) return 0;
+    return sizes_of(cfg).total;
+}
+
+kivi_status kivi_cache_create(const kivi_config *cfg, void *dev_mem, size_t dev_bytes,
+                              kivi_cache **out) {
+    if (!out || !dev_mem) return KIVI_ERR_INVALID_ARG;
+    kivi_status st = validate(cfg);
+    if (st != KIVI_OK) return st;
+    if ((uintptr_t)dev_mem % kAlign != 0) return KIVI_ERR_INVALID_ARG;
+    const Sizes s = sizes_of(cfg);
+    if (dev_bytes < s.total) return KIVI_ERR_BUFFER_TOO_SMALL;
+    kivi_cache *c = new (std::nothrow) kivi_cache;
+    if (!c) return KIVI_ERR_INVALID_ARG;
+    c->cfg = *cfg;
+    c->base = (uint8_t *)dev_mem;
+    c->bytes = dev_bytes;
+    c->off_blocks = s.off_blocks;
+    c->off_ring_k = s.off_ring_k;
+    c->off_ring_v = s.off_ring_v;
+    c->max_groups = s.max_groups;
+    c->block_bytes = s.block_bytes;
+    c->code_bytes = s.code_bytes;
+    c->ring_cap = s.ring_cap;
+    c->esize = s.esize;
+    c->n = 0;
+    c->q = 0;
+    *out = c;
+    return KIVI_OK;
+}
+
+kivi_status kivi_cache_destroy(kivi_cache *c) {
+    delete c;
+    return KIVI_OK;
+}
+
+kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new, kivi_append_plan *p) {
+    if (!c || !p || n_new < 0) return KIVI_ERR_INVALID_ARG;
+    if (n_new > c->cfg.max_tokens - c->n) return KIVI_ERR_CAPACITY;
+    const int64_t n = c->n + n_new;
+    const int64_t q_new = quantized_prefix(c->cfg, n);
+    p->n_old = c->n;
+    p->n_new_total = n;
+    p->q_old = c->q;
+    p->q_new = q_new;
+    p->flush_token_begin = c->q;
+    p->flush_token_end = q_new;
+    p->ring_token_begin = q_new > c->n ? q_new : c->n;
+    p->ring_token_end = n;
+    return KIVI_OK;
+}
+
+kivi_status kivi_append(kivi_cache *c, const void *k, const void *v, int64_t n_new,
+                        uint32_t flags, hipStream_t stream) {
+    if (!c || flags != 0 || n_new < 0) return KIVI_ERR_INVALID_ARG;
+    if (n_new > 0 && (!k || !v)) return KIVI_ERR_INVALID_ARG;
+    kivi_append_plan p;
+    kivi_status st = kivi_plan_append(c, n_new, &p);
+    if (st != KIVI_OK) return st;
+    const int32_t streams = c->cfg.batch * c->cfg.n_kv_heads;
+
+    if (p.flush_token_end > p.flush_token_begin) {
+        QuantizeArgs a;
+        a.blocks = c->base + c->off_blocks;
+        a.max_groups = c->max_groups;
+        a.block_bytes = c->block_bytes;
+        a.in_k = k;
+        a.in_v = v;
+        a.n_new = n_new;
+        a.ring_k = c->base + c->off_ring_k;
+        a.ring_v = c->base + c->off_ring_v;
+        a.ring_cap = c->ring_cap;
+        a.n_old = p.n_old;
+        a.group_begin = p.flush_token_begin / c->cfg.group;
+        a.group_end = p.flush_token_end / c->cfg.group;
+        a.streams = streams;
+        a.is_f32 = c->cfg.kv_dtype == KIVI_F32;
+        a.bits = c->cfg.bits;
+        if (launch_quantize(a, stream) != hipSuccess) return KIVI_ERR_HIP;
+    }
+    if (p.ring_token_end > p.ring_token_begin) {
+        RingArgs r;
+        r.in_k = k;
+        r.in_v = v;
+        r.n_new = n_new;
+        r.n_old = p.n_old;
+        r.ring_k = c->base + c->off_ring_k;
+        r.ring_v = c->base + c->off_ring_v;
+        r.ring_cap = c->ring_cap;
+        r.tok_begin = p.ring_token_begin;
+        r.tok_end = p.ring_token_end;
+        r.streams = streams;
+        r.esize = c->esize;
+        if (launch_ring_append(r, stream) != hipSuccess) return KIVI_ERR_HIP;
+    }
+    c->n = p.n_new_total;
+    c->q = p.q_new;
+    return KIVI_OK;
+}
+
+kivi_status kivi_flush(kivi_cache *c, hipStream_t stream) {
+    (void)stream;
+    if (!c) return KIVI_ERR_INVALID_ARG;
+    return KIVI_OK;
+}
+
+size_t kivi_decode_workspace_bytes(const kivi_cache *c) {
+    if (!c) return 0;
+    // decode_split_plan never makes more than ceil(kTargetWaves / streams)
+    // split items per stream, whatever n is; plus one residual item.
+    const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
+    const int64_t items = (kTargetWaves + streams - 1) / streams + 1;
+    const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
+    return (size_t)(bhq * items * (c->cfg.head_dim + 2) * 4);
+}
+
+kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits, int32_t *gps) {
+    if (!c || !splits || !gps) return KIVI_ERR_INVALID_ARG;
+    decode_split_plan(c, c->q, splits, gps);
+    return KIVI_OK;
+}
+
+kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, float softmax_scale,
+                             float *out, void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!c || !q || !out || !workspace) return KIVI_ERR_INVALID_ARG;
+    if (q_dtype != KIVI_F16 && q_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
+    if (c->n == 0) return KIVI_ERR_STATE;
+    if (ws_bytes < kivi_decode_workspace_bytes(c)) return KIVI_ERR_BUFFER_TOO_SMALL;
+    DecodeArgs a;
+    int32_t splits, gps;
+    decode_split_plan(c, c->q, &splits, &gps);
+    const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
+    const int64_t items = splits + 1;
+    a.blocks = c->base + c->off_blocks;
+    a.max_groups = c->max_groups;
+    a.block_bytes = c->block_bytes;
+    a.ring_k = c->base + c->off_ring_k;
+    a.ring_v = c->base + c->off_ring_v;
+    a.ring_cap = c->ring_cap;
+    a.ring_is_f32 = c->cfg.kv_dtype == KIVI_F32;
+    a.q = q;
+    a.q_is_f32 = q_dtype == KIVI_F32;
+    a.out = out;
+    a.part_o = (float *)workspace;
+    a.part_ml = (float *)workspace + bhq * items * c->cfg.head_dim;
+    a.batch = c->cfg.batch;
+    a.kv_heads = c->cfg.n_kv_heads;
+    a.q_heads = c->cfg.n_q_heads;
+    a.bits = c->cfg.bits;
+    a.n_tokens = c->n;
+    a.n_quant = c->q;
+    a.splits = splits;
+    a.groups_per_split = gps;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)c->cfg.head_dim);
+    a.sm_log2 = scale * 1.4426950408889634f;
+    if (launch_decode(a, stream) != hipSuccess) return KIVI_ERR_HIP;
+    return KIVI_OK;
+}
+
+kivi_status kivi_get_layout(const kivi_cache *c, kivi_layout *o) {
+    if (!c || !o) return KIVI_ERR_INVALID_ARG;
+    o->blocks = c->off_blocks;
+    o->ring_k = c->off_ring_k;
+    o->ring_v = c->off_ring_v;
+    o->block_bytes = (size_t)c->block_bytes;
+    o->code_bytes = (size_t)c->code_bytes;
+    o->off_kcode = 0;
+    o->off_vcode = (size_t)c->code_bytes;
+    o->off_kscale = 2 * (size_t)c->code_bytes;
+    o->off_kzero = o->off_kscale + 2 * (size_t)c->cfg.head_dim;
+    o->off_vscale = o->off_kzero + 2 * (size_t)c->cfg.head_dim;
+    o->off_vzero = o->off_vscale + 2 * (size_t)c->cfg.head_dim;
+    o->max_groups = c->max_groups;
+    o->ring_capacity = c->ring_cap;
+    o->n_tokens = c->n;
+    o->n_quantized = c->q;
+    return KIVI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Private interface between the C-ABI front end (kivi_api.cpp) and the HIP
+// kernels (kivi_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace kivi {
+
+constexpr int kHeadDim = 128;   // D: channels per head
+constexpr int kGroup = 32;      // G: tokens per key group / channels per value group
+
+// Quantize tokens [group_begin*G, group_end*G) of every stream into packed
+// blocks.  Token t < n_old is read from ring slot t % ring_cap, later tokens
+// from row (t - n_old) of the appended chunk.
+struct QuantizeArgs {
+    uint8_t *blocks;            // [streams][max_groups][block_bytes]
+    int64_t max_groups;
+    int64_t block_bytes;
+    const void *in_k, *in_v;    // [streams][n_new][D] chunk (kv dtype)
+    int64_t n_new;
+    const void *ring_k, *ring_v;// [streams][ring_cap][D] (kv dtype)
+    int64_t ring_cap;
+    int64_t n_old;
+    int64_t group_begin, group_end;
+    int32_t streams;
+    int32_t is_f32;             // kv dtype: 0 fp16, 1 fp32
+    int32_t bits;               // 2 or 4
+};
+
+// Copy tokens [tok_begin, tok_end) of every stream from the appended chunk
+// into the ring.
+struct RingArgs {
+    const void *in_k, *in_v;
+    int64_t n_new, n_old;
+    void *ring_k, *ring_v;
+    int64_t ring_cap;
+    int64_t tok_begin, tok_end;
+    int32_t streams;
+    int32_t esize;              // bytes per element (2 or 4)
+};
+
+struct DecodeArgs {
+    const uint8_t *blocks;
+    int64_t max_groups;
+    int64_t block_bytes;
+    const void *ring_k, *ring_v;
+    int64_t ring_cap;
+    int32_t ring_is_f32;
+    const void *q;              // [B][Hq][D]
+    int32_t q_is_f32;
+    float *out;                 // [B][Hq][D] float32
+    float *part_o;              // [B*Hq][n_items_per_stream][D]
+    float *part_ml;             // [B*Hq][n_items_per_stream][2]  (m log2, l)
+    int32_t batch, kv_heads, q_heads;
+    int32_t bits;
+    int64_t n_tokens, n_quant;  // n, Q(n)
+    int32_t splits;             // work items per stream over quantized groups
+    int32_t groups_per_split;
+    float sm_log2;              // softmax scale * log2(e)
+};
+
+hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s);
+hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace kivi

@@ -1,0 +1,612 @@
+// kivi_kernels.hip -- KIVI hot-path kernels for CDNA4 (gfx950), wave64.
+//
+// What the kernels compute (pages cited by title and section):
+//  * quantize: "KIVI - 2-bit KV cache quantisation" (cookbook notebook),
+//    "Asymmetric 2-bit quantiser": per group zero = min, scale =
+//    (max - min) / (2^b - 1) with scale 1 for a constant group, code =
+//    round((x - zero) / scale) clamped to [0, 2^b - 1].  Keys are grouped
+//    per channel over G consecutive tokens, values per token over G
+//    consecutive channels ("KIVI", VeloxQuant-MLX docs, "How it works" 1-2).
+//  * residual ring + whole-group flush: same docs, items 3-4.
+//  * decode attention with dequantization inside the products:
+//    "[Paper review] KIVI ... (ICML'24)", 1.3 decoding step and 3.2
+//    system-level implementation (fused dequantize + matmul).
+//
+// Packed block of one (stream, token group) -- see also include/kivi.h:
+//   [K codes | V codes | K scale[128] | K zero[128] | V scale[4][32] | V zero[4][32]]
+// Code area order (b bits per code, 64 lanes, 2b dwords per lane): lane l's
+// dword w is dword (w/4)*256 + 4*l + (w%4).  Within a dword, slot i
+// (0 <= i < 16/b) of half h sits at bit 16h + b*i and feeds matrix-core
+// operand o = w*(4/b) + i/4 at position kk = 2*(i%4) + h:
+//   keys:   token = 16*(o/4) + l%16,   channel = 32*(o%4) + 8*(l/16) + kk
+//   values: channel = 16*o + l%16,     token = 4*(l/16) + kk%4 + 16*(kk/4)
+// so that  ((dword >> (b*(4*(o%(4/b)) + m))) & mask2)  is, as two fp16 bit
+// patterns, the pair (kk = 2m, 2m+1) of operand o -- one shift and one AND
+// per two codes, and every lane's 16 bytes are exactly its own operands.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+#include "kivi_internal.h"
+
+namespace kivi {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = kHeadDim;
+constexpr int G = kGroup;
+
+// ===========================================================================
+// Quantization: one wavefront per (stream, token group, K-or-V).
+// ===========================================================================
+
+// Row t of a stream: from the ring if it was appended earlier, else from the
+// new chunk.
+template <typename T>
+__device__ __forceinline__ const T *source_row(const QuantizeArgs &a, const void *ring,
+                                               const void *in, int64_t stream, int64_t t) {
+    if (t < a.n_old)
+        return (const T *)ring + (stream * a.ring_cap + t % a.ring_cap) * D;
+    return (const T *)in + (stream * a.n_new + (t - a.n_old)) * D;
+}
+
+__device__ __forceinline__ void load8(const _Float16 *p, float *x) {
+    uint4 u = *(const uint4 *)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        h2 v = __builtin_bit_cast(h2, w[e]);
+        x[2 * e] = (float)v[0];
+        x[2 * e + 1] = (float)v[1];
+    }
+}
+
+__device__ __forceinline__ void load8(const float *p, float *x) {
+    float4 u0 = *(const float4 *)p, u1 = *(const float4 *)(p + 4);
+    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+}
+
+__device__ __forceinline__ float xmin(float v, int m) { return fminf(v, __shfl_xor(v, m)); }
+__device__ __forceinline__ float xmax(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
+
+// Code of one element: IEEE float32 subtract and divide, round half to even,
+// clamp -- exactly the quantiser's formula, no reassociation.
+__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float L) {
+    float d = x - mn;
+    float t = d / s;
+    float c = __builtin_rintf(t);
+    c = fminf(fmaxf(c, 0.0f), L);
+    return (uint32_t)c;
+}
+
+__device__ __forceinline__ void group_params(float mn, float mx, float L, float &mn_out,
+                                             float &s_out) {
+    if (mn == 0.0f) mn = 0.0f;      // a zero minimum is +0 whatever the sign
+    float s = (mx - mn) / L;
+    if (s == 0.0f) s = 1.0f;        // constant group
+    mn_out = mn;
+    s_out = s;
+}
+
+constexpr int kLdsRow = 136;        // 128 code bytes + 8 pad (fewer bank conflicts)
+
+template <int BITS, typename T>
+__global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
+    __shared__ uint8_t codes_lds[G * kLdsRow];
+    const int l = threadIdx.x;
+    const int64_t ngr = a.group_end - a.group_begin;
+    const int64_t task = blockIdx.x;
+    const int is_v = (int)(task & 1);
+    const int64_t rest = task >> 1;
+    const int64_t stream = rest / ngr;
+    const int64_t g = a.group_begin + rest % ngr;
+    const float L = (float)((1 << BITS) - 1);
+
+    // Load the 32 x 128 tile: load i covers rows 4i..4i+3; lane l holds row
+    // 4i + l/16, channels 8*(l%16) .. +7.
+    const void *ring = is_v ? a.ring_v : a.ring_k;
+    const void *in = is_v ? a.in_v : a.in_k;
+    const int rsub = l >> 4;
+    const int c0 = 8 * (l & 15);
+    float x[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const T *row = source_row<T>(a, ring, in, stream, g * G + 4 * i + rsub);
+        load8(row + c0, x[i]);
+    }
+
+    uint8_t *blk = a.blocks + (stream * a.max_groups + g) * a.block_bytes;
+    const int cbytes = BITS * G * D / 8;
+    _Float16 *side = (_Float16 *)(blk + 2 * cbytes);   // kscale, kzero, vscale, vzero
+
+    uint32_t code8[8][2];   // per row i: 8 codes as bytes (two dwords)
+    if (!is_v) {
+        // keys: group = one channel over the 32 rows
+        float mn[8], s[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            float lo = x[0][e], hi = x[0][e];
+#pragma unroll
+            for (int i = 1; i < 8; i++) { lo = fminf(lo, x[i][e]); hi = fmaxf(hi, x[i][e]); }
+            lo = xmin(xmin(lo, 16), 32);
+            hi = xmax(xmax(hi, 16), 32);
+            group_params(lo, hi, L, mn[e], s[e]);
+        }
+        if (l < 16) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                side[c0 + e] = (_Float16)s[e];
+                side[D + c0 + e] = (_Float16)mn[e];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) lo |= quant_code(x[i][e], mn[e], s[e], L) << (8 * e);
+#pragma unroll
+            for (int e = 0; e < 4; e++) hi |= quant_code(x[i][4 + e], mn[4 + e], s[4 + e], L) << (8 * e);
+            code8[i][0] = lo;
+            code8[i][1] = hi;
+        }
+    } else {
+        // values: group = one row over 32 channels (4 lanes of a quad)
+        const int cg = (l & 15) >> 2;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float lo = x[i][0], hi = x[i][0];
+#pragma unroll
+            for (int e = 1; e < 8; e++) { lo = fminf(lo, x[i][e]); hi = fmaxf(hi, x[i][e]); }
+            lo = xmin(xmin(lo, 1), 2);
+            hi = xmax(xmax(hi, 1), 2);
+            float mn, s;
+            group_params(lo, hi, L, mn, s);
+            if ((l & 3) == 0) {
+                const int r = 4 * i + rsub;
+                side[2 * D + cg * G + r] = (_Float16)s;
+                side[3 * D + cg * G + r] = (_Float16)mn;
+            }
+            uint32_t c_lo = 0, c_hi = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) c_lo |= quant_code(x[i][e], mn, s, L) << (8 * e);
+#pragma unroll
+            for (int e = 0; e < 4; e++) c_hi |= quant_code(x[i][4 + e], mn, s, L) << (8 * e);
+            code8[i][0] = c_lo;
+            code8[i][1] = c_hi;
+        }
+    }
+
+    // Redistribute codes (one byte each) through LDS into the packed order.
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        uint2 v = {code8[i][0], code8[i][1]};
+        *(uint2 *)&codes_lds[(4 * i + rsub) * kLdsRow + c0] = v;
+    }
+    __syncthreads();
+
+    constexpr int DPL = 2 * BITS;          // dwords per lane
+    constexpr int OPD = 4 / BITS;          // operands per dword
+    uint32_t outw[DPL];
+#pragma unroll
+    for (int w = 0; w < DPL; w++) outw[w] = 0;
+#pragma unroll
+    for (int o = 0; o < 8; o++) {
+        uint32_t cb[8];
+        if (!is_v) {
+            const int tok = 16 * (o >> 2) + (l & 15);
+            const int ch = 32 * (o & 3) + 8 * (l >> 4);
+            uint2 v = *(const uint2 *)&codes_lds[tok * kLdsRow + ch];
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) {
+                cb[kk] = (v.x >> (8 * kk)) & 0xFF;
+                cb[4 + kk] = (v.y >> (8 * kk)) & 0xFF;
+            }
+        } else {
+            const int ch = 16 * o + (l & 15);
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++) {
+                const int tok = 4 * (l >> 4) + (kk & 3) + 16 * (kk >> 2);
+                cb[kk] = codes_lds[tok * kLdsRow + ch];
+            }
+        }
+        const int w = o / OPD;
+        const int base = BITS * 4 * (o % OPD);
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++)
+            outw[w] |= cb[kk] << (16 * (kk & 1) + base + BITS * (kk >> 1));
+    }
+    uint32_t *dst = (uint32_t *)(blk + (is_v ? cbytes : 0));
+#pragma unroll
+    for (int w4 = 0; w4 < DPL / 4; w4++) {
+        uint4 v = {outw[4 * w4], outw[4 * w4 + 1], outw[4 * w4 + 2], outw[4 * w4 + 3]};
+        *(uint4 *)&dst[w4 * 256 + 4 * l] = v;
+    }
+}
+
+// ===========================================================================
+// Residual ring append: copy rows [tok_begin, tok_end) of the chunk into
+// ring slot t % ring_cap.  16 bytes per thread.
+// ===========================================================================
+__global__ __launch_bounds__(256) void ring_append_kernel(RingArgs a) {
+    const int64_t row_vec = (int64_t)D * a.esize / 16;
+    const int64_t ntok = a.tok_end - a.tok_begin;
+    const int64_t per_tensor = (int64_t)a.streams * ntok * row_vec;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < 2 * per_tensor;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int which = idx >= per_tensor;
+        int64_t r = idx - which * per_tensor;
+        const int64_t v = r % row_vec;
+        r /= row_vec;
+        const int64_t t = a.tok_begin + r % ntok;
+        const int64_t stream = r / ntok;
+        const uint4 *src = (const uint4 *)((const uint8_t *)(which ? a.in_v : a.in_k) +
+                                           (stream * a.n_new + (t - a.n_old)) * D * a.esize);
+        uint4 *dst = (uint4 *)((uint8_t *)(which ? a.ring_v : a.ring_k) +
+                               (stream * a.ring_cap + t % a.ring_cap) * D * a.esize);
+        dst[v] = src[v];
+    }
+}
+
+// ===========================================================================
+// Decode attention.
+//
+// Work items (one wavefront each): first one "tail" item per stream over the
+// full-precision residual, then `splits` items per stream over whole groups
+// of the quantized prefix.  Each writes an unnormalized partial (m, l, o)
+// in the log2 domain; decode_combine_kernel merges them.
+//
+// Quantized groups use the matrix cores (v_mfma_f32_16x16x32_f16).  With
+// GQ query heads per KV head, column j of every B operand belongs to query
+// head j % GQ, so the scores come out replicated across columns and each
+// lane already holds what it needs for the value product:
+//   scores  S^T[token][j]   = sum_c code_K[token][c] * (q[j%GQ][c] * kscale[c])
+//                             + sum_c q[j%GQ][c] * kzero[c]
+//   values  O^T[chan][j]    = sum_t code_V[t][chan] * (p[t][j%GQ] * vscale[t][cg(j)])
+//                             + sum_t p[t][j%GQ] * vzero[t][cg(j)]
+// where cg(j) = j / GQ picks the value channel group whose scale the column
+// carries; only the M-tiles of that group are kept from each column.
+// Codes enter the matrix core as fp16 subnormal bit patterns (value
+// code * 2^-24, exact), so unpacking is a shift and an AND; the 2^24 is
+// folded into the softmax scale and the final store.
+// ===========================================================================
+
+__device__ __forceinline__ float xsum_rows(float v) {
+    // sum over the four 16-lane rows (lanes j, j+16, j+32, j+48)
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+__device__ __forceinline__ float xmax_rows(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+template <int BITS>
+__device__ __forceinline__ h8 unpack_operand(const uint32_t *w, int o) {
+    constexpr int OPD = 4 / BITS;
+    constexpr uint32_t M1 = (1u << BITS) - 1u;
+    constexpr uint32_t MASK = M1 | (M1 << 16);
+    const uint32_t x = w[o / OPD];
+    const int base = BITS * 4 * (o % OPD);
+    uint32_t r[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++) r[m] = (x >> (base + BITS * m)) & MASK;
+    uint4 u = {r[0], r[1], r[2], r[3]};
+    return __builtin_bit_cast(h8, u);
+}
+
+__device__ __forceinline__ h8 pack_h8(const h2 *v) {
+    h8 r;
+#pragma unroll
+    for (int m = 0; m < 4; m++) { r[2 * m] = v[m][0]; r[2 * m + 1] = v[m][1]; }
+    return r;
+}
+
+__device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t idx) {
+    return a.q_is_f32 ? ((const float *)a.q)[idx] : (float)((const _Float16 *)a.q)[idx];
+}
+
+// Tail item: full-precision residual tokens [n_quant, n) of one stream.
+// Lane l owns channels 2l, 2l+1; one token per iteration, online softmax.
+template <int GQ>
+__device__ void decode_tail(const DecodeArgs &a, int stream) {
+    const int l = threadIdx.x & 63;
+    const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
+    const int items = a.splits + 1;
+    float q0[GQ], q1[GQ], m[GQ], ls[GQ], a0[GQ], a1[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; h++) {
+        const int64_t qrow = ((int64_t)b * a.q_heads + hk * GQ + h) * D;
+        q0[h] = load_q(a, qrow + 2 * l);
+        q1[h] = load_q(a, qrow + 2 * l + 1);
+        m[h] = -INFINITY;
+        ls[h] = 0.f;
+        a0[h] = 0.f;
+        a1[h] = 0.f;
+    }
+    for (int64_t t = a.n_quant; t < a.n_tokens; t++) {
+        const int64_t row = ((int64_t)stream * a.ring_cap + t % a.ring_cap) * D + 2 * l;
+        float k0, k1, v0, v1;
+        if (a.ring_is_f32) {
+            k0 = ((const float *)a.ring_k)[row];
+            k1 = ((const float *)a.ring_k)[row + 1];
+            v0 = ((const float *)a.ring_v)[row];
+            v1 = ((const float *)a.ring_v)[row + 1];
+        } else {
+            h2 kk = *(const h2 *)((const _Float16 *)a.ring_k + row);
+            h2 vv = *(const h2 *)((const _Float16 *)a.ring_v + row);
+            k0 = (float)kk[0]; k1 = (float)kk[1];
+            v0 = (float)vv[0]; v1 = (float)vv[1];
+        }
+#pragma unroll
+        for (int h = 0; h < GQ; h++) {
+            float s = wave_sum(__builtin_fmaf(q0[h], k0, q1[h] * k1)) * a.sm_log2;
+            float mn = fmaxf(m[h], s);
+            float al = __builtin_amdgcn_exp2f(m[h] - mn);
+            float p = __builtin_amdgcn_exp2f(s - mn);
+            ls[h] = __builtin_fmaf(ls[h], al, p);
+            a0[h] = __builtin_fmaf(a0[h], al, p * v0);
+            a1[h] = __builtin_fmaf(a1[h], al, p * v1);
+            m[h] = mn;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; h++) {
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * items + a.splits;
+        float2 ov = {a0[h], a1[h]};
+        *(float2 *)&a.part_o[pi * D + 2 * l] = ov;
+        if (l == 0) {
+            a.part_ml[2 * pi] = m[h];
+            a.part_ml[2 * pi + 1] = ls[h];
+        }
+    }
+}
+
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kTwoM24 = 5.9604644775390625e-08f;
+
+template <int BITS, int GQ>
+__device__ void decode_split(const DecodeArgs &a, int stream, int sp) {
+    constexpr int CB = BITS * G * D / 8;       // code bytes per tensor per block
+    constexpr int DPL = 2 * BITS;              // code dwords per lane
+    const int l = threadIdx.x & 63;
+    const int j = l & 15, Gl = l >> 4;
+    const int h = j % GQ;
+    const int cg = (j / GQ) & 3;
+    const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
+    const int hq = hk * GQ + h;
+    const int items = a.splits + 1;
+    const int64_t ng = a.n_quant / G;
+    const int64_t g0 = (int64_t)sp * a.groups_per_split;
+    const int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
+
+    // q as fp16 pairs in B-operand order: slice s, pair m -> channels
+    // 32s + 8*Gl + 2m, +1.
+    h2 qB[4][4];
+    const int64_t qrow = ((int64_t)b * a.q_heads + hq) * D;
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const int c = 32 * s + 8 * Gl + 2 * m;
+            qB[s][m][0] = (_Float16)load_q(a, qrow + c);
+            qB[s][m][1] = (_Float16)load_q(a, qrow + c + 1);
+        }
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    const float cs = a.sm_log2 * kTwo24;        // score units -> log2 units
+
+    float m_run = -INFINITY, l_run = 0.f, vb = 0.f;
+    f4 accV[8];
+#pragma unroll
+    for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t g = g0; g < g1; g++) {
+        const uint8_t *blk = a.blocks + ((int64_t)stream * a.max_groups + g) * a.block_bytes;
+        uint32_t kc[DPL], vc[DPL];
+#pragma unroll
+        for (int w4 = 0; w4 < DPL / 4; w4++) {
+            uint4 u = *(const uint4 *)(blk + w4 * 1024 + 16 * l);
+            kc[4 * w4] = u.x; kc[4 * w4 + 1] = u.y; kc[4 * w4 + 2] = u.z; kc[4 * w4 + 3] = u.w;
+            uint4 v = *(const uint4 *)(blk + CB + w4 * 1024 + 16 * l);
+            vc[4 * w4] = v.x; vc[4 * w4 + 1] = v.y; vc[4 * w4 + 2] = v.z; vc[4 * w4 + 3] = v.w;
+        }
+        const uint8_t *side = blk + 2 * CB;
+        h2 ks[4][4], kz[4][4];
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            uint4 us = *(const uint4 *)(side + 2 * (32 * s + 8 * Gl));
+            uint4 uz = *(const uint4 *)(side + 2 * D + 2 * (32 * s + 8 * Gl));
+            ks[s][0] = __builtin_bit_cast(h2, us.x); ks[s][1] = __builtin_bit_cast(h2, us.y);
+            ks[s][2] = __builtin_bit_cast(h2, us.z); ks[s][3] = __builtin_bit_cast(h2, us.w);
+            kz[s][0] = __builtin_bit_cast(h2, uz.x); kz[s][1] = __builtin_bit_cast(h2, uz.y);
+            kz[s][2] = __builtin_bit_cast(h2, uz.z); kz[s][3] = __builtin_bit_cast(h2, uz.w);
+        }
+        h2 vs[4], vz[4];
+        {
+            const uint8_t *vsb = side + 4 * D + 2 * (G * cg + 4 * Gl);
+            const uint8_t *vzb = side + 6 * D + 2 * (G * cg + 4 * Gl);
+            uint2 s0 = *(const uint2 *)vsb, s1 = *(const uint2 *)(vsb + 32);
+            uint2 z0 = *(const uint2 *)vzb, z1 = *(const uint2 *)(vzb + 32);
+            vs[0] = __builtin_bit_cast(h2, s0.x); vs[1] = __builtin_bit_cast(h2, s0.y);
+            vs[2] = __builtin_bit_cast(h2, s1.x); vs[3] = __builtin_bit_cast(h2, s1.y);
+            vz[0] = __builtin_bit_cast(h2, z0.x); vz[1] = __builtin_bit_cast(h2, z0.y);
+            vz[2] = __builtin_bit_cast(h2, z1.x); vz[3] = __builtin_bit_cast(h2, z1.y);
+        }
+
+        // Keys: fold the scale into q, the zero into a per-head bias.  The
+        // product q * kscale (22 significant bits) is carried as an fp16
+        // pair hi + lo with lo = fma(q, kscale, -hi) rounded once, so the
+        // matrix core sees it (almost) exactly.
+        h2 qh[4][4], ql[4][4];
+        float kb = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                qh[s][m] = qB[s][m] * ks[s][m];
+                ql[s][m] = __builtin_elementwise_fma(qB[s][m], ks[s][m], -qh[s][m]);
+                kb = __builtin_amdgcn_fdot2(qB[s][m], kz[s][m], kb, false);
+            }
+        kb = xsum_rows(kb) * kTwoM24;
+        f4 S[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            S[t] = (f4){kb, kb, kb, kb};
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const h8 A = unpack_operand<BITS>(kc, 4 * t + s);
+                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack_h8(qh[s]), S[t], 0, 0, 0);
+                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack_h8(ql[s]), S[t], 0, 0, 0);
+            }
+        }
+
+        // Online softmax (log2 domain).  Lane (j, Gl) holds tokens
+        // 4Gl + e (tile 0) and 16 + 4Gl + e (tile 1) of head j % GQ.
+        float mt = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+        mt = xmax_rows(mt) * cs;
+        const float m_new = fmaxf(m_run, mt);
+        if (__any(m_new > m_run)) {
+            const float al = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+            for (int o = 0; o < 8; o++) accV[o] *= al;
+            l_run *= al;
+            vb *= al;
+            m_run = m_new;
+        }
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][e], cs, -m_run));
+            p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[1][e], cs, -m_run));
+        }
+        h2 P[4], ps[4];
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            P[m][0] = (_Float16)p[2 * m];
+            P[m][1] = (_Float16)p[2 * m + 1];
+            l_run = __builtin_amdgcn_fdot2(P[m], ones, l_run, false);
+            vb = __builtin_amdgcn_fdot2(P[m], vz[m], vb, false);
+            ps[m] = P[m] * vs[m];
+        }
+        const h8 B = pack_h8(ps);
+#pragma unroll
+        for (int o = 0; o < 8; o++)
+            accV[o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_operand<BITS>(vc, o), B,
+                                                            accV[o], 0, 0, 0);
+    }
+
+    const float l_tot = xsum_rows(l_run);
+    const float vb_tot = xsum_rows(vb);
+    const int64_t pi = ((int64_t)b * a.q_heads + hq) * items + sp;
+    if (j < 4 * GQ) {
+#pragma unroll
+        for (int o = 0; o < 8; o++) {
+            if ((o >> 1) == cg) {
+                float4 v;
+                v.x = __builtin_fmaf(accV[o][0], kTwo24, vb_tot);
+                v.y = __builtin_fmaf(accV[o][1], kTwo24, vb_tot);
+                v.z = __builtin_fmaf(accV[o][2], kTwo24, vb_tot);
+                v.w = __builtin_fmaf(accV[o][3], kTwo24, vb_tot);
+                *(float4 *)&a.part_o[pi * D + 16 * o + 4 * Gl] = v;
+            }
+        }
+    }
+    if (j < GQ && Gl == 0) {
+        a.part_ml[2 * pi] = m_run;
+        a.part_ml[2 * pi + 1] = l_tot;
+    }
+}
+
+template <int BITS, int GQ>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+    const int wave = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    const int streams = a.batch * a.kv_heads;
+    if (item >= (int64_t)streams * (a.splits + 1)) return;
+    if (item < streams) {
+        decode_tail<GQ>(a, (int)item);
+        return;
+    }
+    const int64_t it = item - streams;
+    decode_split<BITS, GQ>(a, (int)(it / a.splits), (int)(it % a.splits));
+}
+
+// Merge the partials of one (batch, query head): one thread per channel.
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+    const int64_t bh = blockIdx.x;
+    const int c = threadIdx.x;
+    const int items = a.splits + 1;
+    const float *ml = a.part_ml + bh * items * 2;
+    float M = -INFINITY;
+    for (int s = 0; s < items; s++)
+        if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
+    float Ls = 0.f, acc = 0.f;
+    for (int s = 0; s < items; s++) {
+        const float ls = ml[2 * s + 1];
+        if (ls > 0.f) {
+            const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+            Ls = __builtin_fmaf(ls, w, Ls);
+            acc = __builtin_fmaf(a.part_o[(bh * items + s) * D + c], w, acc);
+        }
+    }
+    a.out[bh * D + c] = acc / Ls;
+}
+
+// ===========================================================================
+// Launchers
+// ===========================================================================
+hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
+    const int64_t tasks = (int64_t)a.streams * (a.group_end - a.group_begin) * 2;
+    if (tasks <= 0) return hipSuccess;
+    dim3 grid((unsigned)tasks), block(64);
+    if (a.bits == 2) {
+        if (a.is_f32) hipLaunchKernelGGL((quantize_kernel<2, float>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((quantize_kernel<2, _Float16>), grid, block, 0, s, a);
+    } else {
+        if (a.is_f32) hipLaunchKernelGGL((quantize_kernel<4, float>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((quantize_kernel<4, _Float16>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {
+    const int64_t ntok = a.tok_end - a.tok_begin;
+    if (ntok <= 0) return hipSuccess;
+    const int64_t vecs = 2 * (int64_t)a.streams * ntok * D * a.esize / 16;
+    int64_t blocks = (vecs + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int BITS>
+static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
+    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4>), grid, dim3(256), 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<BITS, 1>), grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
+    const int streams = a.batch * a.kv_heads;
+    const int gq = a.q_heads / a.kv_heads;
+    const int64_t items = (int64_t)streams * (a.splits + 1);
+    dim3 grid((unsigned)((items + 3) / 4));
+    if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
+    else launch_decode_bits<4>(a, gq, grid, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(a.batch * a.q_heads)), dim3(128), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+}  // namespace kivi

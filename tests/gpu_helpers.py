@@ -1,0 +1,87 @@
+"""Shared helpers of the GPU parity tests: run libkivi through its C ABI and
+compare with the CPU oracle on the same inputs."""
+import sys
+
+import numpy as np
+
+TOL = 2e-3   # decode attention: max over (b, hq) of |o - r|_inf / |r|_inf
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(np_dtype):
+    import torch
+    return torch.float16 if np_dtype == np.float16 else torch.float32
+
+
+def new_cache(B, H, Hq, max_tokens, bits=2, R=128, dtype=np.float16):
+    from kv_cache_quantization_amd import KiviCache
+    return KiviCache(B, H, Hq, max_tokens, bits=bits, residual=R,
+                     kv_dtype=torch_dtype(dtype), device="cuda")
+
+
+def to_dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def gpu_blocks(cache, n_groups, streams=None):
+    import torch
+    torch.cuda.synchronize()
+    blk = cache.blocks_view()
+    if streams is not None:
+        blk = blk[list(streams)]
+    return blk[:, :n_groups].cpu().numpy()
+
+
+def check_cache(orc, cache, k, v, streams=None, label=""):
+    """Bit-exact check of packed blocks, ring contents and (n, Q) against the
+    oracle built from the full K, V ([B, H, n, D] numpy, or only the streams
+    listed in `streams`, given as [len(streams), n, D] arrays in k, v)."""
+    lo = cache.layout()
+    c = cache.cfg
+    if streams is None:
+        kk, vv = k, v
+    else:
+        kk, vv = k[None], v[None]     # [1, S, n, D]: the sampled streams as one batch row
+    n = kk.shape[2]
+    ref = orc.build_cache(kk, vv, c.bits, c.group, c.residual)
+    assert lo.n_tokens == n, (label, lo.n_tokens, n)
+    assert lo.n_quantized == ref["qk"], (label, lo.n_quantized, ref["qk"])
+    ng = ref["qk"] // c.group
+    if ng:
+        want = orc.pack_blocks(ref, ng)
+        got = gpu_blocks(cache, ng, streams)
+        if not np.array_equal(want, got):
+            bad = np.argwhere(want != got)
+            raise AssertionError("%s: %d packed bytes differ, first (stream, group, byte) %s" %
+                                 (label, len(bad), bad[:5].tolist()))
+    # ring: tokens [Q, n) in slot t % C, verbatim
+    rk, rv = cache.ring_views()
+    rk = rk.reshape(-1, lo.ring_capacity, c.head_dim).cpu().numpy()
+    rv = rv.reshape(-1, lo.ring_capacity, c.head_dim).cpu().numpy()
+    sel = list(range(rk.shape[0])) if streams is None else list(streams)
+    kf = kk.reshape(-1, n, c.head_dim)
+    vf = vv.reshape(-1, n, c.head_dim)
+    for i, s in enumerate(sel):
+        for t in range(ref["qk"], n):
+            slot = t % lo.ring_capacity
+            assert np.array_equal(rk[s, slot].view(np.uint8), kf[i, t].view(np.uint8)), (label, s, t)
+            assert np.array_equal(rv[s, slot].view(np.uint8), vf[i, t].view(np.uint8)), (label, s, t)
+    return ref
+
+
+def rel_err(out, ref):
+    """max over rows of |o - r|_inf / |r|_inf (rows = last axis vectors)."""
+    out = out.reshape(-1, out.shape[-1]).astype(np.float64)
+    ref = ref.reshape(-1, ref.shape[-1]).astype(np.float64)
+    return float((np.abs(out - ref).max(1) / np.abs(ref).max(1)).max())
+
+
+def oracle_decode(orc, k, v, q, bits, G, R, sm_scale=None):
+    ref = orc.build_cache(k, v, bits, G, R)
+    kh, vh = orc.dequant_cache(k, v, ref)
+    return orc.decode_attn(q, kh, vh, sm_scale)
