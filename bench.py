@@ -1,0 +1,200 @@
+#!/usr/bin/env python
+"""KIVI hot path on one MI355X: prefill quantization and decode attention
+over the packed 2-bit cache.
+
+One step = one pass of the whole path over one batch of synthetic input:
+a one-shot append of the context (K per-channel and V per-token quantization,
+packing, residual-ring copy) followed by one decode-attention step (split-K
+pass + combine).  The inputs are generated on the device before timing.  Each
+phase is timed with HIP events recorded on the stream the kernels run on.  A
+1 GiB eviction *read* of an unrelated buffer precedes each phase, so that
+neither phase finds its data in the 256 MB Infinity Cache and neither pays for
+write-backs of dirty lines left by the previous one (evicting by writing would
+leave the cache full of dirty lines and put their write-back inside the timed
+phase).
+
+Prints one JSON line; `value` is decode-attention GB/s of algorithmic bytes
+(packed codes + fp16 zero/scale + fp16 residual + q + out).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def decode_bytes(B, H, Hq, n, Q, bits, D=128, G=32):
+    per_stream = Q * D * 2 * bits / 8 + (Q // G) * D * 4 + Q * (D // G) * 4 + (n - Q) * D * 2 * 2
+    return B * H * per_stream + B * Hq * D * (2 + 4)
+
+
+def append_bytes(B, H, n, Q, bits, D=128, G=32, esize=2):
+    """One-shot append of n tokens: read K and V (esize B per element), write
+    codes (b/8 B) and zero/scale (4/G B) for the Q quantized tokens, copy the
+    n - Q residual rows into the ring (read + write)."""
+    q_el = B * H * Q * D * 2
+    r_el = B * H * (n - Q) * D * 2
+    return q_el * (esize + bits / 8 + 4 / G) + r_el * 2 * esize
+
+
+def cpu_baseline(k_dev, v_dev, q_dev, bits, R, H, Hq, sample_b):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload
+    (the first `sample_b` batch entries: sample_b * H streams)."""
+    import numpy as np
+    import oracle
+    k = k_dev[:sample_b].cpu().numpy()
+    v = v_dev[:sample_b].cpu().numpy()
+    q = q_dev[:sample_b].cpu().numpy()
+    n = k.shape[2]
+    t0 = time.perf_counter()
+    c = oracle.build_cache(k, v, bits, 32, R)
+    t1 = time.perf_counter()
+    kh, vh = oracle.dequant_cache(k, v, c)
+    oracle.decode_attn(q, kh, vh)
+    t2 = time.perf_counter()
+    Q = c["qk"]
+    return dict(
+        value=decode_bytes(sample_b, H, Hq, n, Q, bits) / (t2 - t1) / 1e9,
+        unit="GB/s", cores=1, kind="oracle",
+        quantize_GBps=append_bytes(sample_b, H, n, Q, bits) / (t1 - t0) / 1e9,
+        sample="%d of the workload's batch entries (%d streams x %d tokens); decode = "
+               "dequantize + fp64 attention, quantize = build_cache; single-threaded C"
+               % (sample_b, sample_b * H, n),
+        seconds=dict(quantize=t1 - t0, decode=t2 - t1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--bits", type=int, default=2, choices=(2, 4))
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--context", type=int, default=32768)
+    ap.add_argument("--residual", type=int, default=128)
+    ap.add_argument("--chunk", type=int, default=0, help="prefill chunk (0: one shot)")
+    ap.add_argument("--cpu-sample", type=int, default=2, help="batch entries timed on the CPU oracle (0: skip)")
+    ap.add_argument("--no-evict", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kv_cache_quantization_amd import KiviCache, synth
+
+    B, H, Hq, D = args.batch, 8, 32, 128
+    n, R, bits = args.context, args.residual, args.bits
+    chunk = args.chunk or n
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # inputs resident in HBM before any timing
+    chunks = []
+    for ci in range(0, n, chunk):
+        cn = min(chunk, n - ci)
+        chunks.append(synth.kv_device(3, B, H, cn, D, chunk=ci // chunk, device=dev))
+    q = synth.queries_device(3, B, Hq, D, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    cache = KiviCache(B, H, Hq, n, bits=bits, residual=R, device=dev)
+    cache.workspace()
+    evict = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
+    evict_out = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(evs):
+        cache.reset()
+        if not args.no_evict:
+            torch.amax(evict, dim=0, out=evict_out)
+        evs[0].record(stream)
+        for k, v in chunks:
+            cache.append(k, v)
+        evs[1].record(stream)
+        if not args.no_evict:
+            torch.amax(evict, dim=0, out=evict_out)
+        evs[2].record(stream)
+        cache.decode(q, out=out)
+        evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    t_app = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps / 1e3
+    t_dec = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps / 1e3
+    lo = cache.layout()
+    Q = lo.n_quantized
+    dbytes = decode_bytes(B, H, Hq, n, Q, bits)
+    abytes = append_bytes(B, H, n, Q, bits)
+    dec_gbps = dbytes / t_dec / 1e9
+    app_gbps = abytes / t_app / 1e9
+    splits, gps = cache.decode_plan()
+
+    rec = {
+        "metric": "decode-attn GB/s over packed 2-bit KV (% of HBM peak); quantize GB/s",
+        "value": round(dec_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u%d codes, f16 side data, f32 accumulate" % bits,
+        "data": "synthetic: K,V ~ N(0,1) fp16 with 4 outlier key channels x5 per KV head, "
+                "q ~ N(0,1) fp16, seeded torch generator on the device",
+        "config": {
+            "workload": "KIVI %d-bit decode over a one-shot prefill: batch %d, 8 KV heads, "
+                        "32 query heads, head_dim 128, context %d, group 32, residual %d%s"
+                        % (bits, B, n, R, "" if chunk == n else ", prefill in %d-token chunks" % chunk),
+            "batch": B, "kv_heads": H, "q_heads": Hq, "head_dim": D, "context": n,
+            "group": 32, "residual": R, "bits": bits, "quantized_tokens": Q,
+            "decode_splits_per_stream": splits, "groups_per_split": gps,
+        },
+        "decode": {"ms": round(t_dec * 1e3, 4), "GBps": round(dec_gbps, 1),
+                   "bytes": int(dbytes), "pct_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2)},
+        "quantize": {"ms": round(t_app * 1e3, 4), "GBps": round(app_gbps, 1),
+                     "bytes": int(abytes), "pct_hbm_peak": round(100 * app_gbps / HBM_PEAK_GBPS, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode (split-K pass + combine, one kivi_decode_attn call)",
+            "achieved": round(dec_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "roofline_quantize": {
+            "bound": "hbm", "kernel": "append (quantize + ring copy, one kivi_append call)",
+            "achieved": round(app_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(app_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+        },
+        "timing": "HIP events on the launch stream around each phase; mean over the timed steps;"
+                  " 1 GiB eviction read before each phase (outside the phase events)"
+                  if not args.no_evict else "HIP events, no eviction (warm)",
+    }
+    if args.cpu_sample > 0:
+        k0, v0 = chunks[0]
+        if chunk == n:
+            rec["cpu_baseline"] = cpu_baseline(k0, v0, q, bits, R, H, Hq, args.cpu_sample)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # separate IEEE operations the definition states; FMAs are written explicitly
 # where the decode path wants them.  Packed fp32 instructions are disabled.
 COMMON = [
-    "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wno-inline-asm",
     "-I", os.path.join(ROOT, "include"),
 ]
 DEVICE = [
@@ -27,25 +27,27 @@ DEVICE = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
     objs = []
     tmpdir = os.path.join(HERE, "_build")
     os.makedirs(tmpdir, exist_ok=True)
+    extra_all = tuple(extra)
     units = [("kivi_kernels.hip", DEVICE), ("kivi_api.cpp", ["-D__HIP_PLATFORM_AMD__"])]
     for src, extra in units:
         obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC] + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + COMMON + extra + (list(extra_all) if src.endswith(".hip") else []) + \
+            ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
         objs.append(obj)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

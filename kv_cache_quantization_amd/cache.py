@@ -40,6 +40,12 @@ class KiviCache:
         self.handle = _k.kivi_cache_create(self.cfg, self.buffer.data_ptr(), nbytes)
         self._ws = None
 
+    def reset(self) -> None:
+        """Forget every token: a fresh host handle over the same buffer."""
+        _k.kivi_cache_destroy(self.handle)
+        self.handle = None
+        self.handle = _k.kivi_cache_create(self.cfg, self.buffer.data_ptr(), self.buffer.numel())
+
     def __del__(self):
         h = getattr(self, "handle", None)
         if h:

@@ -35,7 +35,9 @@ struct kivi_cache {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kTargetWaves = 4096;   // decode work items aimed for per launch
+// Decode work items aimed for per launch: 256 compute units x 12 resident
+// wavefronts (3 per SIMD at <= 168 registers per lane), i.e. one round.
+constexpr int kTargetWaves = 3072;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -94,7 +96,9 @@ void decode_split_plan(const kivi_cache *c, int64_t q, int32_t *splits, int32_t 
         *gps = 1;
         return;
     }
-    int64_t want = (kTargetWaves + streams - 1) / streams;
+    // One wavefront per work item; aim for one full round of resident
+    // wavefronts (one residual item per stream plus `want` split items).
+    int64_t want = kTargetWaves / streams - 1;
     if (want < 1) want = 1;
     if (want > ng) want = ng;
     const int64_t g = (ng + want - 1) / want;
@@ -228,10 +232,12 @@ kivi_status kivi_flush(kivi_cache *c, hipStream_t stream) {
 
 size_t kivi_decode_workspace_bytes(const kivi_cache *c) {
     if (!c) return 0;
-    // decode_split_plan never makes more than ceil(kTargetWaves / streams)
+    // decode_split_plan never makes more than max(1, kTargetWaves / streams - 1)
     // split items per stream, whatever n is; plus one residual item.
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
-    const int64_t items = (kTargetWaves + streams - 1) / streams + 1;
+    int64_t splits = kTargetWaves / streams - 1;
+    if (splits < 1) splits = 1;
+    const int64_t items = splits + 1;
     const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
     return (size_t)(bhq * items * (c->cfg.head_dim + 2) * 4);
 }

@@ -33,6 +33,8 @@ namespace kivi {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = kHeadDim;
 constexpr int G = kGroup;
@@ -252,10 +254,10 @@ __global__ __launch_bounds__(256) void ring_append_kernel(RingArgs a) {
 // ===========================================================================
 // Decode attention.
 //
-// Work items (one wavefront each): first one "tail" item per stream over the
-// full-precision residual, then `splits` items per stream over whole groups
-// of the quantized prefix.  Each writes an unnormalized partial (m, l, o)
-// in the log2 domain; decode_combine_kernel merges them.
+// Work items (one wavefront = one workgroup each): first one "tail" item per
+// stream over the full-precision residual, then `splits` items per stream
+// over whole groups of the quantized prefix.  Each writes an unnormalized
+// partial (m, l, o) in the log2 domain; decode_combine_kernel merges them.
 //
 // Quantized groups use the matrix cores (v_mfma_f32_16x16x32_f16).  With
 // GQ query heads per KV head, column j of every B operand belongs to query
@@ -270,6 +272,13 @@ __global__ __launch_bounds__(256) void ring_append_kernel(RingArgs a) {
 // Codes enter the matrix core as fp16 subnormal bit patterns (value
 // code * 2^-24, exact), so unpacking is a shift and an AND; the 2^24 is
 // folded into the softmax scale and the final store.
+//
+// Memory pipeline: a lane's 16 bytes of K codes and 16 bytes of V codes are
+// exactly its own operands, so they go straight to registers; the 1 KiB of
+// zero/scale data of a group is loaded coalesced (16 bytes per lane) and
+// staged through 1 KiB of LDS so every lane can read the entries of its own
+// channels / tokens.  The next group's loads are issued before the current
+// group is computed.
 // ===========================================================================
 
 __device__ __forceinline__ float xsum_rows(float v) {
@@ -310,17 +319,180 @@ __device__ __forceinline__ h8 pack_h8(const h2 *v) {
     return r;
 }
 
+__device__ __forceinline__ void split4(u32x4 u, h2 *v) {
+    v[0] = __builtin_bit_cast(h2, u.x);
+    v[1] = __builtin_bit_cast(h2, u.y);
+    v[2] = __builtin_bit_cast(h2, u.z);
+    v[3] = __builtin_bit_cast(h2, u.w);
+}
+
+__device__ __forceinline__ void split4(uint4 u, h2 *v) {
+    v[0] = __builtin_bit_cast(h2, u.x);
+    v[1] = __builtin_bit_cast(h2, u.y);
+    v[2] = __builtin_bit_cast(h2, u.z);
+    v[3] = __builtin_bit_cast(h2, u.w);
+}
+
 __device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t idx) {
     return a.q_is_f32 ? ((const float *)a.q)[idx] : (float)((const _Float16 *)a.q)[idx];
 }
 
-// Tail item: full-precision residual tokens [n_quant, n) of one stream.
-// Lane l owns channels 2l, 2l+1; one token per iteration, online softmax.
+// q of query head hq as fp16 pairs in B-operand order: slice s, pair m ->
+// channels 32s + 8*Gl + 2m, +1 (one 16-byte load per slice for fp16 q).
+__device__ __forceinline__ void load_q_operand(const DecodeArgs &a, int64_t qrow, int Gl,
+                                               h2 (&qB)[4][4]) {
+    if (a.q_is_f32) {
+        const float *q = (const float *)a.q + qrow + 8 * Gl;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const float4 x0 = *(const float4 *)(q + 32 * s);
+            const float4 x1 = *(const float4 *)(q + 32 * s + 4);
+            qB[s][0] = (h2){(_Float16)x0.x, (_Float16)x0.y};
+            qB[s][1] = (h2){(_Float16)x0.z, (_Float16)x0.w};
+            qB[s][2] = (h2){(_Float16)x1.x, (_Float16)x1.y};
+            qB[s][3] = (h2){(_Float16)x1.z, (_Float16)x1.w};
+        }
+    } else {
+        const _Float16 *q = (const _Float16 *)a.q + qrow + 8 * Gl;
+#pragma unroll
+        for (int s = 0; s < 4; s++) split4(*(const uint4 *)(q + 32 * s), qB[s]);
+    }
+}
+
+// Online-softmax step over the 8 scores a lane holds (two 16-token tiles),
+// shared by the quantized and the residual paths.  Returns p as fp16 pairs in
+// value-operand order.
+__device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float cs, float &m_run,
+                                             float &l_run, float &vb, f4 (&accV)[8], h2 (&P)[4]) {
+    float mt = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
+                     fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
+    mt = xmax_rows(mt) * cs;
+    const float m_new = fmaxf(m_run, mt);
+    if (__any(m_new > m_run)) {
+        const float al = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int o = 0; o < 8; o++) accV[o] *= al;
+        l_run *= al;
+        vb *= al;
+        m_run = m_new;
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], cs, -m_run));
+        p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[e], cs, -m_run));
+    }
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        P[m][0] = (_Float16)p[2 * m];
+        P[m][1] = (_Float16)p[2 * m + 1];
+        l_run = __builtin_amdgcn_fdot2(P[m], ones, l_run, false);
+    }
+}
+
+// Store a partial: lanes whose column carries value channel group cg write
+// the two M-tiles of that group; one lane per head writes (m, l).
 template <int GQ>
-__device__ void decode_tail(const DecodeArgs &a, int stream) {
+__device__ __forceinline__ void store_partial(const DecodeArgs &a, int64_t pi, int l,
+                                              const f4 (&accV)[8], float scale, float bias,
+                                              float m_run, float l_tot) {
+    const int j = l & 15, Gl = l >> 4;
+    const int cg = (j / GQ) & 3;
+    if (j < 4 * GQ) {
+        // tiles 2cg and 2cg+1, chosen with selects (a lane-dependent array
+        // index would push the accumulators to scratch memory)
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const f4 t = cg == 0 ? accV[e] : cg == 1 ? accV[2 + e] : cg == 2 ? accV[4 + e]
+                                                                                : accV[6 + e];
+            float4 v;
+            v.x = __builtin_fmaf(t[0], scale, bias);
+            v.y = __builtin_fmaf(t[1], scale, bias);
+            v.z = __builtin_fmaf(t[2], scale, bias);
+            v.w = __builtin_fmaf(t[3], scale, bias);
+            *(float4 *)&a.part_o[pi * D + 16 * (2 * cg + e) + 4 * Gl] = v;
+        }
+    }
+    if (j < GQ && Gl == 0) {
+        a.part_ml[2 * pi] = m_run;
+        a.part_ml[2 * pi + 1] = l_tot;
+    }
+}
+
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kTwoM24 = 5.9604644775390625e-08f;
+
+// Residual item, fp16 ring: tokens [n_quant, n) in chunks of 32 through the
+// same matrix-core products (K rows and q are exact fp16, no scale/zero).
+template <int GQ>
+__device__ void decode_tail_f16(const DecodeArgs &a, int stream) {
+    const int l = threadIdx.x & 63;
+    const int j = l & 15, Gl = l >> 4;
+    const int h = j % GQ;
+    const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
+    const int hq = hk * GQ + h;
+    const int items = a.splits + 1;
+    h2 qB[4][4];
+    load_q_operand(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
+    const _Float16 *rk = (const _Float16 *)a.ring_k + (int64_t)stream * a.ring_cap * D;
+    const _Float16 *rv = (const _Float16 *)a.ring_v + (int64_t)stream * a.ring_cap * D;
+    float m_run = -INFINITY, l_run = 0.f, vb = 0.f;
+    f4 accV[8];
+#pragma unroll
+    for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int64_t base = a.n_quant; base < a.n_tokens; base += G) {
+        f4 S[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int64_t tok = base + 16 * t + (l & 15);
+            const bool ok = tok < a.n_tokens;
+            const int64_t tc = ok ? tok : a.n_tokens - 1;
+            const _Float16 *row = rk + (tc % a.ring_cap) * D + 8 * Gl;
+            S[t] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                uint4 u = *(const uint4 *)(row + 32 * s);
+                if (!ok) u = (uint4){0u, 0u, 0u, 0u};
+                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, u),
+                                                             pack_h8(qB[s]), S[t], 0, 0, 0);
+            }
+            // lane (j, Gl) holds tokens base + 16t + 4Gl + e
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                if (base + 16 * t + 4 * Gl + e >= a.n_tokens) S[t][e] = -INFINITY;
+        }
+        h2 P[4];
+        softmax_step(S[0], S[1], a.sm_log2, m_run, l_run, vb, accV, P);
+        const h8 Bp = pack_h8(P);
+#pragma unroll
+        for (int o = 0; o < 8; o++) {
+            const int c = 16 * o + (l & 15);
+            h8 A;
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++) {
+                // unconditional load from a valid slot, then zero past the end
+                const int64_t tok = base + 4 * Gl + (kk & 3) + 16 * (kk >> 2);
+                const int64_t tc = tok < a.n_tokens ? tok : a.n_tokens - 1;
+                const _Float16 x = rv[(tc % a.ring_cap) * D + c];
+                A[kk] = tok < a.n_tokens ? x : (_Float16)0.0f;
+            }
+            accV[o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bp, accV[o], 0, 0, 0);
+        }
+    }
+    const int64_t pi = ((int64_t)b * a.q_heads + hq) * items + a.splits;
+    store_partial<GQ>(a, pi, l, accV, 1.0f, 0.0f, m_run, xsum_rows(l_run));
+}
+
+// Residual item, fp32 ring: one token per step on the vector ALUs (lane l
+// owns channels 2l, 2l+1), online softmax in the log2 domain.
+template <int GQ>
+__device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
     const int l = threadIdx.x & 63;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const int items = a.splits + 1;
+    const float *rk = (const float *)a.ring_k;
+    const float *rv = (const float *)a.ring_v;
     float q0[GQ], q1[GQ], m[GQ], ls[GQ], a0[GQ], a1[GQ];
 #pragma unroll
     for (int h = 0; h < GQ; h++) {
@@ -334,18 +506,7 @@ __device__ void decode_tail(const DecodeArgs &a, int stream) {
     }
     for (int64_t t = a.n_quant; t < a.n_tokens; t++) {
         const int64_t row = ((int64_t)stream * a.ring_cap + t % a.ring_cap) * D + 2 * l;
-        float k0, k1, v0, v1;
-        if (a.ring_is_f32) {
-            k0 = ((const float *)a.ring_k)[row];
-            k1 = ((const float *)a.ring_k)[row + 1];
-            v0 = ((const float *)a.ring_v)[row];
-            v1 = ((const float *)a.ring_v)[row + 1];
-        } else {
-            h2 kk = *(const h2 *)((const _Float16 *)a.ring_k + row);
-            h2 vv = *(const h2 *)((const _Float16 *)a.ring_v + row);
-            k0 = (float)kk[0]; k1 = (float)kk[1];
-            v0 = (float)vv[0]; v1 = (float)vv[1];
-        }
+        const float k0 = rk[row], k1 = rk[row + 1], v0 = rv[row], v1 = rv[row + 1];
 #pragma unroll
         for (int h = 0; h < GQ; h++) {
             float s = wave_sum(__builtin_fmaf(q0[h], k0, q1[h] * k1)) * a.sm_log2;
@@ -370,12 +531,55 @@ __device__ void decode_tail(const DecodeArgs &a, int stream) {
     }
 }
 
-constexpr float kTwo24 = 16777216.0f;
-constexpr float kTwoM24 = 5.9604644775390625e-08f;
+// LDS pipeline of packed blocks.  Each group's block (codes + side data,
+// 3 KiB at 2 bits, 5 KiB at 4 bits) is copied verbatim into one of NST LDS
+// stages with global_load_lds_dwordx4 (64 lanes x 16 bytes = 1 KiB per
+// instruction, straight from HBM into LDS, no registers), NST - 1 groups
+// ahead of the one being computed.  The copies are issued and awaited with
+// inline assembly: the compiler's own wait insertion would otherwise wait for
+// every outstanding copy before each LDS read.
+template <int BITS>
+struct Pipe {
+    static constexpr int CB = BITS * G * D / 8;         // code bytes per tensor
+    static constexpr int BB = 2 * CB + 4 * D * 2;       // block bytes
+    static constexpr int DPG = BB / 1024;               // 1 KiB copies per group
+    static constexpr int NST = BITS == 2 ? 4 : 2;       // stages
+};
+
+__device__ __forceinline__ void dma_1k(const uint8_t *src_lane, uint32_t lds_dst) {
+    // LDS destination: M0 + 16 * lane
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src_lane), "s"(lds_dst)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int BITS>
+__device__ __forceinline__ void issue_group(const uint8_t *blk, uint32_t stage, int l) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // prior reads of the stage done
+#pragma unroll
+    for (int c = 0; c < Pipe<BITS>::DPG; c++)
+        dma_1k(blk + c * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(stage + c * 1024));
+}
+
+// Wait until at most `r` groups (issued after the one needed) are in flight.
+template <int BITS>
+__device__ __forceinline__ void wait_groups_after(int r) {
+    constexpr int P = Pipe<BITS>::DPG;
+    if (r >= 3) wait_vm<3 * P>();
+    else if (r == 2) wait_vm<2 * P>();
+    else if (r == 1) wait_vm<P>();
+    else wait_vm<0>();
+}
 
 template <int BITS, int GQ>
-__device__ void decode_split(const DecodeArgs &a, int stream, int sp) {
-    constexpr int CB = BITS * G * D / 8;       // code bytes per tensor per block
+__device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *pipe) {
+    using PP = Pipe<BITS>;
     constexpr int DPL = 2 * BITS;              // code dwords per lane
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
@@ -388,19 +592,8 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp) {
     const int64_t g0 = (int64_t)sp * a.groups_per_split;
     const int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
 
-    // q as fp16 pairs in B-operand order: slice s, pair m -> channels
-    // 32s + 8*Gl + 2m, +1.
     h2 qB[4][4];
-    const int64_t qrow = ((int64_t)b * a.q_heads + hq) * D;
-#pragma unroll
-    for (int s = 0; s < 4; s++)
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const int c = 32 * s + 8 * Gl + 2 * m;
-            qB[s][m][0] = (_Float16)load_q(a, qrow + c);
-            qB[s][m][1] = (_Float16)load_q(a, qrow + c + 1);
-        }
-    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    load_q_operand(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
     const float cs = a.sm_log2 * kTwo24;        // score units -> log2 units
 
     float m_run = -INFINITY, l_run = 0.f, vb = 0.f;
@@ -408,157 +601,155 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp) {
 #pragma unroll
     for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
 
+    const uint8_t *sblk = a.blocks + (int64_t)stream * a.max_groups * a.block_bytes;
+    const uint32_t pbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)pipe;
+    // q must be in registers before the copies start, and the compiler must
+    // know it (its wait tracking does not see the inline-assembly copies).
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+        for (int m = 0; m < 4; m++) asm volatile("" : : "v"(qB[s][m]));
+    wait_vm<0>();
+    int64_t issued = g0;
+    for (int st = 0; st < PP::NST - 1 && issued < g1; st++, issued++)
+        issue_group<BITS>(sblk + issued * PP::BB, pbase + (uint32_t)((issued - g0) % PP::NST) * PP::BB, l);
+
     for (int64_t g = g0; g < g1; g++) {
-        const uint8_t *blk = a.blocks + ((int64_t)stream * a.max_groups + g) * a.block_bytes;
+        if (issued < g1) {
+            issue_group<BITS>(sblk + issued * PP::BB,
+                              pbase + (uint32_t)((issued - g0) % PP::NST) * PP::BB, l);
+            issued++;
+        }
+        wait_groups_after<BITS>((int)(issued - 1 - g));
+        const uint8_t *stg = pipe + ((g - g0) % PP::NST) * PP::BB;
+        const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
         uint32_t kc[DPL], vc[DPL];
 #pragma unroll
-        for (int w4 = 0; w4 < DPL / 4; w4++) {
-            uint4 u = *(const uint4 *)(blk + w4 * 1024 + 16 * l);
+        for (int w4 = 0; w4 < BITS / 2; w4++) {
+            const uint4 u = *(const uint4 *)(stg + w4 * 1024 + 16 * l);
+            const uint4 v = *(const uint4 *)(stg + PP::CB + w4 * 1024 + 16 * l);
             kc[4 * w4] = u.x; kc[4 * w4 + 1] = u.y; kc[4 * w4 + 2] = u.z; kc[4 * w4 + 3] = u.w;
-            uint4 v = *(const uint4 *)(blk + CB + w4 * 1024 + 16 * l);
             vc[4 * w4] = v.x; vc[4 * w4 + 1] = v.y; vc[4 * w4 + 2] = v.z; vc[4 * w4 + 3] = v.w;
         }
-        const uint8_t *side = blk + 2 * CB;
-        h2 ks[4][4], kz[4][4];
+        // side data as 16-byte units: kscale 0..15, kzero 16..31, vscale
+        // 32..47, vzero 48..63 (channel c at byte 2c of its array, value token
+        // t of channel group cg at byte 2(32cg + t)).
+        float kb = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            uint4 us = *(const uint4 *)(side + 2 * (32 * s + 8 * Gl));
-            uint4 uz = *(const uint4 *)(side + 2 * D + 2 * (32 * s + 8 * Gl));
-            ks[s][0] = __builtin_bit_cast(h2, us.x); ks[s][1] = __builtin_bit_cast(h2, us.y);
-            ks[s][2] = __builtin_bit_cast(h2, us.z); ks[s][3] = __builtin_bit_cast(h2, us.w);
-            kz[s][0] = __builtin_bit_cast(h2, uz.x); kz[s][1] = __builtin_bit_cast(h2, uz.y);
-            kz[s][2] = __builtin_bit_cast(h2, uz.z); kz[s][3] = __builtin_bit_cast(h2, uz.w);
+            h2 kz[4];
+            split4(side[16 + 4 * s + Gl], kz);
+#pragma unroll
+            for (int m = 0; m < 4; m++) kb = __builtin_amdgcn_fdot2(qB[s][m], kz[m], kb, false);
         }
-        h2 vs[4], vz[4];
+        kb = xsum_rows(kb) * kTwoM24;
+        f4 S0 = (f4){kb, kb, kb, kb}, S1 = S0;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            // q * kscale carried as an fp16 pair hi + lo, lo = fma(q, kscale,
+            // -hi) rounded once: the matrix core sees the product (almost) exactly.
+            h2 ks[4], qh[4], ql[4];
+            split4(side[4 * s + Gl], ks);
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                qh[m] = qB[s][m] * ks[m];
+                ql[m] = __builtin_elementwise_fma(qB[s][m], ks[m], -qh[m]);
+            }
+            const h8 A0 = unpack_operand<BITS>(kc, s), A1 = unpack_operand<BITS>(kc, 4 + s);
+            const h8 Bh = pack_h8(qh), Bl = pack_h8(ql);
+            S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, S1, 0, 0, 0);
+            S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1, 0, 0, 0);
+        }
+        h2 P[4];
+        softmax_step(S0, S1, cs, m_run, l_run, vb, accV, P);
+        h2 vs[4], vz[4], ps[4];
         {
-            const uint8_t *vsb = side + 4 * D + 2 * (G * cg + 4 * Gl);
-            const uint8_t *vzb = side + 6 * D + 2 * (G * cg + 4 * Gl);
-            uint2 s0 = *(const uint2 *)vsb, s1 = *(const uint2 *)(vsb + 32);
-            uint2 z0 = *(const uint2 *)vzb, z1 = *(const uint2 *)(vzb + 32);
-            vs[0] = __builtin_bit_cast(h2, s0.x); vs[1] = __builtin_bit_cast(h2, s0.y);
-            vs[2] = __builtin_bit_cast(h2, s1.x); vs[3] = __builtin_bit_cast(h2, s1.y);
+            const uint2 *s2 = (const uint2 *)side;
+            const uint2 a0 = s2[64 + 8 * cg + Gl], a1 = s2[64 + 8 * cg + Gl + 4];
+            const uint2 z0 = s2[96 + 8 * cg + Gl], z1 = s2[96 + 8 * cg + Gl + 4];
+            vs[0] = __builtin_bit_cast(h2, a0.x); vs[1] = __builtin_bit_cast(h2, a0.y);
+            vs[2] = __builtin_bit_cast(h2, a1.x); vs[3] = __builtin_bit_cast(h2, a1.y);
             vz[0] = __builtin_bit_cast(h2, z0.x); vz[1] = __builtin_bit_cast(h2, z0.y);
             vz[2] = __builtin_bit_cast(h2, z1.x); vz[3] = __builtin_bit_cast(h2, z1.y);
         }
-
-        // Keys: fold the scale into q, the zero into a per-head bias.  The
-        // product q * kscale (22 significant bits) is carried as an fp16
-        // pair hi + lo with lo = fma(q, kscale, -hi) rounded once, so the
-        // matrix core sees it (almost) exactly.
-        h2 qh[4][4], ql[4][4];
-        float kb = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; s++)
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                qh[s][m] = qB[s][m] * ks[s][m];
-                ql[s][m] = __builtin_elementwise_fma(qB[s][m], ks[s][m], -qh[s][m]);
-                kb = __builtin_amdgcn_fdot2(qB[s][m], kz[s][m], kb, false);
-            }
-        kb = xsum_rows(kb) * kTwoM24;
-        f4 S[2];
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-            S[t] = (f4){kb, kb, kb, kb};
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-                const h8 A = unpack_operand<BITS>(kc, 4 * t + s);
-                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack_h8(qh[s]), S[t], 0, 0, 0);
-                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pack_h8(ql[s]), S[t], 0, 0, 0);
-            }
-        }
-
-        // Online softmax (log2 domain).  Lane (j, Gl) holds tokens
-        // 4Gl + e (tile 0) and 16 + 4Gl + e (tile 1) of head j % GQ.
-        float mt = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-        mt = xmax_rows(mt) * cs;
-        const float m_new = fmaxf(m_run, mt);
-        if (__any(m_new > m_run)) {
-            const float al = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-            for (int o = 0; o < 8; o++) accV[o] *= al;
-            l_run *= al;
-            vb *= al;
-            m_run = m_new;
-        }
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][e], cs, -m_run));
-            p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[1][e], cs, -m_run));
-        }
-        h2 P[4], ps[4];
 #pragma unroll
         for (int m = 0; m < 4; m++) {
-            P[m][0] = (_Float16)p[2 * m];
-            P[m][1] = (_Float16)p[2 * m + 1];
-            l_run = __builtin_amdgcn_fdot2(P[m], ones, l_run, false);
             vb = __builtin_amdgcn_fdot2(P[m], vz[m], vb, false);
             ps[m] = P[m] * vs[m];
         }
-        const h8 B = pack_h8(ps);
+        const h8 Bv = pack_h8(ps);
 #pragma unroll
         for (int o = 0; o < 8; o++)
-            accV[o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_operand<BITS>(vc, o), B,
+            accV[o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_operand<BITS>(vc, o), Bv,
                                                             accV[o], 0, 0, 0);
     }
-
-    const float l_tot = xsum_rows(l_run);
-    const float vb_tot = xsum_rows(vb);
     const int64_t pi = ((int64_t)b * a.q_heads + hq) * items + sp;
-    if (j < 4 * GQ) {
-#pragma unroll
-        for (int o = 0; o < 8; o++) {
-            if ((o >> 1) == cg) {
-                float4 v;
-                v.x = __builtin_fmaf(accV[o][0], kTwo24, vb_tot);
-                v.y = __builtin_fmaf(accV[o][1], kTwo24, vb_tot);
-                v.z = __builtin_fmaf(accV[o][2], kTwo24, vb_tot);
-                v.w = __builtin_fmaf(accV[o][3], kTwo24, vb_tot);
-                *(float4 *)&a.part_o[pi * D + 16 * o + 4 * Gl] = v;
-            }
-        }
-    }
-    if (j < GQ && Gl == 0) {
-        a.part_ml[2 * pi] = m_run;
-        a.part_ml[2 * pi + 1] = l_tot;
-    }
+    store_partial<GQ>(a, pi, l, accV, kTwo24, xsum_rows(vb), m_run, xsum_rows(l_run));
 }
 
 template <int BITS, int GQ>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-    const int wave = threadIdx.x >> 6;
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t pipe[Pipe<BITS>::NST * Pipe<BITS>::BB];
+    const int64_t item = blockIdx.x;
     const int streams = a.batch * a.kv_heads;
-    if (item >= (int64_t)streams * (a.splits + 1)) return;
     if (item < streams) {
-        decode_tail<GQ>(a, (int)item);
+        if (a.ring_is_f32) decode_tail_f32<GQ>(a, (int)item);
+        else decode_tail_f16<GQ>(a, (int)item);
         return;
     }
     const int64_t it = item - streams;
-    decode_split<BITS, GQ>(a, (int)(it / a.splits), (int)(it % a.splits));
+    decode_split<BITS, GQ>(a, (int)(it / a.splits), (int)(it % a.splits), pipe);
 }
 
-// Merge the partials of one (batch, query head): one thread per channel.
+// Merge the partials of one (batch, query head).  The split weights
+// 2^(m_s - M) are computed once in LDS; each thread then sums one channel.
+constexpr int kMaxItems = 4160;
+
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+    __shared__ float w[kMaxItems];
+    __shared__ float red[128];
     const int64_t bh = blockIdx.x;
     const int c = threadIdx.x;
     const int items = a.splits + 1;
     const float *ml = a.part_ml + bh * items * 2;
     float M = -INFINITY;
-    for (int s = 0; s < items; s++)
+    for (int s = c; s < items; s += 128)
         if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
-    float Ls = 0.f, acc = 0.f;
-    for (int s = 0; s < items; s++) {
-        const float ls = ml[2 * s + 1];
-        if (ls > 0.f) {
-            const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-            Ls = __builtin_fmaf(ls, w, Ls);
-            acc = __builtin_fmaf(a.part_o[(bh * items + s) * D + c], w, acc);
-        }
+    red[c] = M;
+    __syncthreads();
+    for (int off = 64; off > 0; off >>= 1) {
+        if (c < off) red[c] = fmaxf(red[c], red[c + off]);
+        __syncthreads();
     }
-    a.out[bh * D + c] = acc / Ls;
+    M = red[0];
+    __syncthreads();
+    float Lp = 0.f;
+    for (int s = c; s < items; s += 128) {
+        const float ls = ml[2 * s + 1];
+        const float ws = ls > 0.f ? __builtin_amdgcn_exp2f(ml[2 * s] - M) : 0.f;
+        w[s] = ws;
+        Lp = __builtin_fmaf(ls, ws, Lp);
+    }
+    red[c] = Lp;
+    __syncthreads();
+    for (int off = 64; off > 0; off >>= 1) {
+        if (c < off) red[c] += red[c + off];
+        __syncthreads();
+    }
+    const float L = red[0];
+    const float *po = a.part_o + bh * items * D + c;
+    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+    int s = 0;
+    for (; s + 4 <= items; s += 4) {
+        acc0 = __builtin_fmaf(po[(int64_t)s * D], w[s], acc0);
+        acc1 = __builtin_fmaf(po[(int64_t)(s + 1) * D], w[s + 1], acc1);
+        acc2 = __builtin_fmaf(po[(int64_t)(s + 2) * D], w[s + 2], acc2);
+        acc3 = __builtin_fmaf(po[(int64_t)(s + 3) * D], w[s + 3], acc3);
+    }
+    for (; s < items; s++) acc0 = __builtin_fmaf(po[(int64_t)s * D], w[s], acc0);
+    a.out[bh * D + c] = ((acc0 + acc1) + (acc2 + acc3)) / L;
 }
 
 // ===========================================================================
@@ -590,16 +781,17 @@ hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {
 
 template <int BITS>
 static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
-    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4>), grid, dim3(256), 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<BITS, 1>), grid, dim3(256), 0, s, a);
+    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4>), grid, dim3(64), 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<BITS, 1>), grid, dim3(64), 0, s, a);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const int streams = a.batch * a.kv_heads;
     const int gq = a.q_heads / a.kv_heads;
     const int64_t items = (int64_t)streams * (a.splits + 1);
-    dim3 grid((unsigned)((items + 3) / 4));
+    if (a.splits + 1 > kMaxItems) return hipErrorInvalidValue;
+    dim3 grid((unsigned)items);
     if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
     else launch_decode_bits<4>(a, gq, grid, s);
     hipError_t e = hipGetLastError();

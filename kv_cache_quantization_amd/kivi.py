@@ -11,7 +11,7 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkivi.so")
+LIB_PATH = os.environ.get("KIVI_LIB") or os.path.join(HERE, "libkivi.so")
 
 KIVI_OK = 0
 KIVI_ERR_INVALID_ARG = 1
