@@ -21,9 +21,13 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wno-inline-asm",
     "-I", os.path.join(ROOT, "include"),
 ]
+# MFMA results in VGPRs rather than AGPRs: the decode loop also touches its
+# accumulators with vector ALU code, and an AGPR home costs a copy in and out
+# per group (and the registers of a fourth wave per SIMD).
 DEVICE = [
     "--offload-arch=gfx950", "-x", "hip",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

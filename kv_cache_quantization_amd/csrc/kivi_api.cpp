@@ -35,9 +35,10 @@ struct kivi_cache {
 namespace {
 
 constexpr size_t kAlign = 256;
-// Decode work items aimed for per launch: 256 compute units x 12 resident
-// wavefronts (3 per SIMD at <= 168 registers per lane), i.e. one round.
-constexpr int kTargetWaves = 3072;
+// Decode work items aimed for per launch: 256 compute units x 16 resident
+// wavefronts (4 per SIMD: <= 128 registers per lane and <= 10 KiB of LDS
+// each), i.e. one round.
+constexpr int kTargetWaves = 4096;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

@@ -298,16 +298,32 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Matrix-core operand o from a lane's code dwords.  Pair m of the operand
+// (positions kk = 2m, 2m+1) is taken with one AND, in place: at 2 bits the
+// codes of pair m sit at bits 2m and 16 + 2m of the (for odd o, 8-bit
+// shifted) dword, so the fp16 subnormals read code * 4^m * 2^-24; at 4 bits
+// pairs m = 0,1 sit at bits 4m, 16 + 4m and pairs 2,3 at the same bits of
+// the dword shifted by 8, reading code * 16^(m&1) * 2^-24.  The factor
+// 2^kScaleLog2<BITS>(m) is divided out of the other operand.
+template <int BITS>
+__device__ __forceinline__ constexpr int kScaleLog2(int m) {
+    return BITS == 2 ? 2 * m : BITS == 4 ? 4 * (m & 1) : 0;
+}
+
 template <int BITS>
 __device__ __forceinline__ h8 unpack_operand(const uint32_t *w, int o) {
-    constexpr int OPD = 4 / BITS;
     constexpr uint32_t M1 = (1u << BITS) - 1u;
     constexpr uint32_t MASK = M1 | (M1 << 16);
-    const uint32_t x = w[o / OPD];
-    const int base = BITS * 4 * (o % OPD);
     uint32_t r[4];
+    if (BITS == 2) {
+        const uint32_t x = (o & 1) ? (w[o >> 1] >> 8) : w[o >> 1];
 #pragma unroll
-    for (int m = 0; m < 4; m++) r[m] = (x >> (base + BITS * m)) & MASK;
+        for (int m = 0; m < 4; m++) r[m] = x & (MASK << (2 * m));
+    } else {
+        const uint32_t x = w[o], y = x >> 8;
+#pragma unroll
+        for (int m = 0; m < 4; m++) r[m] = (m < 2 ? x : y) & (MASK << (4 * (m & 1)));
+    }
     uint4 u = {r[0], r[1], r[2], r[3]};
     return __builtin_bit_cast(h8, u);
 }
@@ -360,10 +376,14 @@ __device__ __forceinline__ void load_q_operand(const DecodeArgs &a, int64_t qrow
 }
 
 // Online-softmax step over the 8 scores a lane holds (two 16-token tiles),
-// shared by the quantized and the residual paths.  Returns p as fp16 pairs in
-// value-operand order.
+// shared by the quantized and the residual paths.  Returns p as fp16 pairs
+// in value-operand order, pair m pre-divided by 2^kScaleLog2<SB>(m) (SB = 0:
+// no scaling); l_run accumulates the unscaled sum.  nm[m] caches
+// -m_run - kScaleLog2<SB>(m).
+template <int SB>
 __device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float cs, float &m_run,
-                                             float &l_run, float &vb, f4 (&accV)[8], h2 (&P)[4]) {
+                                             float (&nm)[4], float &l_run, float (&vb)[4],
+                                             f4 (&accV)[8], h2 (&P)[4]) {
     float mt = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
                      fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
     mt = xmax_rows(mt) * cs;
@@ -373,21 +393,26 @@ __device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float c
 #pragma unroll
         for (int o = 0; o < 8; o++) accV[o] *= al;
         l_run *= al;
-        vb *= al;
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            vb[m] *= al;
+            nm[m] = -m_new - (float)kScaleLog2<SB>(m);
+        }
         m_run = m_new;
     }
     float p[8];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], cs, -m_run));
-        p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[e], cs, -m_run));
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], cs, nm[e >> 1]));
+        p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[e], cs, nm[2 + (e >> 1)]));
     }
-    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int m = 0; m < 4; m++) {
+        const _Float16 up = (_Float16)(float)(1 << kScaleLog2<SB>(m));
+        const h2 w = {up, up};
         P[m][0] = (_Float16)p[2 * m];
         P[m][1] = (_Float16)p[2 * m + 1];
-        l_run = __builtin_amdgcn_fdot2(P[m], ones, l_run, false);
+        l_run = __builtin_amdgcn_fdot2(P[m], w, l_run, false);
     }
 }
 
@@ -437,7 +462,8 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream) {
     load_q_operand(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
     const _Float16 *rk = (const _Float16 *)a.ring_k + (int64_t)stream * a.ring_cap * D;
     const _Float16 *rv = (const _Float16 *)a.ring_v + (int64_t)stream * a.ring_cap * D;
-    float m_run = -INFINITY, l_run = 0.f, vb = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    float nm[4] = {INFINITY, INFINITY, INFINITY, INFINITY}, vb[4] = {0.f, 0.f, 0.f, 0.f};
     f4 accV[8];
 #pragma unroll
     for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -463,7 +489,7 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream) {
                 if (base + 16 * t + 4 * Gl + e >= a.n_tokens) S[t][e] = -INFINITY;
         }
         h2 P[4];
-        softmax_step(S[0], S[1], a.sm_log2, m_run, l_run, vb, accV, P);
+        softmax_step<0>(S[0], S[1], a.sm_log2, m_run, nm, l_run, vb, accV, P);
         const h8 Bp = pack_h8(P);
 #pragma unroll
         for (int o = 0; o < 8; o++) {
@@ -543,7 +569,7 @@ struct Pipe {
     static constexpr int CB = BITS * G * D / 8;         // code bytes per tensor
     static constexpr int BB = 2 * CB + 4 * D * 2;       // block bytes
     static constexpr int DPG = BB / 1024;               // 1 KiB copies per group
-    static constexpr int NST = BITS == 2 ? 4 : 2;       // stages
+    static constexpr int NST = BITS == 2 ? 3 : 2;       // stages
 };
 
 __device__ __forceinline__ void dma_1k(const uint8_t *src_lane, uint32_t lds_dst) {
@@ -592,11 +618,20 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int64_t g0 = (int64_t)sp * a.groups_per_split;
     const int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
 
+    // q pair m divided by 2^kScaleLog2(m): it meets key codes read in place
     h2 qB[4][4];
     load_q_operand(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
+        const h2 d2 = {dn, dn};
+#pragma unroll
+        for (int s = 0; s < 4; s++) qB[s][m] = qB[s][m] * d2;
+    }
     const float cs = a.sm_log2 * kTwo24;        // score units -> log2 units
 
-    float m_run = -INFINITY, l_run = 0.f, vb = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    float nm[4] = {INFINITY, INFINITY, INFINITY, INFINITY}, vb[4] = {0.f, 0.f, 0.f, 0.f};
     f4 accV[8];
 #pragma unroll
     for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -634,14 +669,17 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
         // side data as 16-byte units: kscale 0..15, kzero 16..31, vscale
         // 32..47, vzero 48..63 (channel c at byte 2c of its array, value token
         // t of channel group cg at byte 2(32cg + t)).
-        float kb = 0.f;
+        float kbm[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             h2 kz[4];
             split4(side[16 + 4 * s + Gl], kz);
 #pragma unroll
-            for (int m = 0; m < 4; m++) kb = __builtin_amdgcn_fdot2(qB[s][m], kz[m], kb, false);
+            for (int m = 0; m < 4; m++) kbm[m] = __builtin_amdgcn_fdot2(qB[s][m], kz[m], kbm[m], false);
         }
+        float kb = kbm[0];
+#pragma unroll
+        for (int m = 1; m < 4; m++) kb = __builtin_fmaf(kbm[m], (float)(1 << kScaleLog2<BITS>(m)), kb);
         kb = xsum_rows(kb) * kTwoM24;
         f4 S0 = (f4){kb, kb, kb, kb}, S1 = S0;
 #pragma unroll
@@ -663,7 +701,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
             S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1, 0, 0, 0);
         }
         h2 P[4];
-        softmax_step(S0, S1, cs, m_run, l_run, vb, accV, P);
+        softmax_step<BITS>(S0, S1, cs, m_run, nm, l_run, vb, accV, P);
         h2 vs[4], vz[4], ps[4];
         {
             const uint2 *s2 = (const uint2 *)side;
@@ -676,7 +714,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
         }
 #pragma unroll
         for (int m = 0; m < 4; m++) {
-            vb = __builtin_amdgcn_fdot2(P[m], vz[m], vb, false);
+            vb[m] = __builtin_amdgcn_fdot2(P[m], vz[m], vb[m], false);
             ps[m] = P[m] * vs[m];
         }
         const h8 Bv = pack_h8(ps);
@@ -685,8 +723,11 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
             accV[o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_operand<BITS>(vc, o), Bv,
                                                             accV[o], 0, 0, 0);
     }
+    float vbt = vb[0];
+#pragma unroll
+    for (int m = 1; m < 4; m++) vbt = __builtin_fmaf(vb[m], (float)(1 << kScaleLog2<BITS>(m)), vbt);
     const int64_t pi = ((int64_t)b * a.q_heads + hq) * items + sp;
-    store_partial<GQ>(a, pi, l, accV, kTwo24, xsum_rows(vb), m_run, xsum_rows(l_run));
+    store_partial<GQ>(a, pi, l, accV, kTwo24, xsum_rows(vbt), m_run, xsum_rows(l_run));
 }
 
 template <int BITS, int GQ>
