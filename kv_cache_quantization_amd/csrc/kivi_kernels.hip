@@ -281,16 +281,29 @@ __global__ __launch_bounds__(256) void ring_append_kernel(RingArgs a) {
 // group is computed.
 // ===========================================================================
 
+// Reductions over the four 16-lane rows (lanes j, j+16, j+32, j+48) with
+// gfx950's v_permlane32_swap (exchange the two 32-lane halves) and
+// v_permlane16_swap (exchange odd and even rows): vector-ALU moves, no LDS
+// round trip.  s_nop 1 covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void swap_halves(float &a, float &b) {
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows(float &a, float &b) {
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
 __device__ __forceinline__ float xsum_rows(float v) {
-    // sum over the four 16-lane rows (lanes j, j+16, j+32, j+48)
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    float a = v, b = v;
+    swap_halves(a, b);
+    float c = a + b, d = c;
+    swap_rows(c, d);
+    return c + d;
 }
 __device__ __forceinline__ float xmax_rows(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    float a = v, b = v;
+    swap_halves(a, b);
+    float c = fmaxf(a, b), d = c;
+    swap_rows(c, d);
+    return fmaxf(c, d);
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -381,12 +394,12 @@ __device__ __forceinline__ void load_q_operand(const DecodeArgs &a, int64_t qrow
 // no scaling); l_run accumulates the unscaled sum.  nm[m] caches
 // -m_run - kScaleLog2<SB>(m).
 template <int SB>
-__device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float cs, float &m_run,
-                                             float (&nm)[4], float &l_run, float (&vb)[4],
-                                             f4 (&accV)[8], h2 (&P)[4]) {
+__device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float cs, float kbl,
+                                             float &m_run, float (&nm)[4], float &l_run,
+                                             float (&vb)[4], f4 (&accV)[8], h2 (&P)[4]) {
     float mt = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
                      fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
-    mt = xmax_rows(mt) * cs;
+    mt = __builtin_fmaf(xmax_rows(mt), cs, kbl);
     const float m_new = fmaxf(m_run, mt);
     if (__any(m_new > m_run)) {
         const float al = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -400,11 +413,14 @@ __device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float c
         }
         m_run = m_new;
     }
+    float nk[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++) nk[m] = nm[m] + kbl;
     float p[8];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], cs, nm[e >> 1]));
-        p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[e], cs, nm[2 + (e >> 1)]));
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], cs, nk[e >> 1]));
+        p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[e], cs, nk[2 + (e >> 1)]));
     }
 #pragma unroll
     for (int m = 0; m < 4; m++) {
@@ -489,7 +505,7 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream) {
                 if (base + 16 * t + 4 * Gl + e >= a.n_tokens) S[t][e] = -INFINITY;
         }
         h2 P[4];
-        softmax_step<0>(S[0], S[1], a.sm_log2, m_run, nm, l_run, vb, accV, P);
+        softmax_step<0>(S[0], S[1], a.sm_log2, 0.0f, m_run, nm, l_run, vb, accV, P);
         const h8 Bp = pack_h8(P);
 #pragma unroll
         for (int o = 0; o < 8; o++) {
@@ -604,7 +620,8 @@ __device__ __forceinline__ void wait_groups_after(int r) {
 }
 
 template <int BITS, int GQ>
-__device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *pipe) {
+__device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *pipe,
+                             uint4 *q_lds) {
     using PP = Pipe<BITS>;
     constexpr int DPL = 2 * BITS;              // code dwords per lane
     const int l = threadIdx.x & 63;
@@ -621,6 +638,23 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     // q pair m divided by 2^kScaleLog2(m): it meets key codes read in place
     h2 qB[4][4];
     load_q_operand(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
+    // Unscaled fp16 q of the GQ heads staged in LDS (16 bytes per lane, head
+    // (l/16) % GQ, channels 8*(l%16)..+7): B operand of the key-zero product.
+    {
+        const int64_t qoff = ((int64_t)b * a.q_heads + hk * GQ + (l >> 4) % GQ) * D + 8 * (l & 15);
+        uint4 u;
+        if (a.q_is_f32) {
+            const float *qf = (const float *)a.q + qoff;
+            const float4 x0 = *(const float4 *)qf, x1 = *(const float4 *)(qf + 4);
+            h2 t0 = {(_Float16)x0.x, (_Float16)x0.y}, t1 = {(_Float16)x0.z, (_Float16)x0.w};
+            h2 t2 = {(_Float16)x1.x, (_Float16)x1.y}, t3 = {(_Float16)x1.z, (_Float16)x1.w};
+            u.x = __builtin_bit_cast(uint32_t, t0); u.y = __builtin_bit_cast(uint32_t, t1);
+            u.z = __builtin_bit_cast(uint32_t, t2); u.w = __builtin_bit_cast(uint32_t, t3);
+        } else {
+            u = *(const uint4 *)((const _Float16 *)a.q + qoff);
+        }
+        q_lds[l] = u;
+    }
 #pragma unroll
     for (int m = 0; m < 4; m++) {
         const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
@@ -669,19 +703,16 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
         // side data as 16-byte units: kscale 0..15, kzero 16..31, vscale
         // 32..47, vzero 48..63 (channel c at byte 2c of its array, value token
         // t of channel group cg at byte 2(32cg + t)).
-        float kbm[4] = {0.f, 0.f, 0.f, 0.f};
+        // key-zero bias sum_c q[c] kzero[c] on the matrix core: A = kzero of
+        // the lane's channels (the same for every token row), B = unscaled q;
+        // every row of Sk then holds the bias of its column's head.
+        f4 Sk = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            h2 kz[4];
-            split4(side[16 + 4 * s + Gl], kz);
-#pragma unroll
-            for (int m = 0; m < 4; m++) kbm[m] = __builtin_amdgcn_fdot2(qB[s][m], kz[m], kbm[m], false);
-        }
-        float kb = kbm[0];
-#pragma unroll
-        for (int m = 1; m < 4; m++) kb = __builtin_fmaf(kbm[m], (float)(1 << kScaleLog2<BITS>(m)), kb);
-        kb = xsum_rows(kb) * kTwoM24;
-        f4 S0 = (f4){kb, kb, kb, kb}, S1 = S0;
+        for (int s = 0; s < 4; s++)
+            Sk = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(h8, side[16 + 4 * s + Gl]),
+                __builtin_bit_cast(h8, q_lds[16 * (j % GQ) + 4 * s + Gl]), Sk, 0, 0, 0);
+        f4 S0 = (f4){0.f, 0.f, 0.f, 0.f}, S1 = S0;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             // q * kscale carried as an fp16 pair hi + lo, lo = fma(q, kscale,
@@ -701,7 +732,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
             S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1, 0, 0, 0);
         }
         h2 P[4];
-        softmax_step<BITS>(S0, S1, cs, m_run, nm, l_run, vb, accV, P);
+        softmax_step<BITS>(S0, S1, cs, Sk[0] * a.sm_log2, m_run, nm, l_run, vb, accV, P);
         h2 vs[4], vz[4], ps[4];
         {
             const uint2 *s2 = (const uint2 *)side;
@@ -733,6 +764,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
 template <int BITS, int GQ>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t pipe[Pipe<BITS>::NST * Pipe<BITS>::BB];
+    __shared__ uint4 q_lds[64];
     const int64_t item = blockIdx.x;
     const int streams = a.batch * a.kv_heads;
     if (item < streams) {
@@ -741,7 +773,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         return;
     }
     const int64_t it = item - streams;
-    decode_split<BITS, GQ>(a, (int)(it / a.splits), (int)(it % a.splits), pipe);
+    decode_split<BITS, GQ>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
 }
 
 // Merge the partials of one (batch, query head).  The split weights
