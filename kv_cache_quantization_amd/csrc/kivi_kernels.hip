@@ -39,194 +39,425 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int D = kHeadDim;
 constexpr int G = kGroup;
 
+// Four fp16 pairs from 16 loaded bytes.
+__device__ __forceinline__ void split4(u32x4 u, h2 *v) {
+    v[0] = __builtin_bit_cast(h2, u.x);
+    v[1] = __builtin_bit_cast(h2, u.y);
+    v[2] = __builtin_bit_cast(h2, u.z);
+    v[3] = __builtin_bit_cast(h2, u.w);
+}
+
+__device__ __forceinline__ void split4(uint4 u, h2 *v) {
+    v[0] = __builtin_bit_cast(h2, u.x);
+    v[1] = __builtin_bit_cast(h2, u.y);
+    v[2] = __builtin_bit_cast(h2, u.z);
+    v[3] = __builtin_bit_cast(h2, u.w);
+}
+
 // ===========================================================================
-// Quantization: one wavefront per (stream, token group, K-or-V).
+// Cross-lane exchanges with gfx950's v_permlane32_swap (exchange the two
+// 32-lane halves of a pair of registers) and v_permlane16_swap (exchange odd
+// and even 16-lane rows): vector-ALU moves, no LDS round trip.  s_nop 1
+// covers the VALU-write -> permlane-read hazard.
+// ===========================================================================
+__device__ __forceinline__ void swap_halves(float &a, float &b) {
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows(float &a, float &b) {
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// ===========================================================================
+// Quantization: one wavefront per (stream, token group, K-or-V) task.
+//
+// Load layout.  Lane l = 16q + c holds the 16-byte channel chunk c
+// (channels 8c .. 8c+7) of eight rows of the 32-token tile:
+//   keys    row 4j + q                 (j = 0..7)
+//   values  row 4q + j%4 + 16*(j/4)    (j = 0..7)
+// A key group (one channel over the 32 tokens) then spans lanes c, c+16,
+// c+32, c+48 and a value group (one token over 32 channels) the four lanes of
+// a quad.  Eight codes that land in the same matrix-core operand (a "unit":
+// the 8 channels of one key row, or one value channel over the lane's 8 rows)
+// are computed by one lane, so the move into packed order (through LDS) is
+// one 16- or 32-bit unit per operand instead of one byte per code.
+//
+// Codes.  The quantiser's code is round-half-even of RN(d / s) with
+// d = RN(x - zero).  The kernel forms t = RN(x * y + RN(-zero * y)) with one
+// FMA, y = v_rcp_f32(s) (within 1 ulp of 1/s).  For t <= 16 that is within
+// 5 * 2^-20 + 2^-24 * |zero * y| of RN(d / s), so both round to the same
+// integer unless t lies within (four times) that distance of a
+// half-integer.  A unit with such an element, or with a scale outside
+// [2^-126, inf), is recomputed with the IEEE subtract and divide.  The scale itself, RN((max - min) / L), is computed as
+// q0 = RN(rng * RN(1/L)) corrected by one FMA residual step, which equals the
+// IEEE quotient for L = 3 and L = 15 and every positive finite rng (checked
+// exhaustively against IEEE division on the CPU).
 // ===========================================================================
 
-// Row t of a stream: from the ring if it was appended earlier, else from the
-// new chunk.
+// Rows of the tile [t0, t0 + 32) of one stream: row r is token t0 + r, read
+// from ring slot (t0 + r) % ring_cap if it was appended earlier (t < n_old),
+// else from row t - n_old of the new chunk.  ring_cap >= 32, so the slot
+// wraps at most once inside a tile.
 template <typename T>
-__device__ __forceinline__ const T *source_row(const QuantizeArgs &a, const void *ring,
-                                               const void *in, int64_t stream, int64_t t) {
-    if (t < a.n_old)
-        return (const T *)ring + (stream * a.ring_cap + t % a.ring_cap) * D;
-    return (const T *)in + (stream * a.n_new + (t - a.n_old)) * D;
-}
-
-__device__ __forceinline__ void load8(const _Float16 *p, float *x) {
-    uint4 u = *(const uint4 *)p;
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        h2 v = __builtin_bit_cast(h2, w[e]);
-        x[2 * e] = (float)v[0];
-        x[2 * e + 1] = (float)v[1];
+struct RowSource {
+    const T *in;        // chunk row of token t0 (may be "negative" if t0 < n_old)
+    const T *ring;      // ring base of the stream
+    int n_from_ring;    // rows r < n_from_ring come from the ring (0..32)
+    int slot0, cap;
+    __device__ __forceinline__ RowSource(const QuantizeArgs &a, const void *ring_, const void *in_,
+                                         int64_t stream, int64_t t0) {
+        const int64_t old = a.n_old - t0;
+        n_from_ring = old <= 0 ? 0 : (old >= G ? G : (int)old);
+        in = (const T *)in_ + (stream * a.n_new + (t0 - a.n_old)) * D;
+        ring = (const T *)ring_ + stream * a.ring_cap * D;
+        cap = (int)a.ring_cap;
+        slot0 = n_from_ring ? (int)(t0 % a.ring_cap) : 0;
     }
-}
-
-__device__ __forceinline__ void load8(const float *p, float *x) {
-    float4 u0 = *(const float4 *)p, u1 = *(const float4 *)(p + 4);
-    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-}
-
-__device__ __forceinline__ float xmin(float v, int m) { return fminf(v, __shfl_xor(v, m)); }
-__device__ __forceinline__ float xmax(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
-
-// Code of one element: IEEE float32 subtract and divide, round half to even,
-// clamp -- exactly the quantiser's formula, no reassociation.
-__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float L) {
-    float d = x - mn;
-    float t = d / s;
-    float c = __builtin_rintf(t);
-    c = fminf(fmaxf(c, 0.0f), L);
-    return (uint32_t)c;
-}
-
-__device__ __forceinline__ void group_params(float mn, float mx, float L, float &mn_out,
-                                             float &s_out) {
-    if (mn == 0.0f) mn = 0.0f;      // a zero minimum is +0 whatever the sign
-    float s = (mx - mn) / L;
-    if (s == 0.0f) s = 1.0f;        // constant group
-    mn_out = mn;
-    s_out = s;
-}
-
-constexpr int kLdsRow = 136;        // 128 code bytes + 8 pad (fewer bank conflicts)
-
-template <int BITS, typename T>
-__global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
-    __shared__ uint8_t codes_lds[G * kLdsRow];
-    const int l = threadIdx.x;
-    const int64_t ngr = a.group_end - a.group_begin;
-    const int64_t task = blockIdx.x;
-    const int is_v = (int)(task & 1);
-    const int64_t rest = task >> 1;
-    const int64_t stream = rest / ngr;
-    const int64_t g = a.group_begin + rest % ngr;
-    const float L = (float)((1 << BITS) - 1);
-
-    // Load the 32 x 128 tile: load i covers rows 4i..4i+3; lane l holds row
-    // 4i + l/16, channels 8*(l%16) .. +7.
-    const void *ring = is_v ? a.ring_v : a.ring_k;
-    const void *in = is_v ? a.in_v : a.in_k;
-    const int rsub = l >> 4;
-    const int c0 = 8 * (l & 15);
-    float x[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const T *row = source_row<T>(a, ring, in, stream, g * G + 4 * i + rsub);
-        load8(row + c0, x[i]);
+    __device__ __forceinline__ const T *row(int r) const {
+        int slot = slot0 + r;
+        slot = slot >= cap ? slot - cap : slot;
+        return r < n_from_ring ? ring + slot * D : in + r * D;
     }
+};
 
-    uint8_t *blk = a.blocks + (stream * a.max_groups + g) * a.block_bytes;
-    const int cbytes = BITS * G * D / 8;
-    _Float16 *side = (_Float16 *)(blk + 2 * cbytes);   // kscale, kzero, vscale, vzero
+template <bool IS_V>
+__device__ __forceinline__ int tile_row(int j, int q) {
+    return IS_V ? 4 * q + (j & 3) + 16 * (j >> 2) : 4 * j + q;
+}
 
-    uint32_t code8[8][2];   // per row i: 8 codes as bytes (two dwords)
-    if (!is_v) {
-        // keys: group = one channel over the 32 rows
-        float mn[8], s[8];
+// The lane's 8 rows x 8 channels, as loaded.
+template <typename T> struct Tile;
+template <> struct Tile<_Float16> {
+    h2 v[8][4];
+    __device__ __forceinline__ float at(int j, int e) const { return (float)v[j][e >> 1][e & 1]; }
+    // x * y + c with one rounding (v_fma_mix_f32 takes the fp16 x directly)
+    __device__ __forceinline__ float fma(int j, int e, float y, float c) const {
+        return __builtin_fmaf((float)v[j][e >> 1][e & 1], y, c);
+    }
+};
+template <> struct Tile<float> {
+    float v[8][8];
+    __device__ __forceinline__ float at(int j, int e) const { return v[j][e]; }
+    __device__ __forceinline__ float fma(int j, int e, float y, float c) const {
+        return __builtin_fmaf(v[j][e], y, c);
+    }
+};
+
+__device__ __forceinline__ void load_row(Tile<_Float16> &t, int j, const _Float16 *p) {
+    split4(*(const uint4 *)p, t.v[j]);
+}
+__device__ __forceinline__ void load_row(Tile<float> &t, int j, const float *p) {
+    const float4 u0 = *(const float4 *)p, u1 = *(const float4 *)(p + 4);
+    t.v[j][0] = u0.x; t.v[j][1] = u0.y; t.v[j][2] = u0.z; t.v[j][3] = u0.w;
+    t.v[j][4] = u1.x; t.v[j][5] = u1.y; t.v[j][6] = u1.z; t.v[j][7] = u1.w;
+}
+
+// IEEE 754-2019 minimum / maximum (NaN-propagating, -0 < +0): no input
+// quieting needed, and gfx950 has three-input packed forms.
+__device__ __forceinline__ h2 hmin(h2 a, h2 b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ h2 hmax(h2 a, h2 b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float fmin_(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ float fmax_(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+template <typename V>
+__device__ __forceinline__ float as_f(V v) { return __builtin_bit_cast(float, v); }
+template <typename V>
+__device__ __forceinline__ V from_f(float f) { return __builtin_bit_cast(V, f); }
+
+// Min / max over the four lanes c, c+16, c+32, c+48 (all lanes get the result).
+template <bool MAX, typename V>
+__device__ __forceinline__ V reduce_q(V v) {
+    float a = as_f(v), b = a;
+    swap_halves(a, b);
+    V m = MAX ? __builtin_elementwise_maximum(from_f<V>(a), from_f<V>(b))
+              : __builtin_elementwise_minimum(from_f<V>(a), from_f<V>(b));
+    float c = as_f(m), d = c;
+    swap_rows(c, d);
+    return MAX ? __builtin_elementwise_maximum(from_f<V>(c), from_f<V>(d))
+               : __builtin_elementwise_minimum(from_f<V>(c), from_f<V>(d));
+}
+
+// Min / max over the four lanes of a quad (DPP quad permutations).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, true));
+}
+template <bool MAX, typename V>
+__device__ __forceinline__ V reduce_quad(V v) {
+    V o = from_f<V>(dpp<0xB1>(as_f(v)));          // lanes [1,0,3,2]
+    v = MAX ? __builtin_elementwise_maximum(v, o) : __builtin_elementwise_minimum(v, o);
+    o = from_f<V>(dpp<0x4E>(as_f(v)));            // lanes [2,3,0,1]
+    return MAX ? __builtin_elementwise_maximum(v, o) : __builtin_elementwise_minimum(v, o);
+}
+
+// Per-group minimum and maximum for the lane's 8 groups (k = 0..7: channel
+// 8c + k for keys, row j = k for values).
+template <bool IS_V>
+__device__ __forceinline__ void group_minmax(const Tile<_Float16> &t, float (&lo)[8],
+                                             float (&hi)[8]) {
+    if (!IS_V) {
+        h2 mn[4], mx[4];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            float lo = x[0][e], hi = x[0][e];
+        for (int p = 0; p < 4; p++) mn[p] = mx[p] = t.v[0][p];
 #pragma unroll
-            for (int i = 1; i < 8; i++) { lo = fminf(lo, x[i][e]); hi = fmaxf(hi, x[i][e]); }
-            lo = xmin(xmin(lo, 16), 32);
-            hi = xmax(xmax(hi, 16), 32);
-            group_params(lo, hi, L, mn[e], s[e]);
-        }
-        if (l < 16) {
+        for (int j = 1; j < 8; j++)
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                side[c0 + e] = (_Float16)s[e];
-                side[D + c0 + e] = (_Float16)mn[e];
-            }
-        }
+            for (int p = 0; p < 4; p++) { mn[p] = hmin(mn[p], t.v[j][p]); mx[p] = hmax(mx[p], t.v[j][p]); }
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int e = 0; e < 4; e++) lo |= quant_code(x[i][e], mn[e], s[e], L) << (8 * e);
-#pragma unroll
-            for (int e = 0; e < 4; e++) hi |= quant_code(x[i][4 + e], mn[4 + e], s[4 + e], L) << (8 * e);
-            code8[i][0] = lo;
-            code8[i][1] = hi;
+        for (int p = 0; p < 4; p++) {
+            mn[p] = reduce_q<false>(mn[p]);
+            mx[p] = reduce_q<true>(mx[p]);
+            lo[2 * p] = (float)mn[p][0]; lo[2 * p + 1] = (float)mn[p][1];
+            hi[2 * p] = (float)mx[p][0]; hi[2 * p + 1] = (float)mx[p][1];
         }
     } else {
-        // values: group = one row over 32 channels (4 lanes of a quad)
-        const int cg = (l & 15) >> 2;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            float lo = x[i][0], hi = x[i][0];
+        for (int jp = 0; jp < 4; jp++) {
+            h2 a[2], b[2];
 #pragma unroll
-            for (int e = 1; e < 8; e++) { lo = fminf(lo, x[i][e]); hi = fmaxf(hi, x[i][e]); }
-            lo = xmin(xmin(lo, 1), 2);
-            hi = xmax(xmax(hi, 1), 2);
-            float mn, s;
-            group_params(lo, hi, L, mn, s);
-            if ((l & 3) == 0) {
-                const int r = 4 * i + rsub;
-                side[2 * D + cg * G + r] = (_Float16)s;
-                side[3 * D + cg * G + r] = (_Float16)mn;
+            for (int s = 0; s < 2; s++) {
+                const h2 *r = t.v[2 * jp + s];
+                a[s] = hmin(hmin(r[0], r[1]), hmin(r[2], r[3]));
+                b[s] = hmax(hmax(r[0], r[1]), hmax(r[2], r[3]));
             }
-            uint32_t c_lo = 0, c_hi = 0;
+            // (row 2jp, row 2jp+1) pairs
+            h2 mn = hmin((h2){a[0][0], a[1][0]}, (h2){a[0][1], a[1][1]});
+            h2 mx = hmax((h2){b[0][0], b[1][0]}, (h2){b[0][1], b[1][1]});
+            mn = reduce_quad<false>(mn);
+            mx = reduce_quad<true>(mx);
+            lo[2 * jp] = (float)mn[0]; lo[2 * jp + 1] = (float)mn[1];
+            hi[2 * jp] = (float)mx[0]; hi[2 * jp + 1] = (float)mx[1];
+        }
+    }
+}
+
+template <bool IS_V>
+__device__ __forceinline__ void group_minmax(const Tile<float> &t, float (&lo)[8],
+                                             float (&hi)[8]) {
+    if (!IS_V) {
 #pragma unroll
-            for (int e = 0; e < 4; e++) c_lo |= quant_code(x[i][e], mn, s, L) << (8 * e);
+        for (int e = 0; e < 8; e++) {
+            float mn = t.v[0][e], mx = t.v[0][e];
 #pragma unroll
-            for (int e = 0; e < 4; e++) c_hi |= quant_code(x[i][4 + e], mn, s, L) << (8 * e);
-            code8[i][0] = c_lo;
-            code8[i][1] = c_hi;
+            for (int j = 1; j < 8; j++) { mn = fmin_(mn, t.v[j][e]); mx = fmax_(mx, t.v[j][e]); }
+            lo[e] = reduce_q<false>(mn);
+            hi[e] = reduce_q<true>(mx);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            float mn = t.v[j][0], mx = t.v[j][0];
+#pragma unroll
+            for (int e = 1; e < 8; e++) { mn = fmin_(mn, t.v[j][e]); mx = fmax_(mx, t.v[j][e]); }
+            lo[j] = reduce_quad<false>(mn);
+            hi[j] = reduce_quad<true>(mx);
+        }
+    }
+}
+
+// zero = min (+0 for a zero minimum), scale = RN((max - zero) / L), or 1 for a
+// constant group.  RN(x / L) = fma(fma(-q0, L, x), RN(1/L), q0) with
+// q0 = RN(x * RN(1/L)) for every positive finite x (L = 3, 15); +inf and NaN
+// ranges take q0, which is then the quotient itself.
+template <int BITS>
+__device__ __forceinline__ void group_params(float lo, float hi, float &mn, float &s) {
+#pragma clang fp contract(off)
+    constexpr float L = (float)((1 << BITS) - 1);
+    constexpr float yL = 1.0f / L;
+    mn = lo == 0.0f ? 0.0f : lo;
+    const float rng = hi - mn;
+    const float q0 = rng * yL;
+    const float r = __builtin_fmaf(-q0, L, rng);
+    float sv = __builtin_fmaf(r, yL, q0);
+    sv = sv == sv ? sv : q0;
+    s = sv == 0.0f ? 1.0f : sv;
+}
+
+// Exact code: IEEE subtract and divide, round half to even, clamp.
+__device__ __forceinline__ float exact_code(float x, float mn, float s, float L) {
+#pragma clang fp contract(off)
+    const float d = x - mn;
+    const float t = d / s;
+    return fminf(fmaxf(__builtin_rintf(t), 0.0f), L);
+}
+
+// Packed position of code kk (0..7) inside its unit: at 2 bits a 16-bit unit
+// with even kk in the low byte and odd kk in the high byte, two bits apart;
+// at 4 bits a 32-bit unit with even kk in the low half, odd in the high half,
+// four bits apart (accumulated as two 16-bit halves).
+template <int BITS>
+__device__ __forceinline__ constexpr float unit_weight(int kk) {
+    return BITS == 2 ? (float)(1u << (8 * (kk & 1) + 2 * (kk >> 1)))
+                     : (float)(1u << (4 * (kk >> 1)));
+}
+
+// Two floats as an fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, (h2){(_Float16)a, (_Float16)b});
+}
+
+template <int BITS, bool IS_V, bool RING, typename T>
+__device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t stream, int64_t g,
+                                              uint32_t *tr) {
+#pragma clang fp contract(off)
+    constexpr float L = (float)((1 << BITS) - 1);
+    const int l = threadIdx.x;
+    const int q = l >> 4, c = l & 15;
+
+    Tile<T> t;
+    {
+        const RowSource<T> src(a, IS_V ? a.ring_v : a.ring_k, IS_V ? a.in_v : a.in_k, stream, g * G);
+        if (!RING) {
+            const T *base = src.in + 8 * c;
+#pragma unroll
+            for (int j = 0; j < 8; j++) load_row(t, j, base + tile_row<IS_V>(j, q) * D);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++) load_row(t, j, src.row(tile_row<IS_V>(j, q)) + 8 * c);
         }
     }
 
-    // Redistribute codes (one byte each) through LDS into the packed order.
+    float lo[8], hi[8];
+    group_minmax<IS_V>(t, lo, hi);
+    float mn[8], s[8], y[8], cz[8];
+    float smin = INFINITY, smax = 0.0f, czmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        uint2 v = {code8[i][0], code8[i][1]};
-        *(uint2 *)&codes_lds[(4 * i + rsub) * kLdsRow + c0] = v;
+    for (int k = 0; k < 8; k++) {
+        group_params<BITS>(lo[k], hi[k], mn[k], s[k]);
+        y[k] = __builtin_amdgcn_rcpf(s[k]);
+        cz[k] = -mn[k] * y[k];
+        smin = fminf(smin, s[k]);
+        smax = fmaxf(smax, s[k]);
+        czmax = fmaxf(czmax, fabsf(cz[k]));
+    }
+    // Scales outside [2^-126, inf) and NaN (fails both) take the exact path.
+    const bool fast_ok = smin >= 0x1p-126f && smax < INFINITY;
+    // t = RN(x * y + RN(-zero * y)) is within 5 * 2^-20 + 2^-24 * |zero * y|
+    // of RN(RN(x - zero) / s) for t <= 16; the margin below is 4x that.
+    const float near_tie = 0.5f - (0x1p-16f + 0x1p-22f * czmax);
+
+    uint8_t *blk = a.blocks + (stream * a.max_groups + g) * a.block_bytes;
+    constexpr int cbytes = BITS * G * D / 8;
+    _Float16 *side = (_Float16 *)(blk + 2 * cbytes);   // kscale, kzero, vscale, vzero
+
+    // zero / scale as fp16
+    if (!IS_V) {
+        // channels 8c..8c+7: lanes q = 0 store the scales, q = 1 the zeros.
+        if (q < 2) {
+            uint32_t w[4];
+#pragma unroll
+            for (int p = 0; p < 4; p++)
+                w[p] = q == 0 ? pack_f16(s[2 * p], s[2 * p + 1]) : pack_f16(mn[2 * p], mn[2 * p + 1]);
+            *(uint4 *)(side + q * D + 8 * c) = (uint4){w[0], w[1], w[2], w[3]};
+        }
+    } else {
+        // rows 4q..4q+3 (j < 4) and 16+4q.. (j >= 4) of value group c/4; the
+        // four lanes of the quad store scale-low, scale-high, zero-low, zero-high.
+        const int part = c & 3, jh = part & 1;
+        // (selects on named values: an index into s[] / mn[] that depends on
+        // the lane would move those arrays out of registers)
+        const uint32_t s01 = pack_f16(s[0], s[1]), s23 = pack_f16(s[2], s[3]);
+        const uint32_t s45 = pack_f16(s[4], s[5]), s67 = pack_f16(s[6], s[7]);
+        const uint32_t z01 = pack_f16(mn[0], mn[1]), z23 = pack_f16(mn[2], mn[3]);
+        const uint32_t z45 = pack_f16(mn[4], mn[5]), z67 = pack_f16(mn[6], mn[7]);
+        const uint32_t w0 = part == 0 ? s01 : part == 1 ? s45 : part == 2 ? z01 : z45;
+        const uint32_t w1 = part == 0 ? s23 : part == 1 ? s67 : part == 2 ? z23 : z67;
+        *(uint2 *)(side + (2 + (part >> 1)) * D + (c >> 2) * G + 16 * jh + 4 * q) = (uint2){w0, w1};
+    }
+
+    // Units u = 0..7 (key row j = u over channels kk; value channel e = u over
+    // rows kk), parameters indexed by kk for keys and values alike.
+    uint32_t unit[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+        float acc0 = 0.0f, acc1 = 0.0f, rmax = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++) {
+            const float tq = IS_V ? t.fma(kk, u, y[kk], cz[kk]) : t.fma(u, kk, y[kk], cz[kk]);
+            const float cd = __builtin_rintf(tq);
+            rmax = fmaxf(rmax, fabsf(tq - cd));
+            if (kk < (BITS == 4 ? 2 : 1)) (kk ? acc1 : acc0) = cd;   // weight 1
+            else if (BITS == 4 && (kk & 1)) acc1 = __builtin_fmaf(cd, unit_weight<BITS>(kk), acc1);
+            else acc0 = __builtin_fmaf(cd, unit_weight<BITS>(kk), acc0);
+        }
+        if (!(rmax < near_tie) || !fast_ok) {
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++) {
+                const float x = IS_V ? t.at(kk, u) : t.at(u, kk);
+                const float cd = exact_code(x, mn[kk], s[kk], L);
+                if (kk < (BITS == 4 ? 2 : 1)) (kk ? acc1 : acc0) = cd;
+                else if (BITS == 4 && (kk & 1)) acc1 = __builtin_fmaf(cd, unit_weight<BITS>(kk), acc1);
+                else acc0 = __builtin_fmaf(cd, unit_weight<BITS>(kk), acc0);
+            }
+        }
+        unit[u] = BITS == 2 ? (uint32_t)acc0 : ((uint32_t)acc0 | ((uint32_t)acc1 << 16));
+    }
+
+    // Into packed order through LDS.  Target lane L keeps 4 (2-bit) or 8
+    // (4-bit) dwords; the unit of its operand o sits in unit slot
+    // 2*(o%4) + o/4 (16-bit slots at 2 bits, 32-bit slots at 4 bits).
+    constexpr int DPL = 2 * BITS;
+    if (!IS_V) {
+        // key unit (row j = 4*jj + q, chunk c) -> lane (row%16) + 16*(c%4),
+        // operand 4*(row/16) + c/4; rows j and j+4 share the target lane.
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int L_ = 4 * jj + q + 16 * (c & 3);
+            if (BITS == 2)
+                tr[L_ * DPL + (c >> 2)] = unit[jj] | (unit[jj + 4] << 16);
+            else
+                *(uint2 *)&tr[L_ * DPL + 2 * (c >> 2)] = (uint2){unit[jj], unit[jj + 4]};
+        }
+    } else {
+        // value unit (channel 8c + e over the lane's rows) -> lane
+        // 8*(c%2) + e + 16q, operand c/2.
+        const int o = c >> 1;
+        const int slot = 2 * (o & 3) + (o >> 2);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const int L_ = 8 * (c & 1) + e + 16 * q;
+            if (BITS == 2)
+                ((uint16_t *)tr)[L_ * 2 * DPL + slot] = (uint16_t)unit[e];
+            else
+                tr[L_ * DPL + slot] = unit[e];
+        }
     }
     __syncthreads();
 
-    constexpr int DPL = 2 * BITS;          // dwords per lane
-    constexpr int OPD = 4 / BITS;          // operands per dword
     uint32_t outw[DPL];
+    if (BITS == 2) {
+        const uint4 d4 = *(const uint4 *)&tr[l * DPL];
+        outw[0] = __builtin_amdgcn_perm(d4.y, d4.x, 0x05010400u);
+        outw[1] = __builtin_amdgcn_perm(d4.w, d4.z, 0x05010400u);
+        outw[2] = __builtin_amdgcn_perm(d4.y, d4.x, 0x07030602u);
+        outw[3] = __builtin_amdgcn_perm(d4.w, d4.z, 0x07030602u);
+    } else {
+        const uint4 e0 = *(const uint4 *)&tr[l * DPL], e1 = *(const uint4 *)&tr[l * DPL + 4];
+        const uint32_t ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
-    for (int w = 0; w < DPL; w++) outw[w] = 0;
-#pragma unroll
-    for (int o = 0; o < 8; o++) {
-        uint32_t cb[8];
-        if (!is_v) {
-            const int tok = 16 * (o >> 2) + (l & 15);
-            const int ch = 32 * (o & 3) + 8 * (l >> 4);
-            uint2 v = *(const uint2 *)&codes_lds[tok * kLdsRow + ch];
-#pragma unroll
-            for (int kk = 0; kk < 4; kk++) {
-                cb[kk] = (v.x >> (8 * kk)) & 0xFF;
-                cb[4 + kk] = (v.y >> (8 * kk)) & 0xFF;
-            }
-        } else {
-            const int ch = 16 * o + (l & 15);
-#pragma unroll
-            for (int kk = 0; kk < 8; kk++) {
-                const int tok = 4 * (l >> 4) + (kk & 3) + 16 * (kk >> 2);
-                cb[kk] = codes_lds[tok * kLdsRow + ch];
-            }
-        }
-        const int w = o / OPD;
-        const int base = BITS * 4 * (o % OPD);
-#pragma unroll
-        for (int kk = 0; kk < 8; kk++)
-            outw[w] |= cb[kk] << (16 * (kk & 1) + base + BITS * (kk >> 1));
+        for (int o = 0; o < 8; o++) outw[o] = ev[2 * (o & 3) + (o >> 2)];
     }
-    uint32_t *dst = (uint32_t *)(blk + (is_v ? cbytes : 0));
+    uint32_t *dst = (uint32_t *)(blk + (IS_V ? cbytes : 0));
 #pragma unroll
-    for (int w4 = 0; w4 < DPL / 4; w4++) {
-        uint4 v = {outw[4 * w4], outw[4 * w4 + 1], outw[4 * w4 + 2], outw[4 * w4 + 3]};
-        *(uint4 *)&dst[w4 * 256 + 4 * l] = v;
-    }
+    for (int w4 = 0; w4 < DPL / 4; w4++)
+        *(uint4 *)&dst[w4 * 256 + 4 * l] =
+            (uint4){outw[4 * w4], outw[4 * w4 + 1], outw[4 * w4 + 2], outw[4 * w4 + 3]};
 }
 
+// RING: the groups [group_begin, group_end) hold tokens appended earlier
+// (read, at least in part, from the ring); otherwise every row comes from
+// the new chunk.
+template <int BITS, typename T, bool RING>
+__global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
+    __shared__ uint32_t tr[64 * 2 * BITS];
+    const uint32_t ngr = (uint32_t)(a.group_end - a.group_begin);
+    const uint32_t task = blockIdx.x;
+    const uint32_t rest = task >> 1;
+    const int64_t stream = rest / ngr;
+    const int64_t g = a.group_begin + rest % ngr;
+    if (task & 1) quantize_task<BITS, true, RING, T>(a, stream, g, tr);
+    else quantize_task<BITS, false, RING, T>(a, stream, g, tr);
+}
 // ===========================================================================
 // Residual ring append: copy rows [tok_begin, tok_end) of the chunk into
 // ring slot t % ring_cap.  16 bytes per thread.
@@ -281,16 +512,7 @@ __global__ __launch_bounds__(256) void ring_append_kernel(RingArgs a) {
 // group is computed.
 // ===========================================================================
 
-// Reductions over the four 16-lane rows (lanes j, j+16, j+32, j+48) with
-// gfx950's v_permlane32_swap (exchange the two 32-lane halves) and
-// v_permlane16_swap (exchange odd and even rows): vector-ALU moves, no LDS
-// round trip.  s_nop 1 covers the VALU-write -> permlane-read hazard.
-__device__ __forceinline__ void swap_halves(float &a, float &b) {
-    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap_rows(float &a, float &b) {
-    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
+// Reductions over the four 16-lane rows (lanes j, j+16, j+32, j+48).
 __device__ __forceinline__ float xsum_rows(float v) {
     float a = v, b = v;
     swap_halves(a, b);
@@ -346,20 +568,6 @@ __device__ __forceinline__ h8 pack_h8(const h2 *v) {
 #pragma unroll
     for (int m = 0; m < 4; m++) { r[2 * m] = v[m][0]; r[2 * m + 1] = v[m][1]; }
     return r;
-}
-
-__device__ __forceinline__ void split4(u32x4 u, h2 *v) {
-    v[0] = __builtin_bit_cast(h2, u.x);
-    v[1] = __builtin_bit_cast(h2, u.y);
-    v[2] = __builtin_bit_cast(h2, u.z);
-    v[3] = __builtin_bit_cast(h2, u.w);
-}
-
-__device__ __forceinline__ void split4(uint4 u, h2 *v) {
-    v[0] = __builtin_bit_cast(h2, u.x);
-    v[1] = __builtin_bit_cast(h2, u.y);
-    v[2] = __builtin_bit_cast(h2, u.z);
-    v[3] = __builtin_bit_cast(h2, u.w);
 }
 
 __device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t idx) {
@@ -828,18 +1036,32 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
 // ===========================================================================
 // Launchers
 // ===========================================================================
-hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
-    const int64_t tasks = (int64_t)a.streams * (a.group_end - a.group_begin) * 2;
-    if (tasks <= 0) return hipSuccess;
-    dim3 grid((unsigned)tasks), block(64);
-    if (a.bits == 2) {
-        if (a.is_f32) hipLaunchKernelGGL((quantize_kernel<2, float>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((quantize_kernel<2, _Float16>), grid, block, 0, s, a);
-    } else {
-        if (a.is_f32) hipLaunchKernelGGL((quantize_kernel<4, float>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((quantize_kernel<4, _Float16>), grid, block, 0, s, a);
+template <int BITS, typename T>
+static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
+    // Groups that start before n_old read rows from the ring.
+    const int64_t ring_groups_end = (a.n_old + G - 1) / G;
+    int64_t split = ring_groups_end < a.group_begin ? a.group_begin : ring_groups_end;
+    if (split > a.group_end) split = a.group_end;
+    if (split > a.group_begin) {
+        QuantizeArgs r = a;
+        r.group_end = split;
+        const int64_t tasks = (int64_t)a.streams * (split - a.group_begin) * 2;
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, true>), dim3((unsigned)tasks), dim3(64), 0, s, r);
+    }
+    if (a.group_end > split) {
+        QuantizeArgs n = a;
+        n.group_begin = split;
+        const int64_t tasks = (int64_t)a.streams * (a.group_end - split) * 2;
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, false>), dim3((unsigned)tasks), dim3(64), 0, s, n);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
+    if (a.group_end <= a.group_begin || a.streams <= 0) return hipSuccess;
+    if ((int64_t)a.streams * (a.group_end - a.group_begin) * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (a.bits == 2) return a.is_f32 ? launch_quantize_t<2, float>(a, s) : launch_quantize_t<2, _Float16>(a, s);
+    return a.is_f32 ? launch_quantize_t<4, float>(a, s) : launch_quantize_t<4, _Float16>(a, s);
 }
 
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {

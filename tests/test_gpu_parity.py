@@ -155,3 +155,59 @@ def test_error_statuses():
         kivi.kivi_decode_attn(cache.handle, q.data_ptr(), kivi.KIVI_F16, 0.0, q.data_ptr(),
                               ws.data_ptr(), 8, 0)
     assert e.value.status in (kivi.KIVI_ERR_STATE, kivi.KIVI_ERR_BUFFER_TOO_SMALL)
+
+
+def _tie_groups(rng, n_groups, bits, dtype):
+    """n_groups x 32 values per group, each group holding its exact minimum
+    and maximum and 30 values at, or a few units in the last place around,
+    the points zero + (k + 1/2) * scale where the quantiser's rounding
+    changes code.  Zero offsets range from 0 to 1000x the group's range."""
+    L = (1 << bits) - 1
+    out = np.empty((n_groups, 32), dtype=dtype)
+    for gi in range(n_groups):
+        kind = gi % 4
+        if kind == 0:
+            mn, span = 0.0, rng.uniform(0.5, 4.0)
+        elif kind == 1:
+            mn, span = rng.uniform(-3, 3), rng.uniform(0.01, 8.0)
+        elif kind == 2:
+            span = rng.uniform(0.05, 2.0)
+            mn = rng.choice([-1, 1]) * span * rng.uniform(50, 1000)
+        else:
+            mn, span = rng.uniform(-1, 1), float(L) * 2.0 ** rng.integers(-8, 3)
+        lo = dtype(mn)
+        hi = dtype(mn + span)
+        if not hi > lo:
+            hi = np.nextafter(lo, dtype(np.inf))
+        s = np.float32(np.float32(np.float32(hi) - np.float32(lo)) / np.float32(L))
+        g = np.empty(32, dtype=dtype)
+        g[0], g[1] = lo, hi
+        for i in range(2, 32):
+            k = rng.integers(0, L)
+            x = dtype(np.float64(lo) + (k + 0.5) * np.float64(s))
+            for _ in range(int(rng.integers(-2, 3))):
+                x = np.nextafter(x, dtype(np.inf))
+            for _ in range(int(rng.integers(0, 3))):
+                x = np.nextafter(x, dtype(-np.inf))
+            g[i] = min(max(x, lo), hi)
+        out[gi] = rng.permutation(g)
+    return out
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_near_ties(orc, bits, dtype):
+    """Values on and next to the rounding boundaries of every group, with
+    small and large zero offsets: the codes must still be bit-exact."""
+    rng = np.random.default_rng(11 + bits)
+    B, H, n, D = 1, 2, 256, 128
+    log("case near-ties bits=%d %s" % (bits, np.dtype(dtype).name))
+    kg = _tie_groups(rng, B * H * (n // 32) * D, bits, dtype)      # key groups: (tg, c) x 32 tokens
+    k = kg.reshape(B, H, n // 32, D, 32).transpose(0, 1, 2, 4, 3).reshape(B, H, n, D)
+    vg = _tie_groups(rng, B * H * n * (D // 32), bits, dtype)      # value groups: (t, cg) x 32 channels
+    v = vg.reshape(B, H, n, D)
+    k[0, 1, 64:96, :] = dtype(7.25)                                # constant key groups
+    v[0, 0, 32, :] = dtype(-0.0)                                   # constant value groups of -0
+    cache = new_cache(B, H, 4 * H, n, bits=bits, R=0, dtype=dtype)
+    cache.append(to_dev(k), to_dev(v))
+    check_cache(orc, cache, k, v, label="near-ties-%d" % bits)
