@@ -15,8 +15,16 @@ phase).
 
 Prints one JSON line; `value` is decode-attention GB/s of algorithmic bytes
 (packed codes + fp16 zero/scale + fp16 residual + q + out).
+
+Also measured in the same run: the bandwidth of a plain device copy (512 MiB
+read + 512 MiB written by one elementwise kernel), the second yardstick for
+"% of peak", and the kernel whose FETCH_SIZE / WRITE_SIZE counter readings
+calibrate the HBM-traffic figures.  `roofline.traffic` is taken from the
+committed counter summary for this workload only while the kernel sources
+still hash to the value recorded with it; otherwise it is null.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +34,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COPY_BYTES = 512 << 20          # per direction
+KERNEL_SOURCES = ("kv_cache_quantization_amd/csrc/kivi_kernels.hip",
+                  "kv_cache_quantization_amd/csrc/kivi_internal.h")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(name, key="traffic_bytes_per_launch"):
+    """HBM bytes per launch from a committed counter summary (profiles/name):
+    lines 'key: value'.  None unless its kernel_source_sha256 matches."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None, "kernel sources changed since the counters were taken"
+    return int(kv[key]), name
 
 
 def decode_bytes(B, H, Hq, n, Q, bits, D=128, G=32):
@@ -71,8 +107,8 @@ def cpu_baseline(k_dev, v_dev, q_dev, bits, R, H, Hq, sample_b):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--bits", type=int, default=2, choices=(2, 4))
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--context", type=int, default=32768)
@@ -110,6 +146,22 @@ def main():
     evict_out = torch.empty((), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    # Copy yardstick: one elementwise kernel reads COPY_BYTES and writes
+    # COPY_BYTES (torch.neg; a same-dtype copy_ would become a DMA blit).
+    csrc = evict[: COPY_BYTES // 4]
+    cdst = torch.empty_like(csrc)
+    copy_ms = []
+    for _ in range(4):
+        torch.amax(evict[COPY_BYTES // 4:], dim=0, out=evict_out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.neg(csrc, out=cdst)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    copy_gbps = 2 * COPY_BYTES / (sorted(copy_ms[1:])[1] / 1e3) / 1e9
+    del cdst
+
     def step(evs):
         cache.reset()
         if not args.no_evict:
@@ -135,8 +187,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    t_app = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps / 1e3
-    t_dec = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps / 1e3
+    app_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
+    dec_ms = sorted(e[2].elapsed_time(e[3]) for e in events)
+    t_app = sum(app_ms) / args.steps / 1e3
+    t_dec = sum(dec_ms) / args.steps / 1e3
     lo = cache.layout()
     Q = lo.n_quantized
     dbytes = decode_bytes(B, H, Hq, n, Q, bits)
@@ -144,6 +198,12 @@ def main():
     dec_gbps = dbytes / t_dec / 1e9
     app_gbps = abytes / t_app / 1e9
     splits, gps = cache.decode_plan()
+    traffic, traffic_src = (None, "workload without a counter summary")
+    atraffic = None
+    if (B, n, R, bits, chunk) == (16, 32768, 128, 2, 32768):
+        traffic, traffic_src = counter_traffic("decode_b16_ctx32768_2bit_counters.txt")
+        atraffic, _ = counter_traffic("decode_b16_ctx32768_2bit_counters.txt",
+                                      "append_traffic_bytes_per_launch")
 
     rec = {
         "metric": "decode-attn GB/s over packed 2-bit KV (% of HBM peak); quantize GB/s",
@@ -167,10 +227,16 @@ def main():
             "group": 32, "residual": R, "bits": bits, "quantized_tokens": Q,
             "decode_splits_per_stream": splits, "groups_per_split": gps,
         },
-        "decode": {"ms": round(t_dec * 1e3, 4), "GBps": round(dec_gbps, 1),
-                   "bytes": int(dbytes), "pct_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2)},
-        "quantize": {"ms": round(t_app * 1e3, 4), "GBps": round(app_gbps, 1),
-                     "bytes": int(abytes), "pct_hbm_peak": round(100 * app_gbps / HBM_PEAK_GBPS, 2)},
+        "decode": {"ms": round(t_dec * 1e3, 4), "median_ms": round(dec_ms[len(dec_ms) // 2], 4),
+                   "GBps": round(dec_gbps, 1), "bytes": int(dbytes),
+                   "pct_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
+                   "pct_copy": round(100 * dec_gbps / copy_gbps, 2)},
+        "quantize": {"ms": round(t_app * 1e3, 4), "median_ms": round(app_ms[len(app_ms) // 2], 4),
+                     "GBps": round(app_gbps, 1), "bytes": int(abytes),
+                     "pct_hbm_peak": round(100 * app_gbps / HBM_PEAK_GBPS, 2),
+                     "pct_copy": round(100 * app_gbps / copy_gbps, 2)},
+        "copy": {"GBps": round(copy_gbps, 1), "bytes": 2 * COPY_BYTES,
+                 "what": "torch.neg over 512 MiB fp32 (read 512 MiB + write 512 MiB), median of 3"},
         "roofline": {
             "bound": "hbm",
             "kernel": "decode (split-K pass + combine, one kivi_decode_attn call)",
@@ -178,12 +244,13 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_source": traffic_src,
         },
         "roofline_quantize": {
             "bound": "hbm", "kernel": "append (quantize + ring copy, one kivi_append call)",
             "achieved": round(app_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(app_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(app_gbps / HBM_PEAK_GBPS, 4), "traffic": atraffic,
         },
         "timing": "HIP events on the launch stream around each phase; mean over the timed steps;"
                   " 1 GiB eviction read before each phase (outside the phase events)"
