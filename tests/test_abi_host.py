@@ -1,0 +1,195 @@
+"""Host-side checks of libkivi's C ABI that need no GPU: the library loads,
+exports every function include/kivi.h declares, validates configurations,
+lays out the device buffer as documented, and plans appends by the window
+flush policy.  Nothing here launches a kernel (every call below returns
+before the library touches the HIP runtime)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from kv_cache_quantization_amd import kivi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kivi.h")
+FAKE_DEV = 1 << 20          # a 256-aligned address that is never dereferenced on the host
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kivi.LIB_PATH):
+        pytest.skip("libkivi.so not built")
+    return kivi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(L):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    assert sorted(kivi.EXPORTED) == names
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kivi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    dyn = set(re.findall(r"\sT\s+(kivi_\w+)$", out, flags=re.M))
+    assert set(names) <= dyn, set(names) - dyn
+    # only the declared C names are exported under the kivi_ prefix
+    assert dyn == set(names), dyn - set(names)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert kivi.kivi_status_string(s)
+    assert kivi.kivi_status_string(kivi.KIVI_OK) == "ok"
+    assert kivi.kivi_status_string(99) == "unknown status"
+
+
+BAD = [
+    (dict(bits=3), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(bits=8), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(residual=48), kivi.KIVI_ERR_INVALID_ARG),      # not a multiple of G
+    (dict(residual=-32), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(max_tokens=0), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(n_q_heads=12, n_kv_heads=8), kivi.KIVI_ERR_INVALID_ARG),   # Hq not a multiple of H
+    (dict(kv_dtype=7), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(policy=1), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(head_dim=64), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(group=64), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(n_q_heads=64, n_kv_heads=8), kivi.KIVI_ERR_UNSUPPORTED),   # GQA 8
+    (dict(n_q_heads=24, n_kv_heads=8), kivi.KIVI_ERR_UNSUPPORTED),   # GQA 3
+]
+
+
+@pytest.mark.parametrize("over,status", BAD)
+def test_invalid_configs(L, over, status):
+    args = dict(batch=2, n_kv_heads=8, n_q_heads=32, bits=2, residual=128, max_tokens=4096)
+    args.update(over)
+    cfg = kivi.make_config(**args)
+    if "reserved" in over:
+        cfg.reserved = over["reserved"]
+    assert kivi.kivi_cache_bytes(cfg) == 0
+    h = ctypes.c_void_p()
+    assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV, 1 << 40, ctypes.byref(h)) == status
+    assert h.value is None
+
+
+def test_reserved_and_null_arguments(L):
+    cfg = kivi.make_config(1, 1, 1)
+    cfg.reserved = 1
+    h = ctypes.c_void_p()
+    assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV, 1 << 40,
+                               ctypes.byref(h)) == kivi.KIVI_ERR_INVALID_ARG
+    cfg.reserved = 0
+    assert L.kivi_cache_create(None, FAKE_DEV, 1 << 40, ctypes.byref(h)) == kivi.KIVI_ERR_INVALID_ARG
+    assert L.kivi_cache_create(ctypes.byref(cfg), None, 1 << 40,
+                               ctypes.byref(h)) == kivi.KIVI_ERR_INVALID_ARG
+    assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV, 1 << 40, None) == kivi.KIVI_ERR_INVALID_ARG
+    assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV + 16, 1 << 40,
+                               ctypes.byref(h)) == kivi.KIVI_ERR_INVALID_ARG   # misaligned
+    need = kivi.kivi_cache_bytes(cfg)
+    assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV, need - 1,
+                               ctypes.byref(h)) == kivi.KIVI_ERR_BUFFER_TOO_SMALL
+    assert L.kivi_plan_append(None, 1, None) == kivi.KIVI_ERR_INVALID_ARG
+    assert L.kivi_decode_workspace_bytes(None) == 0
+    assert L.kivi_get_layout(None, None) == kivi.KIVI_ERR_INVALID_ARG
+
+
+def align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,H,Hq,bits,R,T,dt,esize", [
+    (1, 1, 1, 2, 0, 1024, kivi.KIVI_F32, 4),
+    (1, 8, 32, 2, 32, 4096, kivi.KIVI_F16, 2),
+    (16, 8, 32, 2, 128, 32768, kivi.KIVI_F16, 2),
+    (32, 8, 32, 4, 128, 131072, kivi.KIVI_F16, 2),
+    (3, 5, 10, 4, 64, 1000, kivi.KIVI_F16, 2),
+])
+def test_sizes_and_layout(L, orc, B, H, Hq, bits, R, T, dt, esize):
+    """Buffer size and block layout as include/kivi.h documents them; the
+    block size also equals the oracle's 2*b*G*D/8 + 4*D*2 (cookbook notebook,
+    storage formula: b bits per code plus two fp16 numbers per group)."""
+    D, G = 128, 32
+    cfg = kivi.make_config(B, H, Hq, bits=bits, residual=R, max_tokens=T, kv_dtype=dt)
+    S = B * H
+    bb = 2 * bits * G * D // 8 + 4 * D * 2
+    assert bb == orc.block_bytes(bits)
+    blocks = align(S * (T // G) * bb)
+    ring = align(S * (R + G) * D * esize)
+    assert kivi.kivi_cache_bytes(cfg) == blocks + 2 * ring
+    h = kivi.kivi_cache_create(cfg, FAKE_DEV, blocks + 2 * ring)
+    try:
+        lo = kivi.kivi_get_layout(h)
+        assert (lo.blocks, lo.ring_k, lo.ring_v) == (0, blocks, blocks + ring)
+        assert lo.block_bytes == bb and lo.code_bytes == bits * G * D // 8
+        cb = lo.code_bytes
+        assert (lo.off_kcode, lo.off_vcode, lo.off_kscale, lo.off_kzero, lo.off_vscale,
+                lo.off_vzero) == (0, cb, 2 * cb, 2 * cb + 2 * D, 2 * cb + 4 * D, 2 * cb + 6 * D)
+        assert lo.max_groups == T // G and lo.ring_capacity == R + G
+        assert (lo.n_tokens, lo.n_quantized) == (0, 0)
+        assert kivi.kivi_decode_plan(h) == (0, 1)
+        ws = kivi.kivi_decode_workspace_bytes(h)
+        assert ws > 0 and ws % (B * Hq * (D + 2) * 4) == 0
+    finally:
+        kivi.kivi_cache_destroy(h)
+
+
+@pytest.mark.parametrize("R", [0, 32, 128])
+def test_plan_append_matches_window_policy(L, orc, R):
+    """Q(n) = G * floor(max(0, n - R) / G) ("KIVI", VeloxQuant-MLX docs,
+    'How it works' 3-4), compared with the oracle's prefix for every n of a
+    first append."""
+    T = 700
+    cfg = kivi.make_config(1, 2, 8, bits=2, residual=R, max_tokens=T)
+    h = kivi.kivi_cache_create(cfg, FAKE_DEV, kivi.kivi_cache_bytes(cfg))
+    try:
+        for n in range(0, T + 1):
+            p = kivi.kivi_plan_append(h, n)
+            qk, qv = orc.quantized_prefix(n, 32, R)
+            assert qk == qv == p.q_new, (n, qk, qv, p.q_new)
+            assert (p.n_old, p.n_new_total, p.q_old) == (0, n, 0)
+            assert (p.flush_token_begin, p.flush_token_end) == (0, p.q_new)
+            assert (p.ring_token_begin, p.ring_token_end) == (p.q_new, n)
+            assert p.ring_token_end - p.ring_token_begin < R + 32     # fits the ring
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_plan_append(h, T + 1)
+        assert e.value.status == kivi.KIVI_ERR_CAPACITY
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_plan_append(h, -1)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+    finally:
+        kivi.kivi_cache_destroy(h)
+
+
+def test_host_error_paths(L):
+    """Errors that the front end returns before any device work: the cache
+    is left unchanged."""
+    cfg = kivi.make_config(1, 1, 4, bits=2, residual=32, max_tokens=64)
+    h = kivi.kivi_cache_create(cfg, FAKE_DEV, kivi.kivi_cache_bytes(cfg))
+    try:
+        with pytest.raises(kivi.KiviError) as e:                       # empty cache
+            kivi.kivi_decode_attn(h, FAKE_DEV, kivi.KIVI_F16, 0.0, FAKE_DEV, FAKE_DEV, 1 << 30, 0)
+        assert e.value.status == kivi.KIVI_ERR_STATE
+        with pytest.raises(kivi.KiviError) as e:                       # over capacity
+            kivi.kivi_append(h, FAKE_DEV, FAKE_DEV, 65, 0, 0)
+        assert e.value.status == kivi.KIVI_ERR_CAPACITY
+        with pytest.raises(kivi.KiviError) as e:                       # unknown flags
+            kivi.kivi_append(h, FAKE_DEV, FAKE_DEV, 1, 1, 0)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        with pytest.raises(kivi.KiviError) as e:                       # missing rows
+            kivi.kivi_append(h, None, None, 1, 0, 0)
+        assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        kivi.kivi_append(h, None, None, 0, 0, 0)                       # empty append: no-op
+        kivi.kivi_flush(h, 0)
+        lo = kivi.kivi_get_layout(h)
+        assert (lo.n_tokens, lo.n_quantized) == (0, 0)
+    finally:
+        kivi.kivi_cache_destroy(h)
