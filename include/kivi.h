@@ -44,7 +44,7 @@ typedef enum {
     KIVI_ERR_UNSUPPORTED = 2,      /* valid KIVI, but not a shape built here */
     KIVI_ERR_CAPACITY = 3,         /* n + n_new > max_tokens                 */
     KIVI_ERR_BUFFER_TOO_SMALL = 4, /* device buffer or workspace too small  */
-    KIVI_ERR_STATE = 5,            /* e.g. decode on an empty cache          */
+    KIVI_ERR_STATE = 5,            /* decode on an empty / unflushed cache   */
     KIVI_ERR_HIP = 6               /* a kernel launch failed                 */
 } kivi_status;
 
@@ -54,6 +54,15 @@ typedef enum { KIVI_F16 = 0, KIVI_F32 = 1 } kivi_dtype;
    stream is Q(n) = G * floor(max(0, n - R) / G) for keys and values alike
    ("KIVI" VeloxQuant-MLX docs, "How it works" items 3-4). */
 typedef enum { KIVI_FLUSH_WINDOW = 0 } kivi_flush_policy;
+
+/* kivi_append flags. */
+enum {
+    /* Copy the new rows into the ring only and leave the quantization of
+       newly aged groups to a later kivi_flush (or to the next append without
+       this flag).  All unquantized tokens must then fit the ring:
+       n - q <= R + G, else KIVI_ERR_CAPACITY. */
+    KIVI_DEFER_FLUSH = 1u
+};
 
 typedef struct {
     int32_t batch;        /* B  >= 1                                          */
@@ -120,16 +129,20 @@ kivi_status kivi_cache_destroy(kivi_cache *c);
    Enqueues, in this order: quantization of tokens [q_old, q_new) (K per
    channel, V per token; token t < n_old is read from the ring, later tokens
    from k/v), then the copy of tokens [max(q_new, n_old), n) into the ring.
-   flags must be 0.  Errors: INVALID_ARG (null handle, null k/v with
-   n_new > 0, n_new < 0, flags), CAPACITY (n + n_new > max_tokens), HIP. */
+   flags: 0 or KIVI_DEFER_FLUSH (then only the ring copy of [n_old, n) is
+   enqueued and q is left as it was).  Errors: INVALID_ARG (null handle,
+   null k/v with n_new > 0, n_new < 0, unknown flags), CAPACITY
+   (n + n_new > max_tokens; with KIVI_DEFER_FLUSH also n + n_new - q > R + G),
+   HIP. */
 kivi_status kivi_append(kivi_cache *c, const void *k, const void *v,
                         int64_t n_new, uint32_t flags, hipStream_t stream);
 
-/* Make the cache canonical.  Under the window policy every append already
-   leaves it canonical, so this only validates the handle. */
+/* Make the cache canonical: quantize tokens [q, Q(n)) that deferred appends
+   left in the ring (nothing to do after appends without KIVI_DEFER_FLUSH).
+   Idempotent.  Errors: INVALID_ARG, HIP. */
 kivi_status kivi_flush(kivi_cache *c, hipStream_t stream);
 
-/* Host-only: what kivi_append(c, ..., n_new, ...) would enqueue. */
+/* Host-only: what kivi_append(c, ..., n_new, 0, ...) would enqueue. */
 kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new,
                              kivi_append_plan *out);
 
@@ -149,7 +162,8 @@ kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits,
    q: device [B][Hq][D] in q_dtype; out: device float32 [B][Hq][D];
    softmax_scale <= 0 selects 1/sqrt(D); workspace: device, ws_bytes >=
    kivi_decode_workspace_bytes(c).  Errors: INVALID_ARG (null pointers, bad
-   q_dtype), STATE (n == 0), BUFFER_TOO_SMALL, HIP. */
+   q_dtype), STATE (n == 0, or a deferred flush pending: q < Q(n)),
+   BUFFER_TOO_SMALL, HIP. */
 kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype,
                              float softmax_scale, float *out, void *workspace,
                              size_t ws_bytes, hipStream_t stream);

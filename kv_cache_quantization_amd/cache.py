@@ -67,8 +67,10 @@ class KiviCache:
         return _k.kivi_decode_plan(self.handle)
 
     # -- hot path -------------------------------------------------------------
-    def append(self, k: torch.Tensor, v: torch.Tensor) -> None:
-        """Append [B, H, n_new, D] rows (contiguous, kv dtype, on the device)."""
+    def append(self, k: torch.Tensor, v: torch.Tensor, defer_flush: bool = False) -> None:
+        """Append [B, H, n_new, D] rows (contiguous, kv dtype, on the device).
+        defer_flush: only copy into the ring (KIVI_DEFER_FLUSH); a later
+        flush() or plain append quantizes the aged groups."""
         c = self.cfg
         shape = (c.batch, c.n_kv_heads, k.shape[2], c.head_dim)
         for t in (k, v):
@@ -78,7 +80,8 @@ class KiviCache:
                                  (self.kv_dtype, shape, self.device))
         n_new = k.shape[2]
         _k.kivi_append(self.handle, k.data_ptr() if n_new else None,
-                       v.data_ptr() if n_new else None, n_new, 0,
+                       v.data_ptr() if n_new else None, n_new,
+                       _k.KIVI_DEFER_FLUSH if defer_flush else 0,
                        _stream_handle(self.device))
 
     def flush(self) -> None:

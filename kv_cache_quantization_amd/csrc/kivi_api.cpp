@@ -177,57 +177,90 @@ kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new, kivi_append_pla
     return KIVI_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Quantize tokens [p.flush_token_begin, p.flush_token_end) of every stream
+// (t < p.n_old from the ring, later ones from k / v).
+kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *k, const void *v,
+                          int64_t n_new, hipStream_t stream) {
+    if (p.flush_token_end <= p.flush_token_begin) return KIVI_OK;
+    QuantizeArgs a;
+    a.blocks = c->base + c->off_blocks;
+    a.max_groups = c->max_groups;
+    a.block_bytes = c->block_bytes;
+    a.in_k = k;
+    a.in_v = v;
+    a.n_new = n_new;
+    a.ring_k = c->base + c->off_ring_k;
+    a.ring_v = c->base + c->off_ring_v;
+    a.ring_cap = c->ring_cap;
+    a.n_old = p.n_old;
+    a.group_begin = p.flush_token_begin / c->cfg.group;
+    a.group_end = p.flush_token_end / c->cfg.group;
+    a.streams = c->cfg.batch * c->cfg.n_kv_heads;
+    a.is_f32 = c->cfg.kv_dtype == KIVI_F32;
+    a.bits = c->cfg.bits;
+    return launch_quantize(a, stream) == hipSuccess ? KIVI_OK : KIVI_ERR_HIP;
+}
+
+// Copy tokens [begin, end) (all >= n_old) of every stream into the ring.
+kivi_status enqueue_ring(kivi_cache *c, const void *k, const void *v, int64_t n_new,
+                         int64_t n_old, int64_t begin, int64_t end, hipStream_t stream) {
+    if (end <= begin) return KIVI_OK;
+    RingArgs r;
+    r.in_k = k;
+    r.in_v = v;
+    r.n_new = n_new;
+    r.n_old = n_old;
+    r.ring_k = c->base + c->off_ring_k;
+    r.ring_v = c->base + c->off_ring_v;
+    r.ring_cap = c->ring_cap;
+    r.tok_begin = begin;
+    r.tok_end = end;
+    r.streams = c->cfg.batch * c->cfg.n_kv_heads;
+    r.esize = c->esize;
+    return launch_ring_append(r, stream) == hipSuccess ? KIVI_OK : KIVI_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
 kivi_status kivi_append(kivi_cache *c, const void *k, const void *v, int64_t n_new,
                         uint32_t flags, hipStream_t stream) {
-    if (!c || flags != 0 || n_new < 0) return KIVI_ERR_INVALID_ARG;
+    if (!c || (flags & ~(uint32_t)KIVI_DEFER_FLUSH) != 0 || n_new < 0) return KIVI_ERR_INVALID_ARG;
     if (n_new > 0 && (!k || !v)) return KIVI_ERR_INVALID_ARG;
     kivi_append_plan p;
     kivi_status st = kivi_plan_append(c, n_new, &p);
     if (st != KIVI_OK) return st;
-    const int32_t streams = c->cfg.batch * c->cfg.n_kv_heads;
-
-    if (p.flush_token_end > p.flush_token_begin) {
-        QuantizeArgs a;
-        a.blocks = c->base + c->off_blocks;
-        a.max_groups = c->max_groups;
-        a.block_bytes = c->block_bytes;
-        a.in_k = k;
-        a.in_v = v;
-        a.n_new = n_new;
-        a.ring_k = c->base + c->off_ring_k;
-        a.ring_v = c->base + c->off_ring_v;
-        a.ring_cap = c->ring_cap;
-        a.n_old = p.n_old;
-        a.group_begin = p.flush_token_begin / c->cfg.group;
-        a.group_end = p.flush_token_end / c->cfg.group;
-        a.streams = streams;
-        a.is_f32 = c->cfg.kv_dtype == KIVI_F32;
-        a.bits = c->cfg.bits;
-        if (launch_quantize(a, stream) != hipSuccess) return KIVI_ERR_HIP;
+    if (flags & KIVI_DEFER_FLUSH) {
+        // every unquantized token must stay addressable in the ring
+        if (p.n_new_total - c->q > c->ring_cap) return KIVI_ERR_CAPACITY;
+        st = enqueue_ring(c, k, v, n_new, p.n_old, p.n_old, p.n_new_total, stream);
+        if (st != KIVI_OK) return st;
+        c->n = p.n_new_total;
+        return KIVI_OK;
     }
-    if (p.ring_token_end > p.ring_token_begin) {
-        RingArgs r;
-        r.in_k = k;
-        r.in_v = v;
-        r.n_new = n_new;
-        r.n_old = p.n_old;
-        r.ring_k = c->base + c->off_ring_k;
-        r.ring_v = c->base + c->off_ring_v;
-        r.ring_cap = c->ring_cap;
-        r.tok_begin = p.ring_token_begin;
-        r.tok_end = p.ring_token_end;
-        r.streams = streams;
-        r.esize = c->esize;
-        if (launch_ring_append(r, stream) != hipSuccess) return KIVI_ERR_HIP;
-    }
+    st = enqueue_flush(c, p, k, v, n_new, stream);
+    if (st != KIVI_OK) return st;
+    st = enqueue_ring(c, k, v, n_new, p.n_old, p.ring_token_begin, p.ring_token_end, stream);
+    if (st != KIVI_OK) return st;
     c->n = p.n_new_total;
     c->q = p.q_new;
     return KIVI_OK;
 }
 
 kivi_status kivi_flush(kivi_cache *c, hipStream_t stream) {
-    (void)stream;
     if (!c) return KIVI_ERR_INVALID_ARG;
+    kivi_append_plan p;
+    kivi_status st = kivi_plan_append(c, 0, &p);
+    if (st != KIVI_OK) return st;
+    // n_old == n: every token to quantize is read from the ring
+    st = enqueue_flush(c, p, c->base + c->off_ring_k, c->base + c->off_ring_v, 0, stream);
+    if (st != KIVI_OK) return st;
+    c->q = p.q_new;
     return KIVI_OK;
 }
 
@@ -253,7 +286,7 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
                              float *out, void *workspace, size_t ws_bytes, hipStream_t stream) {
     if (!c || !q || !out || !workspace) return KIVI_ERR_INVALID_ARG;
     if (q_dtype != KIVI_F16 && q_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
-    if (c->n == 0) return KIVI_ERR_STATE;
+    if (c->n == 0 || c->q != quantized_prefix(c->cfg, c->n)) return KIVI_ERR_STATE;
     if (ws_bytes < kivi_decode_workspace_bytes(c)) return KIVI_ERR_BUFFER_TOO_SMALL;
     DecodeArgs a;
     int32_t splits, gps;

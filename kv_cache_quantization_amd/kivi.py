@@ -24,6 +24,7 @@ KIVI_ERR_HIP = 6
 KIVI_F16 = 0
 KIVI_F32 = 1
 KIVI_FLUSH_WINDOW = 0
+KIVI_DEFER_FLUSH = 1
 
 # Every symbol include/kivi.h declares.
 EXPORTED = (

@@ -172,23 +172,27 @@ def test_plan_append_matches_window_policy(L, orc, R):
 def test_host_error_paths(L):
     """Errors that the front end returns before any device work: the cache
     is left unchanged."""
-    cfg = kivi.make_config(1, 1, 4, bits=2, residual=32, max_tokens=64)
+    cfg = kivi.make_config(1, 1, 4, bits=2, residual=32, max_tokens=256)
     h = kivi.kivi_cache_create(cfg, FAKE_DEV, kivi.kivi_cache_bytes(cfg))
     try:
         with pytest.raises(kivi.KiviError) as e:                       # empty cache
             kivi.kivi_decode_attn(h, FAKE_DEV, kivi.KIVI_F16, 0.0, FAKE_DEV, FAKE_DEV, 1 << 30, 0)
         assert e.value.status == kivi.KIVI_ERR_STATE
         with pytest.raises(kivi.KiviError) as e:                       # over capacity
-            kivi.kivi_append(h, FAKE_DEV, FAKE_DEV, 65, 0, 0)
+            kivi.kivi_append(h, FAKE_DEV, FAKE_DEV, 257, 0, 0)
         assert e.value.status == kivi.KIVI_ERR_CAPACITY
         with pytest.raises(kivi.KiviError) as e:                       # unknown flags
-            kivi.kivi_append(h, FAKE_DEV, FAKE_DEV, 1, 1, 0)
+            kivi.kivi_append(h, FAKE_DEV, FAKE_DEV, 1, 2, 0)
         assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+        with pytest.raises(kivi.KiviError) as e:                       # deferred rows beyond the ring
+            kivi.kivi_append(h, FAKE_DEV, FAKE_DEV, 32 + 32 + 1, kivi.KIVI_DEFER_FLUSH, 0)
+        assert e.value.status == kivi.KIVI_ERR_CAPACITY
         with pytest.raises(kivi.KiviError) as e:                       # missing rows
             kivi.kivi_append(h, None, None, 1, 0, 0)
         assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
         kivi.kivi_append(h, None, None, 0, 0, 0)                       # empty append: no-op
-        kivi.kivi_flush(h, 0)
+        kivi.kivi_append(h, None, None, 0, kivi.KIVI_DEFER_FLUSH, 0)
+        kivi.kivi_flush(h, 0)                                          # nothing pending: no-op
         lo = kivi.kivi_get_layout(h)
         assert (lo.n_tokens, lo.n_quantized) == (0, 0)
     finally:

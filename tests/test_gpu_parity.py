@@ -211,3 +211,49 @@ def test_near_ties(orc, bits, dtype):
     cache = new_cache(B, H, 4 * H, n, bits=bits, R=0, dtype=dtype)
     cache.append(to_dev(k), to_dev(v))
     check_cache(orc, cache, k, v, label="near-ties-%d" % bits)
+
+
+def test_deferred_flush(orc):
+    """Appends that only fill the ring (KIVI_DEFER_FLUSH), then kivi_flush or
+    a plain append: the cache ends bit-identical to a one-shot prefill, and
+    decode refuses to run while a flush is pending."""
+    import torch
+    from kv_cache_quantization_amd import kivi, synth
+    from kv_cache_quantization_amd import KiviError
+    B, H, Hq, R = 2, 2, 8, 64
+    n = 600
+    k, v = synth.kv_host(21, B, H, n)
+    q = to_dev(synth.queries_host(21, B, Hq))
+    for bits in (2, 4):
+        log("case deferred-flush bits=%d" % bits)
+        cache = new_cache(B, H, Hq, n, bits=bits, R=R)
+        cache.append(to_dev(k[:, :, :300]), to_dev(v[:, :, :300]))
+        pos = 300
+        # deferred appends until the ring is full (n - q == R + G), then flush
+        while True:
+            lo = cache.layout()
+            room = lo.ring_capacity - (lo.n_tokens - lo.n_quantized)
+            if room == 0:
+                break
+            c = min(room, 7)
+            cache.append(to_dev(k[:, :, pos:pos + c]), to_dev(v[:, :, pos:pos + c]), defer_flush=True)
+            pos += c
+        with pytest.raises(KiviError) as e:       # one more token does not fit
+            cache.append(to_dev(k[:, :, pos:pos + 1]), to_dev(v[:, :, pos:pos + 1]), defer_flush=True)
+        assert e.value.status == kivi.KIVI_ERR_CAPACITY
+        with pytest.raises(KiviError) as e:       # decode while a flush is pending
+            cache.decode(q)
+        assert e.value.status == kivi.KIVI_ERR_STATE
+        cache.flush()
+        cache.flush()                             # idempotent
+        check_cache(orc, cache, k[:, :, :pos], v[:, :, :pos], label="deferred-%d" % bits)
+        # deferred appends resolved by a plain append
+        c = 20
+        cache.append(to_dev(k[:, :, pos:pos + c]), to_dev(v[:, :, pos:pos + c]), defer_flush=True)
+        pos += c
+        cache.append(to_dev(k[:, :, pos:n]), to_dev(v[:, :, pos:n]))
+        check_cache(orc, cache, k, v, label="deferred-then-plain-%d" % bits)
+        out = cache.decode(q).cpu().numpy()
+        e = rel_err(out, oracle_decode(orc, k, v, synth.queries_host(21, B, Hq), bits, 32, R))
+        log("  decode rel err %.3g" % e)
+        assert e <= TOL
