@@ -22,6 +22,13 @@
  *  [CQ]  "KV Cache Compression > Cache Quantization" (Language AI Handbook):
  *        uniform quantization, the half-step error bound, QuantizedCache.
  *
+ * Parity status: every function is pinned by tests/test_oracle_pins.py to
+ * what the pages print or to closed forms, except the bit order of the
+ * packed block (code_position / oracle_pack_blocks): the pages fix the
+ * storage cost but not the order, so that order is a layout choice --
+ * parity unpinned beyond its bijectivity (and the GPU decode reading it
+ * back into the oracle's logical attention).
+ *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fPIC -shared
  * (x86-64 SSE arithmetic: every float operation below is one IEEE-754
  * binary32 operation rounded to nearest even; no FMA contraction.)
