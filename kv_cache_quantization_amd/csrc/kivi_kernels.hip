@@ -520,12 +520,14 @@ __device__ __forceinline__ float xsum_rows(float v) {
     swap_rows(c, d);
     return c + d;
 }
+// NaN-propagating maximum (v_maximum3_f32): no operand quieting needed.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float xmax_rows(float v) {
     float a = v, b = v;
     swap_halves(a, b);
-    float c = fmaxf(a, b), d = c;
+    float c = vmax(a, b), d = c;
     swap_rows(c, d);
-    return fmaxf(c, d);
+    return vmax(c, d);
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -605,10 +607,10 @@ template <int SB>
 __device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float cs, float kbl,
                                              float &m_run, float (&nm)[4], float &l_run,
                                              float (&vb)[4], f4 (&accV)[8], h2 (&P)[4]) {
-    float mt = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
-                     fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
+    float mt = vmax(vmax(vmax(S0[0], S0[1]), vmax(S0[2], S0[3])),
+                    vmax(vmax(S1[0], S1[1]), vmax(S1[2], S1[3])));
     mt = __builtin_fmaf(xmax_rows(mt), cs, kbl);
-    const float m_new = fmaxf(m_run, mt);
+    const float m_new = vmax(m_run, mt);
     if (__any(m_new > m_run)) {
         const float al = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
@@ -672,77 +674,167 @@ __device__ __forceinline__ void store_partial(const DecodeArgs &a, int64_t pi, i
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kTwoM24 = 5.9604644775390625e-08f;
 
-// Residual item, fp16 ring: tokens [n_quant, n) in chunks of 32 through the
-// same matrix-core products (K rows and q are exact fp16, no scale/zero).
+// 64 lanes x 16 bytes from global memory straight into LDS (one 1 KiB
+// global_load_lds_dwordx4; LDS destination M0 + 16 * lane), and explicit waits
+// on the vector-memory counter: the compiler's own wait insertion does not see
+// these copies.
+__device__ __forceinline__ void dma_1k(const uint8_t *src_lane, uint32_t lds_dst) {
+    // LDS destination: M0 + 16 * lane
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src_lane), "s"(lds_dst)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Residual items: one per 32-token chunk of the full-precision window
+// [n_quant, n), scheduled ahead of the split items.  All of a chunk's loads
+// are issued up front (one memory round trip per item), the softmax is local
+// to the chunk, and the combine pass merges it like any other partial.
+
+// p * v + acc with v one half of an fp16 pair, rounded once (v_fma_mix_f32).
+// Written out so that the compiler keeps v packed instead of converting every
+// pair to two fp32 registers up front.
+__device__ __forceinline__ float fma_mix_lo(float p, h2 v, float acc) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(p), "v"(v), "v"(acc));
+    return r;
+}
+__device__ __forceinline__ float fma_mix_hi(float p, h2 v, float acc) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+        : "=v"(r) : "v"(p), "v"(v), "v"(acc));
+    return r;
+}
+
+// fp16 ring: scores on the matrix core (K rows and q are exact fp16).  The
+// chunk's V rows are copied HBM -> LDS (8 KiB) alongside the K loads; p.V runs
+// on the vector ALUs -- lane l owns channels 2l, 2l+1 and reads the chunk's p
+// values (32 tokens x GQ heads) broadcast from LDS.
 template <int GQ>
-__device__ void decode_tail_f16(const DecodeArgs &a, int stream) {
+__device__ void decode_tail_f16(const DecodeArgs &a, int stream, int chunk, uint8_t *lds) {
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
     const int h = j % GQ;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
-    const int hq = hk * GQ + h;
-    const int items = a.splits + 1;
+    const int items = a.splits + a.tail_chunks;
+    const int64_t base = a.n_quant + (int64_t)G * chunk;
+    const int64_t left = a.n_tokens - base;
+    const int cnt = left < G ? (int)left : G;            // >= 1
+    const int cap = (int)a.ring_cap;
+    const int slot0 = (int)(base % a.ring_cap);
+    // ring slot of chunk row r (rows past the end read the last valid row;
+    // their scores are masked and their p is 0)
+    auto slot = [&](int r) {
+        const int s2 = slot0 + (r < cnt ? r : cnt - 1);
+        return s2 >= cap ? s2 - cap : s2;
+    };
+    // uniform 64-bit bases + 32-bit per-lane byte offsets (one ring fits 4 GiB)
+    const char *rkb = (const char *)a.ring_k + (int64_t)stream * a.ring_cap * D * 2;
+    const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * 2;
     h2 qB[4][4];
-    load_q_operand(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
-    const _Float16 *rk = (const _Float16 *)a.ring_k + (int64_t)stream * a.ring_cap * D;
-    const _Float16 *rv = (const _Float16 *)a.ring_v + (int64_t)stream * a.ring_cap * D;
-    float m_run = -INFINITY, l_run = 0.f;
-    float nm[4] = {INFINITY, INFINITY, INFINITY, INFINITY}, vb[4] = {0.f, 0.f, 0.f, 0.f};
-    f4 accV[8];
+    load_q_operand(a, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
 #pragma unroll
-    for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
-    for (int64_t base = a.n_quant; base < a.n_tokens; base += G) {
-        f4 S[2];
+    for (int s2 = 0; s2 < 4; s2++)
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-            const int64_t tok = base + 16 * t + (l & 15);
-            const bool ok = tok < a.n_tokens;
-            const int64_t tc = ok ? tok : a.n_tokens - 1;
-            const _Float16 *row = rk + (tc % a.ring_cap) * D + 8 * Gl;
-            S[t] = (f4){0.f, 0.f, 0.f, 0.f};
+        for (int m2 = 0; m2 < 4; m2++) asm volatile("" : : "v"(qB[s2][m2]));
+    wait_vm<0>();      // q in registers before the copies below are counted
+    // V rows -> LDS [32][D] fp16: copy i covers rows 4i .. 4i+3
+    const uint32_t vbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
 #pragma unroll
-            for (int s = 0; s < 4; s++) {
-                uint4 u = *(const uint4 *)(row + 32 * s);
-                if (!ok) u = (uint4){0u, 0u, 0u, 0u};
-                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, u),
-                                                             pack_h8(qB[s]), S[t], 0, 0, 0);
-            }
-            // lane (j, Gl) holds tokens base + 16t + 4Gl + e
+    for (int i = 0; i < G / 4; i++)
+        dma_1k((const uint8_t *)rvb + (uint32_t)(slot(4 * i + Gl) * D * 2 + 16 * j),
+               __builtin_amdgcn_readfirstlane(vbase + 1024u * i));
+    uint4 kr[2][4];
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                if (base + 16 * t + 4 * Gl + e >= a.n_tokens) S[t][e] = -INFINITY;
+    for (int t = 0; t < 2; t++) {
+        const uint32_t off = (uint32_t)(slot(16 * t + j) * D + 8 * Gl) * 2u;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; s2++) kr[t][s2] = *(const uint4 *)(rkb + off + 64u * s2);
+    }
+    f4 S[2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        S[t] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; s2++)
+            S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kr[t][s2]),
+                                                         pack_h8(qB[s2]), S[t], 0, 0, 0);
+    }
+    // lane (j, Gl) holds rows 16t + 4Gl + e of column j (query head j % GQ)
+    float mt = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            if (16 * t + 4 * Gl + e >= cnt) S[t][e] = -INFINITY;
+            mt = vmax(mt, S[t][e]);
         }
-        h2 P[4];
-        softmax_step<0>(S[0], S[1], a.sm_log2, 0.0f, m_run, nm, l_run, vb, accV, P);
-        const h8 Bp = pack_h8(P);
+    const float m = xmax_rows(mt) * a.sm_log2;            // row 0 is always valid
+    float *p_lds = (float *)(lds + G * D * 2);
+    float ls = 0.f;
 #pragma unroll
-        for (int o = 0; o < 8; o++) {
-            const int c = 16 * o + (l & 15);
-            h8 A;
+    for (int t = 0; t < 2; t++)
 #pragma unroll
-            for (int kk = 0; kk < 8; kk++) {
-                // unconditional load from a valid slot, then zero past the end
-                const int64_t tok = base + 4 * Gl + (kk & 3) + 16 * (kk >> 2);
-                const int64_t tc = tok < a.n_tokens ? tok : a.n_tokens - 1;
-                const _Float16 x = rv[(tc % a.ring_cap) * D + c];
-                A[kk] = tok < a.n_tokens ? x : (_Float16)0.0f;
+        for (int e = 0; e < 4; e++) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][e], a.sm_log2, -m));
+            ls += pv;
+            if (j < GQ) p_lds[j * G + 16 * t + 4 * Gl + e] = pv;     // [head][token]
+        }
+    ls = xsum_rows(ls);
+    wait_vm<0>();      // V copies landed
+    __syncthreads();
+    // the lane's two channels of every row, then one accumulation chain per head
+    const h2 *vl = (const h2 *)lds;
+    h2 vr[G];
+#pragma unroll
+    for (int r = 0; r < G; r++) vr[r] = vl[r * (D / 2) + l];
+    float o0[GQ], o1[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; hh++) {
+        float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+        for (int r4 = 0; r4 < G / 4; r4++) {
+            const float4 p4 = *(const float4 *)&p_lds[hh * G + 4 * r4];
+            const float pq[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {             // fp16 v enters the FMA directly
+                x0 = fma_mix_lo(pq[e], vr[4 * r4 + e], x0);
+                x1 = fma_mix_hi(pq[e], vr[4 * r4 + e], x1);
             }
-            accV[o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bp, accV[o], 0, 0, 0);
+        }
+        o0[hh] = x0;
+        o1[hh] = x1;
+    }
+#pragma unroll
+    for (int hh = 0; hh < GQ; hh++) {
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + hh) * items + a.splits + chunk;
+        *(float2 *)&a.part_o[pi * D + 2 * l] = (float2){o0[hh], o1[hh]};
+        if (l == hh) {                      // lane hh: column hh, row group 0
+            a.part_ml[2 * pi] = m;
+            a.part_ml[2 * pi + 1] = ls;
         }
     }
-    const int64_t pi = ((int64_t)b * a.q_heads + hq) * items + a.splits;
-    store_partial<GQ>(a, pi, l, accV, 1.0f, 0.0f, m_run, xsum_rows(l_run));
 }
 
-// Residual item, fp32 ring: one token per step on the vector ALUs (lane l
-// owns channels 2l, 2l+1), online softmax in the log2 domain.
+// fp32 ring: one token per step on the vector ALUs (lane l owns channels 2l,
+// 2l+1), online softmax in the log2 domain.
 template <int GQ>
-__device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
+__device__ void decode_tail_f32(const DecodeArgs &a, int stream, int chunk) {
     const int l = threadIdx.x & 63;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
-    const int items = a.splits + 1;
-    const float *rk = (const float *)a.ring_k;
-    const float *rv = (const float *)a.ring_v;
+    const int items = a.splits + a.tail_chunks;
+    const int64_t base = a.n_quant + (int64_t)G * chunk;
+    const int64_t left = a.n_tokens - base;
+    const int cnt = left < G ? (int)left : G;
+    const int cap = (int)a.ring_cap;
+    int slot = (int)(base % a.ring_cap);
+    const float *rk = (const float *)a.ring_k + (int64_t)stream * a.ring_cap * D;
+    const float *rv = (const float *)a.ring_v + (int64_t)stream * a.ring_cap * D;
     float q0[GQ], q1[GQ], m[GQ], ls[GQ], a0[GQ], a1[GQ];
 #pragma unroll
     for (int h = 0; h < GQ; h++) {
@@ -754,8 +846,9 @@ __device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
         a0[h] = 0.f;
         a1[h] = 0.f;
     }
-    for (int64_t t = a.n_quant; t < a.n_tokens; t++) {
-        const int64_t row = ((int64_t)stream * a.ring_cap + t % a.ring_cap) * D + 2 * l;
+    for (int r = 0; r < cnt; r++) {
+        const int64_t row = (int64_t)slot * D + 2 * l;
+        slot = slot + 1 == cap ? 0 : slot + 1;
         const float k0 = rk[row], k1 = rk[row + 1], v0 = rv[row], v1 = rv[row + 1];
 #pragma unroll
         for (int h = 0; h < GQ; h++) {
@@ -771,7 +864,7 @@ __device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
     }
 #pragma unroll
     for (int h = 0; h < GQ; h++) {
-        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * items + a.splits;
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * items + a.splits + chunk;
         float2 ov = {a0[h], a1[h]};
         *(float2 *)&a.part_o[pi * D + 2 * l] = ov;
         if (l == 0) {
@@ -795,19 +888,6 @@ struct Pipe {
     static constexpr int DPG = BB / 1024;               // 1 KiB copies per group
     static constexpr int NST = BITS == 2 ? 3 : 2;       // stages
 };
-
-__device__ __forceinline__ void dma_1k(const uint8_t *src_lane, uint32_t lds_dst) {
-    // LDS destination: M0 + 16 * lane
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src_lane), "s"(lds_dst)
-                 : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
 
 template <int BITS>
 __device__ __forceinline__ void issue_group(const uint8_t *blk, uint32_t stage, int l) {
@@ -838,10 +918,11 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int cg = (j / GQ) & 3;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const int hq = hk * GQ + h;
-    const int items = a.splits + 1;
+    const int items = a.splits + a.tail_chunks;
     const int64_t ng = a.n_quant / G;
     const int64_t g0 = (int64_t)sp * a.groups_per_split;
     const int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
+    const int n_g = (int)(g1 - g0);             // groups of this split
 
     // q pair m divided by 2^kScaleLog2(m): it meets key codes read in place
     h2 qB[4][4];
@@ -878,7 +959,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
 #pragma unroll
     for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
 
-    const uint8_t *sblk = a.blocks + (int64_t)stream * a.max_groups * a.block_bytes;
+    const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
     const uint32_t pbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)pipe;
     // q must be in registers before the copies start, and the compiler must
     // know it (its wait tracking does not see the inline-assembly copies).
@@ -887,18 +968,22 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
 #pragma unroll
         for (int m = 0; m < 4; m++) asm volatile("" : : "v"(qB[s][m]));
     wait_vm<0>();
-    int64_t issued = g0;
-    for (int st = 0; st < PP::NST - 1 && issued < g1; st++, issued++)
-        issue_group<BITS>(sblk + issued * PP::BB, pbase + (uint32_t)((issued - g0) % PP::NST) * PP::BB, l);
+    // stage ring: `is` is the stage the next copy goes to, `rs` the stage read
+    int issued = 0, is = 0, rs = 0;
+    for (; issued < PP::NST - 1 && issued < n_g; issued++) {
+        issue_group<BITS>(sblk + (int64_t)issued * PP::BB, pbase + (uint32_t)is * PP::BB, l);
+        is = is + 1 == PP::NST ? 0 : is + 1;
+    }
 
-    for (int64_t g = g0; g < g1; g++) {
-        if (issued < g1) {
-            issue_group<BITS>(sblk + issued * PP::BB,
-                              pbase + (uint32_t)((issued - g0) % PP::NST) * PP::BB, l);
+    for (int g = 0; g < n_g; g++) {
+        if (issued < n_g) {
+            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, pbase + (uint32_t)is * PP::BB, l);
+            is = is + 1 == PP::NST ? 0 : is + 1;
             issued++;
         }
-        wait_groups_after<BITS>((int)(issued - 1 - g));
-        const uint8_t *stg = pipe + ((g - g0) % PP::NST) * PP::BB;
+        wait_groups_after<BITS>(issued - 1 - g);
+        const uint8_t *stg = pipe + rs * PP::BB;
+        rs = rs + 1 == PP::NST ? 0 : rs + 1;
         const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
         uint32_t kc[DPL], vc[DPL];
 #pragma unroll
@@ -974,13 +1059,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t pipe[Pipe<BITS>::NST * Pipe<BITS>::BB];
     __shared__ uint4 q_lds[64];
     const int64_t item = blockIdx.x;
-    const int streams = a.batch * a.kv_heads;
-    if (item < streams) {
-        if (a.ring_is_f32) decode_tail_f32<GQ>(a, (int)item);
-        else decode_tail_f16<GQ>(a, (int)item);
+    const int64_t n_tail = (int64_t)a.batch * a.kv_heads * a.tail_chunks;
+    if (item < n_tail) {
+        const int stream = (int)(item / a.tail_chunks), chunk = (int)(item % a.tail_chunks);
+        if (a.ring_is_f32) decode_tail_f32<GQ>(a, stream, chunk);
+        else decode_tail_f16<GQ>(a, stream, chunk, pipe);
         return;
     }
-    const int64_t it = item - streams;
+    const int64_t it = item - n_tail;
     decode_split<BITS, GQ>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
 }
 
@@ -993,7 +1079,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     __shared__ float red[128];
     const int64_t bh = blockIdx.x;
     const int c = threadIdx.x;
-    const int items = a.splits + 1;
+    const int items = a.splits + a.tail_chunks;
     const float *ml = a.part_ml + bh * items * 2;
     float M = -INFINITY;
     for (int s = c; s < items; s += 128)
@@ -1084,8 +1170,9 @@ static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const int streams = a.batch * a.kv_heads;
     const int gq = a.q_heads / a.kv_heads;
-    const int64_t items = (int64_t)streams * (a.splits + 1);
-    if (a.splits + 1 > kMaxItems) return hipErrorInvalidValue;
+    const int64_t items = (int64_t)streams * (a.splits + a.tail_chunks);
+    if (a.splits + a.tail_chunks > kMaxItems || items <= 0 || items > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
     dim3 grid((unsigned)items);
     if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
     else launch_decode_bits<4>(a, gq, grid, s);
