@@ -151,8 +151,7 @@ size_t kivi_decode_workspace_bytes(const kivi_cache *c);
 
 /* How decode splits the quantized prefix at the current n: *splits work
    items per stream over whole groups, *groups_per_split groups each (plus
-   ceil((n - Q) / G) items per stream over the full-precision residual, G
-   tokens each). Host-only. */
+   one item per stream for the full-precision residual). Host-only. */
 kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits,
                              int32_t *groups_per_split);
 

@@ -37,7 +37,7 @@ namespace {
 constexpr size_t kAlign = 256;
 // Decode work items aimed for per launch: 256 compute units x 16 resident
 // wavefronts (4 per SIMD: <= 128 registers per lane and <= 10 KiB of LDS
-// each), i.e. one round, residual items included.
+// each), i.e. one round.
 constexpr int kTargetWaves = 4096;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -89,17 +89,12 @@ int64_t quantized_prefix(const kivi_config &c, int64_t n) {
     return aged / c.group * c.group;
 }
 
-// Residual items of an n-token stream: one per G tokens of [Q, n).
+// G-token chunks of the residual [Q, n) (walked by one item per stream).
 int64_t tail_chunks_of(const kivi_cache *c, int64_t n, int64_t q) {
     return (n - q + c->cfg.group - 1) / c->cfg.group;
 }
 
-// Upper bound of tail_chunks_of on a canonical cache: n - Q < R + G.
-int64_t max_tail_chunks(const kivi_cache *c) {
-    return ((int64_t)c->cfg.residual + 2 * c->cfg.group - 2) / c->cfg.group;
-}
-
-void decode_split_plan(const kivi_cache *c, int64_t n, int64_t q, int32_t *splits, int32_t *gps) {
+void decode_split_plan(const kivi_cache *c, int64_t q, int32_t *splits, int32_t *gps) {
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
     const int64_t ng = q / c->cfg.group;
     if (ng == 0) {
@@ -108,8 +103,8 @@ void decode_split_plan(const kivi_cache *c, int64_t n, int64_t q, int32_t *split
         return;
     }
     // One wavefront per work item; aim for one full round of resident
-    // wavefronts: the residual items of every stream plus `want` split items.
-    int64_t want = kTargetWaves / streams - tail_chunks_of(c, n, q);
+    // wavefronts (one residual item per stream plus `want` split items).
+    int64_t want = kTargetWaves / streams - 1;
     if (want < 1) want = 1;
     if (want > ng) want = ng;
     const int64_t g = (ng + want - 1) / want;
@@ -276,18 +271,19 @@ kivi_status kivi_flush(kivi_cache *c, hipStream_t stream) {
 
 size_t kivi_decode_workspace_bytes(const kivi_cache *c) {
     if (!c) return 0;
-    // decode_split_plan makes at most max(1, kTargetWaves / streams - chunks)
-    // split items per stream, plus `chunks` residual items, whatever n is.
+    // decode_split_plan never makes more than max(1, kTargetWaves / streams - 1)
+    // split items per stream, whatever n is; plus one residual item.
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
-    int64_t items = kTargetWaves / streams;
-    if (items < 1 + max_tail_chunks(c)) items = 1 + max_tail_chunks(c);
+    int64_t splits = kTargetWaves / streams - 1;
+    if (splits < 1) splits = 1;
+    const int64_t items = splits + 1;
     const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
     return (size_t)(bhq * items * (c->cfg.head_dim + 2) * 4);
 }
 
 kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits, int32_t *gps) {
     if (!c || !splits || !gps) return KIVI_ERR_INVALID_ARG;
-    decode_split_plan(c, c->n, c->q, splits, gps);
+    decode_split_plan(c, c->q, splits, gps);
     return KIVI_OK;
 }
 
@@ -299,10 +295,10 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
     if (ws_bytes < kivi_decode_workspace_bytes(c)) return KIVI_ERR_BUFFER_TOO_SMALL;
     DecodeArgs a;
     int32_t splits, gps;
-    decode_split_plan(c, c->n, c->q, &splits, &gps);
+    decode_split_plan(c, c->q, &splits, &gps);
     const int64_t chunks = tail_chunks_of(c, c->n, c->q);
     const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
-    const int64_t items = splits + chunks;
+    const int64_t items = splits + 1;
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
     a.block_bytes = c->block_bytes;

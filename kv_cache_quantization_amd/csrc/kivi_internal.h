@@ -56,7 +56,7 @@ struct DecodeArgs {
     int64_t n_tokens, n_quant;  // n, Q(n)
     int32_t splits;             // work items per stream over quantized groups
     int32_t groups_per_split;
-    int32_t tail_chunks;        // work items per stream over the residual, G tokens each
+    int32_t tail_chunks;        // G-token chunks of the residual (walked by one item)
     float sm_log2;              // softmax scale * log2(e)
 };
 

@@ -674,6 +674,12 @@ __device__ __forceinline__ void store_partial(const DecodeArgs &a, int64_t pi, i
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kTwoM24 = 5.9604644775390625e-08f;
 
+// Order this wavefront's LDS accesses around a point (cross-lane exchange
+// through LDS inside one wave; LDS executes a wave's operations in order).
+__device__ __forceinline__ void lds_sync_wave() {
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+}
+
 // 64 lanes x 16 bytes from global memory straight into LDS (one 1 KiB
 // global_load_lds_dwordx4; LDS destination M0 + 16 * lane), and explicit waits
 // on the vector-memory counter: the compiler's own wait insertion does not see
@@ -691,10 +697,10 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Residual items: one per 32-token chunk of the full-precision window
-// [n_quant, n), scheduled ahead of the split items.  All of a chunk's loads
-// are issued up front (one memory round trip per item), the softmax is local
-// to the chunk, and the combine pass merges it like any other partial.
+// Residual item: one per stream over the full-precision window [n_quant, n),
+// taken 32 tokens (one chunk) at a time.  Each chunk's loads are issued
+// together (one memory round trip per chunk), its softmax is local and is
+// merged into the item's running state.
 
 // p * v + acc with v one half of an fp16 pair, rounded once (v_fma_mix_f32).
 // Written out so that the compiler keeps v packed instead of converting every
@@ -711,31 +717,27 @@ __device__ __forceinline__ float fma_mix_hi(float p, h2 v, float acc) {
     return r;
 }
 
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
 // fp16 ring: scores on the matrix core (K rows and q are exact fp16).  The
 // chunk's V rows are copied HBM -> LDS (8 KiB) alongside the K loads; p.V runs
 // on the vector ALUs -- lane l owns channels 2l, 2l+1 and reads the chunk's p
 // values (32 tokens x GQ heads) broadcast from LDS.
 template <int GQ>
-__device__ void decode_tail_f16(const DecodeArgs &a, int stream, int chunk, uint8_t *lds) {
+__device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
     const int h = j % GQ;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
-    const int items = a.splits + a.tail_chunks;
-    const int64_t base = a.n_quant + (int64_t)G * chunk;
-    const int64_t left = a.n_tokens - base;
-    const int cnt = left < G ? (int)left : G;            // >= 1
+    const int items = a.splits + 1;
     const int cap = (int)a.ring_cap;
-    const int slot0 = (int)(base % a.ring_cap);
-    // ring slot of chunk row r (rows past the end read the last valid row;
-    // their scores are masked and their p is 0)
-    auto slot = [&](int r) {
-        const int s2 = slot0 + (r < cnt ? r : cnt - 1);
-        return s2 >= cap ? s2 - cap : s2;
-    };
     // uniform 64-bit bases + 32-bit per-lane byte offsets (one ring fits 4 GiB)
     const char *rkb = (const char *)a.ring_k + (int64_t)stream * a.ring_cap * D * 2;
     const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * 2;
+    const uint32_t vbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+    float *p_lds = (float *)(lds + G * D * 2);
     h2 qB[4][4];
     load_q_operand(a, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
 #pragma unroll
@@ -743,80 +745,101 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, int chunk, uint
 #pragma unroll
         for (int m2 = 0; m2 < 4; m2++) asm volatile("" : : "v"(qB[s2][m2]));
     wait_vm<0>();      // q in registers before the copies below are counted
-    // V rows -> LDS [32][D] fp16: copy i covers rows 4i .. 4i+3
-    const uint32_t vbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+    // running state: per head (m, l) (wave-uniform) and the lane's two channels
+    float Mr[GQ], Lr[GQ], O0[GQ], O1[GQ];
 #pragma unroll
-    for (int i = 0; i < G / 4; i++)
-        dma_1k((const uint8_t *)rvb + (uint32_t)(slot(4 * i + Gl) * D * 2 + 16 * j),
-               __builtin_amdgcn_readfirstlane(vbase + 1024u * i));
-    uint4 kr[2][4];
+    for (int hh = 0; hh < GQ; hh++) { Mr[hh] = -INFINITY; Lr[hh] = 0.f; O0[hh] = O1[hh] = 0.f; }
+    int slot0 = (int)(a.n_quant % a.ring_cap);
+    for (int chunk = 0; chunk < a.tail_chunks; chunk++) {
+        const int64_t left = a.n_tokens - a.n_quant - (int64_t)G * chunk;
+        const int cnt = left < G ? (int)left : G;        // >= 1
+        // ring slot of chunk row r (rows past the end read the last valid
+        // row; their scores are masked and their p is 0)
+        auto slot = [&](int r) {
+            const int s2 = slot0 + (r < cnt ? r : cnt - 1);
+            return s2 >= cap ? s2 - cap : s2;
+        };
+        lds_sync_wave();   // the previous chunk's LDS reads are done
+        // V rows -> LDS [32][D] fp16: copy i covers rows 4i .. 4i+3
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-        const uint32_t off = (uint32_t)(slot(16 * t + j) * D + 8 * Gl) * 2u;
+        for (int i = 0; i < G / 4; i++)
+            dma_1k((const uint8_t *)rvb + (uint32_t)(slot(4 * i + Gl) * D * 2 + 16 * j),
+                   __builtin_amdgcn_readfirstlane(vbase + 1024u * i));
+        uint4 kr[2][4];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; s2++) kr[t][s2] = *(const uint4 *)(rkb + off + 64u * s2);
-    }
-    f4 S[2];
+        for (int t = 0; t < 2; t++) {
+            const uint32_t off = (uint32_t)(slot(16 * t + j) * D + 8 * Gl) * 2u;
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-        S[t] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s2 = 0; s2 < 4; s2++)
-            S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kr[t][s2]),
-                                                         pack_h8(qB[s2]), S[t], 0, 0, 0);
-    }
-    // lane (j, Gl) holds rows 16t + 4Gl + e of column j (query head j % GQ)
-    float mt = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; t++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            if (16 * t + 4 * Gl + e >= cnt) S[t][e] = -INFINITY;
-            mt = vmax(mt, S[t][e]);
+            for (int s2 = 0; s2 < 4; s2++) kr[t][s2] = *(const uint4 *)(rkb + off + 64u * s2);
         }
-    const float m = xmax_rows(mt) * a.sm_log2;            // row 0 is always valid
-    float *p_lds = (float *)(lds + G * D * 2);
-    float ls = 0.f;
+        slot0 = slot0 + G >= cap ? slot0 + G - cap : slot0 + G;
+        f4 S[2];
 #pragma unroll
-    for (int t = 0; t < 2; t++)
+        for (int t = 0; t < 2; t++) {
+            S[t] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][e], a.sm_log2, -m));
-            ls += pv;
-            if (j < GQ) p_lds[j * G + 16 * t + 4 * Gl + e] = pv;     // [head][token]
+            for (int s2 = 0; s2 < 4; s2++)
+                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kr[t][s2]),
+                                                             pack_h8(qB[s2]), S[t], 0, 0, 0);
         }
-    ls = xsum_rows(ls);
-    wait_vm<0>();      // V copies landed
-    __syncthreads();
-    // the lane's two channels of every row, then one accumulation chain per head
-    const h2 *vl = (const h2 *)lds;
-    h2 vr[G];
+        // lane (j, Gl) holds rows 16t + 4Gl + e of column j (query head j % GQ)
+        float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < G; r++) vr[r] = vl[r * (D / 2) + l];
-    float o0[GQ], o1[GQ];
+        for (int t = 0; t < 2; t++)
 #pragma unroll
-    for (int hh = 0; hh < GQ; hh++) {
-        float x0 = 0.f, x1 = 0.f;
-#pragma unroll
-        for (int r4 = 0; r4 < G / 4; r4++) {
-            const float4 p4 = *(const float4 *)&p_lds[hh * G + 4 * r4];
-            const float pq[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-            for (int e = 0; e < 4; e++) {             // fp16 v enters the FMA directly
-                x0 = fma_mix_lo(pq[e], vr[4 * r4 + e], x0);
-                x1 = fma_mix_hi(pq[e], vr[4 * r4 + e], x1);
+            for (int e = 0; e < 4; e++) {
+                if (16 * t + 4 * Gl + e >= cnt) S[t][e] = -INFINITY;
+                mt = vmax(mt, S[t][e]);
             }
+        const float m = xmax_rows(mt) * a.sm_log2;        // row 0 is always valid
+        float ls = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][e], a.sm_log2, -m));
+                ls += pv;
+                if (j < GQ) p_lds[j * G + 16 * t + 4 * Gl + e] = pv;     // [head][token]
+            }
+        ls = xsum_rows(ls);
+        wait_vm<0>();      // V copies landed
+        lds_sync_wave();
+        // the lane's two channels of every row, then one accumulation chain per head
+        const h2 *vl = (const h2 *)lds;
+        h2 vr[G];
+#pragma unroll
+        for (int r = 0; r < G; r++) vr[r] = vl[r * (D / 2) + l];
+#pragma unroll
+        for (int hh = 0; hh < GQ; hh++) {
+            float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+            for (int r4 = 0; r4 < G / 4; r4++) {
+                const float4 p4 = *(const float4 *)&p_lds[hh * G + 4 * r4];
+                const float pq[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {         // fp16 v enters the FMA directly
+                    x0 = fma_mix_lo(pq[e], vr[4 * r4 + e], x0);
+                    x1 = fma_mix_hi(pq[e], vr[4 * r4 + e], x1);
+                }
+            }
+            // merge into the running state (head hh's (m, l) sit in lane hh)
+            const float mc = readlane_f(m, hh), lc = readlane_f(ls, hh);
+            const float mn = fmaxf(Mr[hh], mc);
+            const float fo = __builtin_amdgcn_exp2f(Mr[hh] - mn);
+            const float fc = __builtin_amdgcn_exp2f(mc - mn);
+            O0[hh] = __builtin_fmaf(O0[hh], fo, x0 * fc);
+            O1[hh] = __builtin_fmaf(O1[hh], fo, x1 * fc);
+            Lr[hh] = __builtin_fmaf(Lr[hh], fo, lc * fc);
+            Mr[hh] = mn;
         }
-        o0[hh] = x0;
-        o1[hh] = x1;
     }
 #pragma unroll
     for (int hh = 0; hh < GQ; hh++) {
-        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + hh) * items + a.splits + chunk;
-        *(float2 *)&a.part_o[pi * D + 2 * l] = (float2){o0[hh], o1[hh]};
-        if (l == hh) {                      // lane hh: column hh, row group 0
-            a.part_ml[2 * pi] = m;
-            a.part_ml[2 * pi + 1] = ls;
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + hh) * items + a.splits;
+        *(float2 *)&a.part_o[pi * D + 2 * l] = (float2){O0[hh], O1[hh]};
+        if (l == 0) {
+            a.part_ml[2 * pi] = Mr[hh];
+            a.part_ml[2 * pi + 1] = Lr[hh];
         }
     }
 }
@@ -824,15 +847,12 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, int chunk, uint
 // fp32 ring: one token per step on the vector ALUs (lane l owns channels 2l,
 // 2l+1), online softmax in the log2 domain.
 template <int GQ>
-__device__ void decode_tail_f32(const DecodeArgs &a, int stream, int chunk) {
+__device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
     const int l = threadIdx.x & 63;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
-    const int items = a.splits + a.tail_chunks;
-    const int64_t base = a.n_quant + (int64_t)G * chunk;
-    const int64_t left = a.n_tokens - base;
-    const int cnt = left < G ? (int)left : G;
+    const int items = a.splits + 1;
     const int cap = (int)a.ring_cap;
-    int slot = (int)(base % a.ring_cap);
+    int slot = (int)(a.n_quant % a.ring_cap);
     const float *rk = (const float *)a.ring_k + (int64_t)stream * a.ring_cap * D;
     const float *rv = (const float *)a.ring_v + (int64_t)stream * a.ring_cap * D;
     float q0[GQ], q1[GQ], m[GQ], ls[GQ], a0[GQ], a1[GQ];
@@ -846,7 +866,7 @@ __device__ void decode_tail_f32(const DecodeArgs &a, int stream, int chunk) {
         a0[h] = 0.f;
         a1[h] = 0.f;
     }
-    for (int r = 0; r < cnt; r++) {
+    for (int64_t t = a.n_quant; t < a.n_tokens; t++) {
         const int64_t row = (int64_t)slot * D + 2 * l;
         slot = slot + 1 == cap ? 0 : slot + 1;
         const float k0 = rk[row], k1 = rk[row + 1], v0 = rv[row], v1 = rv[row + 1];
@@ -864,7 +884,7 @@ __device__ void decode_tail_f32(const DecodeArgs &a, int stream, int chunk) {
     }
 #pragma unroll
     for (int h = 0; h < GQ; h++) {
-        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * items + a.splits + chunk;
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * items + a.splits;
         float2 ov = {a0[h], a1[h]};
         *(float2 *)&a.part_o[pi * D + 2 * l] = ov;
         if (l == 0) {
@@ -918,7 +938,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int cg = (j / GQ) & 3;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const int hq = hk * GQ + h;
-    const int items = a.splits + a.tail_chunks;
+    const int items = a.splits + 1;
     const int64_t ng = a.n_quant / G;
     const int64_t g0 = (int64_t)sp * a.groups_per_split;
     const int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
@@ -1059,14 +1079,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t pipe[Pipe<BITS>::NST * Pipe<BITS>::BB];
     __shared__ uint4 q_lds[64];
     const int64_t item = blockIdx.x;
-    const int64_t n_tail = (int64_t)a.batch * a.kv_heads * a.tail_chunks;
-    if (item < n_tail) {
-        const int stream = (int)(item / a.tail_chunks), chunk = (int)(item % a.tail_chunks);
-        if (a.ring_is_f32) decode_tail_f32<GQ>(a, stream, chunk);
-        else decode_tail_f16<GQ>(a, stream, chunk, pipe);
+    const int64_t streams = (int64_t)a.batch * a.kv_heads;
+    if (item < streams) {
+        if (a.ring_is_f32) decode_tail_f32<GQ>(a, (int)item);
+        else decode_tail_f16<GQ>(a, (int)item, pipe);
         return;
     }
-    const int64_t it = item - n_tail;
+    const int64_t it = item - streams;
     decode_split<BITS, GQ>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
 }
 
@@ -1079,7 +1098,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     __shared__ float red[128];
     const int64_t bh = blockIdx.x;
     const int c = threadIdx.x;
-    const int items = a.splits + a.tail_chunks;
+    const int items = a.splits + 1;
     const float *ml = a.part_ml + bh * items * 2;
     float M = -INFINITY;
     for (int s = c; s < items; s += 128)
@@ -1170,9 +1189,8 @@ static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const int streams = a.batch * a.kv_heads;
     const int gq = a.q_heads / a.kv_heads;
-    const int64_t items = (int64_t)streams * (a.splits + a.tail_chunks);
-    if (a.splits + a.tail_chunks > kMaxItems || items <= 0 || items > 0x7FFFFFFF)
-        return hipErrorInvalidValue;
+    const int64_t items = (int64_t)streams * (a.splits + 1);
+    if (a.splits + 1 > kMaxItems || items > 0x7FFFFFFF) return hipErrorInvalidValue;
     dim3 grid((unsigned)items);
     if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
     else launch_decode_bits<4>(a, gq, grid, s);
