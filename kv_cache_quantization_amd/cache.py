@@ -49,8 +49,13 @@ class KiviCache:
     def __del__(self):
         h = getattr(self, "handle", None)
         if h:
-            _k.kivi_cache_destroy(h)
             self.handle = None
+            try:
+                _k.kivi_cache_destroy(h)
+            except (TypeError, AttributeError):
+                # interpreter shutdown: the binding module is already torn
+                # down, and the host handle goes with the process
+                pass
 
     # -- shape helpers ------------------------------------------------------
     @property

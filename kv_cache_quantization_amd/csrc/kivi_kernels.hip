@@ -598,30 +598,45 @@ __device__ __forceinline__ void load_q_operand(const DecodeArgs &a, int64_t qrow
     }
 }
 
-// Online-softmax step over the 8 scores a lane holds (two 16-token tiles),
-// shared by the quantized and the residual paths.  Returns p as fp16 pairs
-// in value-operand order, pair m pre-divided by 2^kScaleLog2<SB>(m) (SB = 0:
-// no scaling); l_run accumulates the unscaled sum.  nm[m] caches
-// -m_run - kScaleLog2<SB>(m).
+// Online softmax with a lazy maximum: a score may exceed the running maximum
+// m_run by up to kSlack (log2 units) before the state is rescaled, so the
+// cross-row reduction of the maximum and the rescale run only when some score
+// passes m_thr = m_run + kSlack.  p is pre-divided by a further 2^kSlack,
+// which keeps every fp16 p at or below 1.
+constexpr int kSlack = 1;
+
+template <int SB>
+__device__ __forceinline__ constexpr int pair_shift(int m) {
+    return kScaleLog2<SB>(m) + kSlack;
+}
+
+// One step over the 8 scores a lane holds (two 16-token tiles).  Returns p as
+// fp16 pairs in value-operand order, pair m pre-divided by 2^pair_shift(m)
+// (kScaleLog2<SB>(m) + kSlack).  The unscaled sum of p runs on the matrix
+// core: A holds the weights 2^pair_shift(m) in every row, so each row of
+// Lsum carries the running sum of its column.  nm[m] caches
+// -m_run - pair_shift(m).
 template <int SB>
 __device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float cs, float kbl,
-                                             float &m_run, float (&nm)[4], float &l_run,
-                                             float (&vb)[4], f4 (&accV)[8], h2 (&P)[4]) {
+                                             float &m_run, float &m_thr, float (&nm)[4],
+                                             f4 &Lsum, float (&vb)[4], f4 (&accV)[8],
+                                             h2 (&P)[4]) {
     float mt = vmax(vmax(vmax(S0[0], S0[1]), vmax(S0[2], S0[3])),
                     vmax(vmax(S1[0], S1[1]), vmax(S1[2], S1[3])));
-    mt = __builtin_fmaf(xmax_rows(mt), cs, kbl);
-    const float m_new = vmax(m_run, mt);
-    if (__any(m_new > m_run)) {
+    mt = __builtin_fmaf(mt, cs, kbl);               // this lane's maximum, log2 units
+    if (__any(mt > m_thr)) {
+        const float m_new = vmax(m_run, xmax_rows(mt));
         const float al = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
         for (int o = 0; o < 8; o++) accV[o] *= al;
-        l_run *= al;
+        Lsum *= al;
 #pragma unroll
         for (int m = 0; m < 4; m++) {
             vb[m] *= al;
-            nm[m] = -m_new - (float)kScaleLog2<SB>(m);
+            nm[m] = -m_new - (float)pair_shift<SB>(m);
         }
         m_run = m_new;
+        m_thr = m_new + (float)kSlack;
     }
     float nk[4];
 #pragma unroll
@@ -632,14 +647,14 @@ __device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float c
         p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], cs, nk[e >> 1]));
         p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[e], cs, nk[2 + (e >> 1)]));
     }
+    h8 W;
 #pragma unroll
     for (int m = 0; m < 4; m++) {
-        const _Float16 up = (_Float16)(float)(1 << kScaleLog2<SB>(m));
-        const h2 w = {up, up};
         P[m][0] = (_Float16)p[2 * m];
         P[m][1] = (_Float16)p[2 * m + 1];
-        l_run = __builtin_amdgcn_fdot2(P[m], w, l_run, false);
+        W[2 * m] = W[2 * m + 1] = (_Float16)(float)(1 << pair_shift<SB>(m));
     }
+    Lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(W, pack_h8(P), Lsum, 0, 0, 0);
 }
 
 // Store a partial: lanes whose column carries value channel group cg write
@@ -973,7 +988,8 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     }
     const float cs = a.sm_log2 * kTwo24;        // score units -> log2 units
 
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, m_thr = -INFINITY;
+    f4 Lsum = (f4){0.f, 0.f, 0.f, 0.f};
     float nm[4] = {INFINITY, INFINITY, INFINITY, INFINITY}, vb[4] = {0.f, 0.f, 0.f, 0.f};
     f4 accV[8];
 #pragma unroll
@@ -1045,7 +1061,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
             S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1, 0, 0, 0);
         }
         h2 P[4];
-        softmax_step<BITS>(S0, S1, cs, Sk[0] * a.sm_log2, m_run, nm, l_run, vb, accV, P);
+        softmax_step<BITS>(S0, S1, cs, Sk[0] * a.sm_log2, m_run, m_thr, nm, Lsum, vb, accV, P);
         h2 vs[4], vz[4], ps[4];
         {
             const uint2 *s2 = (const uint2 *)side;
@@ -1070,8 +1086,10 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     float vbt = vb[0];
 #pragma unroll
     for (int m = 1; m < 4; m++) vbt = __builtin_fmaf(vb[m], (float)(1 << kScaleLog2<BITS>(m)), vbt);
+    vbt *= (float)(1 << kSlack);
     const int64_t pi = ((int64_t)b * a.q_heads + hq) * items + sp;
-    store_partial<GQ>(a, pi, l, accV, kTwo24, xsum_rows(vbt), m_run, xsum_rows(l_run));
+    store_partial<GQ>(a, pi, l, accV, kTwo24 * (float)(1 << kSlack), xsum_rows(vbt), m_run,
+                      Lsum[0]);
 }
 
 template <int BITS, int GQ>
