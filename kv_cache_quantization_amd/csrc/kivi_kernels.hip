@@ -578,9 +578,10 @@ __device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t idx) {
 
 // q of query head hq as fp16 pairs in B-operand order: slice s, pair m ->
 // channels 32s + 8*Gl + 2m, +1 (one 16-byte load per slice for fp16 q).
+template <bool QF32>
 __device__ __forceinline__ void load_q_operand(const DecodeArgs &a, int64_t qrow, int Gl,
                                                h2 (&qB)[4][4]) {
-    if (a.q_is_f32) {
+    if constexpr (QF32) {
         const float *q = (const float *)a.q + qrow + 8 * Gl;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
@@ -740,7 +741,7 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 // chunk's V rows are copied HBM -> LDS (8 KiB) alongside the K loads; p.V runs
 // on the vector ALUs -- lane l owns channels 2l, 2l+1 and reads the chunk's p
 // values (32 tokens x GQ heads) broadcast from LDS.
-template <int GQ>
+template <int GQ, bool QF32>
 __device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
@@ -754,12 +755,9 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
     const uint32_t vbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
     float *p_lds = (float *)(lds + G * D * 2);
     h2 qB[4][4];
-    load_q_operand(a, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
-#pragma unroll
-    for (int s2 = 0; s2 < 4; s2++)
-#pragma unroll
-        for (int m2 = 0; m2 < 4; m2++) asm volatile("" : : "v"(qB[s2][m2]));
-    wait_vm<0>();      // q in registers before the copies below are counted
+    // (no wait here: the first chunk's loads overlap those of q, and the
+    // compiler's wait before the first use of q also covers the copies)
+    load_q_operand<QF32>(a, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
     // running state: per head (m, l) (wave-uniform) and the lane's two channels
     float Mr[GQ], Lr[GQ], O0[GQ], O1[GQ];
 #pragma unroll
@@ -942,7 +940,7 @@ __device__ __forceinline__ void wait_groups_after(int r) {
     else wait_vm<0>();
 }
 
-template <int BITS, int GQ>
+template <int BITS, int GQ, bool QF32>
 __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *pipe,
                              uint4 *q_lds) {
     using PP = Pipe<BITS>;
@@ -959,26 +957,43 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
     const int n_g = (int)(g1 - g0);             // groups of this split
 
-    // q pair m divided by 2^kScaleLog2(m): it meets key codes read in place
+    const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
+    const uint32_t pbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)pipe;
+    // q of the lane's head in B-operand order, and the unscaled fp16 q of the
+    // GQ heads for LDS (16 bytes per lane, head (l/16) % GQ, channels
+    // 8*(l%16)..+7: B operand of the key-zero product).  The first copies go
+    // out before either is used, so the prologue costs one memory round trip.
+    // (The compiler's own wait before the first use of q also covers the
+    // copies, which it does not see: loads complete in order.)
     h2 qB[4][4];
-    load_q_operand(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
-    // Unscaled fp16 q of the GQ heads staged in LDS (16 bytes per lane, head
-    // (l/16) % GQ, channels 8*(l%16)..+7): B operand of the key-zero product.
+    load_q_operand<QF32>(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
+    uint4 uq;
     {
         const int64_t qoff = ((int64_t)b * a.q_heads + hk * GQ + (l >> 4) % GQ) * D + 8 * (l & 15);
-        uint4 u;
-        if (a.q_is_f32) {
+        if constexpr (QF32) {
             const float *qf = (const float *)a.q + qoff;
             const float4 x0 = *(const float4 *)qf, x1 = *(const float4 *)(qf + 4);
             h2 t0 = {(_Float16)x0.x, (_Float16)x0.y}, t1 = {(_Float16)x0.z, (_Float16)x0.w};
             h2 t2 = {(_Float16)x1.x, (_Float16)x1.y}, t3 = {(_Float16)x1.z, (_Float16)x1.w};
-            u.x = __builtin_bit_cast(uint32_t, t0); u.y = __builtin_bit_cast(uint32_t, t1);
-            u.z = __builtin_bit_cast(uint32_t, t2); u.w = __builtin_bit_cast(uint32_t, t3);
+            uq.x = __builtin_bit_cast(uint32_t, t0); uq.y = __builtin_bit_cast(uint32_t, t1);
+            uq.z = __builtin_bit_cast(uint32_t, t2); uq.w = __builtin_bit_cast(uint32_t, t3);
         } else {
-            u = *(const uint4 *)((const _Float16 *)a.q + qoff);
+            uq = *(const uint4 *)((const _Float16 *)a.q + qoff);
         }
-        q_lds[l] = u;
     }
+    // stage ring: `is` is the stage the next copy goes to, `rs` the stage read
+    int issued = 0, is = 0, rs = 0;
+    for (; issued < PP::NST - 1 && issued < n_g; issued++) {
+        issue_group<BITS>(sblk + (int64_t)issued * PP::BB, pbase + (uint32_t)is * PP::BB, l);
+        is = is + 1 == PP::NST ? 0 : is + 1;
+    }
+    // first uses of q: after the copies above (volatile asm keeps the order)
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+        for (int m = 0; m < 4; m++) asm volatile("" : "+v"(qB[s][m]));
+    asm volatile("" : "+v"(uq.x), "+v"(uq.y), "+v"(uq.z), "+v"(uq.w));
+    q_lds[l] = uq;
 #pragma unroll
     for (int m = 0; m < 4; m++) {
         const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
@@ -994,22 +1009,6 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     f4 accV[8];
 #pragma unroll
     for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
-
-    const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
-    const uint32_t pbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)pipe;
-    // q must be in registers before the copies start, and the compiler must
-    // know it (its wait tracking does not see the inline-assembly copies).
-#pragma unroll
-    for (int s = 0; s < 4; s++)
-#pragma unroll
-        for (int m = 0; m < 4; m++) asm volatile("" : : "v"(qB[s][m]));
-    wait_vm<0>();
-    // stage ring: `is` is the stage the next copy goes to, `rs` the stage read
-    int issued = 0, is = 0, rs = 0;
-    for (; issued < PP::NST - 1 && issued < n_g; issued++) {
-        issue_group<BITS>(sblk + (int64_t)issued * PP::BB, pbase + (uint32_t)is * PP::BB, l);
-        is = is + 1 == PP::NST ? 0 : is + 1;
-    }
 
     for (int g = 0; g < n_g; g++) {
         if (issued < n_g) {
@@ -1100,11 +1099,17 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int64_t streams = (int64_t)a.batch * a.kv_heads;
     if (item < streams) {
         if (a.ring_is_f32) decode_tail_f32<GQ>(a, (int)item);
-        else decode_tail_f16<GQ>(a, (int)item, pipe);
+        else if (a.q_is_f32) decode_tail_f16<GQ, true>(a, (int)item, pipe);
+        else decode_tail_f16<GQ, false>(a, (int)item, pipe);
         return;
     }
+    // (q's dtype selects an instantiation: the prologue's loads must not
+    // meet at a control-flow join, where the compiler would wait for them)
     const int64_t it = item - streams;
-    decode_split<BITS, GQ>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
+    if (a.q_is_f32)
+        decode_split<BITS, GQ, true>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
+    else
+        decode_split<BITS, GQ, false>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
 }
 
 // Merge the partials of one (batch, query head).  The split weights
