@@ -60,6 +60,7 @@ def lib():
         L.oracle_dequant_cache.argtypes = [P, P, i32, i32, i32, i64, i32, i32,
                                            i64, i64, P, P, P, P, P, P, P, P]
         L.oracle_decode_attn.argtypes = [P, P, P, i32, i32, i32, i64, i32, f64, P]
+        L.oracle_attn_queries.argtypes = [P, P, P, i32, i32, i32, i64, i64, i32, f64, i32, P]
         L.oracle_block_bytes.restype = i64
         L.oracle_block_bytes.argtypes = [i32]
         L.oracle_pack_blocks.argtypes = [i32, i32, i64, i32, i64, P, P, P, P, P, P, P]
@@ -188,6 +189,25 @@ def decode_attn(q, khat, vhat, sm_scale: float | None = None) -> np.ndarray:
     out = np.empty((B, Hq, D), np.float32)
     lib().oracle_decode_attn(_p(q), _p(khat), _p(vhat), B, H, Hq, n, D,
                              float(sm_scale), _p(out))
+    return out
+
+
+def attn_queries(q, khat, vhat, causal: bool = False, sm_scale: float | None = None) -> np.ndarray:
+    """T queries per query head: softmax(q K_hat^T * sm_scale [+ mask]) V_hat,
+    fp64 accumulation.  q: [B, Hq, T, D]; khat, vhat: [B, H, n, D] float32.
+    causal: query t is token n - T + t and sees tokens 0 .. n - T + t."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float32))
+    khat = np.ascontiguousarray(khat, dtype=np.float32)
+    vhat = np.ascontiguousarray(vhat, dtype=np.float32)
+    B, Hq, T, D = q.shape
+    _, H, n, _ = khat.shape
+    if causal and T > n:
+        raise ValueError("causal attention needs T <= n")
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, Hq, T, D), np.float32)
+    lib().oracle_attn_queries(_p(q), _p(khat), _p(vhat), B, H, Hq, T, n, D, float(sm_scale),
+                              int(bool(causal)), _p(out))
     return out
 
 

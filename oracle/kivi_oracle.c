@@ -309,6 +309,51 @@ void oracle_decode_attn(const float *q, const float *khat, const float *vhat,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Attention of T queries per (batch, query head) over a (dequantized)       */
+/* cache, fp64 accumulation.  [NB] attn: every row of Q attends over all of  */
+/* K, V (no mask).  causal = 1: the T queries are the last T cached tokens   */
+/* (appended before the call, [RV] 1.3: append, then attend), so query t     */
+/* sits at position n - T + t and sees tokens 0 .. n - T + t.                */
+/* q: [B][Hq][T][D] float32; khat, vhat: [B][H][n][D]; out: [B][Hq][T][D].   */
+/* ------------------------------------------------------------------------ */
+void oracle_attn_queries(const float *q, const float *khat, const float *vhat,
+                         int B, int H, int Hq, int64_t T, int64_t n, int D,
+                         double sm_scale, int causal, float *out)
+{
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    int ratio = Hq / H;
+    for (int b = 0; b < B; b++)
+        for (int hq = 0; hq < Hq; hq++) {
+            int h = hq / ratio;
+            const float *kk = khat + ((int64_t)b * H + h) * n * D;
+            const float *vv = vhat + ((int64_t)b * H + h) * n * D;
+            for (int64_t t = 0; t < T; t++) {
+                const float *qq = q + (((int64_t)b * Hq + hq) * T + t) * D;
+                int64_t seen = causal ? n - T + t + 1 : n;     /* tokens 0 .. seen-1 */
+                double m = -INFINITY;
+                for (int64_t j = 0; j < seen; j++) {
+                    double s = 0.0;
+                    for (int c = 0; c < D; c++) s += (double)qq[c] * (double)kk[j * D + c];
+                    sc[j] = s * sm_scale;
+                    if (sc[j] > m) m = sc[j];
+                }
+                double l = 0.0;
+                for (int c = 0; c < D; c++) acc[c] = 0.0;
+                for (int64_t j = 0; j < seen; j++) {
+                    double p = exp(sc[j] - m);
+                    l += p;
+                    for (int c = 0; c < D; c++) acc[c] += p * (double)vv[j * D + c];
+                }
+                float *o = out + (((int64_t)b * Hq + hq) * T + t) * D;
+                for (int c = 0; c < D; c++) o[c] = (float)(acc[c] / l);
+            }
+        }
+    free(sc);
+    free(acc);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Packed storage of one token group of one (batch, KV-head) stream.         */
 /*                                                                           */
 /* The pages fix the storage cost (b bits per code, two fp16 per group,      */

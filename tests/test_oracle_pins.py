@@ -392,3 +392,87 @@ def test_pack_layout_is_bijective(orc, bits):
                 seen.add(slot)
         assert len(seen) == 32 * 128
     assert orc.block_bytes(bits) == 2 * bits * 32 * 128 // 8 + 4 * 128 * 2
+
+
+# ---------------------------------------------------------------------------
+# Attention of several queries per head (notebook attn over every row of Q;
+# review 1.3: the new tokens are appended, then attend)
+# ---------------------------------------------------------------------------
+def test_attn_queries_matches_torch_sdpa(orc):
+    """Against torch's scaled_dot_product_attention in float64, without a mask
+    and with the causal mask aligned to the end of the cache (query t is token
+    n - T + t)."""
+    import torch
+    rng = np.random.default_rng(21)
+    B, H, Hq, T, n, D = 2, 2, 8, 5, 40, 16
+    q = rng.standard_normal((B, Hq, T, D)).astype(np.float32)
+    k = rng.standard_normal((B, H, n, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, n, D)).astype(np.float32)
+    kt = torch.from_numpy(k).double().repeat_interleave(Hq // H, dim=1)
+    vt = torch.from_numpy(v).double().repeat_interleave(Hq // H, dim=1)
+    mask = torch.tensor([[j <= n - T + t for j in range(n)] for t in range(T)])
+    for causal in (False, True):
+        out = orc.attn_queries(q, k, v, causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q).double(), kt, vt, attn_mask=mask if causal else None).numpy()
+        np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-7)
+
+
+def test_attn_queries_reduces_to_decode(orc):
+    """One query without a mask is the decode step; under the causal mask
+    query t is the decode step over the first n - T + t + 1 tokens."""
+    rng = np.random.default_rng(22)
+    B, H, Hq, T, n, D = 1, 2, 4, 6, 33, 128
+    q = rng.standard_normal((B, Hq, T, D)).astype(np.float32)
+    k = rng.standard_normal((B, H, n, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, n, D)).astype(np.float32)
+    np.testing.assert_array_equal(orc.attn_queries(q[:, :, :1], k, v)[:, :, 0],
+                                  orc.decode_attn(q[:, :, 0], k, v))
+    out = orc.attn_queries(q, k, v, causal=True)
+    for t in range(T):
+        seen = n - T + t + 1
+        np.testing.assert_array_equal(out[:, :, t],
+                                      orc.decode_attn(q[:, :, t], k[:, :, :seen], v[:, :, :seen]))
+
+
+def test_attn_queries_causal_closed_forms(orc):
+    """Causal: with T = n the first query sees only token 0 (its value row);
+    q = 0 gives the mean of the visible value rows."""
+    rng = np.random.default_rng(23)
+    B, H, n, D = 1, 1, 12, 128
+    k = rng.standard_normal((B, H, n, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, n, D)).astype(np.float32)
+    out = orc.attn_queries(rng.standard_normal((B, 1, n, D)).astype(np.float32), k, v, causal=True)
+    np.testing.assert_allclose(out[0, 0, 0], v[0, 0, 0], rtol=1e-6)
+    T = 5
+    out = orc.attn_queries(np.zeros((B, 1, T, D), np.float32), k, v, causal=True)
+    for t in range(T):
+        seen = n - T + t + 1
+        np.testing.assert_allclose(out[0, 0, t], v[0, 0, :seen].astype(np.float64).mean(0),
+                                   rtol=1e-5, atol=1e-6)
+    with pytest.raises(ValueError):
+        orc.attn_queries(np.zeros((B, 1, n + 1, D), np.float32), k, v, causal=True)
+
+
+def test_attn_queries_notebook_checks(orc):
+    """The notebook's attention check over all 1024 rows of its Q (seed 1),
+    with the quantized K, V against the unquantized ones."""
+    from kv_cache_quantization_amd import synth
+    import torch
+    chk = golden("notebook_checks.json")["checks"]
+    K, V, _ = synth.notebook_inputs()
+    K2, V2 = K[0, 0], V[0, 0]
+    Q = torch.randn(1, 1024, 128, generator=torch.Generator().manual_seed(1)).numpy()
+    q = Q.reshape(1, 1, 1024, 128)
+
+    def att(kk, vv):
+        return orc.attn_queries(q, kk.reshape(1, 1, 1024, 128), vv.reshape(1, 1, 1024, 128))[0, 0]
+
+    ref = att(K2, V2)
+    rel2 = np.linalg.norm(ref - att(orc.fake_quant_2d(K2, 0, 2, 32), orc.fake_quant_2d(V2, 1, 2, 32))) \
+        / np.linalg.norm(ref)
+    rel4 = np.linalg.norm(ref - att(orc.fake_quant_2d(K2, 0, 4, 32), orc.fake_quant_2d(V2, 1, 4, 32))) \
+        / np.linalg.norm(ref)
+    assert rel4 < chk["rel_err_4bit_max"]
+    lo, hi = chk["rel_err_2bit_open_interval"]
+    assert lo < rel2 < hi
