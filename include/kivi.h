@@ -168,6 +168,36 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype,
                              float softmax_scale, float *out, void *workspace,
                              size_t ws_bytes, hipStream_t stream);
 
+/* Attention of T queries per (batch, query head) over all n cached tokens
+   (the dequantized groups followed by the full-precision residual):
+   out[b][hq][t][:] = softmax(scale * q[b][hq][t] . K_hat^T + mask) V_hat, the
+   notebook's attention over every row of Q ("Attention output: quantised vs
+   fp16" in [NB]).  causal = 0: every query sees all n tokens.  causal = 1:
+   the queries are the last T cached tokens (appended before the call, as in
+   [RV] 1.3), so query t sees tokens 0 .. n - T + t; needs T <= n.  T = 1
+   without the mask is the decode step.  Query head hq reads KV head
+   hq / (Hq / H).
+   q: device [B][Hq][T][D] in q_dtype; out: device float32 [B][Hq][T][D];
+   softmax_scale <= 0 selects 1/sqrt(D); workspace: device, ws_bytes >=
+   kivi_attn_workspace_bytes(c, T) (may be 0, then workspace may be NULL).
+   Errors: INVALID_ARG (null pointers, T < 1, bad q_dtype or causal, causal
+   with T > n), STATE (n == 0 or a deferred flush pending), UNSUPPORTED
+   (float32 cache with residual tokens; B * Hq * T >= 2^31),
+   BUFFER_TOO_SMALL, HIP. */
+kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T,
+                      int32_t causal, float softmax_scale, float *out,
+                      void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes kivi_attn needs for T queries at any n <= max_tokens
+   (0: none needed).  0 also for a null cache or T < 1. */
+size_t kivi_attn_workspace_bytes(const kivi_cache *c, int64_t T);
+
+/* How kivi_attn splits the work at the current n: *qblocks query blocks per
+   stream (8 x 16/GQ queries each), *splits ranges of *groups_per_split
+   groups (the last also walks the residual).  Host-only. */
+kivi_status kivi_attn_plan(const kivi_cache *c, int64_t T, int32_t *qblocks,
+                           int32_t *splits, int32_t *groups_per_split);
+
 /* Offsets, sizes and the current n / Q(n) (host-only). */
 kivi_status kivi_get_layout(const kivi_cache *c, kivi_layout *out);
 

@@ -39,6 +39,7 @@ class KiviCache:
         self.buffer = self._raw[off:off + nbytes]
         self.handle = _k.kivi_cache_create(self.cfg, self.buffer.data_ptr(), nbytes)
         self._ws = None
+        self._attn_ws = None
 
     def reset(self) -> None:
         """Forget every token: a fresh host handle over the same buffer."""
@@ -113,6 +114,31 @@ class KiviCache:
         qd = _k.KIVI_F16 if q.dtype == torch.float16 else _k.KIVI_F32
         _k.kivi_decode_attn(self.handle, q.data_ptr(), qd, float(softmax_scale), out.data_ptr(),
                             ws.data_ptr(), ws.numel(), _stream_handle(self.device))
+        return out
+
+    def attn(self, q: torch.Tensor, causal: bool = False, softmax_scale: float = 0.0,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+        """T queries per head over every cached token; q: [B, Hq, T, D].
+        causal: the queries are the last T cached tokens (query t sees tokens
+        0 .. n - T + t)."""
+        c = self.cfg
+        if q.dim() != 4 or tuple(q.shape[:2]) != (c.batch, c.n_q_heads) or \
+                q.shape[3] != c.head_dim or q.shape[2] < 1 or not q.is_contiguous() or \
+                q.dtype not in (torch.float16, torch.float32) or q.device != self.device:
+            raise ValueError("attn expects contiguous fp16/fp32 q of shape (%d, %d, T, %d)" %
+                             (c.batch, c.n_q_heads, c.head_dim))
+        T = q.shape[2]
+        if out is None:
+            out = torch.empty((c.batch, c.n_q_heads, T, c.head_dim), dtype=torch.float32,
+                              device=self.device)
+        n = _k.kivi_attn_workspace_bytes(self.handle, T)
+        if n > 0 and (self._attn_ws is None or self._attn_ws.numel() < n):
+            self._attn_ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        ws = self._attn_ws if n > 0 else None
+        qd = _k.KIVI_F16 if q.dtype == torch.float16 else _k.KIVI_F32
+        _k.kivi_attn(self.handle, q.data_ptr(), qd, T, int(bool(causal)), float(softmax_scale),
+                     out.data_ptr(), ws.data_ptr() if ws is not None else None,
+                     ws.numel() if ws is not None else 0, _stream_handle(self.device))
         return out
 
     # -- raw views (tests read the packed cache through the layout) -----------

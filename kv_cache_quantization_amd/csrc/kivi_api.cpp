@@ -39,6 +39,8 @@ constexpr size_t kAlign = 256;
 // wavefronts (4 per SIMD: <= 128 registers per lane and <= 10 KiB of LDS
 // each), i.e. one round.
 constexpr int kTargetWaves = 4096;
+// Compute units of one MI355X (the attention plan aims at two workgroups each).
+constexpr int kComputeUnits = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -110,6 +112,36 @@ void decode_split_plan(const kivi_cache *c, int64_t q, int32_t *splits, int32_t 
     const int64_t g = (ng + want - 1) / want;
     *gps = (int32_t)g;
     *splits = (int32_t)((ng + g - 1) / g);
+}
+
+// Attention of T queries: 16 / GQ queries per wavefront, kAttnWaves
+// wavefronts per workgroup (one query block), and the groups split so that
+// about two workgroups per compute unit are in flight.
+void attn_plan(const kivi_cache *c, int64_t T, int64_t q, int32_t *qblocks, int32_t *splits,
+               int32_t *gps) {
+    const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
+    const int gq = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+    const int64_t qt = 16 / gq;
+    const int64_t cbs = (T + qt - 1) / qt;
+    const int64_t qb = (cbs + kAttnWaves - 1) / kAttnWaves;
+    *qblocks = (int32_t)qb;
+    const int64_t ng = q / c->cfg.group;
+    int64_t want = 2 * kComputeUnits / (streams * qb);
+    if (want < 1) want = 1;
+    if (want > (ng + 3) / 4) want = (ng + 3) / 4;       // >= 4 groups per split
+    if (want < 1) want = 1;
+    const int64_t g = ng > 0 ? (ng + want - 1) / want : 1;
+    *gps = (int32_t)g;
+    *splits = ng > 0 ? (int32_t)((ng + g - 1) / g) : 1;
+}
+
+int64_t attn_max_splits(const kivi_cache *c, int64_t T) {
+    const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
+    const int gq = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+    const int64_t qt = 16 / gq;
+    const int64_t qb = ((T + qt - 1) / qt + kAttnWaves - 1) / kAttnWaves;
+    int64_t want = 2 * kComputeUnits / (streams * qb);
+    return want < 1 ? 1 : want;
 }
 
 }  // namespace
@@ -323,6 +355,65 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)c->cfg.head_dim);
     a.sm_log2 = scale * 1.4426950408889634f;
     if (launch_decode(a, stream) != hipSuccess) return KIVI_ERR_HIP;
+    return KIVI_OK;
+}
+
+size_t kivi_attn_workspace_bytes(const kivi_cache *c, int64_t T) {
+    if (!c || T < 1) return 0;
+    const int64_t splits = attn_max_splits(c, T);
+    if (splits <= 1) return 0;
+    const int64_t rows = (int64_t)c->cfg.batch * c->cfg.n_q_heads * T;
+    return (size_t)(rows * splits * (c->cfg.head_dim + 2) * 4);
+}
+
+kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, int32_t causal,
+                      float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                      hipStream_t stream) {
+    if (!c || !q || !out || T < 1) return KIVI_ERR_INVALID_ARG;
+    if (q_dtype != KIVI_F16 && q_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return KIVI_ERR_INVALID_ARG;
+    if (c->n == 0 || c->q != quantized_prefix(c->cfg, c->n)) return KIVI_ERR_STATE;
+    if (causal && T > c->n) return KIVI_ERR_INVALID_ARG;
+    if (c->cfg.kv_dtype != KIVI_F16 && c->n > c->q) return KIVI_ERR_UNSUPPORTED;
+    const int64_t rows = (int64_t)c->cfg.batch * c->cfg.n_q_heads * T;
+    if (rows > 0x7FFFFFFF) return KIVI_ERR_UNSUPPORTED;
+    const size_t need = kivi_attn_workspace_bytes(c, T);
+    if (need > 0 && (!workspace || ws_bytes < need)) return KIVI_ERR_BUFFER_TOO_SMALL;
+    AttnArgs a;
+    int32_t qblocks, splits, gps;
+    attn_plan(c, T, c->q, &qblocks, &splits, &gps);
+    a.blocks = c->base + c->off_blocks;
+    a.max_groups = c->max_groups;
+    a.block_bytes = c->block_bytes;
+    a.ring_k = c->base + c->off_ring_k;
+    a.ring_v = c->base + c->off_ring_v;
+    a.ring_cap = c->ring_cap;
+    a.q = q;
+    a.q_is_f32 = q_dtype == KIVI_F32;
+    a.out = out;
+    a.part_o = (float *)workspace;
+    a.part_ml = splits > 1 ? (float *)workspace + rows * splits * c->cfg.head_dim : nullptr;
+    a.batch = c->cfg.batch;
+    a.kv_heads = c->cfg.n_kv_heads;
+    a.q_heads = c->cfg.n_q_heads;
+    a.bits = c->cfg.bits;
+    a.n_tokens = c->n;
+    a.n_quant = c->q;
+    a.T = T;
+    a.causal = causal;
+    a.qblocks = qblocks;
+    a.splits = splits;
+    a.groups_per_split = gps;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)c->cfg.head_dim);
+    a.sm_log2 = scale * 1.4426950408889634f;
+    if (launch_attn(a, stream) != hipSuccess) return KIVI_ERR_HIP;
+    return KIVI_OK;
+}
+
+kivi_status kivi_attn_plan(const kivi_cache *c, int64_t T, int32_t *qblocks, int32_t *splits,
+                           int32_t *groups_per_split) {
+    if (!c || T < 1 || !qblocks || !splits || !groups_per_split) return KIVI_ERR_INVALID_ARG;
+    attn_plan(c, T, c->q, qblocks, splits, groups_per_split);
     return KIVI_OK;
 }
 

@@ -60,8 +60,37 @@ struct DecodeArgs {
     float sm_log2;              // softmax scale * log2(e)
 };
 
+// Attention of T queries per (batch, query head) over the cache.  One
+// workgroup per (stream, query block, split): its wavefronts each take 16/GQ
+// queries x GQ heads and share the K/V blocks of the split's groups; the
+// last split also walks the fp16 residual.
+struct AttnArgs {
+    const uint8_t *blocks;
+    int64_t max_groups;
+    int64_t block_bytes;
+    const void *ring_k, *ring_v;  // fp16 ring
+    int64_t ring_cap;
+    const void *q;              // [B][Hq][T][D]
+    int32_t q_is_f32;
+    float *out;                 // [B][Hq][T][D] float32
+    float *part_o;              // [B*Hq*T][splits][D] (splits > 1)
+    float *part_ml;             // [B*Hq*T][splits][2]  (m log2, l)
+    int32_t batch, kv_heads, q_heads;
+    int32_t bits;
+    int64_t n_tokens, n_quant;  // n, Q(n)
+    int64_t T;                  // queries per (batch, query head)
+    int32_t causal;             // query t is token n - T + t and sees tokens <= it
+    int32_t qblocks;            // query blocks per stream
+    int32_t splits;             // group ranges per (stream, query block)
+    int32_t groups_per_split;
+    float sm_log2;              // softmax scale * log2(e)
+};
+
 hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
+
+constexpr int kAttnWaves = 8;   // wavefronts per attention workgroup
 
 }  // namespace kivi

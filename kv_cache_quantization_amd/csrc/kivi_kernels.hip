@@ -579,10 +579,10 @@ __device__ __forceinline__ float load_q(const DecodeArgs &a, int64_t idx) {
 // q of query head hq as fp16 pairs in B-operand order: slice s, pair m ->
 // channels 32s + 8*Gl + 2m, +1 (one 16-byte load per slice for fp16 q).
 template <bool QF32>
-__device__ __forceinline__ void load_q_operand(const DecodeArgs &a, int64_t qrow, int Gl,
+__device__ __forceinline__ void load_q_operand(const void *qp, int64_t qrow, int Gl,
                                                h2 (&qB)[4][4]) {
     if constexpr (QF32) {
-        const float *q = (const float *)a.q + qrow + 8 * Gl;
+        const float *q = (const float *)qp + qrow + 8 * Gl;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             const float4 x0 = *(const float4 *)(q + 32 * s);
@@ -593,7 +593,7 @@ __device__ __forceinline__ void load_q_operand(const DecodeArgs &a, int64_t qrow
             qB[s][3] = (h2){(_Float16)x1.z, (_Float16)x1.w};
         }
     } else {
-        const _Float16 *q = (const _Float16 *)a.q + qrow + 8 * Gl;
+        const _Float16 *q = (const _Float16 *)qp + qrow + 8 * Gl;
 #pragma unroll
         for (int s = 0; s < 4; s++) split4(*(const uint4 *)(q + 32 * s), qB[s]);
     }
@@ -757,7 +757,7 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
     h2 qB[4][4];
     // (no wait here: the first chunk's loads overlap those of q, and the
     // compiler's wait before the first use of q also covers the copies)
-    load_q_operand<QF32>(a, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
+    load_q_operand<QF32>(a.q, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
     // running state: per head (m, l) (wave-uniform) and the lane's two channels
     float Mr[GQ], Lr[GQ], O0[GQ], O1[GQ];
 #pragma unroll
@@ -966,7 +966,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     // (The compiler's own wait before the first use of q also covers the
     // copies, which it does not see: loads complete in order.)
     h2 qB[4][4];
-    load_q_operand<QF32>(a, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
+    load_q_operand<QF32>(a.q, ((int64_t)b * a.q_heads + hq) * D, Gl, qB);
     uint4 uq;
     {
         const int64_t qoff = ((int64_t)b * a.q_heads + hk * GQ + (l >> 4) % GQ) * D + 8 * (l & 15);
@@ -1112,17 +1112,20 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         decode_split<BITS, GQ, false>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
 }
 
-// Merge the partials of one (batch, query head).  The split weights
-// 2^(m_s - M) are computed once in LDS; each thread then sums one channel.
+// Merge the partials of one output row (a (batch, query head) of the decode
+// step, or a (batch, query head, query) of the attention of T queries):
+// part_o [rows][items][D], part_ml [rows][items][2].  The weights 2^(m_s - M)
+// are computed once in LDS; each thread then sums one channel.
 constexpr int kMaxItems = 4160;
 
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(128) void combine_rows_kernel(const float *part_o,
+                                                           const float *part_ml, float *out,
+                                                           int items) {
     __shared__ float w[kMaxItems];
     __shared__ float red[128];
-    const int64_t bh = blockIdx.x;
+    const int64_t row = blockIdx.x;
     const int c = threadIdx.x;
-    const int items = a.splits + 1;
-    const float *ml = a.part_ml + bh * items * 2;
+    const float *ml = part_ml + row * items * 2;
     float M = -INFINITY;
     for (int s = c; s < items; s += 128)
         if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
@@ -1148,7 +1151,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
         __syncthreads();
     }
     const float L = red[0];
-    const float *po = a.part_o + bh * items * D + c;
+    const float *po = part_o + row * items * D + c;
     float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
     int s = 0;
     for (; s + 4 <= items; s += 4) {
@@ -1158,7 +1161,317 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
         acc3 = __builtin_fmaf(po[(int64_t)(s + 3) * D], w[s + 3], acc3);
     }
     for (; s < items; s++) acc0 = __builtin_fmaf(po[(int64_t)s * D], w[s], acc0);
-    a.out[bh * D + c] = ((acc0 + acc1) + (acc2 + acc3)) / L;
+    out[row * D + c] = ((acc0 + acc1) + (acc2 + acc3)) / L;
+}
+
+// ===========================================================================
+// Attention of T queries per (batch, query head) over the packed cache
+// ===========================================================================
+// The same products as the decode path, with the matrix core's 16 columns
+// holding QT = 16 / GQ queries x GQ heads (column j: query j / GQ of the
+// wavefront's block, head j % GQ): no column is a replica, so each value
+// channel group gets its own B operand.  The kAttnWaves wavefronts of a
+// workgroup share each group's block: wavefront 0 copies it HBM -> LDS and
+// one barrier per group hands it to all.  p is kept as P_s = 2^(s - m - kSlack)
+// in fp16 (<= 1); the sums of p and of p * vzero run on the matrix core, and
+// every accumulator carries the same 2^-kSlack, which cancels in o = acc / l.
+
+// Online-softmax step over the 8 scores a lane holds.  nm caches -m_run -
+// kSlack.  Returns P_s as fp16 pairs in operand order.
+__device__ __forceinline__ void attn_softmax(f4 &S0, f4 &S1, float cs, float kbl, float &m_run,
+                                             float &m_thr, float &nm, f4 &Lsum, f4 &Vz,
+                                             f4 (&accV)[8], h2 (&Ps)[4]) {
+    float mt = vmax(vmax(vmax(S0[0], S0[1]), vmax(S0[2], S0[3])),
+                    vmax(vmax(S1[0], S1[1]), vmax(S1[2], S1[3])));
+    mt = __builtin_fmaf(mt, cs, kbl);
+    if (__any(mt > m_thr)) {
+        const float m_new = vmax(m_run, xmax_rows(mt));
+        const float al = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int o = 0; o < 8; o++) accV[o] *= al;
+        Lsum *= al;
+        Vz *= al;
+        nm = -m_new - (float)kSlack;
+        m_run = m_new;
+        m_thr = m_new + (float)kSlack;
+    }
+    const float nk = nm + kbl;
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], cs, nk));
+        p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[e], cs, nk));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        Ps[m][0] = (_Float16)p[2 * m];
+        Ps[m][1] = (_Float16)p[2 * m + 1];
+    }
+}
+
+// Scores of rows past `last_ok` (and, causally, of tokens past the lane's
+// query) become -inf.  Row r of tile t is token tok0 + 16t + 4Gl + e.
+__device__ __forceinline__ void mask_scores(f4 &S0, f4 &S1, int64_t tok0, int Gl, int cnt,
+                                            int64_t pq) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const int r0 = 4 * Gl + e, r1 = 16 + 4 * Gl + e;
+        if (r0 >= cnt || tok0 + r0 > pq) S0[e] = -INFINITY;
+        if (r1 >= cnt || tok0 + r1 > pq) S1[e] = -INFINITY;
+    }
+}
+
+template <int BITS, int GQ, bool QF32>
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
+    using PP = Pipe<BITS>;
+    constexpr int W = kAttnWaves;
+    constexpr int QT = 16 / GQ;                 // queries per wavefront
+    constexpr int DPL = 2 * BITS;
+    constexpr int VTS = 40;                     // fp16 per transposed value row (80 B)
+    __shared__ __attribute__((aligned(16))) uint8_t ring[PP::NST * PP::BB];
+    __shared__ uint4 qs[W][4][64];              // unscaled fp16 q, B-operand order
+    __shared__ __attribute__((aligned(16))) _Float16 vt[D * VTS];
+
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int j = l & 15, Gl = l >> 4;
+    const int h = j % GQ;
+    const int split = (int)(blockIdx.x % (unsigned)a.splits);
+    const int64_t sq = blockIdx.x / (unsigned)a.splits;
+    const int qb = (int)(sq % a.qblocks);
+    const int stream = (int)(sq / a.qblocks);
+    const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
+    const int64_t T = a.T, n = a.n_tokens;
+    const int64_t qi0 = ((int64_t)qb * W + w) * QT;     // the wavefront's first query
+    const int64_t qi = qi0 + j / GQ;                    // the lane's column's query
+    const bool col_ok = qi < T, wave_ok = qi0 < T;
+    // last token each column sees; the workgroup's last query bounds the work
+    const int64_t pq = a.causal ? n - T + qi : n - 1;
+    const int64_t pq_wave = a.causal ? n - T + qi0 : n - 1;     // smallest in the wave
+    int64_t qi_wg = ((int64_t)qb + 1) * W * QT - 1;
+    if (qi_wg > T - 1) qi_wg = T - 1;
+    const int64_t pq_wg = a.causal ? n - T + qi_wg : n - 1;
+
+    const int64_t ng = a.n_quant / G;
+    const int64_t g0 = (int64_t)split * a.groups_per_split;
+    int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
+    if (g1 > pq_wg / G + 1) g1 = pq_wg / G + 1;        // groups past every query
+    const int n_g = g1 > g0 ? (int)(g1 - g0) : 0;
+
+    const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
+    const uint32_t rbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
+    h2 qB[4][4];
+    const int64_t qrow = (((int64_t)b * a.q_heads + hk * GQ + h) * T + (col_ok ? qi : 0)) * D;
+    load_q_operand<QF32>(a.q, qrow, Gl, qB);
+    int issued = 0, is = 0, rs = 0;
+    if (w == 0) {
+        for (; issued < PP::NST - 1 && issued < n_g; issued++) {
+            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, rbase + (uint32_t)is * PP::BB, l);
+            is = is + 1 == PP::NST ? 0 : is + 1;
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            asm volatile("" : "+v"(qB[s][m]));
+            if (!col_ok) qB[s][m] = (h2){(_Float16)0.f, (_Float16)0.f};
+        }
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+        uint4 u;
+        u.x = __builtin_bit_cast(uint32_t, qB[s][0]); u.y = __builtin_bit_cast(uint32_t, qB[s][1]);
+        u.z = __builtin_bit_cast(uint32_t, qB[s][2]); u.w = __builtin_bit_cast(uint32_t, qB[s][3]);
+        qs[w][s][l] = u;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
+        const h2 d2 = {dn, dn};
+#pragma unroll
+        for (int s = 0; s < 4; s++) qB[s][m] = qB[s][m] * d2;
+    }
+    h8 ones;
+#pragma unroll
+    for (int i = 0; i < 8; i++) ones[i] = (_Float16)1.0f;
+
+    float m_run = -INFINITY, m_thr = -INFINITY, nm = 0.f;
+    f4 Lsum = (f4){0.f, 0.f, 0.f, 0.f}, Vz = Lsum;
+    f4 accV[8];
+#pragma unroll
+    for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
+    const float csq = a.sm_log2 * kTwo24;
+
+    for (int g = 0; g < n_g; g++) {
+        if (w == 0) wait_groups_after<BITS>(issued - 1 - g);
+        __syncthreads();            // group g landed; every wave is done with g - 1
+        if (w == 0 && issued < n_g) {
+            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, rbase + (uint32_t)is * PP::BB, l);
+            is = is + 1 == PP::NST ? 0 : is + 1;
+            issued++;
+        }
+        const uint8_t *stg = ring + rs * PP::BB;
+        rs = rs + 1 == PP::NST ? 0 : rs + 1;
+        if (!wave_ok) continue;
+        const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
+        const uint2 *s2 = (const uint2 *)side;
+        uint32_t kc[DPL], vc[DPL];
+#pragma unroll
+        for (int w4 = 0; w4 < BITS / 2; w4++) {
+            const uint4 u = *(const uint4 *)(stg + w4 * 1024 + 16 * l);
+            const uint4 v = *(const uint4 *)(stg + PP::CB + w4 * 1024 + 16 * l);
+            kc[4 * w4] = u.x; kc[4 * w4 + 1] = u.y; kc[4 * w4 + 2] = u.z; kc[4 * w4 + 3] = u.w;
+            vc[4 * w4] = v.x; vc[4 * w4 + 1] = v.y; vc[4 * w4 + 2] = v.z; vc[4 * w4 + 3] = v.w;
+        }
+        // key-zero bias (every row of a column holds it), then the code products
+        f4 Sk = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+            Sk = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, side[16 + 4 * s + Gl]),
+                                                       __builtin_bit_cast(h8, qs[w][s][l]), Sk, 0,
+                                                       0, 0);
+        f4 S0 = (f4){0.f, 0.f, 0.f, 0.f}, S1 = S0;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            h2 ks[4], qh[4], ql[4];
+            split4(side[4 * s + Gl], ks);
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                qh[m] = qB[s][m] * ks[m];
+                ql[m] = __builtin_elementwise_fma(qB[s][m], ks[m], -qh[m]);
+            }
+            const h8 A0 = unpack_operand<BITS>(kc, s), A1 = unpack_operand<BITS>(kc, 4 + s);
+            const h8 Bh = pack_h8(qh), Bl = pack_h8(ql);
+            S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, S1, 0, 0, 0);
+            S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1, 0, 0, 0);
+        }
+        const int64_t tok0 = (g0 + g) * G;
+        if (tok0 + G - 1 > pq_wave) mask_scores(S0, S1, tok0, Gl, G, pq);
+        h2 Ps[4];
+        attn_softmax(S0, S1, csq, Sk[0] * a.sm_log2, m_run, m_thr, nm, Lsum, Vz, accV, Ps);
+        const h8 Bp = pack_h8(Ps);
+        Lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bp, Lsum, 0, 0, 0);
+        {
+            // value-zero bias: A row r carries vzero of channel group r % 4
+            const int cz = j & 3;
+            const uint2 z0 = s2[96 + 8 * cz + Gl], z1 = s2[96 + 8 * cz + Gl + 4];
+            const uint4 zz = {z0.x, z0.y, z1.x, z1.y};
+            Vz = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, zz), Bp, Vz, 0, 0, 0);
+        }
+        h2 Pc[4];
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
+            Pc[m] = m == 0 ? Ps[m] : Ps[m] * (h2){dn, dn};
+        }
+#pragma unroll
+        for (int cg = 0; cg < 4; cg++) {
+            const uint2 a0 = s2[64 + 8 * cg + Gl], a1 = s2[64 + 8 * cg + Gl + 4];
+            h2 ps[4];
+            ps[0] = Pc[0] * __builtin_bit_cast(h2, a0.x);
+            ps[1] = Pc[1] * __builtin_bit_cast(h2, a0.y);
+            ps[2] = Pc[2] * __builtin_bit_cast(h2, a1.x);
+            ps[3] = Pc[3] * __builtin_bit_cast(h2, a1.y);
+            const h8 Bv = pack_h8(ps);
+            accV[2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_operand<BITS>(vc, 2 * cg),
+                                                                 Bv, accV[2 * cg], 0, 0, 0);
+            accV[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                unpack_operand<BITS>(vc, 2 * cg + 1), Bv, accV[2 * cg + 1], 0, 0, 0);
+        }
+    }
+    // code products carry 2^-24: bring them to the residual's units
+#pragma unroll
+    for (int o = 0; o < 8; o++) accV[o] *= kTwo24;
+
+    // The last split walks the fp16 residual [Q, n) in 32-token chunks: the
+    // workgroup stages the chunk's value rows transposed in LDS (channel
+    // rows), each wavefront reads its K rows straight from the ring.
+    if (split == a.splits - 1 && n > a.n_quant) {
+        const int64_t nres = n - a.n_quant;
+        const int cap = (int)a.ring_cap;
+        const char *rkb = (const char *)a.ring_k + (int64_t)stream * a.ring_cap * D * 2;
+        const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * 2;
+        const int slot_q = (int)(a.n_quant % a.ring_cap);
+        for (int64_t c0 = 0; c0 < nres && a.n_quant + c0 <= pq_wg; c0 += G) {
+            const int cnt = nres - c0 < G ? (int)(nres - c0) : G;
+            auto slot = [&](int r) {
+                int s3 = slot_q + (int)(c0 % a.ring_cap) + (r < cnt ? r : cnt - 1);
+                while (s3 >= cap) s3 -= cap;
+                return s3;
+            };
+            __syncthreads();        // the previous chunk's transposed rows are read
+            for (int idx = threadIdx.x; idx < G * (D / 8); idx += 64 * W) {
+                const int r = idx >> 4, piece = idx & 15;
+                const uint4 v16 = *(const uint4 *)(rvb + (int64_t)slot(r) * D * 2 + 16 * piece);
+                h2 hv[4];
+                split4(v16, hv);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    vt[(8 * piece + 2 * i) * VTS + r] = hv[i][0];
+                    vt[(8 * piece + 2 * i + 1) * VTS + r] = hv[i][1];
+                }
+            }
+            __syncthreads();
+            if (!wave_ok) continue;
+            f4 S[2];
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const char *krow = rkb + (int64_t)slot(16 * t + j) * D * 2 + 16 * Gl;
+                S[t] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; s++)
+                    S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(h8, *(const uint4 *)(krow + 64 * s)),
+                        __builtin_bit_cast(h8, qs[w][s][l]), S[t], 0, 0, 0);
+            }
+            mask_scores(S[0], S[1], a.n_quant + c0, Gl, cnt, pq);
+            h2 Ps[4];
+            attn_softmax(S[0], S[1], a.sm_log2, 0.f, m_run, m_thr, nm, Lsum, Vz, accV, Ps);
+            const h8 Bp = pack_h8(Ps);
+            Lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bp, Lsum, 0, 0, 0);
+#pragma unroll
+            for (int o = 0; o < 8; o++) {
+                const _Float16 *row = vt + (16 * o + j) * VTS;
+                const uint2 v0 = *(const uint2 *)(row + 4 * Gl);
+                const uint2 v1 = *(const uint2 *)(row + 16 + 4 * Gl);
+                const uint4 vv = {v0.x, v0.y, v1.x, v1.y};
+                accV[o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, vv), Bp,
+                                                                accV[o], 0, 0, 0);
+            }
+        }
+    }
+
+    if (!wave_ok || !col_ok) return;
+    // lane (j, Gl) holds channels 16o + 4Gl + e of its column; Vz[e] is the
+    // bias of channel group e (rows repeat with period 4)
+    const int64_t row = ((int64_t)b * a.q_heads + hk * GQ + h) * T + qi;
+    const float L = Lsum[0];
+    if (a.splits == 1) {
+        const float inv = 1.0f / L;
+#pragma unroll
+        for (int o = 0; o < 8; o++) {
+            const float bz = Vz[o / 2];
+            float4 v;
+            v.x = (accV[o][0] + bz) * inv;
+            v.y = (accV[o][1] + bz) * inv;
+            v.z = (accV[o][2] + bz) * inv;
+            v.w = (accV[o][3] + bz) * inv;
+            *(float4 *)&a.out[row * D + 16 * o + 4 * Gl] = v;
+        }
+    } else {
+        const int64_t pi = row * a.splits + split;
+#pragma unroll
+        for (int o = 0; o < 8; o++) {
+            const float bz = Vz[o / 2];
+            const float4 v = {accV[o][0] + bz, accV[o][1] + bz, accV[o][2] + bz, accV[o][3] + bz};
+            *(float4 *)&a.part_o[pi * D + 16 * o + 4 * Gl] = v;
+        }
+        if (Gl == 0) {
+            a.part_ml[2 * pi] = m_run;
+            a.part_ml[2 * pi + 1] = L;
+        }
+    }
 }
 
 // ===========================================================================
@@ -1219,8 +1532,38 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     else launch_decode_bits<4>(a, gq, grid, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(a.batch * a.q_heads)), dim3(128), 0,
-                       s, a);
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)(a.batch * a.q_heads)), dim3(128), 0,
+                       s, (const float *)a.part_o, (const float *)a.part_ml, a.out, a.splits + 1);
+    return hipGetLastError();
+}
+
+template <int BITS, bool QF32>
+static void launch_attn_bits(const AttnArgs &a, int gq, dim3 grid, hipStream_t s) {
+    const dim3 block(64 * kAttnWaves);
+    if (gq == 4) hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32>), grid, block, 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32>), grid, block, 0, s, a);
+}
+
+hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
+    const int64_t streams = (int64_t)a.batch * a.kv_heads;
+    const int gq = a.q_heads / a.kv_heads;
+    const int64_t workgroups = streams * a.qblocks * a.splits;
+    const int64_t rows = (int64_t)a.batch * a.q_heads * a.T;
+    if (a.splits < 1 || a.splits > kMaxItems || workgroups > 0x7FFFFFFF || rows > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)workgroups);
+    if (a.bits == 2) {
+        if (a.q_is_f32) launch_attn_bits<2, true>(a, gq, grid, s);
+        else launch_attn_bits<2, false>(a, gq, grid, s);
+    } else {
+        if (a.q_is_f32) launch_attn_bits<4, true>(a, gq, grid, s);
+        else launch_attn_bits<4, false>(a, gq, grid, s);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1) return e;
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)rows), dim3(128), 0, s,
+                       (const float *)a.part_o, (const float *)a.part_ml, a.out, a.splits);
     return hipGetLastError();
 }
 

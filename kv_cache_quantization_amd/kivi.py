@@ -30,7 +30,8 @@ KIVI_DEFER_FLUSH = 1
 EXPORTED = (
     "kivi_cache_bytes", "kivi_cache_create", "kivi_cache_destroy", "kivi_append",
     "kivi_flush", "kivi_plan_append", "kivi_decode_workspace_bytes",
-    "kivi_decode_plan", "kivi_decode_attn", "kivi_get_layout", "kivi_status_string",
+    "kivi_decode_plan", "kivi_decode_attn", "kivi_attn", "kivi_attn_workspace_bytes",
+    "kivi_attn_plan", "kivi_get_layout", "kivi_status_string",
 )
 
 
@@ -96,6 +97,13 @@ def lib():
         L.kivi_decode_plan.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kivi_decode_attn.restype = i32
         L.kivi_decode_attn.argtypes = [P, P, i32, ctypes.c_float, P, P, sz, P]
+        L.kivi_attn.restype = i32
+        L.kivi_attn.argtypes = [P, P, i32, i64, i32, ctypes.c_float, P, P, sz, P]
+        L.kivi_attn_workspace_bytes.restype = sz
+        L.kivi_attn_workspace_bytes.argtypes = [P, i64]
+        L.kivi_attn_plan.restype = i32
+        L.kivi_attn_plan.argtypes = [P, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                     ctypes.POINTER(i32)]
         L.kivi_get_layout.restype = i32
         L.kivi_get_layout.argtypes = [P, ctypes.POINTER(kivi_layout)]
         L.kivi_status_string.restype = ctypes.c_char_p
@@ -159,6 +167,23 @@ def kivi_decode_attn(handle: int, q: int, q_dtype: int, softmax_scale: float, ou
                      workspace: int, ws_bytes: int, stream: int) -> None:
     _check(lib().kivi_decode_attn(handle, q, q_dtype, softmax_scale, out, workspace,
                                   ws_bytes, stream), "kivi_decode_attn")
+
+
+def kivi_attn(handle: int, q: int, q_dtype: int, T: int, causal: int, softmax_scale: float,
+              out: int, workspace: int, ws_bytes: int, stream: int) -> None:
+    _check(lib().kivi_attn(handle, q, q_dtype, T, causal, softmax_scale, out, workspace,
+                           ws_bytes, stream), "kivi_attn")
+
+
+def kivi_attn_workspace_bytes(handle: int, T: int) -> int:
+    return int(lib().kivi_attn_workspace_bytes(handle, T))
+
+
+def kivi_attn_plan(handle: int, T: int):
+    qb, s, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().kivi_attn_plan(handle, T, ctypes.byref(qb), ctypes.byref(s), ctypes.byref(g)),
+           "kivi_attn_plan")
+    return qb.value, s.value, g.value
 
 
 def kivi_get_layout(handle: int) -> kivi_layout:

@@ -81,6 +81,21 @@ def queries_host(cfg_id: int, B: int, Hq: int, D: int = 128, step: int = 0,
     return rng.standard_normal((B, Hq, D), dtype=np.float32).astype(dtype)
 
 
+def queries_multi_host(cfg_id: int, B: int, Hq: int, T: int, D: int = 128, dtype=np.float16):
+    """T query rows per (batch, query head): [B, Hq, T, D], row t drawn as
+    queries_host(..., step=t)."""
+    return np.stack([queries_host(cfg_id, B, Hq, D, step=t, dtype=dtype) for t in range(T)],
+                    axis=2)
+
+
+def queries_multi_device(cfg_id: int, B: int, Hq: int, T: int, D: int = 128, device="cuda"):
+    """[B, Hq, T, D] float16 query rows drawn on the device."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(_torch_seed(cfg_id, TENSOR_Q, "multi", T))
+    return torch.randn((B, Hq, T, D), generator=g, device=device,
+                       dtype=torch.float32).to(torch.float16)
+
+
 def _torch_seed(*key) -> int:
     h = hashlib.sha256(("kivi-synth-" + "-".join(str(k) for k in key)).encode()).digest()
     return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
