@@ -104,6 +104,46 @@ def cpu_baseline(k_dev, v_dev, q_dev, bits, R, H, Hq, sample_b):
         seconds=dict(quantize=t1 - t0, decode=t2 - t1))
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
+
+
+def attn_measure(cache, B, Hq, n, T, stream, evict, evict_out, do_evict):
+    """The attention of T causal queries per head (the last T cached tokens,
+    as in a chunked-prefill step) over the cache the decode steps built.
+    Useful flops: 2 * 2 * D per (query, visible token, query head)."""
+    import torch
+    from kv_cache_quantization_amd import synth, kivi
+    D = 128
+    qm = synth.queries_multi_device(3, B, Hq, T, D)
+    out = torch.empty((B, Hq, T, D), dtype=torch.float32, device=qm.device)
+    ms = []
+    for i in range(6):
+        if do_evict:
+            torch.amax(evict, dim=0, out=evict_out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.attn(qm, causal=True, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 1:
+            ms.append(e0.elapsed_time(e1))
+    t = sum(ms) / len(ms) / 1e3
+    seen = sum(n - T + t_ + 1 for t_ in range(T))
+    flops = 4.0 * D * B * Hq * seen
+    tf = flops / t / 1e12
+    qb, splits, gps = kivi.kivi_attn_plan(cache.handle, T)
+    return {
+        "workload": "attention of %d causal queries per head (the last %d cached tokens) over "
+                    "the same cache, fp16 queries" % (T, T),
+        "T": T, "ms": round(t * 1e3, 4), "median_ms": round(sorted(ms)[len(ms) // 2], 4),
+        "useful_flops": flops,
+        "plan": {"query_blocks": qb, "splits": splits, "groups_per_split": gps},
+        "roofline": {"bound": "mfma", "kernel": "attn (one kivi_attn call)",
+                     "achieved": round(tf, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +156,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk (0: one shot)")
     ap.add_argument("--cpu-sample", type=int, default=2, help="batch entries timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-evict", action="store_true")
+    ap.add_argument("--attn-queries", type=int, default=256,
+                    help="also time the attention of this many causal queries per head over "
+                         "the same cache (a chunked-prefill step; 0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -256,6 +299,9 @@ def main():
                   " 1 GiB eviction read before each phase (outside the phase events)"
                   if not args.no_evict else "HIP events, no eviction (warm)",
     }
+    if args.attn_queries > 0:
+        rec["attn"] = attn_measure(cache, B, Hq, n, args.attn_queries, stream, evict, evict_out,
+                                   not args.no_evict)
     if args.cpu_sample > 0:
         k0, v0 = chunks[0]
         if chunk == n:

@@ -138,3 +138,40 @@ def test_capacity_b32_131072_chunked(bits):
                    "capacity-%d" % bits)
     del cache
     torch.cuda.empty_cache()
+
+
+def test_attn_long_context_b16():
+    """Attention of T = 256 causal queries (a chunked-prefill step) and of 16
+    unmasked queries over the long-context cache (batch 16, context 32768,
+    2-bit, residual 128), in the launch configuration the benchmark times.
+    Sampled streams and query rows are checked against the oracle: causal row
+    t is the decode step over the first n - T + t + 1 dequantized tokens."""
+    import torch
+    from kv_cache_quantization_amd import KiviCache, synth
+    import oracle as orc
+    B, n, R, bits = 16, 32768, 128, 2
+    log("case attn long-context B=%d n=%d" % (B, n))
+    k, v = synth.kv_device(3, B, H, n)
+    cache = KiviCache(B, H, HQ, n, bits=bits, residual=R, device="cuda:0")
+    cache.append(k, v)
+    sample = [(0, 0), (15, 7)]
+    ks = {s: k[s].cpu().numpy() for s in sample}
+    vs = {s: v[s].cpu().numpy() for s in sample}
+    del k, v
+    for T, causal, rows in ((256, True, (0, 100, 255)), (16, False, (0, 15))):
+        qm = synth.queries_multi_device(3, B, HQ, T)
+        out = cache.attn(qm, causal=causal).cpu().numpy()
+        qh = qm.cpu().numpy()
+        assert np.isfinite(out).all()
+        for (b, h) in sample:
+            ref_c = orc.build_cache(ks[(b, h)][None, None], vs[(b, h)][None, None], bits, G, R)
+            kh, vh = orc.dequant_cache(ks[(b, h)][None, None], vs[(b, h)][None, None], ref_c)
+            for t in rows:
+                seen = n - T + t + 1 if causal else n
+                q1 = qh[b, GQ * h:GQ * (h + 1), t][None]
+                ref = orc.decode_attn(q1, kh[:, :, :seen], vh[:, :, :seen])
+                e = rel_err(out[b, GQ * h:GQ * (h + 1), t], ref[0])
+                log("  T=%d causal=%d stream (%d, %d) row %d: rel err %.3g" % (T, causal, b, h, t, e))
+                assert e <= TOL, (T, causal, b, h, t, e)
+    del cache
+    torch.cuda.empty_cache()
