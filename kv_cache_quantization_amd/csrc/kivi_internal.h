@@ -92,5 +92,6 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
 
 constexpr int kAttnWaves = 8;   // wavefronts per attention workgroup
+constexpr int kAttnBlocks = 1;  // 16-column blocks per attention wavefront (2 measured no faster)
 
 }  // namespace kivi

@@ -1221,15 +1221,15 @@ __device__ __forceinline__ void mask_scores(f4 &S0, f4 &S1, int64_t tok0, int Gl
     }
 }
 
-template <int BITS, int GQ, bool QF32>
+template <int BITS, int GQ, bool QF32, int CB>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
     using PP = Pipe<BITS>;
     constexpr int W = kAttnWaves;
-    constexpr int QT = 16 / GQ;                 // queries per wavefront
+    constexpr int QT = 16 / GQ;                 // queries per column block
     constexpr int DPL = 2 * BITS;
     constexpr int VTS = 40;                     // fp16 per transposed value row (80 B)
     __shared__ __attribute__((aligned(16))) uint8_t ring[PP::NST * PP::BB];
-    __shared__ uint4 qs[W][4][64];              // unscaled fp16 q, B-operand order
+    __shared__ uint4 qs[W][CB][4][64];          // unscaled fp16 q, B-operand order
     __shared__ __attribute__((aligned(16))) _Float16 vt[D * VTS];
 
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1241,15 +1241,21 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
     const int stream = (int)(sq / a.qblocks);
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const int64_t T = a.T, n = a.n_tokens;
-    const int64_t qi0 = ((int64_t)qb * W + w) * QT;     // the wavefront's first query
-    const int64_t qi = qi0 + j / GQ;                    // the lane's column's query
-    const bool col_ok = qi < T, wave_ok = qi0 < T;
-    // last token each column sees; the workgroup's last query bounds the work
-    const int64_t pq = a.causal ? n - T + qi : n - 1;
-    const int64_t pq_wave = a.causal ? n - T + qi0 : n - 1;     // smallest in the wave
-    int64_t qi_wg = ((int64_t)qb + 1) * W * QT - 1;
+    // column block c of this wavefront: queries qi0[c] .. qi0[c] + QT - 1
+    const int64_t qw0 = ((int64_t)qb * W + w) * CB * QT;
+    const bool wave_ok = qw0 < T;
+    const int64_t pq_wave = a.causal ? n - T + qw0 : n - 1;   // smallest in the wave
+    int64_t qi_wg = ((int64_t)qb + 1) * W * CB * QT - 1;
     if (qi_wg > T - 1) qi_wg = T - 1;
     const int64_t pq_wg = a.causal ? n - T + qi_wg : n - 1;
+    int64_t qi[CB], pq[CB];
+    bool col_ok[CB];
+#pragma unroll
+    for (int c = 0; c < CB; c++) {
+        qi[c] = qw0 + c * QT + j / GQ;
+        col_ok[c] = qi[c] < T;
+        pq[c] = a.causal ? n - T + qi[c] : n - 1;             // last token the column sees
+    }
 
     const int64_t ng = a.n_quant / G;
     const int64_t g0 = (int64_t)split * a.groups_per_split;
@@ -1259,9 +1265,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
 
     const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
     const uint32_t rbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
-    h2 qB[4][4];
-    const int64_t qrow = (((int64_t)b * a.q_heads + hk * GQ + h) * T + (col_ok ? qi : 0)) * D;
-    load_q_operand<QF32>(a.q, qrow, Gl, qB);
+    h2 qB[CB][4][4];
+#pragma unroll
+    for (int c = 0; c < CB; c++) {
+        const int64_t qrow =
+            (((int64_t)b * a.q_heads + hk * GQ + h) * T + (col_ok[c] ? qi[c] : 0)) * D;
+        load_q_operand<QF32>(a.q, qrow, Gl, qB[c]);
+    }
     int issued = 0, is = 0, rs = 0;
     if (w == 0) {
         for (; issued < PP::NST - 1 && issued < n_g; issued++) {
@@ -1270,35 +1280,47 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
         }
     }
 #pragma unroll
-    for (int s = 0; s < 4; s++)
+    for (int c = 0; c < CB; c++) {
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            asm volatile("" : "+v"(qB[s][m]));
-            if (!col_ok) qB[s][m] = (h2){(_Float16)0.f, (_Float16)0.f};
+        for (int s = 0; s < 4; s++)
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                asm volatile("" : "+v"(qB[c][s][m]));
+                if (!col_ok[c]) qB[c][s][m] = (h2){(_Float16)0.f, (_Float16)0.f};
+            }
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            uint4 u;
+            u.x = __builtin_bit_cast(uint32_t, qB[c][s][0]);
+            u.y = __builtin_bit_cast(uint32_t, qB[c][s][1]);
+            u.z = __builtin_bit_cast(uint32_t, qB[c][s][2]);
+            u.w = __builtin_bit_cast(uint32_t, qB[c][s][3]);
+            qs[w][c][s][l] = u;
         }
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
-        uint4 u;
-        u.x = __builtin_bit_cast(uint32_t, qB[s][0]); u.y = __builtin_bit_cast(uint32_t, qB[s][1]);
-        u.z = __builtin_bit_cast(uint32_t, qB[s][2]); u.w = __builtin_bit_cast(uint32_t, qB[s][3]);
-        qs[w][s][l] = u;
-    }
+        for (int m = 0; m < 4; m++) {
+            const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
+            const h2 d2 = {dn, dn};
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-        const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
-        const h2 d2 = {dn, dn};
-#pragma unroll
-        for (int s = 0; s < 4; s++) qB[s][m] = qB[s][m] * d2;
+            for (int s = 0; s < 4; s++) qB[c][s][m] = qB[c][s][m] * d2;
+        }
     }
     h8 ones;
 #pragma unroll
     for (int i = 0; i < 8; i++) ones[i] = (_Float16)1.0f;
 
-    float m_run = -INFINITY, m_thr = -INFINITY, nm = 0.f;
-    f4 Lsum = (f4){0.f, 0.f, 0.f, 0.f}, Vz = Lsum;
-    f4 accV[8];
+    float m_run[CB], m_thr[CB], nm[CB];
+    f4 Lsum[CB], Vz[CB], accV[CB][8];
 #pragma unroll
-    for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CB; c++) {
+        m_run[c] = -INFINITY;
+        m_thr[c] = -INFINITY;
+        nm[c] = 0.f;
+        Lsum[c] = (f4){0.f, 0.f, 0.f, 0.f};
+        Vz[c] = Lsum[c];
+#pragma unroll
+        for (int o = 0; o < 8; o++) accV[c][o] = (f4){0.f, 0.f, 0.f, 0.f};
+    }
     const float csq = a.sm_log2 * kTwo24;
 
     for (int g = 0; g < n_g; g++) {
@@ -1322,67 +1344,92 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
             kc[4 * w4] = u.x; kc[4 * w4 + 1] = u.y; kc[4 * w4 + 2] = u.z; kc[4 * w4 + 3] = u.w;
             vc[4 * w4] = v.x; vc[4 * w4 + 1] = v.y; vc[4 * w4 + 2] = v.z; vc[4 * w4 + 3] = v.w;
         }
-        // key-zero bias (every row of a column holds it), then the code products
-        f4 Sk = (f4){0.f, 0.f, 0.f, 0.f};
+        // key-zero bias (every row of a column holds it), then the code
+        // products: each key operand is unpacked once for all column blocks
+        f4 Sk[CB], S0[CB], S1[CB];
 #pragma unroll
-        for (int s = 0; s < 4; s++)
-            Sk = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, side[16 + 4 * s + Gl]),
-                                                       __builtin_bit_cast(h8, qs[w][s][l]), Sk, 0,
-                                                       0, 0);
-        f4 S0 = (f4){0.f, 0.f, 0.f, 0.f}, S1 = S0;
+        for (int c = 0; c < CB; c++) {
+            Sk[c] = (f4){0.f, 0.f, 0.f, 0.f};
+            S0[c] = Sk[c];
+            S1[c] = Sk[c];
+        }
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            h2 ks[4], qh[4], ql[4];
-            split4(side[4 * s + Gl], ks);
+            const h8 kz = __builtin_bit_cast(h8, side[16 + 4 * s + Gl]);
 #pragma unroll
-            for (int m = 0; m < 4; m++) {
-                qh[m] = qB[s][m] * ks[m];
-                ql[m] = __builtin_elementwise_fma(qB[s][m], ks[m], -qh[m]);
-            }
+            for (int c = 0; c < CB; c++)
+                Sk[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    kz, __builtin_bit_cast(h8, qs[w][c][s][l]), Sk[c], 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            h2 ks[4];
+            split4(side[4 * s + Gl], ks);
             const h8 A0 = unpack_operand<BITS>(kc, s), A1 = unpack_operand<BITS>(kc, 4 + s);
-            const h8 Bh = pack_h8(qh), Bl = pack_h8(ql);
-            S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, S1, 0, 0, 0);
-            S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < CB; c++) {
+                h2 qh[4], ql[4];
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    qh[m] = qB[c][s][m] * ks[m];
+                    ql[m] = __builtin_elementwise_fma(qB[c][s][m], ks[m], -qh[m]);
+                }
+                const h8 Bh = pack_h8(qh), Bl = pack_h8(ql);
+                S0[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, S0[c], 0, 0, 0);
+                S1[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, S1[c], 0, 0, 0);
+                S0[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, S0[c], 0, 0, 0);
+                S1[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1[c], 0, 0, 0);
+            }
         }
         const int64_t tok0 = (g0 + g) * G;
-        if (tok0 + G - 1 > pq_wave) mask_scores(S0, S1, tok0, Gl, G, pq);
-        h2 Ps[4];
-        attn_softmax(S0, S1, csq, Sk[0] * a.sm_log2, m_run, m_thr, nm, Lsum, Vz, accV, Ps);
-        const h8 Bp = pack_h8(Ps);
-        Lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bp, Lsum, 0, 0, 0);
-        {
-            // value-zero bias: A row r carries vzero of channel group r % 4
-            const int cz = j & 3;
-            const uint2 z0 = s2[96 + 8 * cz + Gl], z1 = s2[96 + 8 * cz + Gl + 4];
-            const uint4 zz = {z0.x, z0.y, z1.x, z1.y};
-            Vz = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, zz), Bp, Vz, 0, 0, 0);
-        }
-        h2 Pc[4];
+        const bool masked = tok0 + G - 1 > pq_wave;
+        h2 Pc[CB][4];
+        const int cz = j & 3;
+        const uint2 z0 = s2[96 + 8 * cz + Gl], z1 = s2[96 + 8 * cz + Gl + 4];
+        const uint4 zz = {z0.x, z0.y, z1.x, z1.y};
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
-            Pc[m] = m == 0 ? Ps[m] : Ps[m] * (h2){dn, dn};
+        for (int c = 0; c < CB; c++) {
+            if (masked) mask_scores(S0[c], S1[c], tok0, Gl, G, pq[c]);
+            h2 Ps[4];
+            attn_softmax(S0[c], S1[c], csq, Sk[c][0] * a.sm_log2, m_run[c], m_thr[c], nm[c],
+                         Lsum[c], Vz[c], accV[c], Ps);
+            const h8 Bp = pack_h8(Ps);
+            Lsum[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bp, Lsum[c], 0, 0, 0);
+            // value-zero bias: A row r carries vzero of channel group r % 4
+            Vz[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, zz), Bp, Vz[c],
+                                                          0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
+                Pc[c][m] = m == 0 ? Ps[m] : Ps[m] * (h2){dn, dn};
+            }
         }
 #pragma unroll
         for (int cg = 0; cg < 4; cg++) {
             const uint2 a0 = s2[64 + 8 * cg + Gl], a1 = s2[64 + 8 * cg + Gl + 4];
-            h2 ps[4];
-            ps[0] = Pc[0] * __builtin_bit_cast(h2, a0.x);
-            ps[1] = Pc[1] * __builtin_bit_cast(h2, a0.y);
-            ps[2] = Pc[2] * __builtin_bit_cast(h2, a1.x);
-            ps[3] = Pc[3] * __builtin_bit_cast(h2, a1.y);
-            const h8 Bv = pack_h8(ps);
-            accV[2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_operand<BITS>(vc, 2 * cg),
-                                                                 Bv, accV[2 * cg], 0, 0, 0);
-            accV[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                unpack_operand<BITS>(vc, 2 * cg + 1), Bv, accV[2 * cg + 1], 0, 0, 0);
+            const h2 v0 = __builtin_bit_cast(h2, a0.x), v1 = __builtin_bit_cast(h2, a0.y);
+            const h2 v2 = __builtin_bit_cast(h2, a1.x), v3 = __builtin_bit_cast(h2, a1.y);
+            const h8 U0 = unpack_operand<BITS>(vc, 2 * cg), U1 = unpack_operand<BITS>(vc, 2 * cg + 1);
+#pragma unroll
+            for (int c = 0; c < CB; c++) {
+                h2 ps[4];
+                ps[0] = Pc[c][0] * v0;
+                ps[1] = Pc[c][1] * v1;
+                ps[2] = Pc[c][2] * v2;
+                ps[3] = Pc[c][3] * v3;
+                const h8 Bv = pack_h8(ps);
+                accV[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(U0, Bv, accV[c][2 * cg],
+                                                                        0, 0, 0);
+                accV[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    U1, Bv, accV[c][2 * cg + 1], 0, 0, 0);
+            }
         }
     }
     // code products carry 2^-24: bring them to the residual's units
 #pragma unroll
-    for (int o = 0; o < 8; o++) accV[o] *= kTwo24;
+    for (int c = 0; c < CB; c++)
+#pragma unroll
+        for (int o = 0; o < 8; o++) accV[c][o] *= kTwo24;
 
     // The last split walks the fp16 residual [Q, n) in 32-token chunks: the
     // workgroup stages the chunk's value rows transposed in LDS (channel
@@ -1414,62 +1461,78 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
             }
             __syncthreads();
             if (!wave_ok) continue;
-            f4 S[2];
+            f4 S[CB][2];
+#pragma unroll
+            for (int c = 0; c < CB; c++) S[c][0] = S[c][1] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < 2; t++) {
                 const char *krow = rkb + (int64_t)slot(16 * t + j) * D * 2 + 16 * Gl;
-                S[t] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; s++)
-                    S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(h8, *(const uint4 *)(krow + 64 * s)),
-                        __builtin_bit_cast(h8, qs[w][s][l]), S[t], 0, 0, 0);
+                for (int s = 0; s < 4; s++) {
+                    const h8 kk = __builtin_bit_cast(h8, *(const uint4 *)(krow + 64 * s));
+#pragma unroll
+                    for (int c = 0; c < CB; c++)
+                        S[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            kk, __builtin_bit_cast(h8, qs[w][c][s][l]), S[c][t], 0, 0, 0);
+                }
             }
-            mask_scores(S[0], S[1], a.n_quant + c0, Gl, cnt, pq);
-            h2 Ps[4];
-            attn_softmax(S[0], S[1], a.sm_log2, 0.f, m_run, m_thr, nm, Lsum, Vz, accV, Ps);
-            const h8 Bp = pack_h8(Ps);
-            Lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bp, Lsum, 0, 0, 0);
+            h8 Bp[CB];
+#pragma unroll
+            for (int c = 0; c < CB; c++) {
+                mask_scores(S[c][0], S[c][1], a.n_quant + c0, Gl, cnt, pq[c]);
+                h2 Ps[4];
+                attn_softmax(S[c][0], S[c][1], a.sm_log2, 0.f, m_run[c], m_thr[c], nm[c], Lsum[c],
+                             Vz[c], accV[c], Ps);
+                Bp[c] = pack_h8(Ps);
+                Lsum[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bp[c], Lsum[c], 0, 0, 0);
+            }
 #pragma unroll
             for (int o = 0; o < 8; o++) {
                 const _Float16 *row = vt + (16 * o + j) * VTS;
                 const uint2 v0 = *(const uint2 *)(row + 4 * Gl);
                 const uint2 v1 = *(const uint2 *)(row + 16 + 4 * Gl);
                 const uint4 vv = {v0.x, v0.y, v1.x, v1.y};
-                accV[o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, vv), Bp,
-                                                                accV[o], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < CB; c++)
+                    accV[c][o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, vv),
+                                                                       Bp[c], accV[c][o], 0, 0, 0);
             }
         }
     }
 
-    if (!wave_ok || !col_ok) return;
+    if (!wave_ok) return;
     // lane (j, Gl) holds channels 16o + 4Gl + e of its column; Vz[e] is the
     // bias of channel group e (rows repeat with period 4)
-    const int64_t row = ((int64_t)b * a.q_heads + hk * GQ + h) * T + qi;
-    const float L = Lsum[0];
-    if (a.splits == 1) {
-        const float inv = 1.0f / L;
 #pragma unroll
-        for (int o = 0; o < 8; o++) {
-            const float bz = Vz[o / 2];
-            float4 v;
-            v.x = (accV[o][0] + bz) * inv;
-            v.y = (accV[o][1] + bz) * inv;
-            v.z = (accV[o][2] + bz) * inv;
-            v.w = (accV[o][3] + bz) * inv;
-            *(float4 *)&a.out[row * D + 16 * o + 4 * Gl] = v;
-        }
-    } else {
-        const int64_t pi = row * a.splits + split;
+    for (int c = 0; c < CB; c++) {
+        if (!col_ok[c]) continue;
+        const int64_t row = ((int64_t)b * a.q_heads + hk * GQ + h) * T + qi[c];
+        const float L = Lsum[c][0];
+        if (a.splits == 1) {
+            const float inv = 1.0f / L;
 #pragma unroll
-        for (int o = 0; o < 8; o++) {
-            const float bz = Vz[o / 2];
-            const float4 v = {accV[o][0] + bz, accV[o][1] + bz, accV[o][2] + bz, accV[o][3] + bz};
-            *(float4 *)&a.part_o[pi * D + 16 * o + 4 * Gl] = v;
-        }
-        if (Gl == 0) {
-            a.part_ml[2 * pi] = m_run;
-            a.part_ml[2 * pi + 1] = L;
+            for (int o = 0; o < 8; o++) {
+                const float bz = Vz[c][o / 2];
+                float4 v;
+                v.x = (accV[c][o][0] + bz) * inv;
+                v.y = (accV[c][o][1] + bz) * inv;
+                v.z = (accV[c][o][2] + bz) * inv;
+                v.w = (accV[c][o][3] + bz) * inv;
+                *(float4 *)&a.out[row * D + 16 * o + 4 * Gl] = v;
+            }
+        } else {
+            const int64_t pi = row * a.splits + split;
+#pragma unroll
+            for (int o = 0; o < 8; o++) {
+                const float bz = Vz[c][o / 2];
+                const float4 v = {accV[c][o][0] + bz, accV[c][o][1] + bz, accV[c][o][2] + bz,
+                                  accV[c][o][3] + bz};
+                *(float4 *)&a.part_o[pi * D + 16 * o + 4 * Gl] = v;
+            }
+            if (Gl == 0) {
+                a.part_ml[2 * pi] = m_run[c];
+                a.part_ml[2 * pi + 1] = L;
+            }
         }
     }
 }
@@ -1540,9 +1603,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
 template <int BITS, bool QF32>
 static void launch_attn_bits(const AttnArgs &a, int gq, dim3 grid, hipStream_t s) {
     const dim3 block(64 * kAttnWaves);
-    if (gq == 4) hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32>), grid, block, 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32>), grid, block, 0, s, a);
+    if (gq == 4) hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32, kAttnBlocks>), grid, block, 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32, kAttnBlocks>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32, kAttnBlocks>), grid, block, 0, s, a);
 }
 
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
