@@ -367,7 +367,9 @@ void oracle_attn_queries(const float *q, const float *khat, const float *vhat,
 /* Code dword index (within one code area) for lane l (0..63), lane dword w  */
 /* (0..2b-1): (w/4)*256 + 4*l + (w%4).  Inside a dword, the code of slot i   */
 /* (0 <= i < 16/b) in half h (0,1) sits at bit 16*h + b*i and belongs to     */
-/*   operand o = w*(4/b) + i/4,  kk = 2*(i%4) + h.                           */
+/*   operand o = w*(4/b) + i/4,  kk = 2*(i%4) + h        (b = 2, 4)          */
+/*   operand o = w/2,            kk = 4*(w%2) + 2*i + h  (b = 8: an operand  */
+/*                               spans two dwords)                           */
 /* Keys:   token = 16*(o/4) + l%16,      channel = 32*(o%4) + 8*(l/16) + kk  */
 /* Values: channel = 16*o + l%16,        token = 4*(l/16) + kk%4 + 16*(kk/4) */
 /* Only D = 128, G = 32 is laid out this way.                                */
@@ -381,8 +383,8 @@ static void code_position(int bits, int is_v, int token, int channel,
         for (int w = 0; w < dpl; w++)
             for (int h = 0; h < 2; h++)
                 for (int i = 0; i < 16 / bits; i++) {
-                    int o = w * (4 / bits) + i / 4;
-                    int kk = 2 * (i % 4) + h;
+                    int o = bits == 8 ? w / 2 : w * (4 / bits) + i / 4;
+                    int kk = bits == 8 ? 4 * (w % 2) + 2 * i + h : 2 * (i % 4) + h;
                     int t, c;
                     if (!is_v) {
                         t = 16 * (o / 4) + l % 16;

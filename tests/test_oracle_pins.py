@@ -378,7 +378,7 @@ def test_dequantized_cache_consistent(orc):
 # b bits per code plus two fp16 per group).  Pinned by being a bijection onto
 # the code area and by the exact byte count.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_pack_layout_is_bijective(orc, bits):
     seen = set()
     for is_v in (False, True):
@@ -476,3 +476,25 @@ def test_attn_queries_notebook_checks(orc):
     assert rel4 < chk["rel_err_4bit_max"]
     lo, hi = chk["rel_err_2bit_open_interval"]
     assert lo < rel2 < hi
+
+
+def test_notebook_bit_sweep(orc):
+    """[NB] 'Attention quality vs bits-per-value': on the notebook's data the
+    attention error grows as the bit width drops through 8, 4, 3 and 2 bits,
+    and the largest step is the last one (the cliff below 4 bits that the
+    notebook plots)."""
+    from kv_cache_quantization_amd import synth
+    import torch
+    K, V, _ = synth.notebook_inputs()
+    K2, V2 = K[0, 0], V[0, 0]
+    q = torch.randn(1, 1024, 128, generator=torch.Generator().manual_seed(1)).numpy()
+    q = q.reshape(1, 1, 1024, 128)
+    ref = orc.attn_queries(q, K2.reshape(1, 1, 1024, 128), V2.reshape(1, 1, 1024, 128))
+    err = {}
+    for bits in (8, 4, 3, 2):
+        kh = orc.fake_quant_2d(K2, 0, bits, 32).reshape(1, 1, 1024, 128)
+        vh = orc.fake_quant_2d(V2, 1, bits, 32).reshape(1, 1, 1024, 128)
+        err[bits] = np.linalg.norm(ref - orc.attn_queries(q, kh, vh)) / np.linalg.norm(ref)
+    assert err[8] < err[4] < err[3] < err[2]
+    assert err[2] - err[3] > err[3] - err[4] > err[4] - err[8]
+    assert err[8] < 0.01           # 8 bits: near lossless on this data
