@@ -149,7 +149,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--bits", type=int, default=2, choices=(2, 4))
+    ap.add_argument("--bits", type=int, default=2, choices=(2, 4, 8))
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--context", type=int, default=32768)
     ap.add_argument("--residual", type=int, default=128)

@@ -69,7 +69,7 @@ typedef struct {
     int32_t n_kv_heads;   /* H  >= 1                                          */
     int32_t n_q_heads;    /* Hq: a multiple of H; Hq / H in {1, 2, 4}         */
     int32_t head_dim;     /* D: 128                                           */
-    int32_t bits;         /* b: 2 or 4                                        */
+    int32_t bits;         /* b: 2, 4 or 8                                     */
     int32_t group;        /* G: 32                                            */
     int32_t residual;     /* R >= 0, a multiple of G                          */
     int32_t kv_dtype;     /* kivi_dtype of the K/V rows handed to append      */

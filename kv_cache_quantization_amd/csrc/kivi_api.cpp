@@ -48,7 +48,7 @@ kivi_status validate(const kivi_config *c) {
     if (!c) return KIVI_ERR_INVALID_ARG;
     if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_tokens < 1)
         return KIVI_ERR_INVALID_ARG;
-    if (c->bits != 2 && c->bits != 4) return KIVI_ERR_INVALID_ARG;
+    if (c->bits != 2 && c->bits != 4 && c->bits != 8) return KIVI_ERR_INVALID_ARG;
     if (c->group < 1 || c->head_dim < 1 || c->head_dim % c->group != 0) return KIVI_ERR_INVALID_ARG;
     if (c->residual < 0 || c->residual % c->group != 0) return KIVI_ERR_INVALID_ARG;
     if ((int64_t)c->group * c->bits % 64 != 0) return KIVI_ERR_INVALID_ARG;

@@ -24,7 +24,7 @@ struct QuantizeArgs {
     int64_t group_begin, group_end;
     int32_t streams;
     int32_t is_f32;             // kv dtype: 0 fp16, 1 fp32
-    int32_t bits;               // 2 or 4
+    int32_t bits;               // 2, 4 or 8
 };
 
 // Copy tokens [tok_begin, tok_end) of every stream from the appended chunk

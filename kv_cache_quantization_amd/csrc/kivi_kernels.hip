@@ -257,8 +257,8 @@ __device__ __forceinline__ void group_minmax(const Tile<float> &t, float (&lo)[8
 
 // zero = min (+0 for a zero minimum), scale = RN((max - zero) / L), or 1 for a
 // constant group.  RN(x / L) = fma(fma(-q0, L, x), RN(1/L), q0) with
-// q0 = RN(x * RN(1/L)) for every positive finite x (L = 3, 15); +inf and NaN
-// ranges take q0, which is then the quotient itself.
+// q0 = RN(x * RN(1/L)) for every positive finite x (L = 3, 15, 255: checked
+// on all of them); +inf and NaN ranges take q0, which is then the quotient.
 template <int BITS>
 __device__ __forceinline__ void group_params(float lo, float hi, float &mn, float &s) {
 #pragma clang fp contract(off)
@@ -284,7 +284,8 @@ __device__ __forceinline__ float exact_code(float x, float mn, float s, float L)
 // Packed position of code kk (0..7) inside its unit: at 2 bits a 16-bit unit
 // with even kk in the low byte and odd kk in the high byte, two bits apart;
 // at 4 bits a 32-bit unit with even kk in the low half, odd in the high half,
-// four bits apart (accumulated as two 16-bit halves).
+// four bits apart (accumulated as two 16-bit halves); at 8 bits two 32-bit
+// dwords p = kk / 4, code kk at bit 8 * ((kk / 2) % 2) + 16 * (kk % 2).
 template <int BITS>
 __device__ __forceinline__ constexpr float unit_weight(int kk) {
     return BITS == 2 ? (float)(1u << (8 * (kk & 1) + 2 * (kk >> 1)))
@@ -294,6 +295,78 @@ __device__ __forceinline__ constexpr float unit_weight(int kk) {
 // Two floats as an fp16 pair (round to nearest even).
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
     return __builtin_bit_cast(uint32_t, (h2){(_Float16)a, (_Float16)b});
+}
+
+// 8-bit codes: each unit is two dwords, packed with v_cvt_pk_u8_f32, then
+// moved to operand order through LDS (operand o of a lane = its dwords 2o,
+// 2o + 1) and stored as 16 dwords per lane.
+template <bool IS_V, typename TT>
+__device__ __forceinline__ void quantize_pack8(const QuantizeArgs &a, const TT &t,
+                                               const float (&mn)[8], const float (&s)[8],
+                                               const float (&y)[8], const float (&cz)[8],
+                                               float near_tie, bool fast_ok, uint8_t *blk,
+                                               uint32_t *tr) {
+#pragma clang fp contract(off)
+    constexpr float L = 255.0f;
+    constexpr int DPL = 16;
+    constexpr int cbytes = 8 * G * D / 8;
+    const int l = threadIdx.x;
+    const int q = l >> 4, c = l & 15;
+    uint32_t unit[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+        float cd[8];
+        float rmax = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++) {
+            const float tq = IS_V ? t.fma(kk, u, y[kk], cz[kk]) : t.fma(u, kk, y[kk], cz[kk]);
+            cd[kk] = __builtin_rintf(tq);
+            rmax = fmaxf(rmax, fabsf(tq - cd[kk]));
+        }
+        if (!(rmax < near_tie) || !fast_ok) {
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++) {
+                const float x = IS_V ? t.at(kk, u) : t.at(u, kk);
+                cd[kk] = exact_code(x, mn[kk], s[kk], L);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            uint32_t wv = 0;
+            wv = __builtin_amdgcn_cvt_pk_u8_f32(cd[4 * p], 0, wv);
+            wv = __builtin_amdgcn_cvt_pk_u8_f32(cd[4 * p + 2], 1, wv);
+            wv = __builtin_amdgcn_cvt_pk_u8_f32(cd[4 * p + 1], 2, wv);
+            wv = __builtin_amdgcn_cvt_pk_u8_f32(cd[4 * p + 3], 3, wv);
+            unit[u][p] = wv;
+        }
+    }
+    if (!IS_V) {
+        // key unit (row 4*jj + q (+16 for the second tile), chunk c) -> lane
+        // 4*jj + q + 16*(c%4), operand 4*tile + c/4
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int L_ = 4 * jj + q + 16 * (c & 3);
+#pragma unroll
+            for (int r = 0; r < 2; r++) {
+                const int o = 4 * r + (c >> 2);
+                *(uint2 *)&tr[L_ * DPL + 2 * o] = (uint2){unit[jj + 4 * r][0], unit[jj + 4 * r][1]};
+            }
+        }
+    } else {
+        // value unit (channel 8c + e over the lane's rows) -> lane
+        // 8*(c%2) + e + 16q, operand c/2
+        const int o = c >> 1;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const int L_ = 8 * (c & 1) + e + 16 * q;
+            *(uint2 *)&tr[L_ * DPL + 2 * o] = (uint2){unit[e][0], unit[e][1]};
+        }
+    }
+    __syncthreads();
+    uint32_t *dst = (uint32_t *)(blk + (IS_V ? cbytes : 0));
+#pragma unroll
+    for (int w4 = 0; w4 < DPL / 4; w4++)
+        *(uint4 *)&dst[w4 * 256 + 4 * l] = *(const uint4 *)&tr[l * DPL + 4 * w4];
 }
 
 template <int BITS, bool IS_V, bool RING, typename T>
@@ -332,9 +405,10 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
     }
     // Scales outside [2^-126, inf) and NaN (fails both) take the exact path.
     const bool fast_ok = smin >= 0x1p-126f && smax < INFINITY;
-    // t = RN(x * y + RN(-zero * y)) is within 5 * 2^-20 + 2^-24 * |zero * y|
-    // of RN(RN(x - zero) / s) for t <= 16; the margin below is 4x that.
-    const float near_tie = 0.5f - (0x1p-16f + 0x1p-22f * czmax);
+    // t = RN(x * y + RN(-zero * y)) is within t * 1.5 * 2^-23 + ulp(t) +
+    // 2^-24 * |zero * y| of RN(RN(x - zero) / s): 5 * 2^-20 + ... for t <= 16,
+    // 2^-14 + ... for t <= 256.  The margin below is about 4x that.
+    const float near_tie = 0.5f - ((BITS == 8 ? 0x1p-12f : 0x1p-16f) + 0x1p-22f * czmax);
 
     uint8_t *blk = a.blocks + (stream * a.max_groups + g) * a.block_bytes;
     constexpr int cbytes = BITS * G * D / 8;
@@ -367,6 +441,10 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
 
     // Units u = 0..7 (key row j = u over channels kk; value channel e = u over
     // rows kk), parameters indexed by kk for keys and values alike.
+    if constexpr (BITS == 8) {
+        quantize_pack8<IS_V>(a, t, mn, s, y, cz, near_tie, fast_ok, blk, tr);
+        return;
+    }
     uint32_t unit[8];
 #pragma unroll
     for (int u = 0; u < 8; u++) {
@@ -556,6 +634,11 @@ __device__ __forceinline__ h8 unpack_operand(const uint32_t *w, int o) {
         const uint32_t x = (o & 1) ? (w[o >> 1] >> 8) : w[o >> 1];
 #pragma unroll
         for (int m = 0; m < 4; m++) r[m] = x & (MASK << (2 * m));
+    } else if (BITS == 8) {
+        // operand o = dwords 2o, 2o + 1; pair m in dword m / 2 at bits
+        // 8 * (m % 2) and 16 + 8 * (m % 2)
+#pragma unroll
+        for (int m = 0; m < 4; m++) r[m] = ((m & 1) ? w[2 * o + (m >> 1)] >> 8 : w[2 * o + (m >> 1)]) & MASK;
     } else {
         const uint32_t x = w[o], y = x >> 8;
 #pragma unroll
@@ -919,7 +1002,7 @@ struct Pipe {
     static constexpr int CB = BITS * G * D / 8;         // code bytes per tensor
     static constexpr int BB = 2 * CB + 4 * D * 2;       // block bytes
     static constexpr int DPG = BB / 1024;               // 1 KiB copies per group
-    static constexpr int NST = BITS == 2 ? 3 : 2;       // stages
+    static constexpr int NST = BITS == 2 ? 3 : 2;       // stages (8 bits: 9 KiB groups)
 };
 
 template <int BITS>
@@ -1565,6 +1648,7 @@ hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
     if (a.group_end <= a.group_begin || a.streams <= 0) return hipSuccess;
     if ((int64_t)a.streams * (a.group_end - a.group_begin) * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (a.bits == 2) return a.is_f32 ? launch_quantize_t<2, float>(a, s) : launch_quantize_t<2, _Float16>(a, s);
+    if (a.bits == 8) return a.is_f32 ? launch_quantize_t<8, float>(a, s) : launch_quantize_t<8, _Float16>(a, s);
     return a.is_f32 ? launch_quantize_t<4, float>(a, s) : launch_quantize_t<4, _Float16>(a, s);
 }
 
@@ -1592,6 +1676,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     if (a.splits + 1 > kMaxItems || items > 0x7FFFFFFF) return hipErrorInvalidValue;
     dim3 grid((unsigned)items);
     if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
+    else if (a.bits == 8) launch_decode_bits<8>(a, gq, grid, s);
     else launch_decode_bits<4>(a, gq, grid, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1619,6 +1704,9 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
     if (a.bits == 2) {
         if (a.q_is_f32) launch_attn_bits<2, true>(a, gq, grid, s);
         else launch_attn_bits<2, false>(a, gq, grid, s);
+    } else if (a.bits == 8) {
+        if (a.q_is_f32) launch_attn_bits<8, true>(a, gq, grid, s);
+        else launch_attn_bits<8, false>(a, gq, grid, s);
     } else {
         if (a.q_is_f32) launch_attn_bits<4, true>(a, gq, grid, s);
         else launch_attn_bits<4, false>(a, gq, grid, s);

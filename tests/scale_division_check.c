@@ -1,5 +1,5 @@
 /* Checks the identity the quantize kernel relies on for the group scale:
- * for L in {3, 15} and a positive finite float x,
+ * for L in {3, 15, 255} and a positive finite float x,
  *     RN(x / L) == fma(fma(-q0, L, x), y, q0),  y = RN(1/L), q0 = RN(x * y)
  * (one FMA residual correction of the product with the rounded reciprocal).
  * Usage: scale_division_check [stride]  -- tests every stride-th positive
@@ -31,9 +31,9 @@ static uint64_t check(float L, uint32_t bits, uint64_t *n) {
 
 int main(int argc, char **argv) {
     const uint64_t stride = argc > 1 ? strtoull(argv[1], NULL, 10) : 1;
-    const float Ls[2] = {3.0f, 15.0f};
+    const float Ls[3] = {3.0f, 15.0f, 255.0f};
     uint64_t bad = 0, n = 0;
-    for (int li = 0; li < 2; li++) {
+    for (int li = 0; li < 3; li++) {
         for (uint64_t b = 1; b < 0x7F800000u; b += stride) bad += check(Ls[li], (uint32_t)b, &n);
         for (uint32_t e = 0; e < 255; e++) {           /* binade ends */
             bad += check(Ls[li], (e << 23) | 1u, &n);

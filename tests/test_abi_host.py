@@ -54,7 +54,8 @@ def test_status_strings(L):
 
 BAD = [
     (dict(bits=3), kivi.KIVI_ERR_INVALID_ARG),
-    (dict(bits=8), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(bits=5), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(bits=16), kivi.KIVI_ERR_INVALID_ARG),
     (dict(residual=48), kivi.KIVI_ERR_INVALID_ARG),      # not a multiple of G
     (dict(residual=-32), kivi.KIVI_ERR_INVALID_ARG),
     (dict(max_tokens=0), kivi.KIVI_ERR_INVALID_ARG),

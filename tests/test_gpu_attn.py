@@ -3,7 +3,7 @@ C ABI) against the oracle's attention over the same dequantized cache.
 
 Bar: max over (b, hq, t) of |o - r|_inf / |r|_inf <= 2e-3, the decode step's
 tolerance.  Cases cover both masks (none, and causal with the queries as the
-last T cached tokens), 1, 2 and 4 query heads per KV head, 2 and 4 bits,
+last T cached tokens), 1, 2 and 4 query heads per KV head, 2, 4 and 8 bits,
 query counts that leave padding columns, queries straddling the quantized
 prefix and the fp16 residual, split ranges merged by the combine kernel and
 a single range writing the output directly, fp32 queries, and the notebook's
@@ -59,6 +59,8 @@ def _run(orc, B, H, Hq, n, T, bits, R, causal, seed, chunks=None, q_dtype=np.flo
     (40, 40, 2, 32, 4, 1),       # T = n: the first query sees only token 0
     (2048, 256, 2, 128, 4, 1),   # several query blocks per stream
     (96, 7, 2, 128, 2, 0),       # everything in the residual window
+    (1000, 100, 8, 128, 4, 1),   # 8-bit codes, causal
+    (600, 16, 8, 64, 2, 0),      # 8-bit codes, split ranges
 ])
 def test_attn_shapes(orc, n, T, bits, R, gq, causal):
     _run(orc, 2, 2, 2 * gq, n, T, bits, R, causal, seed=n + T, label="attn-%d-%d" % (n, T))
@@ -80,7 +82,7 @@ def test_attn_single_query_is_decode(orc):
 
 def test_attn_notebook_full_q(orc):
     """The notebook's attention over all 1024 rows of its Q (seed 1) on its
-    fp32 cache (T=1024, D=128, no residual), 2- and 4-bit: parity with the
+    fp32 cache (T=1024, D=128, no residual), 2-, 4- and 8-bit: parity with the
     oracle, and the notebook's own checks against unquantized attention."""
     import json, os
     import torch
@@ -92,7 +94,7 @@ def test_attn_notebook_full_q(orc):
     q = Q.reshape(1, 1, 1024, 128).astype(np.float32)
     ref_fp = orc.attn_queries(q, K, V)
     rel = {}
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         cache = new_cache(1, 1, 1, 1024, bits=bits, R=0, dtype=np.float32)
         cache.append(to_dev(K), to_dev(V))
         out = cache.attn(to_dev(q)).cpu().numpy()

@@ -46,10 +46,10 @@ def _run(orc, B, H, Hq, n, bits, R, dtype, seed, chunks=None, q_dtype=np.float16
 
 def test_notebook_config_fp32(orc):
     """Single head, T=1024, fp32 K/V from seed 0 with outlier channels, no
-    residual window, 2- and 4-bit, one decode step with the notebook query."""
+    residual window, 2-, 4- and 8-bit, one decode step with the notebook query."""
     from kv_cache_quantization_amd import synth
     K, V, q = synth.notebook_inputs()
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         cache = new_cache(1, 1, 1, 1024, bits=bits, R=0, dtype=np.float32)
         cache.append(to_dev(K), to_dev(V))
         check_cache(orc, cache, K, V, label="notebook-%d" % bits)
@@ -73,6 +73,8 @@ def test_llama_layer_config(orc):
     (1, 4, 32, 4),         # a single token
     (160, 2, 128, 2),      # ring exactly full (n - Q = R + G - ... )
     (2049, 2, 64, 1),
+    (1000, 8, 128, 4),     # 8-bit codes, ragged tail
+    (33, 8, 0, 1),         # 8-bit, one group plus one token
 ])
 def test_shapes_and_tails(orc, n, bits, R, gq):
     _run(orc, 2, 3, 3 * gq, n, bits, R, np.float16, seed=n, label="tail-%d" % n)
@@ -90,7 +92,7 @@ def test_streaming_equals_oneshot(orc):
     chunks = [300] + [1] * 100 + [int(x) for x in rng.integers(1, 20, 10)]
     chunks.append(n - sum(chunks))
     assert chunks[-1] > 0
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         _run(orc, 2, 2, 8, n, bits, 64, np.float16, seed=9, chunks=chunks, label="stream-%d" % bits)
 
 
@@ -119,7 +121,7 @@ def test_special_values(orc):
     k[0, 1, 32:64, 9] = rng.choice([-65504, 65504, 0], 32)        # huge range
     v[0, 1, 101, :] = np.arange(128) * 0.5                        # exact ties
     k[0, 0, 64:96, 3] = np.tile(np.float16([0, 0.5, 1.5, 2.5, 3.0, 1.0, 2.0, 0.25]), 4)
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         cache = new_cache(B, H, 4 * H, n, bits=bits, R=0)
         cache.append(to_dev(k), to_dev(v))
         check_cache(orc, cache, k, v, label="special-%d" % bits)
@@ -195,7 +197,7 @@ def _tie_groups(rng, n_groups, bits, dtype):
 
 
 @pytest.mark.parametrize("dtype", [np.float16, np.float32])
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_near_ties(orc, bits, dtype):
     """Values on and next to the rounding boundaries of every group, with
     small and large zero offsets: the codes must still be bit-exact."""

@@ -1,8 +1,8 @@
 """The quantize kernel forms the group scale RN((max - min) / L) as
 q0 = RN(x * RN(1/L)) plus one FMA residual correction.  This checks that it
-equals the IEEE quotient for L = 3 and 15: on every 97th positive finite
+equals the IEEE quotient for L = 3, 15 and 255: on every 97th positive finite
 float and both ends of every binade by default, on all 2^31 - 2^23 of them
-with KIVI_EXHAUSTIVE=1 (about 45 s per L)."""
+with KIVI_EXHAUSTIVE=1 (about 40 s per L)."""
 import os
 import subprocess
 
