@@ -409,15 +409,20 @@ int64_t oracle_block_bytes(int bits)
     return 2 * (int64_t)(bits * G * D / 8) + 4 * (int64_t)D * 2;
 }
 
-/* Pack the first nq tokens of each stream (nq a multiple of G, and the K and
-   V prefixes equal, as under the window policy) into blocks:
-   out [B*H][max_groups][block_bytes].  Uses the logical arrays of
-   oracle_build_cache for the same nq. */
-void oracle_pack_blocks(int B, int H, int64_t nq, int bits, int64_t max_groups,
-                        const uint8_t *kcodes, const uint16_t *kzero16,
-                        const uint16_t *kscale16,
-                        const uint8_t *vcodes, const uint16_t *vzero16,
-                        const uint16_t *vscale16, uint8_t *out)
+/* Pack the quantized tokens of each stream into blocks:
+   out [B*H][max_groups][block_bytes].  Keys of the first nk tokens (nk a
+   multiple of G) and values of the first nv tokens, from the logical arrays
+   of oracle_build_cache for the same (nk, nv): kcodes [B*H][nk][D], kzero16 /
+   kscale16 [B*H][nk/G][D], vcodes [B*H][nv][D], vzero16 / vscale16
+   [B*H][nv][D/G].  Every code or side entry of a token that is not quantized
+   (a value row at or past nv inside a block that holds value rows) is 0;
+   blocks past both prefixes are left as they are. */
+void oracle_pack_blocks_kv(int B, int H, int64_t nk, int64_t nv, int bits,
+                           int64_t max_groups,
+                           const uint8_t *kcodes, const uint16_t *kzero16,
+                           const uint16_t *kscale16,
+                           const uint8_t *vcodes, const uint16_t *vzero16,
+                           const uint16_t *vscale16, uint8_t *out)
 {
     const int D = 128, G = 32;
     const int64_t cbytes = bits * G * D / 8;
@@ -432,7 +437,9 @@ void oracle_pack_blocks(int B, int H, int64_t nq, int bits, int64_t max_groups,
             code_position(bits, 0, t, c, &kd[t * D + c], &kb[t * D + c]);
             code_position(bits, 1, t, c, &vd[t * D + c], &vb[t * D + c]);
         }
-    int64_t ng = nq / G;
+    int64_t ngk = nk / G;
+    int64_t ngv = (nv + G - 1) / G;
+    int64_t ng = ngk > ngv ? ngk : ngv;
     for (int64_t s = 0; s < (int64_t)B * H; s++)
         for (int64_t j = 0; j < ng; j++) {
             uint8_t *blk = out + (s * max_groups + j) * bb;
@@ -442,29 +449,48 @@ void oracle_pack_blocks(int B, int H, int64_t nq, int bits, int64_t max_groups,
             uint16_t *kz = ks + D;
             uint16_t *vs = kz + D;
             uint16_t *vz = vs + D;
-            memset(blk, 0, (size_t)(2 * cbytes));
-            for (int t = 0; t < G; t++)
+            if (j < ngk) {
+                memset(kc, 0, (size_t)cbytes);
+                for (int t = 0; t < G; t++)
+                    for (int c = 0; c < D; c++) {
+                        uint32_t ck = kcodes[(s * nk + j * G + t) * D + c];
+                        kc[kd[t * D + c]] |= ck << kb[t * D + c];
+                    }
                 for (int c = 0; c < D; c++) {
-                    int64_t tok = j * G + t;
-                    uint32_t ck = kcodes[(s * nq + tok) * D + c];
-                    uint32_t cv = vcodes[(s * nq + tok) * D + c];
-                    kc[kd[t * D + c]] |= ck << kb[t * D + c];
-                    vc[vd[t * D + c]] |= cv << vb[t * D + c];
+                    ks[c] = kscale16[(s * ngk + j) * D + c];
+                    kz[c] = kzero16[(s * ngk + j) * D + c];
                 }
-            for (int c = 0; c < D; c++) {
-                ks[c] = kscale16[(s * ng + j) * D + c];
-                kz[c] = kzero16[(s * ng + j) * D + c];
             }
-            for (int cg = 0; cg < D / G; cg++)
+            if (j < ngv) {
+                memset(vc, 0, (size_t)cbytes);
                 for (int t = 0; t < G; t++) {
-                    vs[cg * G + t] = vscale16[(s * nq + j * G + t) * (D / G) + cg];
-                    vz[cg * G + t] = vzero16[(s * nq + j * G + t) * (D / G) + cg];
+                    int64_t tok = j * G + t;
+                    for (int c = 0; c < D; c++) {
+                        uint32_t cv = tok < nv ? vcodes[(s * nv + tok) * D + c] : 0;
+                        vc[vd[t * D + c]] |= cv << vb[t * D + c];
+                    }
+                    for (int cg = 0; cg < D / G; cg++) {
+                        vs[cg * G + t] = tok < nv ? vscale16[(s * nv + tok) * (D / G) + cg] : 0;
+                        vz[cg * G + t] = tok < nv ? vzero16[(s * nv + tok) * (D / G) + cg] : 0;
+                    }
                 }
+            }
         }
     free(kd);
     free(vd);
     free(kb);
     free(vb);
+}
+
+/* The window policy's blocks: keys and values of the first nq tokens. */
+void oracle_pack_blocks(int B, int H, int64_t nq, int bits, int64_t max_groups,
+                        const uint8_t *kcodes, const uint16_t *kzero16,
+                        const uint16_t *kscale16,
+                        const uint8_t *vcodes, const uint16_t *vzero16,
+                        const uint16_t *vscale16, uint8_t *out)
+{
+    oracle_pack_blocks_kv(B, H, nq, nq, bits, max_groups, kcodes, kzero16, kscale16,
+                          vcodes, vzero16, vscale16, out);
 }
 
 /* Position of one code in the packed area (exported for the layout tests). */
