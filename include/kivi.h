@@ -50,17 +50,26 @@ typedef enum {
 
 typedef enum { KIVI_F16 = 0, KIVI_F32 = 1 } kivi_dtype;
 
-/* Flush policy.  KIVI_FLUSH_WINDOW: the quantized prefix of an n-token
-   stream is Q(n) = G * floor(max(0, n - R) / G) for keys and values alike
-   ("KIVI" VeloxQuant-MLX docs, "How it works" items 3-4). */
-typedef enum { KIVI_FLUSH_WINDOW = 0 } kivi_flush_policy;
+/* Flush policy: which tokens of an n-token stream are quantized.
+   KIVI_FLUSH_WINDOW: keys and values alike up to Q(n) = G * floor(max(0,
+   n - R) / G) ("KIVI" VeloxQuant-MLX docs, "How it works" items 3-4: the
+   newest R tokens stay full precision, aged tokens move in whole groups).
+   KIVI_FLUSH_PAPER (needs R > 0): keys up to Q_K(n) = n - (n mod R), values
+   up to Q_V(n) = max(0, n - R) ("[Paper review] KIVI ...", 3.2.2 and the
+   prefill / decoding phases of Algorithm 1 in 3.2.3: the key residual is
+   quantized R tokens at once when it fills up, the oldest value of the
+   residual one token per step).  In the group holding Q_V the value codes
+   and side data of tokens >= Q_V are 0.  kivi_attn supports only the window
+   policy. */
+typedef enum { KIVI_FLUSH_WINDOW = 0, KIVI_FLUSH_PAPER = 1 } kivi_flush_policy;
 
 /* kivi_append flags. */
 enum {
     /* Copy the new rows into the ring only and leave the quantization of
        newly aged groups to a later kivi_flush (or to the next append without
        this flag).  All unquantized tokens must then fit the ring:
-       n - q <= R + G, else KIVI_ERR_CAPACITY. */
+       n - G * floor(q_v / G) <= R + G (q_v: quantized value tokens, = q
+       under the window policy), else KIVI_ERR_CAPACITY. */
     KIVI_DEFER_FLUSH = 1u
 };
 
@@ -88,7 +97,8 @@ typedef struct kivi_cache kivi_cache;   /* opaque host-side handle */
    the codes is described in the kernel source (it follows the matrix-core
    operand layout).  Ring: [B*H][ring_capacity][D] in kv_dtype for K and for
    V; token t of a stream lives in slot t mod ring_capacity while it is in
-   the full-precision residual [n_quantized, n_tokens). */
+   [G * floor(n_vquantized / G), n_tokens), which holds the key residual
+   [n_quantized, n_tokens) and the value residual [n_vquantized, n_tokens). */
 typedef struct {
     size_t blocks, ring_k, ring_v;      /* region offsets                     */
     size_t block_bytes, code_bytes;
@@ -96,17 +106,21 @@ typedef struct {
     int64_t max_groups;
     int64_t ring_capacity;              /* R + G                              */
     int64_t n_tokens;                   /* n                                  */
-    int64_t n_quantized;                /* Q(n), a multiple of G              */
+    int64_t n_quantized;                /* key tokens quantized: Q(n) / Q_K(n) */
+    int64_t n_vquantized;               /* value tokens quantized: Q(n) / Q_V(n) */
 } kivi_layout;
 
 /* What an append of n_new tokens will do (pure host computation). */
 typedef struct {
     int64_t n_old, n_new_total;         /* n before / after                   */
-    int64_t q_old, q_new;               /* quantized prefix before / after    */
-    int64_t flush_token_begin;          /* tokens [q_old, q_new) are quantized */
-    int64_t flush_token_end;            /*   (token t < n_old read from ring)  */
-    int64_t ring_token_begin;           /* tokens [max(q_new, n_old), n) are   */
-    int64_t ring_token_end;             /*   copied into the ring              */
+    int64_t q_old, q_new;               /* key prefix before / after          */
+    int64_t flush_token_begin;          /* keys of tokens [q_old, q_new) are  */
+    int64_t flush_token_end;            /*   quantized (t < n_old from ring)  */
+    int64_t ring_token_begin;           /* tokens [max(G floor(v_flush_token_ */
+    int64_t ring_token_end;             /*   end / G), n_old), n) -> the ring  */
+    int64_t v_flush_token_begin;        /* values of tokens [qv_old, qv_new)  */
+    int64_t v_flush_token_end;          /*   are quantized (= the key range   */
+                                        /*   under the window policy)         */
 } kivi_append_plan;
 
 /* Bytes of device memory a cache with this config needs (0 if the config is
@@ -126,20 +140,20 @@ kivi_status kivi_cache_destroy(kivi_cache *c);
 /* Append n_new >= 0 tokens to every stream.  k, v: device, contiguous
    [B][H][n_new][D] in kv_dtype (may be NULL when n_new == 0); they are read
    by kernels enqueued on `stream` and must stay valid until those finish.
-   Enqueues, in this order: quantization of tokens [q_old, q_new) (K per
-   channel, V per token; token t < n_old is read from the ring, later tokens
-   from k/v), then the copy of tokens [max(q_new, n_old), n) into the ring.
-   flags: 0 or KIVI_DEFER_FLUSH (then only the ring copy of [n_old, n) is
-   enqueued and q is left as it was).  Errors: INVALID_ARG (null handle,
-   null k/v with n_new > 0, n_new < 0, unknown flags), CAPACITY
-   (n + n_new > max_tokens; with KIVI_DEFER_FLUSH also n + n_new - q > R + G),
-   HIP. */
+   Enqueues, in this order: quantization of the newly aged tokens (see
+   kivi_append_plan: K per channel in whole groups, V per token; token t <
+   n_old is read from the ring, later tokens from k/v), then the copy of the
+   plan's ring range into the ring.  flags: 0 or KIVI_DEFER_FLUSH (then only
+   the ring copy of [n_old, n) is enqueued and the quantized prefixes are
+   left as they were).  Errors: INVALID_ARG (null handle, null k/v with
+   n_new > 0, n_new < 0, unknown flags), CAPACITY (n + n_new > max_tokens;
+   with KIVI_DEFER_FLUSH also when the ring would overflow, see above), HIP. */
 kivi_status kivi_append(kivi_cache *c, const void *k, const void *v,
                         int64_t n_new, uint32_t flags, hipStream_t stream);
 
-/* Make the cache canonical: quantize tokens [q, Q(n)) that deferred appends
-   left in the ring (nothing to do after appends without KIVI_DEFER_FLUSH).
-   Idempotent.  Errors: INVALID_ARG, HIP. */
+/* Make the cache canonical: quantize the tokens that deferred appends left
+   in the ring up to the policy's prefixes (nothing to do after appends
+   without KIVI_DEFER_FLUSH).  Idempotent.  Errors: INVALID_ARG, HIP. */
 kivi_status kivi_flush(kivi_cache *c, hipStream_t stream);
 
 /* Host-only: what kivi_append(c, ..., n_new, 0, ...) would enqueue. */
@@ -150,15 +164,18 @@ kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new,
 size_t kivi_decode_workspace_bytes(const kivi_cache *c);
 
 /* How decode splits the quantized prefix at the current n: *splits work
-   items per stream over whole groups, *groups_per_split groups each (plus
-   one item per stream for the full-precision residual). Host-only. */
+   items per stream over the groups with key and value codes,
+   *groups_per_split groups each (plus one item per stream for the
+   full-precision residual and, under the paper policy, one for the groups
+   whose value codes stop inside or before them). Host-only. */
 kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits,
                              int32_t *groups_per_split);
 
 /* One decode-attention step over all n cached tokens of every stream:
    out[b][hq][:] = softmax(scale * q[b][hq] . K_hat^T) V_hat, where K_hat and
-   V_hat are the dequantized groups (code * scale + zero) followed by the
-   full-precision residual, and query head hq reads KV head hq / (Hq / H).
+   V_hat are the dequantized tokens (code * scale + zero) followed by the
+   full-precision residual (under the paper policy the key and value
+   residuals differ), and query head hq reads KV head hq / (Hq / H).
    q: device [B][Hq][D] in q_dtype; out: device float32 [B][Hq][D];
    softmax_scale <= 0 selects 1/sqrt(D); workspace: device, ws_bytes >=
    kivi_decode_workspace_bytes(c).  Errors: INVALID_ARG (null pointers, bad
@@ -182,7 +199,7 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype,
    kivi_attn_workspace_bytes(c, T) (may be 0, then workspace may be NULL).
    Errors: INVALID_ARG (null pointers, T < 1, bad q_dtype or causal, causal
    with T > n), STATE (n == 0 or a deferred flush pending), UNSUPPORTED
-   (float32 cache with residual tokens; B * Hq * T >= 2^31),
+   (float32 cache with residual tokens; the paper policy; B * Hq * T >= 2^31),
    BUFFER_TOO_SMALL, HIP. */
 kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T,
                       int32_t causal, float softmax_scale, float *out,

@@ -1,14 +1,21 @@
 // kivi_api.cpp -- the C ABI of libkivi (declared in include/kivi.h): config
-// validation, the device-buffer layout, the n / Q(n) bookkeeping of the
-// window flush policy, and stream-ordered kernel launches.
+// validation, the device-buffer layout, the n / Q(n) bookkeeping of the two
+// flush policies, and stream-ordered kernel launches.
 //
-// Flush schedule ("KIVI", VeloxQuant-MLX docs, "How it works" items 3-4):
-// the newest R tokens stay in full precision and aged tokens are quantized
-// only in whole groups of G, so the quantized prefix of an n-token stream is
-// Q(n) = G * floor(max(0, n - R) / G).  An append from n_old to n therefore
-// quantizes tokens [Q(n_old), Q(n)) and keeps [max(Q(n), n_old), n) in the
-// ring; the ring (capacity R + G) never holds more than n - Q(n) < R + G
-// tokens.
+// Window policy ("KIVI", VeloxQuant-MLX docs, "How it works" items 3-4): the
+// newest R tokens stay in full precision and aged tokens are quantized only
+// in whole groups of G, so keys and values share the quantized prefix
+// Q(n) = G * floor(max(0, n - R) / G).  An append from n_old to n quantizes
+// tokens [Q(n_old), Q(n)) and keeps [max(Q(n), n_old), n) in the ring; the
+// ring (capacity R + G) never holds more than n - Q(n) < R + G tokens.
+//
+// Paper policy ("[Paper review] KIVI ...", 3.2.2 and the prefill / decoding
+// phases of Algorithm 1 in 3.2.3): keys keep r = n mod R tokens in full
+// precision, Q_K(n) = n - r (R tokens are quantized at once when the key
+// residual fills up), and values keep the newest R, Q_V(n) = max(0, n - R)
+// (one token is quantized per decoding step).  Q_K >= Q_V, and the ring holds
+// tokens from G * floor(Q_V / G) (the start of the value group holding Q_V,
+// which is re-quantized whole as its rows arrive) to n: fewer than R + G.
 #include <math.h>
 #include <new>
 #include <stdint.h>
@@ -29,7 +36,8 @@ struct kivi_cache {
     int64_t ring_cap;
     int esize;
     int64_t n;      // tokens cached per stream
-    int64_t q;      // tokens quantized per stream, Q(n)
+    int64_t q;      // key tokens quantized per stream, Q(n) / Q_K(n)
+    int64_t qv;     // value tokens quantized per stream (= q under the window policy)
 };
 
 namespace {
@@ -54,7 +62,8 @@ kivi_status validate(const kivi_config *c) {
     if ((int64_t)c->group * c->bits % 64 != 0) return KIVI_ERR_INVALID_ARG;
     if (c->n_q_heads % c->n_kv_heads != 0) return KIVI_ERR_INVALID_ARG;
     if (c->kv_dtype != KIVI_F16 && c->kv_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
-    if (c->policy != KIVI_FLUSH_WINDOW) return KIVI_ERR_INVALID_ARG;
+    if (c->policy != KIVI_FLUSH_WINDOW && c->policy != KIVI_FLUSH_PAPER) return KIVI_ERR_INVALID_ARG;
+    if (c->policy == KIVI_FLUSH_PAPER && c->residual == 0) return KIVI_ERR_INVALID_ARG;
     if (c->reserved != 0) return KIVI_ERR_INVALID_ARG;
     // Shapes the kernels are built for.
     if (c->head_dim != kHeadDim || c->group != kGroup) return KIVI_ERR_UNSUPPORTED;
@@ -86,9 +95,24 @@ Sizes sizes_of(const kivi_config *c) {
     return s;
 }
 
-int64_t quantized_prefix(const kivi_config &c, int64_t n) {
+// Quantized prefixes of keys and values of an n-token stream.
+struct Prefix {
+    int64_t k, v;
+};
+
+Prefix prefix_of(const kivi_config &c, int64_t n) {
     const int64_t aged = n > c.residual ? n - c.residual : 0;
-    return aged / c.group * c.group;
+    if (c.policy == KIVI_FLUSH_PAPER) return {n - n % c.residual, aged};
+    const int64_t q = aged / c.group * c.group;
+    return {q, q};
+}
+
+// Lowest token the ring holds: the start of the value group holding Q_V.
+int64_t ring_low(const kivi_config &c, int64_t qv) { return qv / c.group * c.group; }
+
+bool canonical(const kivi_cache *c) {
+    const Prefix p = prefix_of(c->cfg, c->n);
+    return c->q == p.k && c->qv == p.v;
 }
 
 // G-token chunks of the residual [Q, n) (walked by one item per stream).
@@ -190,6 +214,7 @@ kivi_status kivi_cache_create(const kivi_config *cfg, void *dev_mem, size_t dev_
     c->esize = s.esize;
     c->n = 0;
     c->q = 0;
+    c->qv = 0;
     *out = c;
     return KIVI_OK;
 }
@@ -203,15 +228,18 @@ kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new, kivi_append_pla
     if (!c || !p || n_new < 0) return KIVI_ERR_INVALID_ARG;
     if (n_new > c->cfg.max_tokens - c->n) return KIVI_ERR_CAPACITY;
     const int64_t n = c->n + n_new;
-    const int64_t q_new = quantized_prefix(c->cfg, n);
+    const Prefix q_new = prefix_of(c->cfg, n);
+    const int64_t lo = ring_low(c->cfg, q_new.v);
     p->n_old = c->n;
     p->n_new_total = n;
     p->q_old = c->q;
-    p->q_new = q_new;
+    p->q_new = q_new.k;
     p->flush_token_begin = c->q;
-    p->flush_token_end = q_new;
-    p->ring_token_begin = q_new > c->n ? q_new : c->n;
+    p->flush_token_end = q_new.k;
+    p->ring_token_begin = lo > c->n ? lo : c->n;
     p->ring_token_end = n;
+    p->v_flush_token_begin = c->qv;
+    p->v_flush_token_end = q_new.v;
     return KIVI_OK;
 }
 
@@ -219,11 +247,15 @@ kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new, kivi_append_pla
 
 namespace {
 
-// Quantize tokens [p.flush_token_begin, p.flush_token_end) of every stream
-// (t < p.n_old from the ring, later ones from k / v).
-kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *k, const void *v,
-                          int64_t n_new, hipStream_t stream) {
-    if (p.flush_token_end <= p.flush_token_begin) return KIVI_OK;
+// Quantize groups [group_begin, group_end) of every stream: kinds 1 = keys,
+// 2 = values, 3 = both; value rows at or past v_limit are left out (codes and
+// side data 0).  Tokens t < p.n_old are read from the ring, later ones from
+// k / v.
+kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const void *k,
+                             const void *v, int64_t n_new, int64_t group_begin,
+                             int64_t group_end, int kinds, int64_t v_limit,
+                             hipStream_t stream) {
+    if (group_end <= group_begin) return KIVI_OK;
     QuantizeArgs a;
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
@@ -235,12 +267,35 @@ kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *
     a.ring_v = c->base + c->off_ring_v;
     a.ring_cap = c->ring_cap;
     a.n_old = p.n_old;
-    a.group_begin = p.flush_token_begin / c->cfg.group;
-    a.group_end = p.flush_token_end / c->cfg.group;
+    a.group_begin = group_begin;
+    a.group_end = group_end;
     a.streams = c->cfg.batch * c->cfg.n_kv_heads;
     a.is_f32 = c->cfg.kv_dtype == KIVI_F32;
     a.bits = c->cfg.bits;
+    a.kinds = kinds;
+    a.v_limit = v_limit;
     return launch_quantize(a, stream) == hipSuccess ? KIVI_OK : KIVI_ERR_HIP;
+}
+
+// Everything the plan quantizes.  Window policy: the groups [q_old, q_new) /
+// G, keys and values together.  Paper policy: the key groups [q_old, q_new) /
+// G, then the value groups touched by [qv_old, qv_new): whole groups, and the
+// group holding qv_new up to that token (re-quantized whole on every append
+// that adds rows to it; its earlier rows come out identical).
+kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *k, const void *v,
+                          int64_t n_new, hipStream_t stream) {
+    const int64_t G = c->cfg.group;
+    constexpr int64_t kNoLimit = INT64_MAX;
+    if (c->cfg.policy != KIVI_FLUSH_PAPER)
+        return enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
+                                p.flush_token_end / G, 3, kNoLimit, stream);
+    kivi_status st = enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
+                                      p.flush_token_end / G, 1, kNoLimit, stream);
+    if (st != KIVI_OK || p.v_flush_token_end <= p.v_flush_token_begin) return st;
+    const int64_t g0 = p.v_flush_token_begin / G, gw = p.v_flush_token_end / G;
+    st = enqueue_quantize(c, p, k, v, n_new, g0, gw, 2, kNoLimit, stream);
+    if (st != KIVI_OK || p.v_flush_token_end % G == 0) return st;
+    return enqueue_quantize(c, p, k, v, n_new, gw, gw + 1, 2, p.v_flush_token_end, stream);
 }
 
 // Copy tokens [begin, end) (all >= n_old) of every stream into the ring.
@@ -274,8 +329,8 @@ kivi_status kivi_append(kivi_cache *c, const void *k, const void *v, int64_t n_n
     kivi_status st = kivi_plan_append(c, n_new, &p);
     if (st != KIVI_OK) return st;
     if (flags & KIVI_DEFER_FLUSH) {
-        // every unquantized token must stay addressable in the ring
-        if (p.n_new_total - c->q > c->ring_cap) return KIVI_ERR_CAPACITY;
+        // every token the next flush reads must stay addressable in the ring
+        if (p.n_new_total - ring_low(c->cfg, c->qv) > c->ring_cap) return KIVI_ERR_CAPACITY;
         st = enqueue_ring(c, k, v, n_new, p.n_old, p.n_old, p.n_new_total, stream);
         if (st != KIVI_OK) return st;
         c->n = p.n_new_total;
@@ -287,6 +342,7 @@ kivi_status kivi_append(kivi_cache *c, const void *k, const void *v, int64_t n_n
     if (st != KIVI_OK) return st;
     c->n = p.n_new_total;
     c->q = p.q_new;
+    c->qv = p.v_flush_token_end;
     return KIVI_OK;
 }
 
@@ -299,24 +355,26 @@ kivi_status kivi_flush(kivi_cache *c, hipStream_t stream) {
     st = enqueue_flush(c, p, c->base + c->off_ring_k, c->base + c->off_ring_v, 0, stream);
     if (st != KIVI_OK) return st;
     c->q = p.q_new;
+    c->qv = p.v_flush_token_end;
     return KIVI_OK;
 }
 
 size_t kivi_decode_workspace_bytes(const kivi_cache *c) {
     if (!c) return 0;
     // decode_split_plan never makes more than max(1, kTargetWaves / streams - 1)
-    // split items per stream, whatever n is; plus one residual item.
+    // split items per stream, whatever n is; plus one residual item, and under
+    // the paper policy one item for the groups with partial value codes.
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
     int64_t splits = kTargetWaves / streams - 1;
     if (splits < 1) splits = 1;
-    const int64_t items = splits + 1;
+    const int64_t items = splits + (c->cfg.policy == KIVI_FLUSH_PAPER ? 2 : 1);
     const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
     return (size_t)(bhq * items * (c->cfg.head_dim + 2) * 4);
 }
 
 kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits, int32_t *gps) {
     if (!c || !splits || !gps) return KIVI_ERR_INVALID_ARG;
-    decode_split_plan(c, c->q, splits, gps);
+    decode_split_plan(c, ring_low(c->cfg, c->qv), splits, gps);
     return KIVI_OK;
 }
 
@@ -324,14 +382,18 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
                              float *out, void *workspace, size_t ws_bytes, hipStream_t stream) {
     if (!c || !q || !out || !workspace) return KIVI_ERR_INVALID_ARG;
     if (q_dtype != KIVI_F16 && q_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
-    if (c->n == 0 || c->q != quantized_prefix(c->cfg, c->n)) return KIVI_ERR_STATE;
+    if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
     if (ws_bytes < kivi_decode_workspace_bytes(c)) return KIVI_ERR_BUFFER_TOO_SMALL;
     DecodeArgs a;
+    // groups [0, nq / G): key and value codes (split items); [nq, q): key
+    // codes, value codes below qv (paper policy only); [q, n): the residual
+    const int64_t nq = ring_low(c->cfg, c->qv);
+    const int32_t mixed = (int32_t)((c->q - nq) / c->cfg.group);
     int32_t splits, gps;
-    decode_split_plan(c, c->q, &splits, &gps);
+    decode_split_plan(c, nq, &splits, &gps);
     const int64_t chunks = tail_chunks_of(c, c->n, c->q);
     const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
-    const int64_t items = splits + 1;
+    const int64_t items = splits + 1 + (mixed > 0 ? 1 : 0);
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
     a.block_bytes = c->block_bytes;
@@ -349,10 +411,14 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
     a.q_heads = c->cfg.n_q_heads;
     a.bits = c->cfg.bits;
     a.n_tokens = c->n;
-    a.n_quant = c->q;
+    a.n_quant = nq;
+    a.n_tail = c->q;
+    a.n_vquant = c->qv;
+    a.mixed_groups = mixed;
     a.splits = splits;
     a.groups_per_split = gps;
     a.tail_chunks = (int32_t)chunks;
+    a.items = (int32_t)items;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)c->cfg.head_dim);
     a.sm_log2 = scale * 1.4426950408889634f;
     if (launch_decode(a, stream) != hipSuccess) return KIVI_ERR_HIP;
@@ -373,8 +439,9 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     if (!c || !q || !out || T < 1) return KIVI_ERR_INVALID_ARG;
     if (q_dtype != KIVI_F16 && q_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return KIVI_ERR_INVALID_ARG;
-    if (c->n == 0 || c->q != quantized_prefix(c->cfg, c->n)) return KIVI_ERR_STATE;
+    if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
     if (causal && T > c->n) return KIVI_ERR_INVALID_ARG;
+    if (c->cfg.policy == KIVI_FLUSH_PAPER) return KIVI_ERR_UNSUPPORTED;
     if (c->cfg.kv_dtype != KIVI_F16 && c->n > c->q) return KIVI_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)c->cfg.batch * c->cfg.n_q_heads * T;
     if (rows > 0x7FFFFFFF) return KIVI_ERR_UNSUPPORTED;
@@ -435,6 +502,7 @@ kivi_status kivi_get_layout(const kivi_cache *c, kivi_layout *o) {
     o->ring_capacity = c->ring_cap;
     o->n_tokens = c->n;
     o->n_quantized = c->q;
+    o->n_vquantized = c->qv;
     return KIVI_OK;
 }
 

@@ -25,6 +25,8 @@ struct QuantizeArgs {
     int32_t streams;
     int32_t is_f32;             // kv dtype: 0 fp16, 1 fp32
     int32_t bits;               // 2, 4 or 8
+    int32_t kinds;              // 1: key groups, 2: value groups, 3: both
+    int64_t v_limit;            // value codes / side data of tokens >= v_limit are written 0
 };
 
 // Copy tokens [tok_begin, tok_end) of every stream from the appended chunk
@@ -53,10 +55,16 @@ struct DecodeArgs {
     float *part_ml;             // [B*Hq][n_items_per_stream][2]  (m log2, l)
     int32_t batch, kv_heads, q_heads;
     int32_t bits;
-    int64_t n_tokens, n_quant;  // n, Q(n)
+    int64_t n_tokens;           // n
+    int64_t n_quant;            // groups [0, n_quant / G) hold key and value codes
+    int64_t n_tail;             // fp16 keys and values from here to n (the residual)
+    int64_t n_vquant;           // value codes exist for tokens < n_vquant
+    int32_t mixed_groups;       // groups from n_quant / G on with key codes but value
+                                // codes only below n_vquant (paper policy; else 0)
     int32_t splits;             // work items per stream over quantized groups
     int32_t groups_per_split;
     int32_t tail_chunks;        // G-token chunks of the residual (walked by one item)
+    int32_t items;              // partials per (batch, query head): splits, residual, mixed
     float sm_log2;              // softmax scale * log2(e)
 };
 

@@ -145,6 +145,14 @@ template <> struct Tile<float> {
 __device__ __forceinline__ void load_row(Tile<_Float16> &t, int j, const _Float16 *p) {
     split4(*(const uint4 *)p, t.v[j]);
 }
+__device__ __forceinline__ void zero_row(Tile<_Float16> &t, int j) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) t.v[j][e] = (h2){(_Float16)0.0f, (_Float16)0.0f};
+}
+__device__ __forceinline__ void zero_row(Tile<float> &t, int j) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) t.v[j][e] = 0.0f;
+}
 __device__ __forceinline__ void load_row(Tile<float> &t, int j, const float *p) {
     const float4 u0 = *(const float4 *)p, u1 = *(const float4 *)(p + 4);
     t.v[j][0] = u0.x; t.v[j][1] = u0.y; t.v[j][2] = u0.z; t.v[j][3] = u0.w;
@@ -386,7 +394,13 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
             for (int j = 0; j < 8; j++) load_row(t, j, base + tile_row<IS_V>(j, q) * D);
         } else {
 #pragma unroll
-            for (int j = 0; j < 8; j++) load_row(t, j, src.row(tile_row<IS_V>(j, q)) + 8 * c);
+            for (int j = 0; j < 8; j++) {
+                const int r = tile_row<IS_V>(j, q);
+                // value rows at or past v_limit are not quantized (they need
+                // not exist yet): zeros in, codes 0 out
+                if (IS_V && g * G + r >= a.v_limit) zero_row(t, j);
+                else load_row(t, j, src.row(r) + 8 * c);
+            }
         }
     }
 
@@ -428,10 +442,14 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
         // rows 4q..4q+3 (j < 4) and 16+4q.. (j >= 4) of value group c/4; the
         // four lanes of the quad store scale-low, scale-high, zero-low, zero-high.
         const int part = c & 3, jh = part & 1;
+        float sv[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++)     // rows past v_limit store scale 0 (their zero is +0)
+            sv[k] = RING && g * G + tile_row<true>(k, q) >= a.v_limit ? 0.0f : s[k];
         // (selects on named values: an index into s[] / mn[] that depends on
         // the lane would move those arrays out of registers)
-        const uint32_t s01 = pack_f16(s[0], s[1]), s23 = pack_f16(s[2], s[3]);
-        const uint32_t s45 = pack_f16(s[4], s[5]), s67 = pack_f16(s[6], s[7]);
+        const uint32_t s01 = pack_f16(sv[0], sv[1]), s23 = pack_f16(sv[2], sv[3]);
+        const uint32_t s45 = pack_f16(sv[4], sv[5]), s67 = pack_f16(sv[6], sv[7]);
         const uint32_t z01 = pack_f16(mn[0], mn[1]), z23 = pack_f16(mn[2], mn[3]);
         const uint32_t z45 = pack_f16(mn[4], mn[5]), z67 = pack_f16(mn[6], mn[7]);
         const uint32_t w0 = part == 0 ? s01 : part == 1 ? s45 : part == 2 ? z01 : z45;
@@ -525,15 +543,18 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
 // RING: the groups [group_begin, group_end) hold tokens appended earlier
 // (read, at least in part, from the ring); otherwise every row comes from
 // the new chunk.
+// kinds = 3: task 2i is the key group and 2i + 1 the value group of pair i;
+// kinds = 1 / 2: every task is a key / value group.
 template <int BITS, typename T, bool RING>
 __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
     __shared__ uint32_t tr[64 * 2 * BITS];
     const uint32_t ngr = (uint32_t)(a.group_end - a.group_begin);
     const uint32_t task = blockIdx.x;
-    const uint32_t rest = task >> 1;
+    const uint32_t rest = a.kinds == 3 ? task >> 1 : task;
+    const bool is_v = a.kinds == 3 ? (task & 1) != 0 : a.kinds == 2;
     const int64_t stream = rest / ngr;
     const int64_t g = a.group_begin + rest % ngr;
-    if (task & 1) quantize_task<BITS, true, RING, T>(a, stream, g, tr);
+    if (is_v) quantize_task<BITS, true, RING, T>(a, stream, g, tr);
     else quantize_task<BITS, false, RING, T>(a, stream, g, tr);
 }
 // ===========================================================================
@@ -796,7 +817,7 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Residual item: one per stream over the full-precision window [n_quant, n),
+// Residual item: one per stream over the full-precision window [n_tail, n),
 // taken 32 tokens (one chunk) at a time.  Each chunk's loads are issued
 // together (one memory round trip per chunk), its softmax is local and is
 // merged into the item's running state.
@@ -830,7 +851,7 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
     const int j = l & 15, Gl = l >> 4;
     const int h = j % GQ;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
-    const int items = a.splits + 1;
+    const int items = a.items;
     const int cap = (int)a.ring_cap;
     // uniform 64-bit bases + 32-bit per-lane byte offsets (one ring fits 4 GiB)
     const char *rkb = (const char *)a.ring_k + (int64_t)stream * a.ring_cap * D * 2;
@@ -845,9 +866,9 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
     float Mr[GQ], Lr[GQ], O0[GQ], O1[GQ];
 #pragma unroll
     for (int hh = 0; hh < GQ; hh++) { Mr[hh] = -INFINITY; Lr[hh] = 0.f; O0[hh] = O1[hh] = 0.f; }
-    int slot0 = (int)(a.n_quant % a.ring_cap);
+    int slot0 = (int)(a.n_tail % a.ring_cap);
     for (int chunk = 0; chunk < a.tail_chunks; chunk++) {
-        const int64_t left = a.n_tokens - a.n_quant - (int64_t)G * chunk;
+        const int64_t left = a.n_tokens - a.n_tail - (int64_t)G * chunk;
         const int cnt = left < G ? (int)left : G;        // >= 1
         // ring slot of chunk row r (rows past the end read the last valid
         // row; their scores are masked and their p is 0)
@@ -946,9 +967,9 @@ template <int GQ>
 __device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
     const int l = threadIdx.x & 63;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
-    const int items = a.splits + 1;
+    const int items = a.items;
     const int cap = (int)a.ring_cap;
-    int slot = (int)(a.n_quant % a.ring_cap);
+    int slot = (int)(a.n_tail % a.ring_cap);
     const float *rk = (const float *)a.ring_k + (int64_t)stream * a.ring_cap * D;
     const float *rv = (const float *)a.ring_v + (int64_t)stream * a.ring_cap * D;
     float q0[GQ], q1[GQ], m[GQ], ls[GQ], a0[GQ], a1[GQ];
@@ -962,7 +983,7 @@ __device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
         a0[h] = 0.f;
         a1[h] = 0.f;
     }
-    for (int64_t t = a.n_quant; t < a.n_tokens; t++) {
+    for (int64_t t = a.n_tail; t < a.n_tokens; t++) {
         const int64_t row = (int64_t)slot * D + 2 * l;
         slot = slot + 1 == cap ? 0 : slot + 1;
         const float k0 = rk[row], k1 = rk[row + 1], v0 = rv[row], v1 = rv[row + 1];
@@ -1034,7 +1055,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int cg = (j / GQ) & 3;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const int hq = hk * GQ + h;
-    const int items = a.splits + 1;
+    const int items = a.items;
     const int64_t ng = a.n_quant / G;
     const int64_t g0 = (int64_t)sp * a.groups_per_split;
     const int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
@@ -1172,6 +1193,135 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int64_t pi = ((int64_t)b * a.q_heads + hq) * items + sp;
     store_partial<GQ>(a, pi, l, accV, kTwo24 * (float)(1 << kSlack), xsum_rows(vbt), m_run,
                       Lsum[0]);
+}
+
+// Position of the code of (token t, channel c) of a group in its code area:
+// dword index and bit, following the operand layout the quantizer writes
+// (keys: lane (t % 16) + 16 ((c % 32) / 8), operand 4 (t / 16) + c / 32,
+// kk = c % 8; values: lane (c % 16) + 16 ((t % 16) / 4), operand c / 16,
+// kk = t % 4 + 4 (t / 16)).
+template <int BITS>
+__device__ __forceinline__ void code_pos(bool is_v, int t, int c, int &dw, int &bit) {
+    const int lane = is_v ? (c & 15) + 16 * ((t & 15) >> 2) : (t & 15) + 16 * ((c >> 3) & 3);
+    const int o = is_v ? c >> 4 : 4 * (t >> 4) + (c >> 5);
+    const int kk = is_v ? (t & 3) + 4 * (t >> 4) : c & 7;
+    const int h = kk & 1;
+    int w, i;
+    if (BITS == 2) { w = o >> 1; i = 4 * (o & 1) + (kk >> 1); }
+    else if (BITS == 4) { w = o; i = kk >> 1; }
+    else { w = 2 * o + (kk >> 2); i = (kk >> 1) & 1; }
+    dw = (w >> 2) * 256 + 4 * lane + (w & 3);
+    bit = 16 * h + BITS * i;
+}
+
+// Paper policy ([RV] 3.2.2-3.2.3, Algorithm 1): keys are quantized R tokens
+// at a time and values one token at a time, so the groups [n_quant / G,
+// n_tail / G) have key codes while their value codes stop at n_vquant (at
+// most R / G + 1 groups per stream).  One wavefront per stream walks their
+// tokens one at a time, like the float32 residual: lane l owns channels 2l,
+// 2l+1; K-hat and V-hat are dequantized from the block in LDS as code *
+// scale, then + zero, in float32; value rows at or past n_vquant come from
+// the ring (16 rows loaded together).
+template <int BITS, int GQ, bool RF32>
+__device__ void decode_mixed_t(const DecodeArgs &a, int stream, uint8_t *lds) {
+#pragma clang fp contract(off)
+    using PP = Pipe<BITS>;
+    constexpr uint32_t M1 = (1u << BITS) - 1u;
+    constexpr int RB = 16;      // ring rows loaded together
+    const int l = threadIdx.x & 63;
+    const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
+    const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * (RF32 ? 4 : 2);
+    const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+    float q0[GQ], q1[GQ], m[GQ], ls[GQ], a0[GQ], a1[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; h++) {
+        const int64_t qrow = ((int64_t)b * a.q_heads + hk * GQ + h) * D;
+        q0[h] = load_q(a, qrow + 2 * l);
+        q1[h] = load_q(a, qrow + 2 * l + 1);
+        m[h] = -INFINITY;
+        ls[h] = 0.f;
+        a0[h] = 0.f;
+        a1[h] = 0.f;
+    }
+    const int c0 = 2 * l, cgv = c0 / G;
+    const uint32_t *kcode = (const uint32_t *)lds;
+    const uint32_t *vcode = (const uint32_t *)(lds + PP::CB);
+    const _Float16 *side = (const _Float16 *)(lds + 2 * PP::CB);
+    for (int gi = 0; gi < a.mixed_groups; gi++) {
+        const int64_t g = a.n_quant / G + gi;
+        const uint8_t *blk = a.blocks + ((int64_t)stream * a.max_groups + g) * a.block_bytes;
+        lds_sync_wave();            // the previous group's LDS reads are done
+#pragma unroll
+        for (int cc = 0; cc < PP::DPG; cc++)
+            dma_1k(blk + cc * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(lbase + cc * 1024));
+        wait_vm<0>();
+        lds_sync_wave();
+        const float ks0 = (float)side[c0], ks1 = (float)side[c0 + 1];
+        const float kz0 = (float)side[D + c0], kz1 = (float)side[D + c0 + 1];
+        for (int r0 = 0; r0 < G; r0 += RB) {
+            // this half-group's value rows from the ring (slots of tokens below
+            // n_vquant may hold other tokens: those rows are not used)
+            float2 vr[RB];
+#pragma unroll
+            for (int r = 0; r < RB; r++) {
+                const int64_t slot = (g * G + r0 + r) % a.ring_cap;
+                if constexpr (RF32) {
+                    vr[r] = *(const float2 *)(rvb + (slot * D + c0) * 4);
+                } else {
+                    const h2 hv = *(const h2 *)(rvb + (slot * D + c0) * 2);
+                    vr[r] = (float2){(float)hv[0], (float)hv[1]};
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RB; r++) {
+                const int tg = r0 + r;                      // token within the group
+                const int64_t t = g * G + tg;
+                int dk, bk, dv0, bv0, dv1, bv1;
+                code_pos<BITS>(false, tg, c0, dk, bk);      // c0 + 1: same dword, bk + 16
+                code_pos<BITS>(true, tg, c0, dv0, bv0);
+                code_pos<BITS>(true, tg, c0 + 1, dv1, bv1);
+                const uint32_t kw = kcode[dk];
+                const float k0 = (float)((kw >> bk) & M1) * ks0 + kz0;
+                const float k1 = (float)((kw >> (bk + 16)) & M1) * ks1 + kz1;
+                float v0 = vr[r].x, v1 = vr[r].y;
+                if (t < a.n_vquant) {
+                    const float vs = (float)side[2 * D + cgv * G + tg];
+                    const float vz = (float)side[3 * D + cgv * G + tg];
+                    v0 = (float)((vcode[dv0] >> bv0) & M1) * vs + vz;
+                    v1 = (float)((vcode[dv1] >> bv1) & M1) * vs + vz;
+                }
+#pragma unroll
+                for (int h = 0; h < GQ; h++) {
+                    const float sc = wave_sum(__builtin_fmaf(q0[h], k0, q1[h] * k1)) * a.sm_log2;
+                    const float mn = fmaxf(m[h], sc);
+                    const float al = __builtin_amdgcn_exp2f(m[h] - mn);
+                    const float p = __builtin_amdgcn_exp2f(sc - mn);
+                    ls[h] = __builtin_fmaf(ls[h], al, p);
+                    a0[h] = __builtin_fmaf(a0[h], al, p * v0);
+                    a1[h] = __builtin_fmaf(a1[h], al, p * v1);
+                    m[h] = mn;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; h++) {
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * a.items + a.splits + 1;
+        *(float2 *)&a.part_o[pi * D + 2 * l] = (float2){a0[h], a1[h]};
+        if (l == 0) {
+            a.part_ml[2 * pi] = m[h];
+            a.part_ml[2 * pi + 1] = ls[h];
+        }
+    }
+}
+
+// A kernel of its own (one wavefront per stream), so that its registers do
+// not count against the occupancy of decode_kernel.
+template <int BITS, int GQ>
+__global__ __launch_bounds__(64) void decode_mixed_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t blk[Pipe<BITS>::BB];
+    if (a.ring_is_f32) decode_mixed_t<BITS, GQ, true>(a, (int)blockIdx.x, blk);
+    else decode_mixed_t<BITS, GQ, false>(a, (int)blockIdx.x, blk);
 }
 
 template <int BITS, int GQ>
@@ -1625,20 +1775,23 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
 // ===========================================================================
 template <int BITS, typename T>
 static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
-    // Groups that start before n_old read rows from the ring.
-    const int64_t ring_groups_end = (a.n_old + G - 1) / G;
+    const int per = a.kinds == 3 ? 2 : 1;
+    // Groups that start before n_old read rows from the ring; so does a group
+    // whose value rows stop at v_limit (only that instance checks the limit).
+    int64_t ring_groups_end = (a.n_old + G - 1) / G;
+    if (a.kinds != 1 && a.v_limit < a.group_end * G) ring_groups_end = a.group_end;
     int64_t split = ring_groups_end < a.group_begin ? a.group_begin : ring_groups_end;
     if (split > a.group_end) split = a.group_end;
     if (split > a.group_begin) {
         QuantizeArgs r = a;
         r.group_end = split;
-        const int64_t tasks = (int64_t)a.streams * (split - a.group_begin) * 2;
+        const int64_t tasks = (int64_t)a.streams * (split - a.group_begin) * per;
         hipLaunchKernelGGL((quantize_kernel<BITS, T, true>), dim3((unsigned)tasks), dim3(64), 0, s, r);
     }
     if (a.group_end > split) {
         QuantizeArgs n = a;
         n.group_begin = split;
-        const int64_t tasks = (int64_t)a.streams * (a.group_end - split) * 2;
+        const int64_t tasks = (int64_t)a.streams * (a.group_end - split) * per;
         hipLaunchKernelGGL((quantize_kernel<BITS, T, false>), dim3((unsigned)tasks), dim3(64), 0, s, n);
     }
     return hipGetLastError();
@@ -1646,6 +1799,10 @@ static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
 
 hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
     if (a.group_end <= a.group_begin || a.streams <= 0) return hipSuccess;
+    if (a.kinds < 1 || a.kinds > 3) return hipErrorInvalidValue;
+    // every value row the kernel reads must exist: rows >= v_limit are skipped
+    if (a.kinds != 1 && a.v_limit < a.group_end * G && a.v_limit <= (a.group_end - 1) * G)
+        return hipErrorInvalidValue;
     if ((int64_t)a.streams * (a.group_end - a.group_begin) * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (a.bits == 2) return a.is_f32 ? launch_quantize_t<2, float>(a, s) : launch_quantize_t<2, _Float16>(a, s);
     if (a.bits == 8) return a.is_f32 ? launch_quantize_t<8, float>(a, s) : launch_quantize_t<8, _Float16>(a, s);
@@ -1669,11 +1826,29 @@ static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream
     else hipLaunchKernelGGL((decode_kernel<BITS, 1>), grid, dim3(64), 0, s, a);
 }
 
+template <int BITS>
+static void launch_mixed_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
+    if (gq == 4) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 4>), grid, dim3(64), 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 2>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_mixed_kernel<BITS, 1>), grid, dim3(64), 0, s, a);
+}
+
+// decode_kernel: a.splits + 1 items per stream (residual, splits); under the
+// paper policy decode_mixed_kernel writes item a.splits + 1 of every stream.
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const int streams = a.batch * a.kv_heads;
     const int gq = a.q_heads / a.kv_heads;
     const int64_t items = (int64_t)streams * (a.splits + 1);
-    if (a.splits + 1 > kMaxItems || items > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (a.items > kMaxItems || items > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (a.items != a.splits + 1 + (a.mixed_groups > 0 ? 1 : 0)) return hipErrorInvalidValue;
+    if (a.mixed_groups > 0) {
+        const dim3 mgrid((unsigned)streams);
+        if (a.bits == 2) launch_mixed_bits<2>(a, gq, mgrid, s);
+        else if (a.bits == 8) launch_mixed_bits<8>(a, gq, mgrid, s);
+        else launch_mixed_bits<4>(a, gq, mgrid, s);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     dim3 grid((unsigned)items);
     if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
     else if (a.bits == 8) launch_decode_bits<8>(a, gq, grid, s);
@@ -1681,7 +1856,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)(a.batch * a.q_heads)), dim3(128), 0,
-                       s, (const float *)a.part_o, (const float *)a.part_ml, a.out, a.splits + 1);
+                       s, (const float *)a.part_o, (const float *)a.part_ml, a.out, a.items);
     return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ KIVI_ERR_HIP = 6
 KIVI_F16 = 0
 KIVI_F32 = 1
 KIVI_FLUSH_WINDOW = 0
+KIVI_FLUSH_PAPER = 1
 KIVI_DEFER_FLUSH = 1
 
 # Every symbol include/kivi.h declares.
@@ -51,13 +52,15 @@ class kivi_layout(ctypes.Structure):
         "blocks", "ring_k", "ring_v", "block_bytes", "code_bytes", "off_kcode",
         "off_vcode", "off_kscale", "off_kzero", "off_vscale", "off_vzero")] + [
         ("max_groups", ctypes.c_int64), ("ring_capacity", ctypes.c_int64),
-        ("n_tokens", ctypes.c_int64), ("n_quantized", ctypes.c_int64)]
+        ("n_tokens", ctypes.c_int64), ("n_quantized", ctypes.c_int64),
+        ("n_vquantized", ctypes.c_int64)]
 
 
 class kivi_append_plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "n_old", "n_new_total", "q_old", "q_new", "flush_token_begin",
-        "flush_token_end", "ring_token_begin", "ring_token_end")]
+        "flush_token_end", "ring_token_begin", "ring_token_end",
+        "v_flush_token_begin", "v_flush_token_end")]
 
 
 class KiviError(RuntimeError):

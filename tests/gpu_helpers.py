@@ -17,10 +17,10 @@ def torch_dtype(np_dtype):
     return torch.float16 if np_dtype == np.float16 else torch.float32
 
 
-def new_cache(B, H, Hq, max_tokens, bits=2, R=128, dtype=np.float16):
+def new_cache(B, H, Hq, max_tokens, bits=2, R=128, dtype=np.float16, policy=0):
     from kv_cache_quantization_amd import KiviCache
     return KiviCache(B, H, Hq, max_tokens, bits=bits, residual=R,
-                     kv_dtype=torch_dtype(dtype), device="cuda")
+                     kv_dtype=torch_dtype(dtype), device="cuda", policy=policy)
 
 
 def to_dev(x):
@@ -38,9 +38,12 @@ def gpu_blocks(cache, n_groups, streams=None):
 
 
 def check_cache(orc, cache, k, v, streams=None, label=""):
-    """Bit-exact check of packed blocks, ring contents and (n, Q) against the
-    oracle built from the full K, V ([B, H, n, D] numpy, or only the streams
-    listed in `streams`, given as [len(streams), n, D] arrays in k, v)."""
+    """Bit-exact check of packed blocks, ring contents and (n, Q_K, Q_V)
+    against the oracle built from the full K, V ([B, H, n, D] numpy, or only
+    the streams listed in `streams`, given as [len(streams), n, D] arrays in
+    k, v) under the cache's flush policy.  Key parts (codes, scale, zero) are
+    compared for the groups below Q_K, value parts for the groups that hold
+    value rows below Q_V (the rows past Q_V in the last one must be 0)."""
     lo = cache.layout()
     c = cache.cfg
     if streams is None:
@@ -48,18 +51,29 @@ def check_cache(orc, cache, k, v, streams=None, label=""):
     else:
         kk, vv = k[None], v[None]     # [1, S, n, D]: the sampled streams as one batch row
     n = kk.shape[2]
-    ref = orc.build_cache(kk, vv, c.bits, c.group, c.residual)
+    G = c.group
+    ref = orc.build_cache(kk, vv, c.bits, G, c.residual, c.policy)
+    qk, qv = ref["qk"], ref["qv"]
     assert lo.n_tokens == n, (label, lo.n_tokens, n)
-    assert lo.n_quantized == ref["qk"], (label, lo.n_quantized, ref["qk"])
-    ng = ref["qk"] // c.group
+    assert (lo.n_quantized, lo.n_vquantized) == (qk, qv), (label, lo.n_quantized,
+                                                         lo.n_vquantized, qk, qv)
+    ngk, ngv = qk // G, -(-qv // G)
+    ng = max(ngk, ngv)
     if ng:
         want = orc.pack_blocks(ref, ng)
         got = gpu_blocks(cache, ng, streams)
-        if not np.array_equal(want, got):
-            bad = np.argwhere(want != got)
+        cb = lo.code_bytes
+        kpart = np.zeros(lo.block_bytes, bool)
+        kpart[:cb] = True
+        kpart[2 * cb:2 * cb + 4 * c.head_dim] = True        # K scale, K zero
+        mask = np.zeros(want.shape, bool)
+        mask[:, :ngk, :] |= kpart
+        mask[:, :ngv, :] |= ~kpart
+        bad = np.argwhere((want != got) & mask)
+        if len(bad):
             raise AssertionError("%s: %d packed bytes differ, first (stream, group, byte) %s" %
                                  (label, len(bad), bad[:5].tolist()))
-    # ring: tokens [Q, n) in slot t % C, verbatim
+    # ring: key tokens [Q_K, n) and value tokens [Q_V, n) in slot t % C, verbatim
     rk, rv = cache.ring_views()
     rk = rk.reshape(-1, lo.ring_capacity, c.head_dim).cpu().numpy()
     rv = rv.reshape(-1, lo.ring_capacity, c.head_dim).cpu().numpy()
@@ -67,9 +81,11 @@ def check_cache(orc, cache, k, v, streams=None, label=""):
     kf = kk.reshape(-1, n, c.head_dim)
     vf = vv.reshape(-1, n, c.head_dim)
     for i, s in enumerate(sel):
-        for t in range(ref["qk"], n):
+        for t in range(qk, n):
             slot = t % lo.ring_capacity
             assert np.array_equal(rk[s, slot].view(np.uint8), kf[i, t].view(np.uint8)), (label, s, t)
+        for t in range(qv, n):
+            slot = t % lo.ring_capacity
             assert np.array_equal(rv[s, slot].view(np.uint8), vf[i, t].view(np.uint8)), (label, s, t)
     return ref
 
@@ -81,7 +97,7 @@ def rel_err(out, ref):
     return float((np.abs(out - ref).max(1) / np.abs(ref).max(1)).max())
 
 
-def oracle_decode(orc, k, v, q, bits, G, R, sm_scale=None):
-    ref = orc.build_cache(k, v, bits, G, R)
+def oracle_decode(orc, k, v, q, bits, G, R, sm_scale=None, policy=0):
+    ref = orc.build_cache(k, v, bits, G, R, policy)
     kh, vh = orc.dequant_cache(k, v, ref)
     return orc.decode_attn(q, kh, vh, sm_scale)

@@ -61,7 +61,8 @@ BAD = [
     (dict(max_tokens=0), kivi.KIVI_ERR_INVALID_ARG),
     (dict(n_q_heads=12, n_kv_heads=8), kivi.KIVI_ERR_INVALID_ARG),   # Hq not a multiple of H
     (dict(kv_dtype=7), kivi.KIVI_ERR_INVALID_ARG),
-    (dict(policy=1), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(policy=2), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(policy=1, residual=0), kivi.KIVI_ERR_INVALID_ARG),        # paper policy: r = n mod R
     (dict(head_dim=64), kivi.KIVI_ERR_UNSUPPORTED),
     (dict(group=64), kivi.KIVI_ERR_UNSUPPORTED),
     (dict(n_q_heads=64, n_kv_heads=8), kivi.KIVI_ERR_UNSUPPORTED),   # GQA 8
@@ -166,6 +167,41 @@ def test_plan_append_matches_window_policy(L, orc, R):
         with pytest.raises(kivi.KiviError) as e:
             kivi.kivi_plan_append(h, -1)
         assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+    finally:
+        kivi.kivi_cache_destroy(h)
+
+
+@pytest.mark.parametrize("R", [32, 128])
+def test_plan_append_matches_paper_policy(L, orc, R):
+    """Paper policy ("[Paper review] KIVI ...", 3.2.2 and Algorithm 1 in
+    3.2.3): keys quantized up to n - (n mod R), values up to max(0, n - R),
+    compared with the oracle's prefixes for every n of a first append; the
+    ring holds tokens from the start of the value group holding Q_V."""
+    T = 700
+    cfg = kivi.make_config(1, 2, 8, bits=2, residual=R, max_tokens=T,
+                           policy=kivi.KIVI_FLUSH_PAPER)
+    h = kivi.kivi_cache_create(cfg, FAKE_DEV, kivi.kivi_cache_bytes(cfg))
+    try:
+        for n in range(0, T + 1):
+            p = kivi.kivi_plan_append(h, n)
+            qk, qv = orc.quantized_prefix(n, 32, R, orc.POLICY_PAPER)
+            assert (p.q_new, p.v_flush_token_end) == (qk, qv), (n, qk, qv)
+            assert (p.flush_token_begin, p.flush_token_end) == (0, qk)
+            assert (p.v_flush_token_begin, p.v_flush_token_end) == (0, qv)
+            assert qk % 32 == 0 and qk >= qv
+            assert (p.ring_token_begin, p.ring_token_end) == (qv // 32 * 32, n)
+            assert p.ring_token_end - p.ring_token_begin < R + 32     # fits the ring
+        lo = kivi.kivi_get_layout(h)
+        assert (lo.n_tokens, lo.n_quantized, lo.n_vquantized) == (0, 0, 0)
+        # one more partial (mixed-group) item per stream than the window policy
+        cfg_w = kivi.make_config(1, 2, 8, bits=2, residual=R, max_tokens=T)
+        hw = kivi.kivi_cache_create(cfg_w, FAKE_DEV, kivi.kivi_cache_bytes(cfg_w))
+        try:
+            ws_window = kivi.kivi_decode_workspace_bytes(hw)
+        finally:
+            kivi.kivi_cache_destroy(hw)
+        row = 8 * (128 + 2) * 4
+        assert kivi.kivi_decode_workspace_bytes(h) == ws_window + row
     finally:
         kivi.kivi_cache_destroy(h)
 
