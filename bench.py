@@ -69,6 +69,14 @@ def decode_bytes(B, H, Hq, n, Q, bits, D=128, G=32):
     return B * H * per_stream + B * Hq * D * (2 + 4)
 
 
+def decode_bytes_kv(B, H, Hq, n, qk, qv, bits, D=128, G=32):
+    """Decode bytes when keys are quantized up to qk and values up to qv
+    (equal under the window policy: then this is decode_bytes)."""
+    k = qk * D * bits / 8 + (qk // G) * D * 4 + (n - qk) * D * 2
+    v = qv * D * bits / 8 + qv * (D // G) * 4 + (n - qv) * D * 2
+    return B * H * (k + v) + B * Hq * D * (2 + 4)
+
+
 def append_bytes(B, H, n, Q, bits, D=128, G=32, esize=2):
     """One-shot append of n tokens: read K and V (esize B per element), write
     codes (b/8 B) and zero/scale (4/G B) for the Q quantized tokens, copy the
@@ -144,6 +152,106 @@ def attn_measure(cache, B, Hq, n, T, stream, evict, evict_out, do_evict):
     }
 
 
+def streaming_measure(policy, do_evict, evict, evict_out, steps=512, prefill=8192, B=8, R=128,
+                      bits=2):
+    """The streaming workload: batch 8, 8 KV / 32 query heads, a one-shot
+    prefill of 8192 tokens, then `steps` decode steps that each append one
+    token (K, V ~ N(0, 1) fp16, outlier key channels) and run decode
+    attention with a fresh query.
+
+    warm: the steps' per-step working set (about 55 MB) stays in the 256 MB
+    Infinity Cache, as in a real serving loop.  All steps are captured once
+    in a HIP graph (the host cannot issue four launches per step as fast as
+    the GPU runs them) and the graph is replayed from the post-prefill
+    cache, restored between replays; the time is the replay over `steps`.
+    cold: eager steps, each after a 1 GiB eviction read (which also gives
+    the host time to enqueue the step), timed with events per step."""
+    import torch
+    from kv_cache_quantization_amd import KiviCache, synth, kivi
+    H, Hq, D = 8, 32, 128
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    k0, v0 = synth.kv_device(4, B, H, prefill, chunk=0, device=dev)
+    rows = [synth.kv_device(4, B, H, 1, chunk=1 + s, device=dev) for s in range(steps)]
+    qs = [synth.queries_device(4, B, Hq, step=s, device=dev) for s in range(steps)]
+    outs = torch.empty((steps, B, Hq, D), dtype=torch.float32, device=dev)
+    cache = KiviCache(B, H, Hq, prefill + steps, bits=bits, residual=R, device=dev, policy=policy)
+    cache.workspace()
+    cache.append(k0, v0)
+    torch.cuda.synchronize()
+    snap = cache.buffer.clone()
+    n0 = cache.layout()
+
+    # algorithmic bytes of every step: the appended token (K and V rows into
+    # the ring, read + write), the tokens that age out of full precision
+    # (read, codes and side data written), and the decode over all n tokens
+    total = 0
+    flushes = 0
+    n, qk, qv = prefill, n0.n_quantized, n0.n_vquantized
+    for s in range(steps):
+        n += 1
+        if policy == kivi.KIVI_FLUSH_PAPER:
+            nqk, nqv = n - n % R, max(0, n - R)
+        else:
+            nqk = nqv = (max(0, n - R) // 32) * 32
+        quant = B * H * D * ((nqk - qk) + (nqv - qv)) * (2 + bits / 8 + 4 / 32)
+        flushes += nqk > qk
+        qk, qv = nqk, nqv
+        total += B * H * 2 * D * 2 * 2 + quant + decode_bytes_kv(B, H, Hq, n, qk, qv, bits)
+    res = {"policy": "window" if policy == kivi.KIVI_FLUSH_WINDOW else "paper",
+           "steps": steps, "bytes": int(total), "key_flushes": int(flushes)}
+
+    def run_steps():
+        for s in range(steps):
+            cache.append(*rows[s])
+            cache.decode(qs[s], out=outs[s])
+
+    # warm: capture all steps once, replay from the restored post-prefill cache
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.graph(g, stream=side):
+        run_steps()
+    torch.cuda.synchronize()
+    ms = []
+    for i in range(4):
+        cache.buffer.copy_(snap)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i:
+            ms.append(e0.elapsed_time(e1))
+    t = sum(ms) / len(ms) / 1e3
+    res["warm"] = {"us_per_step": round(t / steps * 1e6, 3), "GBps": round(total / t / 1e9, 1),
+                   "timing": "one HIP-graph replay of all steps, mean of 3 replays"}
+    del g
+
+    # cold: eager steps, each after an eviction read, timed per step
+    if do_evict:
+        cache.reset()
+        cache.append(k0, v0)
+        torch.cuda.synchronize()
+        per = []
+        for s in range(steps):
+            torch.amax(evict, dim=0, out=evict_out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            cache.append(*rows[s])
+            cache.decode(qs[s], out=outs[s])
+            e1.record(stream)
+            per.append((e0, e1))
+        torch.cuda.synchronize()
+        tc = sum(a.elapsed_time(b) for a, b in per) / 1e3
+        res["cold"] = {"us_per_step": round(tc / steps * 1e6, 3),
+                       "GBps": round(total / tc / 1e9, 1),
+                       "timing": "events around each eager step, 1 GiB eviction read before each"}
+    del cache, snap
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +264,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk (0: one shot)")
     ap.add_argument("--cpu-sample", type=int, default=2, help="batch entries timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-evict", action="store_true")
+    ap.add_argument("--stream-steps", type=int, default=512,
+                    help="also time the streaming workload (batch 8, prefill 8192, then this many "
+                         "single-token append + decode steps) under both flush policies (0: skip)")
     ap.add_argument("--attn-queries", type=int, default=256,
                     help="also time the attention of this many causal queries per head over "
                          "the same cache (a chunked-prefill step; 0: skip)")
@@ -302,6 +413,16 @@ def main():
     if args.attn_queries > 0:
         rec["attn"] = attn_measure(cache, B, Hq, n, args.attn_queries, stream, evict, evict_out,
                                    not args.no_evict)
+    if args.stream_steps > 0:
+        from kv_cache_quantization_amd import kivi
+        rec["streaming"] = {
+            "workload": "batch 8, 8 KV heads, 32 query heads, head_dim 128, 2-bit, group 32, "
+                        "residual 128: prefill 8192 tokens, then %d steps of (append one token, "
+                        "decode attention)" % args.stream_steps,
+            "policies": [streaming_measure(pol, not args.no_evict, evict, evict_out,
+                                           steps=args.stream_steps)
+                         for pol in (kivi.KIVI_FLUSH_WINDOW, kivi.KIVI_FLUSH_PAPER)],
+        }
     if args.cpu_sample > 0:
         k0, v0 = chunks[0]
         if chunk == n:

@@ -120,23 +120,55 @@ int64_t tail_chunks_of(const kivi_cache *c, int64_t n, int64_t q) {
     return (n - q + c->cfg.group - 1) / c->cfg.group;
 }
 
-void decode_split_plan(const kivi_cache *c, int64_t q, int32_t *splits, int32_t *gps) {
+struct DecodePlan {
+    int32_t splits, gps;        // split items per stream, groups each
+    int32_t tail_items, step;   // residual items per stream, chunks each
+};
+
+// Residual items per stream at most when each chunk is an item of its own.
+constexpr int64_t kMaxTailItems = 64;
+
+// One wavefront per work item; aim for one full round of resident
+// wavefronts.  The residual of `tail_chunks` G-token chunks is one item per
+// stream that walks the chunks in turn, unless the split items are so short
+// (fewer than two groups per residual chunk) that the walk would outlast
+// them: then each chunk is an item of its own (up to kMaxTailItems chunks),
+// and the split items give up the slots.  q: tokens of the groups the split
+// items cover.
+DecodePlan decode_plan_of(const kivi_cache *c, int64_t q, int64_t tail_chunks) {
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
     const int64_t ng = q / c->cfg.group;
+    const bool per_chunk_ok = tail_chunks > 1 && tail_chunks <= kMaxTailItems;
+    DecodePlan p = {0, 1, 1, tail_chunks > 1 ? (int32_t)tail_chunks : 1};
     if (ng == 0) {
-        *splits = 0;
-        *gps = 1;
-        return;
+        if (per_chunk_ok) p = {0, 1, (int32_t)tail_chunks, 1};
+        return p;
     }
-    // One wavefront per work item; aim for one full round of resident
-    // wavefronts (one residual item per stream plus `want` split items).
-    int64_t want = kTargetWaves / streams - 1;
-    if (want < 1) want = 1;
-    if (want > ng) want = ng;
-    const int64_t g = (ng + want - 1) / want;
-    *gps = (int32_t)g;
-    *splits = (int32_t)((ng + g - 1) / g);
+    for (int pass = 0; pass < 2; pass++) {
+        int64_t want = kTargetWaves / streams - p.tail_items;
+        if (want < 1) want = 1;
+        if (want > ng) want = ng;
+        const int64_t g = (ng + want - 1) / want;
+        p.gps = (int32_t)g;
+        p.splits = (int32_t)((ng + g - 1) / g);
+        if (pass == 1 || !per_chunk_ok || g >= 2 * tail_chunks) break;
+        p.tail_items = (int32_t)tail_chunks;
+        p.step = 1;
+    }
+    return p;
 }
+
+// Residual items per stream at most (the key residual is shorter than R + G
+// tokens, so it has at most R / G + 1 chunks).
+int64_t max_tail_items(const kivi_config &cfg) {
+    const int64_t chunks = cfg.residual / cfg.group + 1;
+    return chunks < kMaxTailItems ? chunks : kMaxTailItems;
+}
+
+// Paper policy: the groups with key codes whose value codes stop early
+// (fewer than R / G + 2 of them, since Q_K - Q_V < R) are one item each, up
+// to kMaxTailItems items per stream.
+int64_t max_mixed_items(const kivi_config &cfg) { return max_tail_items(cfg) + 1; }
 
 // Attention of T queries: kAttnBlocks x 16 / GQ queries per wavefront,
 // kAttnWaves wavefronts per workgroup (one query block), and the groups split
@@ -361,20 +393,24 @@ kivi_status kivi_flush(kivi_cache *c, hipStream_t stream) {
 
 size_t kivi_decode_workspace_bytes(const kivi_cache *c) {
     if (!c) return 0;
-    // decode_split_plan never makes more than max(1, kTargetWaves / streams - 1)
-    // split items per stream, whatever n is; plus one residual item, and under
-    // the paper policy one item for the groups with partial value codes.
+    // decode_plan_of never makes more than max(1, kTargetWaves / streams - 1)
+    // split items per stream, whatever n is (fewer when the residual takes
+    // one item per chunk), plus at most one residual item per chunk, and
+    // under the paper policy one item for the groups with partial value codes.
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
     int64_t splits = kTargetWaves / streams - 1;
     if (splits < 1) splits = 1;
-    const int64_t items = splits + (c->cfg.policy == KIVI_FLUSH_PAPER ? 2 : 1);
+    const int64_t items = splits + max_tail_items(c->cfg) +
+                          (c->cfg.policy == KIVI_FLUSH_PAPER ? max_mixed_items(c->cfg) : 0);
     const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
     return (size_t)(bhq * items * (c->cfg.head_dim + 2) * 4);
 }
 
 kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits, int32_t *gps) {
     if (!c || !splits || !gps) return KIVI_ERR_INVALID_ARG;
-    decode_split_plan(c, ring_low(c->cfg, c->qv), splits, gps);
+    const DecodePlan p = decode_plan_of(c, ring_low(c->cfg, c->qv), tail_chunks_of(c, c->n, c->q));
+    *splits = p.splits;
+    *gps = p.gps;
     return KIVI_OK;
 }
 
@@ -389,11 +425,12 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
     // codes, value codes below qv (paper policy only); [q, n): the residual
     const int64_t nq = ring_low(c->cfg, c->qv);
     const int32_t mixed = (int32_t)((c->q - nq) / c->cfg.group);
-    int32_t splits, gps;
-    decode_split_plan(c, nq, &splits, &gps);
     const int64_t chunks = tail_chunks_of(c, c->n, c->q);
+    const DecodePlan plan = decode_plan_of(c, nq, chunks);
     const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
-    const int64_t items = splits + 1 + (mixed > 0 ? 1 : 0);
+    const int32_t mixed_items = mixed <= kMaxTailItems ? mixed : (int32_t)kMaxTailItems;
+    const int32_t mixed_step = mixed > 0 ? (mixed + mixed_items - 1) / mixed_items : 1;
+    const int64_t items = plan.splits + plan.tail_items + (mixed > 0 ? mixed_items : 0);
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
     a.block_bytes = c->block_bytes;
@@ -415,9 +452,13 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
     a.n_tail = c->q;
     a.n_vquant = c->qv;
     a.mixed_groups = mixed;
-    a.splits = splits;
-    a.groups_per_split = gps;
+    a.mixed_items = mixed > 0 ? mixed_items : 0;
+    a.mixed_step = mixed_step;
+    a.splits = plan.splits;
+    a.groups_per_split = plan.gps;
     a.tail_chunks = (int32_t)chunks;
+    a.tail_items = plan.tail_items;
+    a.tail_chunk_step = plan.step;
     a.items = (int32_t)items;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)c->cfg.head_dim);
     a.sm_log2 = scale * 1.4426950408889634f;

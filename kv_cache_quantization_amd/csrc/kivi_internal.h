@@ -61,9 +61,13 @@ struct DecodeArgs {
     int64_t n_vquant;           // value codes exist for tokens < n_vquant
     int32_t mixed_groups;       // groups from n_quant / G on with key codes but value
                                 // codes only below n_vquant (paper policy; else 0)
+    int32_t mixed_items;        // items per stream over them (each takes mixed_step
+    int32_t mixed_step;         //   consecutive groups)
     int32_t splits;             // work items per stream over quantized groups
     int32_t groups_per_split;
-    int32_t tail_chunks;        // G-token chunks of the residual (walked by one item)
+    int32_t tail_chunks;        // G-token chunks of the residual
+    int32_t tail_items;         // residual items per stream (each walks tail_chunk_step
+    int32_t tail_chunk_step;    //   consecutive chunks)
     int32_t items;              // partials per (batch, query head): splits, residual, mixed
     float sm_log2;              // softmax scale * log2(e)
 };

@@ -561,24 +561,40 @@ __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
 // Residual ring append: copy rows [tok_begin, tok_end) of the chunk into
 // ring slot t % ring_cap.  16 bytes per thread.
 // ===========================================================================
-__global__ __launch_bounds__(256) void ring_append_kernel(RingArgs a) {
-    const int64_t row_vec = (int64_t)D * a.esize / 16;
+// Each workgroup copies kRingRows rows (K and V) of the flattened
+// [streams][tokens] range: a row pair is 2 * D * esize / 16 threads, each
+// moving 16 bytes; the row's stream, token and slot are computed once per
+// thread with 32-bit arithmetic where the range allows.
+constexpr int kRingThreads = 256;
+
+__global__ __launch_bounds__(kRingThreads) void ring_append_kernel(RingArgs a) {
+    const int row_vec = D * a.esize / 16;                 // 16-byte pieces of one row
+    const int per_row = 2 * row_vec;                      // K and V
+    const int rows_per_block = kRingThreads / per_row;
     const int64_t ntok = a.tok_end - a.tok_begin;
-    const int64_t per_tensor = (int64_t)a.streams * ntok * row_vec;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < 2 * per_tensor;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int which = idx >= per_tensor;
-        int64_t r = idx - which * per_tensor;
-        const int64_t v = r % row_vec;
-        r /= row_vec;
-        const int64_t t = a.tok_begin + r % ntok;
-        const int64_t stream = r / ntok;
-        const uint4 *src = (const uint4 *)((const uint8_t *)(which ? a.in_v : a.in_k) +
-                                           (stream * a.n_new + (t - a.n_old)) * D * a.esize);
-        uint4 *dst = (uint4 *)((uint8_t *)(which ? a.ring_v : a.ring_k) +
-                               (stream * a.ring_cap + t % a.ring_cap) * D * a.esize);
-        dst[v] = src[v];
+    const int64_t rows = (int64_t)a.streams * ntok;
+    const int64_t r = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / per_row;
+    if (r >= rows) return;
+    const int e = threadIdx.x % per_row;
+    const int which = e >= row_vec;                       // 0: K, 1: V
+    const int v = e - which * row_vec;
+    int64_t stream, t;
+    if (rows <= 0x7FFFFFFF) {
+        const uint32_t r32 = (uint32_t)r, n32 = (uint32_t)ntok;
+        stream = r32 / n32;
+        t = a.tok_begin + (r32 - (uint32_t)stream * n32);
+    } else {
+        stream = r / ntok;
+        t = a.tok_begin + (r - stream * ntok);
     }
+    const uint32_t slot = a.ring_cap <= 0x7FFFFFFF && t <= 0xFFFFFFFFll
+                              ? (uint32_t)t % (uint32_t)a.ring_cap
+                              : (uint32_t)(t % a.ring_cap);
+    const uint4 *src = (const uint4 *)((const uint8_t *)(which ? a.in_v : a.in_k) +
+                                       (stream * a.n_new + (t - a.n_old)) * D * a.esize);
+    uint4 *dst = (uint4 *)((uint8_t *)(which ? a.ring_v : a.ring_k) +
+                           (stream * a.ring_cap + slot) * D * a.esize);
+    dst[v] = src[v];
 }
 
 // ===========================================================================
@@ -817,8 +833,9 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Residual item: one per stream over the full-precision window [n_tail, n),
-// taken 32 tokens (one chunk) at a time.  Each chunk's loads are issued
+// Residual items: tail_items per stream over the full-precision window
+// [n_tail, n); item ti walks chunks [ti * step, (ti + 1) * step) of 32
+// tokens, one at a time.  Each chunk's loads are issued
 // together (one memory round trip per chunk), its softmax is local and is
 // merged into the item's running state.
 
@@ -846,7 +863,7 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 // on the vector ALUs -- lane l owns channels 2l, 2l+1 and reads the chunk's p
 // values (32 tokens x GQ heads) broadcast from LDS.
 template <int GQ, bool QF32>
-__device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
+__device__ void decode_tail_f16(const DecodeArgs &a, int stream, int ti, uint8_t *lds) {
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
     const int h = j % GQ;
@@ -866,8 +883,11 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
     float Mr[GQ], Lr[GQ], O0[GQ], O1[GQ];
 #pragma unroll
     for (int hh = 0; hh < GQ; hh++) { Mr[hh] = -INFINITY; Lr[hh] = 0.f; O0[hh] = O1[hh] = 0.f; }
-    int slot0 = (int)(a.n_tail % a.ring_cap);
-    for (int chunk = 0; chunk < a.tail_chunks; chunk++) {
+    const int c_begin = ti * a.tail_chunk_step;
+    const int c_end = c_begin + a.tail_chunk_step < a.tail_chunks ? c_begin + a.tail_chunk_step
+                                                                   : a.tail_chunks;
+    int slot0 = (int)((a.n_tail + (int64_t)G * c_begin) % a.ring_cap);
+    for (int chunk = c_begin; chunk < c_end; chunk++) {
         const int64_t left = a.n_tokens - a.n_tail - (int64_t)G * chunk;
         const int cnt = left < G ? (int)left : G;        // >= 1
         // ring slot of chunk row r (rows past the end read the last valid
@@ -952,7 +972,7 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
     }
 #pragma unroll
     for (int hh = 0; hh < GQ; hh++) {
-        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + hh) * items + a.splits;
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + hh) * items + a.splits + ti;
         *(float2 *)&a.part_o[pi * D + 2 * l] = (float2){O0[hh], O1[hh]};
         if (l == 0) {
             a.part_ml[2 * pi] = Mr[hh];
@@ -964,12 +984,15 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, uint8_t *lds) {
 // fp32 ring: one token per step on the vector ALUs (lane l owns channels 2l,
 // 2l+1), online softmax in the log2 domain.
 template <int GQ>
-__device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
+__device__ void decode_tail_f32(const DecodeArgs &a, int stream, int ti) {
     const int l = threadIdx.x & 63;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const int items = a.items;
     const int cap = (int)a.ring_cap;
-    int slot = (int)(a.n_tail % a.ring_cap);
+    const int64_t t_begin = a.n_tail + (int64_t)G * ti * a.tail_chunk_step;
+    const int64_t t_stop = t_begin + (int64_t)G * a.tail_chunk_step;
+    const int64_t t_end = t_stop < a.n_tokens ? t_stop : a.n_tokens;
+    int slot = (int)(t_begin % a.ring_cap);
     const float *rk = (const float *)a.ring_k + (int64_t)stream * a.ring_cap * D;
     const float *rv = (const float *)a.ring_v + (int64_t)stream * a.ring_cap * D;
     float q0[GQ], q1[GQ], m[GQ], ls[GQ], a0[GQ], a1[GQ];
@@ -983,7 +1006,7 @@ __device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
         a0[h] = 0.f;
         a1[h] = 0.f;
     }
-    for (int64_t t = a.n_tail; t < a.n_tokens; t++) {
+    for (int64_t t = t_begin; t < t_end; t++) {
         const int64_t row = (int64_t)slot * D + 2 * l;
         slot = slot + 1 == cap ? 0 : slot + 1;
         const float k0 = rk[row], k1 = rk[row + 1], v0 = rv[row], v1 = rv[row + 1];
@@ -1001,7 +1024,7 @@ __device__ void decode_tail_f32(const DecodeArgs &a, int stream) {
     }
 #pragma unroll
     for (int h = 0; h < GQ; h++) {
-        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * items + a.splits;
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * items + a.splits + ti;
         float2 ov = {a0[h], a1[h]};
         *(float2 *)&a.part_o[pi * D + 2 * l] = ov;
         if (l == 0) {
@@ -1217,111 +1240,202 @@ __device__ __forceinline__ void code_pos(bool is_v, int t, int c, int &dw, int &
 // Paper policy ([RV] 3.2.2-3.2.3, Algorithm 1): keys are quantized R tokens
 // at a time and values one token at a time, so the groups [n_quant / G,
 // n_tail / G) have key codes while their value codes stop at n_vquant (at
-// most R / G + 1 groups per stream).  One wavefront per stream walks their
-// tokens one at a time, like the float32 residual: lane l owns channels 2l,
-// 2l+1; K-hat and V-hat are dequantized from the block in LDS as code *
-// scale, then + zero, in float32; value rows at or past n_vquant come from
-// the ring (16 rows loaded together).
-template <int BITS, int GQ, bool RF32>
-__device__ void decode_mixed_t(const DecodeArgs &a, int stream, uint8_t *lds) {
-#pragma clang fp contract(off)
+// most R / G + 1 groups per stream).  Item mi of a stream takes mixed_step of
+// them.  Per group: the block is copied into LDS and the scores come from the
+// matrix core exactly as in decode_split (codes, q * kscale as hi + lo, the
+// key-zero bias); the softmax is local to the group and merged into the
+// item's running state like a residual chunk; p.V runs on the vector ALUs,
+// lane l owning channels 2l, 2l+1, with V-hat = code * scale, then + zero,
+// in float32 for tokens below n_vquant and the ring's rows for the others.
+template <int BITS, int GQ, bool RF32, bool QF32>
+__device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t *lds,
+                               uint4 *q_lds) {
     using PP = Pipe<BITS>;
     constexpr uint32_t M1 = (1u << BITS) - 1u;
-    constexpr int RB = 16;      // ring rows loaded together
     const int l = threadIdx.x & 63;
+    const int j = l & 15, Gl = l >> 4;
+    const int h = j % GQ;
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * (RF32 ? 4 : 2);
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
-    float q0[GQ], q1[GQ], m[GQ], ls[GQ], a0[GQ], a1[GQ];
-#pragma unroll
-    for (int h = 0; h < GQ; h++) {
-        const int64_t qrow = ((int64_t)b * a.q_heads + hk * GQ + h) * D;
-        q0[h] = load_q(a, qrow + 2 * l);
-        q1[h] = load_q(a, qrow + 2 * l + 1);
-        m[h] = -INFINITY;
-        ls[h] = 0.f;
-        a0[h] = 0.f;
-        a1[h] = 0.f;
+    float *p_lds = (float *)(lds + PP::BB);           // [GQ][G]
+    h2 qB[4][4];
+    load_q_operand<QF32>(a.q, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
+    {
+        const int64_t qoff = ((int64_t)b * a.q_heads + hk * GQ + (l >> 4) % GQ) * D + 8 * (l & 15);
+        uint4 uq;
+        if constexpr (QF32) {
+            const float *qf = (const float *)a.q + qoff;
+            const float4 x0 = *(const float4 *)qf, x1 = *(const float4 *)(qf + 4);
+            h2 t0 = {(_Float16)x0.x, (_Float16)x0.y}, t1 = {(_Float16)x0.z, (_Float16)x0.w};
+            h2 t2 = {(_Float16)x1.x, (_Float16)x1.y}, t3 = {(_Float16)x1.z, (_Float16)x1.w};
+            uq.x = __builtin_bit_cast(uint32_t, t0); uq.y = __builtin_bit_cast(uint32_t, t1);
+            uq.z = __builtin_bit_cast(uint32_t, t2); uq.w = __builtin_bit_cast(uint32_t, t3);
+        } else {
+            uq = *(const uint4 *)((const _Float16 *)a.q + qoff);
+        }
+        q_lds[l] = uq;
     }
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
+        const h2 d2 = {dn, dn};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; s2++) qB[s2][m] = qB[s2][m] * d2;
+    }
+    const float cs = a.sm_log2 * kTwo24;
+    float Mr[GQ], Lr[GQ], O0[GQ], O1[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; hh++) { Mr[hh] = -INFINITY; Lr[hh] = 0.f; O0[hh] = O1[hh] = 0.f; }
     const int c0 = 2 * l, cgv = c0 / G;
-    const uint32_t *kcode = (const uint32_t *)lds;
-    const uint32_t *vcode = (const uint32_t *)(lds + PP::CB);
-    const _Float16 *side = (const _Float16 *)(lds + 2 * PP::CB);
-    for (int gi = 0; gi < a.mixed_groups; gi++) {
+    const int g_begin = mi * a.mixed_step;
+    const int g_end = g_begin + a.mixed_step < a.mixed_groups ? g_begin + a.mixed_step
+                                                               : a.mixed_groups;
+    for (int gi = g_begin; gi < g_end; gi++) {
         const int64_t g = a.n_quant / G + gi;
         const uint8_t *blk = a.blocks + ((int64_t)stream * a.max_groups + g) * a.block_bytes;
         lds_sync_wave();            // the previous group's LDS reads are done
 #pragma unroll
         for (int cc = 0; cc < PP::DPG; cc++)
             dma_1k(blk + cc * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(lbase + cc * 1024));
+        // the group's value rows from the ring (slots of tokens below
+        // n_vquant may hold other tokens: those rows are not used)
+        float2 vr[G];
+#pragma unroll
+        for (int r = 0; r < G; r++) {
+            const int64_t slot = (g * G + r) % a.ring_cap;
+            if constexpr (RF32) {
+                vr[r] = *(const float2 *)(rvb + (slot * D + c0) * 4);
+            } else {
+                const h2 hv = *(const h2 *)(rvb + (slot * D + c0) * 2);
+                vr[r] = (float2){(float)hv[0], (float)hv[1]};
+            }
+        }
         wait_vm<0>();
         lds_sync_wave();
-        const float ks0 = (float)side[c0], ks1 = (float)side[c0 + 1];
-        const float kz0 = (float)side[D + c0], kz1 = (float)side[D + c0 + 1];
-        for (int r0 = 0; r0 < G; r0 += RB) {
-            // this half-group's value rows from the ring (slots of tokens below
-            // n_vquant may hold other tokens: those rows are not used)
-            float2 vr[RB];
+        const uint8_t *stg = lds;
+        const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
+        uint32_t kc[2 * BITS];
 #pragma unroll
-            for (int r = 0; r < RB; r++) {
-                const int64_t slot = (g * G + r0 + r) % a.ring_cap;
-                if constexpr (RF32) {
-                    vr[r] = *(const float2 *)(rvb + (slot * D + c0) * 4);
-                } else {
-                    const h2 hv = *(const h2 *)(rvb + (slot * D + c0) * 2);
-                    vr[r] = (float2){(float)hv[0], (float)hv[1]};
-                }
+        for (int w4 = 0; w4 < BITS / 2; w4++) {
+            const uint4 u = *(const uint4 *)(stg + w4 * 1024 + 16 * l);
+            kc[4 * w4] = u.x; kc[4 * w4 + 1] = u.y; kc[4 * w4 + 2] = u.z; kc[4 * w4 + 3] = u.w;
+        }
+        f4 Sk = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; s2++)
+            Sk = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(h8, side[16 + 4 * s2 + Gl]),
+                __builtin_bit_cast(h8, q_lds[16 * (j % GQ) + 4 * s2 + Gl]), Sk, 0, 0, 0);
+        f4 S[2] = {(f4){0.f, 0.f, 0.f, 0.f}, (f4){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; s2++) {
+            h2 ks[4], qh[4], ql[4];
+            split4(side[4 * s2 + Gl], ks);
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                qh[m] = qB[s2][m] * ks[m];
+                ql[m] = __builtin_elementwise_fma(qB[s2][m], ks[m], -qh[m]);
             }
+            const h8 A0 = unpack_operand<BITS>(kc, s2), A1 = unpack_operand<BITS>(kc, 4 + s2);
+            const h8 Bh = pack_h8(qh), Bl = pack_h8(ql);
+            S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, S[0], 0, 0, 0);
+            S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, S[1], 0, 0, 0);
+            S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, S[0], 0, 0, 0);
+            S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S[1], 0, 0, 0);
+        }
+        // lane (j, Gl) holds tokens 16t + 4Gl + e of column j (head j % GQ),
+        // in log2 units after the scale and the key-zero bias
+        const float kbl = Sk[0] * a.sm_log2;
+        float mt = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < RB; r++) {
-                const int tg = r0 + r;                      // token within the group
-                const int64_t t = g * G + tg;
-                int dk, bk, dv0, bv0, dv1, bv1;
-                code_pos<BITS>(false, tg, c0, dk, bk);      // c0 + 1: same dword, bk + 16
-                code_pos<BITS>(true, tg, c0, dv0, bv0);
-                code_pos<BITS>(true, tg, c0 + 1, dv1, bv1);
-                const uint32_t kw = kcode[dk];
-                const float k0 = (float)((kw >> bk) & M1) * ks0 + kz0;
-                const float k1 = (float)((kw >> (bk + 16)) & M1) * ks1 + kz1;
-                float v0 = vr[r].x, v1 = vr[r].y;
-                if (t < a.n_vquant) {
-                    const float vs = (float)side[2 * D + cgv * G + tg];
-                    const float vz = (float)side[3 * D + cgv * G + tg];
-                    v0 = (float)((vcode[dv0] >> bv0) & M1) * vs + vz;
-                    v1 = (float)((vcode[dv1] >> bv1) & M1) * vs + vz;
-                }
+        for (int t = 0; t < 2; t++)
 #pragma unroll
-                for (int h = 0; h < GQ; h++) {
-                    const float sc = wave_sum(__builtin_fmaf(q0[h], k0, q1[h] * k1)) * a.sm_log2;
-                    const float mn = fmaxf(m[h], sc);
-                    const float al = __builtin_amdgcn_exp2f(m[h] - mn);
-                    const float p = __builtin_amdgcn_exp2f(sc - mn);
-                    ls[h] = __builtin_fmaf(ls[h], al, p);
-                    a0[h] = __builtin_fmaf(a0[h], al, p * v0);
-                    a1[h] = __builtin_fmaf(a1[h], al, p * v1);
-                    m[h] = mn;
+            for (int e = 0; e < 4; e++) {
+                S[t][e] = __builtin_fmaf(S[t][e], cs, kbl);
+                mt = vmax(mt, S[t][e]);
+            }
+        const float m = xmax_rows(mt);
+        float ls = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float pv = __builtin_amdgcn_exp2f(S[t][e] - m);
+                ls += pv;
+                if (j < GQ) p_lds[j * G + 16 * t + 4 * Gl + e] = pv;     // [head][token]
+            }
+        ls = xsum_rows(ls);
+        lds_sync_wave();
+        // the lane's two channels of every token of the group
+        {
+#pragma clang fp contract(off)
+            const uint32_t *vcode = (const uint32_t *)(stg + PP::CB);
+            const _Float16 *sd = (const _Float16 *)(stg + 2 * PP::CB);
+#pragma unroll
+            for (int r = 0; r < G; r++) {
+                if (g * G + r < a.n_vquant) {
+                    int dv0, bv0, dv1, bv1;
+                    code_pos<BITS>(true, r, c0, dv0, bv0);
+                    code_pos<BITS>(true, r, c0 + 1, dv1, bv1);
+                    const float vs = (float)sd[2 * D + cgv * G + r];
+                    const float vz = (float)sd[3 * D + cgv * G + r];
+                    vr[r].x = (float)((vcode[dv0] >> bv0) & M1) * vs + vz;
+                    vr[r].y = (float)((vcode[dv1] >> bv1) & M1) * vs + vz;
                 }
             }
         }
+#pragma unroll
+        for (int hh = 0; hh < GQ; hh++) {
+            float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+            for (int r4 = 0; r4 < G / 4; r4++) {
+                const float4 p4 = *(const float4 *)&p_lds[hh * G + 4 * r4];
+                const float pq[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    x0 = __builtin_fmaf(pq[e], vr[4 * r4 + e].x, x0);
+                    x1 = __builtin_fmaf(pq[e], vr[4 * r4 + e].y, x1);
+                }
+            }
+            // merge into the running state (head hh's (m, l) sit in lane hh)
+            const float mc = readlane_f(m, hh), lc = readlane_f(ls, hh);
+            const float mn = fmaxf(Mr[hh], mc);
+            const float fo = __builtin_amdgcn_exp2f(Mr[hh] - mn);
+            const float fc = __builtin_amdgcn_exp2f(mc - mn);
+            O0[hh] = __builtin_fmaf(O0[hh], fo, x0 * fc);
+            O1[hh] = __builtin_fmaf(O1[hh], fo, x1 * fc);
+            Lr[hh] = __builtin_fmaf(Lr[hh], fo, lc * fc);
+            Mr[hh] = mn;
+        }
     }
 #pragma unroll
-    for (int h = 0; h < GQ; h++) {
-        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + h) * a.items + a.splits + 1;
-        *(float2 *)&a.part_o[pi * D + 2 * l] = (float2){a0[h], a1[h]};
+    for (int hh = 0; hh < GQ; hh++) {
+        const int64_t pi = ((int64_t)b * a.q_heads + hk * GQ + hh) * a.items + a.splits +
+                           a.tail_items + mi;
+        *(float2 *)&a.part_o[pi * D + 2 * l] = (float2){O0[hh], O1[hh]};
         if (l == 0) {
-            a.part_ml[2 * pi] = m[h];
-            a.part_ml[2 * pi + 1] = ls[h];
+            a.part_ml[2 * pi] = Mr[hh];
+            a.part_ml[2 * pi + 1] = Lr[hh];
         }
     }
 }
 
-// A kernel of its own (one wavefront per stream), so that its registers do
-// not count against the occupancy of decode_kernel.
+// A kernel of its own (one wavefront per (stream, mixed item)), so that its
+// registers do not count against the occupancy of decode_kernel.
 template <int BITS, int GQ>
 __global__ __launch_bounds__(64) void decode_mixed_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t blk[Pipe<BITS>::BB];
-    if (a.ring_is_f32) decode_mixed_t<BITS, GQ, true>(a, (int)blockIdx.x, blk);
-    else decode_mixed_t<BITS, GQ, false>(a, (int)blockIdx.x, blk);
+    __shared__ __attribute__((aligned(16))) uint8_t blk[Pipe<BITS>::BB + GQ * G * 4];
+    __shared__ uint4 q_lds[64];
+    const int streams = a.batch * a.kv_heads;
+    const int stream = (int)(blockIdx.x % streams), mi = (int)(blockIdx.x / streams);
+    if (a.ring_is_f32) {
+        if (a.q_is_f32) decode_mixed_t<BITS, GQ, true, true>(a, stream, mi, blk, q_lds);
+        else decode_mixed_t<BITS, GQ, true, false>(a, stream, mi, blk, q_lds);
+    } else {
+        if (a.q_is_f32) decode_mixed_t<BITS, GQ, false, true>(a, stream, mi, blk, q_lds);
+        else decode_mixed_t<BITS, GQ, false, false>(a, stream, mi, blk, q_lds);
+    }
 }
 
 template <int BITS, int GQ>
@@ -1330,15 +1444,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     __shared__ uint4 q_lds[64];
     const int64_t item = blockIdx.x;
     const int64_t streams = (int64_t)a.batch * a.kv_heads;
-    if (item < streams) {
-        if (a.ring_is_f32) decode_tail_f32<GQ>(a, (int)item);
-        else if (a.q_is_f32) decode_tail_f16<GQ, true>(a, (int)item, pipe);
-        else decode_tail_f16<GQ, false>(a, (int)item, pipe);
+    if (item < streams * a.tail_items) {
+        const int stream = (int)(item % streams), ti = (int)(item / streams);
+        if (a.ring_is_f32) decode_tail_f32<GQ>(a, stream, ti);
+        else if (a.q_is_f32) decode_tail_f16<GQ, true>(a, stream, ti, pipe);
+        else decode_tail_f16<GQ, false>(a, stream, ti, pipe);
         return;
     }
     // (q's dtype selects an instantiation: the prologue's loads must not
     // meet at a control-flow join, where the compiler would wait for them)
-    const int64_t it = item - streams;
+    const int64_t it = item - streams * a.tail_items;
     if (a.q_is_f32)
         decode_split<BITS, GQ, true>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
     else
@@ -1812,10 +1927,11 @@ hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {
     const int64_t ntok = a.tok_end - a.tok_begin;
     if (ntok <= 0) return hipSuccess;
-    const int64_t vecs = 2 * (int64_t)a.streams * ntok * D * a.esize / 16;
-    int64_t blocks = (vecs + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if (a.esize != 2 && a.esize != 4) return hipErrorInvalidValue;
+    const int64_t rows_per_block = kRingThreads / (2 * D * a.esize / 16);
+    const int64_t blocks = ((int64_t)a.streams * ntok + rows_per_block - 1) / rows_per_block;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)blocks), dim3(kRingThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1833,16 +1949,25 @@ static void launch_mixed_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_
     else hipLaunchKernelGGL((decode_mixed_kernel<BITS, 1>), grid, dim3(64), 0, s, a);
 }
 
-// decode_kernel: a.splits + 1 items per stream (residual, splits); under the
-// paper policy decode_mixed_kernel writes item a.splits + 1 of every stream.
+// decode_kernel: a.tail_items + a.splits items per stream (residual, splits)
+// writing partials a.splits .. a.splits + a.tail_items - 1 and 0 .. a.splits
+// - 1; under the paper policy decode_mixed_kernel's a.mixed_items items per
+// stream write the partials after those.
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const int streams = a.batch * a.kv_heads;
     const int gq = a.q_heads / a.kv_heads;
-    const int64_t items = (int64_t)streams * (a.splits + 1);
+    const int64_t items = (int64_t)streams * (a.splits + a.tail_items);
     if (a.items > kMaxItems || items > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (a.items != a.splits + 1 + (a.mixed_groups > 0 ? 1 : 0)) return hipErrorInvalidValue;
+    if (a.tail_items < 1 || a.tail_chunk_step < 1 ||
+        (int64_t)a.tail_items * a.tail_chunk_step < a.tail_chunks)
+        return hipErrorInvalidValue;
+    if (a.items != a.splits + a.tail_items + (a.mixed_groups > 0 ? a.mixed_items : 0))
+        return hipErrorInvalidValue;
     if (a.mixed_groups > 0) {
-        const dim3 mgrid((unsigned)streams);
+        if (a.mixed_items < 1 || a.mixed_step < 1 ||
+            (int64_t)a.mixed_items * a.mixed_step < a.mixed_groups)
+            return hipErrorInvalidValue;
+        const dim3 mgrid((unsigned)(streams * a.mixed_items));
         if (a.bits == 2) launch_mixed_bits<2>(a, gq, mgrid, s);
         else if (a.bits == 8) launch_mixed_bits<8>(a, gq, mgrid, s);
         else launch_mixed_bits<4>(a, gq, mgrid, s);
