@@ -46,7 +46,10 @@ constexpr size_t kAlign = 256;
 // Decode work items aimed for per launch: 256 compute units x 16 resident
 // wavefronts (4 per SIMD: <= 128 registers per lane and <= 10 KiB of LDS
 // each), i.e. one round.
-constexpr int kTargetWaves = 4096;
+#ifndef KIVI_TARGET_WAVES
+#define KIVI_TARGET_WAVES 4096
+#endif
+constexpr int kTargetWaves = KIVI_TARGET_WAVES;
 // Compute units of one MI355X (the attention plan aims at two workgroups each).
 constexpr int kComputeUnits = 256;
 
