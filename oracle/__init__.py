@@ -64,7 +64,7 @@ def lib():
         L.oracle_block_bytes.restype = i64
         L.oracle_block_bytes.argtypes = [i32]
         L.oracle_pack_blocks.argtypes = [i32, i32, i64, i32, i64, P, P, P, P, P, P, P]
-        L.oracle_pack_blocks_kv.argtypes = [i32, i32, i64, i64, i32, i64, P, P, P, P, P, P, P]
+        L.oracle_pack_blocks_kv.argtypes = [i32, i32, i32, i64, i64, i32, i64, P, P, P, P, P, P, P]
         L.oracle_code_position.argtypes = [i32, i32, i32, i32, P, P]
         L.oracle_fake_quant_2d.argtypes = [P, i32, i32, i32, i32, i32, i32, P]
         L.oracle_f16_to_f32_array.argtypes = [P, P, i64]
@@ -217,17 +217,19 @@ def block_bytes(bits: int) -> int:
 
 
 def pack_blocks(cache: dict, max_groups: int | None = None) -> np.ndarray:
-    """Packed blocks [B*H, max_groups, block_bytes] (u8) of the quantized
-    tokens: keys of the first qk, values of the first qv (a value row at or
-    past qv inside a block that holds value rows packs as 0)."""
-    assert cache["D"] == 128 and cache["G"] == 32
+    """Packed 32-token blocks [B*H, max_groups, block_bytes] (u8) of the
+    quantized tokens: keys of the first qk, values of the first qv (a value
+    row at or past qv inside a block that holds value rows packs as 0); each
+    block carries the zero / scale of its key group and of its tokens' value
+    groups (repeated when G > 32)."""
+    assert cache["D"] == 128 and cache["G"] in (32, 64, 128)
     B, H, qk, qv, bits = cache["B"], cache["H"], cache["qk"], cache["qv"], cache["bits"]
     ng = max(qk // 32, -(-qv // 32))
     if max_groups is None:
         max_groups = ng
     assert max_groups >= ng
     out = np.zeros((B * H, max_groups, block_bytes(bits)), np.uint8)
-    lib().oracle_pack_blocks_kv(B, H, qk, qv, bits, max_groups,
+    lib().oracle_pack_blocks_kv(B, H, cache["G"], qk, qv, bits, max_groups,
                                 _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
                                 _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
                                 _p(out))

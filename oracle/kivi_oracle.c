@@ -409,36 +409,40 @@ int64_t oracle_block_bytes(int bits)
     return 2 * (int64_t)(bits * G * D / 8) + 4 * (int64_t)D * 2;
 }
 
-/* Pack the quantized tokens of each stream into blocks:
-   out [B*H][max_groups][block_bytes].  Keys of the first nk tokens (nk a
-   multiple of G) and values of the first nv tokens, from the logical arrays
-   of oracle_build_cache for the same (nk, nv): kcodes [B*H][nk][D], kzero16 /
-   kscale16 [B*H][nk/G][D], vcodes [B*H][nv][D], vzero16 / vscale16
-   [B*H][nv][D/G].  Every code or side entry of a token that is not quantized
-   (a value row at or past nv inside a block that holds value rows) is 0;
-   blocks past both prefixes are left as they are. */
-void oracle_pack_blocks_kv(int B, int H, int64_t nk, int64_t nv, int bits,
+/* Pack the quantized tokens of each stream into 32-token blocks:
+   out [B*H][max_blocks][block_bytes].  Keys of the first nk tokens (nk a
+   multiple of the group size G, G in {32, 64, 128}) and values of the first
+   nv tokens, from the logical arrays of oracle_build_cache for the same
+   (nk, nv, G): kcodes [B*H][nk][D], kzero16 / kscale16 [B*H][nk/G][D],
+   vcodes [B*H][nv][D], vzero16 / vscale16 [B*H][nv][D/G].  A block holds the
+   zero / scale of the key group it belongs to, and value slot cg (channels
+   32cg .. 32cg+31) of a token holds the zero / scale of the value group
+   containing those channels (both repeated when G > 32).  Every code or side
+   entry of a token that is not quantized (a value row at or past nv inside a
+   block that holds value rows) is 0; blocks past both prefixes are left as
+   they are. */
+void oracle_pack_blocks_kv(int B, int H, int G, int64_t nk, int64_t nv, int bits,
                            int64_t max_groups,
                            const uint8_t *kcodes, const uint16_t *kzero16,
                            const uint16_t *kscale16,
                            const uint8_t *vcodes, const uint16_t *vzero16,
                            const uint16_t *vscale16, uint8_t *out)
 {
-    const int D = 128, G = 32;
-    const int64_t cbytes = bits * G * D / 8;
+    const int D = 128, T = 32;      /* channels; tokens per block */
+    const int64_t cbytes = bits * T * D / 8;
     const int64_t bb = oracle_block_bytes(bits);
     /* position tables for one tile, computed by the search above */
-    int64_t *kd = (int64_t *)malloc(sizeof(int64_t) * G * D);
-    int64_t *vd = (int64_t *)malloc(sizeof(int64_t) * G * D);
-    int *kb = (int *)malloc(sizeof(int) * G * D);
-    int *vb = (int *)malloc(sizeof(int) * G * D);
-    for (int t = 0; t < G; t++)
+    int64_t *kd = (int64_t *)malloc(sizeof(int64_t) * T * D);
+    int64_t *vd = (int64_t *)malloc(sizeof(int64_t) * T * D);
+    int *kb = (int *)malloc(sizeof(int) * T * D);
+    int *vb = (int *)malloc(sizeof(int) * T * D);
+    for (int t = 0; t < T; t++)
         for (int c = 0; c < D; c++) {
             code_position(bits, 0, t, c, &kd[t * D + c], &kb[t * D + c]);
             code_position(bits, 1, t, c, &vd[t * D + c], &vb[t * D + c]);
         }
-    int64_t ngk = nk / G;
-    int64_t ngv = (nv + G - 1) / G;
+    int64_t ngk = nk / T;             /* blocks with key codes */
+    int64_t ngv = (nv + T - 1) / T;   /* blocks with value rows */
     int64_t ng = ngk > ngv ? ngk : ngv;
     for (int64_t s = 0; s < (int64_t)B * H; s++)
         for (int64_t j = 0; j < ng; j++) {
@@ -450,28 +454,32 @@ void oracle_pack_blocks_kv(int B, int H, int64_t nk, int64_t nv, int bits,
             uint16_t *vs = kz + D;
             uint16_t *vz = vs + D;
             if (j < ngk) {
+                /* key group of this block: tokens [jT, jT + T) lie in group jT / G */
+                int64_t kg = (s * (nk / G) + (j * T) / G) * D;
                 memset(kc, 0, (size_t)cbytes);
-                for (int t = 0; t < G; t++)
+                for (int t = 0; t < T; t++)
                     for (int c = 0; c < D; c++) {
-                        uint32_t ck = kcodes[(s * nk + j * G + t) * D + c];
+                        uint32_t ck = kcodes[(s * nk + j * T + t) * D + c];
                         kc[kd[t * D + c]] |= ck << kb[t * D + c];
                     }
                 for (int c = 0; c < D; c++) {
-                    ks[c] = kscale16[(s * ngk + j) * D + c];
-                    kz[c] = kzero16[(s * ngk + j) * D + c];
+                    ks[c] = kscale16[kg + c];
+                    kz[c] = kzero16[kg + c];
                 }
             }
             if (j < ngv) {
                 memset(vc, 0, (size_t)cbytes);
-                for (int t = 0; t < G; t++) {
-                    int64_t tok = j * G + t;
+                for (int t = 0; t < T; t++) {
+                    int64_t tok = j * T + t;
                     for (int c = 0; c < D; c++) {
                         uint32_t cv = tok < nv ? vcodes[(s * nv + tok) * D + c] : 0;
                         vc[vd[t * D + c]] |= cv << vb[t * D + c];
                     }
-                    for (int cg = 0; cg < D / G; cg++) {
-                        vs[cg * G + t] = tok < nv ? vscale16[(s * nv + tok) * (D / G) + cg] : 0;
-                        vz[cg * G + t] = tok < nv ? vzero16[(s * nv + tok) * (D / G) + cg] : 0;
+                    /* slot cg: channels 32cg .. 32cg+31, in value group 32cg / G */
+                    for (int cg = 0; cg < D / T; cg++) {
+                        int64_t vg = (s * nv + tok) * (D / G) + (cg * T) / G;
+                        vs[cg * T + t] = tok < nv ? vscale16[vg] : 0;
+                        vz[cg * T + t] = tok < nv ? vzero16[vg] : 0;
                     }
                 }
             }
@@ -482,14 +490,14 @@ void oracle_pack_blocks_kv(int B, int H, int64_t nk, int64_t nv, int bits,
     free(vb);
 }
 
-/* The window policy's blocks: keys and values of the first nq tokens. */
+/* The window policy's blocks at G = 32: keys and values of the first nq tokens. */
 void oracle_pack_blocks(int B, int H, int64_t nq, int bits, int64_t max_groups,
                         const uint8_t *kcodes, const uint16_t *kzero16,
                         const uint16_t *kscale16,
                         const uint8_t *vcodes, const uint16_t *vzero16,
                         const uint16_t *vscale16, uint8_t *out)
 {
-    oracle_pack_blocks_kv(B, H, nq, nq, bits, max_groups, kcodes, kzero16, kscale16,
+    oracle_pack_blocks_kv(B, H, 32, nq, nq, bits, max_groups, kcodes, kzero16, kscale16,
                           vcodes, vzero16, vscale16, out);
 }
 

@@ -163,13 +163,19 @@ def test_round_half_to_even(orc):
 # 1-2; review 3.2.3 steps C and D).  Perturbing one element may change only
 # the codes and parameters of its own group.
 # ---------------------------------------------------------------------------
-def test_grouping_axes_locality(orc):
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_grouping_axes_locality(orc, G):
+    """A key group is G consecutive tokens of one channel and a value group G
+    consecutive channels of one token (cookbook notebook, K along dim 0 and V
+    along dim 1; [RV] 3.2.3 steps C-D; G = 32, 64 and 128 as in [RV]'s group
+    size ablation): one outlier changes the codes and parameters of its own
+    group only, and codes across the whole group (its first and last quarter)."""
     rng = np.random.default_rng(7)
-    B, H, n, D, G = 1, 1, 96, 128, 32
+    B, H, n, D = 1, 1, 256, 128
     k = rng.standard_normal((B, H, n, D)).astype(np.float32)
     v = rng.standard_normal((B, H, n, D)).astype(np.float32)
     base = orc.build_cache(k, v, 2, G, 0)
-    t, c = 45, 77
+    t, c = 145, 77
     k2, v2 = k.copy(), v.copy()
     k2[0, 0, t, c] = 40.0
     v2[0, 0, t, c] = 40.0
@@ -184,6 +190,10 @@ def test_grouping_axes_locality(orc):
     assert len(dv) > 0 and set(dv[:, 0]) == {t} and set(dv[:, 1] // G) == {c // G}
     dvs = np.argwhere(base["vscale16"][0, 0] != pert["vscale16"][0, 0])
     assert [tuple(x) for x in dvs] == [(t, c // G)]
+    # the changes span the group: its first and its last quarter
+    t0, c0 = t // G * G, c // G * G
+    assert dk[:, 0].min() < t0 + G // 4 and dk[:, 0].max() >= t0 + 3 * G // 4
+    assert dv[:, 1].min() < c0 + G // 4 and dv[:, 1].max() >= c0 + 3 * G // 4
 
 
 # ---------------------------------------------------------------------------
@@ -392,6 +402,41 @@ def test_pack_layout_is_bijective(orc, bits):
                 seen.add(slot)
         assert len(seen) == 32 * 128
     assert orc.block_bytes(bits) == 2 * bits * 32 * 128 // 8 + 4 * 128 * 2
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_pack_blocks_group_sizes(orc, G):
+    """Blocks stay 32 tokens for G = 64 and 128: every block unpacks (through
+    the pinned code positions) to its tokens' logical codes, carries the
+    zero / scale of the key group it lies in, and value slot cg of a token
+    carries the zero / scale of the value group holding channels 32cg .. 32cg
+    + 31."""
+    rng = np.random.default_rng(11)
+    n, D, bits = 256, 128, 2
+    k = rng.standard_normal((1, 1, n, D)).astype(np.float16)
+    v = rng.standard_normal((1, 1, n, D)).astype(np.float16)
+    c = orc.build_cache(k, v, bits, G, 0)
+    blk = orc.pack_blocks(c)[0]
+    cb = bits * 32 * D // 8
+    pos = {(isv, t, ch): orc.code_position(bits, isv, t, ch)
+           for isv in (0, 1) for t in range(32) for ch in range(D)}
+    for j in range(n // 32):
+        words = blk[j, :2 * cb].view(np.uint32)
+        side = blk[j, 2 * cb:].view(np.uint16)
+        for t in range(0, 32, 7):
+            for ch in range(0, D, 5):
+                for isv, codes in ((0, c["kcodes"]), (1, c["vcodes"])):
+                    d, b = pos[(isv, t, ch)]
+                    got = (int(words[isv * cb // 4 + d]) >> b) & ((1 << bits) - 1)
+                    assert got == codes[0, 0, 32 * j + t, ch]
+        assert np.array_equal(side[:D], c["kscale16"][0, 0, 32 * j // G])
+        assert np.array_equal(side[D:2 * D], c["kzero16"][0, 0, 32 * j // G])
+        for cg in range(4):
+            toks = slice(32 * j, 32 * j + 32)
+            assert np.array_equal(side[2 * D + 32 * cg:2 * D + 32 * cg + 32],
+                                  c["vscale16"][0, 0, toks, 32 * cg // G])
+            assert np.array_equal(side[3 * D + 32 * cg:3 * D + 32 * cg + 32],
+                                  c["vzero16"][0, 0, toks, 32 * cg // G])
 
 
 # ---------------------------------------------------------------------------
