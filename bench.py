@@ -261,6 +261,7 @@ def main():
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--context", type=int, default=32768)
     ap.add_argument("--residual", type=int, default=128)
+    ap.add_argument("--group", type=int, default=32, choices=(32, 64, 128))
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk (0: one shot)")
     ap.add_argument("--cpu-sample", type=int, default=2, help="batch entries timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-evict", action="store_true")
@@ -281,7 +282,7 @@ def main():
     from kv_cache_quantization_amd import KiviCache, synth
 
     B, H, Hq, D = args.batch, 8, 32, 128
-    n, R, bits = args.context, args.residual, args.bits
+    n, R, bits, G = args.context, args.residual, args.bits, args.group
     chunk = args.chunk or n
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -294,7 +295,7 @@ def main():
         chunks.append(synth.kv_device(3, B, H, cn, D, chunk=ci // chunk, device=dev))
     q = synth.queries_device(3, B, Hq, D, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    cache = KiviCache(B, H, Hq, n, bits=bits, residual=R, device=dev)
+    cache = KiviCache(B, H, Hq, n, bits=bits, group=G, residual=R, device=dev)
     cache.workspace()
     evict = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
     evict_out = torch.empty((), dtype=torch.float32, device=dev)
@@ -347,14 +348,14 @@ def main():
     t_dec = sum(dec_ms) / args.steps / 1e3
     lo = cache.layout()
     Q = lo.n_quantized
-    dbytes = decode_bytes(B, H, Hq, n, Q, bits)
-    abytes = append_bytes(B, H, n, Q, bits)
+    dbytes = decode_bytes(B, H, Hq, n, Q, bits, G=G)
+    abytes = append_bytes(B, H, n, Q, bits, G=G)
     dec_gbps = dbytes / t_dec / 1e9
     app_gbps = abytes / t_app / 1e9
     splits, gps = cache.decode_plan()
     traffic, traffic_src = (None, "workload without a counter summary")
     atraffic = None
-    if (B, n, R, bits, chunk) == (16, 32768, 128, 2, 32768):
+    if (B, n, R, bits, chunk, G) == (16, 32768, 128, 2, 32768, 32):
         traffic, traffic_src = counter_traffic("decode_b16_ctx32768_2bit_counters.txt")
         atraffic, _ = counter_traffic("decode_b16_ctx32768_2bit_counters.txt",
                                       "append_traffic_bytes_per_launch")
@@ -375,10 +376,10 @@ def main():
                 "q ~ N(0,1) fp16, seeded torch generator on the device",
         "config": {
             "workload": "KIVI %d-bit decode over a one-shot prefill: batch %d, 8 KV heads, "
-                        "32 query heads, head_dim 128, context %d, group 32, residual %d%s"
-                        % (bits, B, n, R, "" if chunk == n else ", prefill in %d-token chunks" % chunk),
+                        "32 query heads, head_dim 128, context %d, group %d, residual %d%s"
+                        % (bits, B, n, G, R, "" if chunk == n else ", prefill in %d-token chunks" % chunk),
             "batch": B, "kv_heads": H, "q_heads": Hq, "head_dim": D, "context": n,
-            "group": 32, "residual": R, "bits": bits, "quantized_tokens": Q,
+            "group": G, "residual": R, "bits": bits, "quantized_tokens": Q,
             "decode_splits_per_stream": splits, "groups_per_split": gps,
         },
         "decode": {"ms": round(t_dec * 1e3, 4), "median_ms": round(dec_ms[len(dec_ms) // 2], 4),
@@ -425,7 +426,7 @@ def main():
         }
     if args.cpu_sample > 0:
         k0, v0 = chunks[0]
-        if chunk == n:
+        if chunk == n and G == 32:
             rec["cpu_baseline"] = cpu_baseline(k0, v0, q, bits, R, H, Hq, args.cpu_sample)
     print(json.dumps(rec), flush=True)
 

@@ -69,7 +69,9 @@ kivi_status validate(const kivi_config *c) {
     if (c->policy == KIVI_FLUSH_PAPER && c->residual == 0) return KIVI_ERR_INVALID_ARG;
     if (c->reserved != 0) return KIVI_ERR_INVALID_ARG;
     // Shapes the kernels are built for.
-    if (c->head_dim != kHeadDim || c->group != kGroup) return KIVI_ERR_UNSUPPORTED;
+    if (c->head_dim != kHeadDim) return KIVI_ERR_UNSUPPORTED;
+    if (c->group != kGroup && c->group != 2 * kGroup && c->group != 4 * kGroup)
+        return KIVI_ERR_UNSUPPORTED;
     const int gq = c->n_q_heads / c->n_kv_heads;
     if (gq != 1 && gq != 2 && gq != 4) return KIVI_ERR_UNSUPPORTED;
     if ((int64_t)c->batch * c->n_kv_heads > (1LL << 24)) return KIVI_ERR_UNSUPPORTED;
@@ -85,8 +87,8 @@ struct Sizes {
 Sizes sizes_of(const kivi_config *c) {
     Sizes s;
     const int64_t streams = (int64_t)c->batch * c->n_kv_heads;
-    s.max_groups = c->max_tokens / c->group;
-    s.code_bytes = (int64_t)c->bits * c->group * c->head_dim / 8;
+    s.max_groups = c->max_tokens / kGroup;     // 32-token blocks
+    s.code_bytes = (int64_t)c->bits * kGroup * c->head_dim / 8;
     s.block_bytes = 2 * s.code_bytes + 4 * (int64_t)c->head_dim * 2;
     s.ring_cap = (int64_t)c->residual + c->group;
     s.esize = c->kv_dtype == KIVI_F32 ? 4 : 2;
@@ -110,8 +112,9 @@ Prefix prefix_of(const kivi_config &c, int64_t n) {
     return {q, q};
 }
 
-// Lowest token the ring holds: the start of the value group holding Q_V.
-int64_t ring_low(const kivi_config &c, int64_t qv) { return qv / c.group * c.group; }
+// Lowest token the ring holds: the start of the 32-token block holding Q_V
+// (= Q_V under the window policy, where Q_V is a multiple of G).
+int64_t ring_low(const kivi_config &, int64_t qv) { return qv / kGroup * kGroup; }
 
 bool canonical(const kivi_cache *c) {
     const Prefix p = prefix_of(c->cfg, c->n);
@@ -120,7 +123,7 @@ bool canonical(const kivi_cache *c) {
 
 // G-token chunks of the residual [Q, n) (walked by one item per stream).
 int64_t tail_chunks_of(const kivi_cache *c, int64_t n, int64_t q) {
-    return (n - q + c->cfg.group - 1) / c->cfg.group;
+    return (n - q + kGroup - 1) / kGroup;
 }
 
 struct DecodePlan {
@@ -140,7 +143,7 @@ constexpr int64_t kMaxTailItems = 64;
 // items cover.
 DecodePlan decode_plan_of(const kivi_cache *c, int64_t q, int64_t tail_chunks) {
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
-    const int64_t ng = q / c->cfg.group;
+    const int64_t ng = q / kGroup;
     const bool per_chunk_ok = tail_chunks > 1 && tail_chunks <= kMaxTailItems;
     DecodePlan p = {0, 1, 1, tail_chunks > 1 ? (int32_t)tail_chunks : 1};
     if (ng == 0) {
@@ -162,9 +165,9 @@ DecodePlan decode_plan_of(const kivi_cache *c, int64_t q, int64_t tail_chunks) {
 }
 
 // Residual items per stream at most (the key residual is shorter than R + G
-// tokens, so it has at most R / G + 1 chunks).
+// tokens, so it has at most (R + G) / 32 chunks of 32).
 int64_t max_tail_items(const kivi_config &cfg) {
-    const int64_t chunks = cfg.residual / cfg.group + 1;
+    const int64_t chunks = (cfg.residual + cfg.group) / kGroup;
     return chunks < kMaxTailItems ? chunks : kMaxTailItems;
 }
 
@@ -184,7 +187,7 @@ void attn_plan(const kivi_cache *c, int64_t T, int64_t q, int32_t *qblocks, int3
     const int64_t cbs = (T + qt - 1) / qt;
     const int64_t qb = (cbs + kAttnWaves * kAttnBlocks - 1) / (kAttnWaves * kAttnBlocks);
     *qblocks = (int32_t)qb;
-    const int64_t ng = q / c->cfg.group;
+    const int64_t ng = q / kGroup;
     int64_t want = 2 * kComputeUnits / (streams * qb);
     if (want < 1) want = 1;
     if (want > (ng + 3) / 4) want = (ng + 3) / 4;       // >= 4 groups per split
@@ -282,15 +285,15 @@ kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new, kivi_append_pla
 
 namespace {
 
-// Quantize groups [group_begin, group_end) of every stream: kinds 1 = keys,
-// 2 = values, 3 = both; value rows at or past v_limit are left out (codes and
-// side data 0).  Tokens t < p.n_old are read from the ring, later ones from
-// k / v.
+// Quantize the 32-token blocks [block_begin, block_end) of every stream:
+// kinds 1 = key groups (G / 32 blocks each), 2 = value blocks, 3 = both;
+// value rows at or past v_limit are left out (codes and side data 0).
+// Tokens t < p.n_old are read from the ring, later ones from k / v.
 kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const void *k,
-                             const void *v, int64_t n_new, int64_t group_begin,
-                             int64_t group_end, int kinds, int64_t v_limit,
+                             const void *v, int64_t n_new, int64_t block_begin,
+                             int64_t block_end, int kinds, int64_t v_limit,
                              hipStream_t stream) {
-    if (group_end <= group_begin) return KIVI_OK;
+    if (block_end <= block_begin) return KIVI_OK;
     QuantizeArgs a;
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
@@ -302,8 +305,9 @@ kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const voi
     a.ring_v = c->base + c->off_ring_v;
     a.ring_cap = c->ring_cap;
     a.n_old = p.n_old;
-    a.group_begin = group_begin;
-    a.group_end = group_end;
+    a.block_begin = block_begin;
+    a.block_end = block_end;
+    a.gt = c->cfg.group / kGroup;
     a.streams = c->cfg.batch * c->cfg.n_kv_heads;
     a.is_f32 = c->cfg.kv_dtype == KIVI_F32;
     a.bits = c->cfg.bits;
@@ -312,14 +316,15 @@ kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const voi
     return launch_quantize(a, stream) == hipSuccess ? KIVI_OK : KIVI_ERR_HIP;
 }
 
-// Everything the plan quantizes.  Window policy: the groups [q_old, q_new) /
-// G, keys and values together.  Paper policy: the key groups [q_old, q_new) /
-// G, then the value groups touched by [qv_old, qv_new): whole groups, and the
-// group holding qv_new up to that token (re-quantized whole on every append
-// that adds rows to it; its earlier rows come out identical).
+// Everything the plan quantizes, in 32-token blocks.  Window policy: the
+// tokens [q_old, q_new), keys and values together.  Paper policy: the key
+// groups of [q_old, q_new), then the value blocks touched by [qv_old,
+// qv_new): whole blocks, and the block holding qv_new up to that token
+// (re-quantized whole on every append that adds rows to it; its earlier rows
+// come out identical, since values are quantized per token).
 kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *k, const void *v,
                           int64_t n_new, hipStream_t stream) {
-    const int64_t G = c->cfg.group;
+    const int64_t G = kGroup;
     constexpr int64_t kNoLimit = INT64_MAX;
     if (c->cfg.policy != KIVI_FLUSH_PAPER)
         return enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
@@ -427,7 +432,7 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
     // groups [0, nq / G): key and value codes (split items); [nq, q): key
     // codes, value codes below qv (paper policy only); [q, n): the residual
     const int64_t nq = ring_low(c->cfg, c->qv);
-    const int32_t mixed = (int32_t)((c->q - nq) / c->cfg.group);
+    const int32_t mixed = (int32_t)((c->q - nq) / kGroup);
     const int64_t chunks = tail_chunks_of(c, c->n, c->q);
     const DecodePlan plan = decode_plan_of(c, nq, chunks);
     const int64_t bhq = (int64_t)c->cfg.batch * c->cfg.n_q_heads;

@@ -9,8 +9,10 @@ namespace kivi {
 constexpr int kHeadDim = 128;   // D: channels per head
 constexpr int kGroup = 32;      // G: tokens per key group / channels per value group
 
-// Quantize tokens [group_begin*G, group_end*G) of every stream into packed
-// blocks.  Token t < n_old is read from ring slot t % ring_cap, later tokens
+// Quantize the 32-token blocks [block_begin, block_end) of every stream.  A
+// key group spans gt = G / 32 blocks (block_begin and block_end are then
+// multiples of gt for key tasks); a value group spans 32 * gt channels of one
+// token.  Token t < n_old is read from ring slot t % ring_cap, later tokens
 // from row (t - n_old) of the appended chunk.
 struct QuantizeArgs {
     uint8_t *blocks;            // [streams][max_groups][block_bytes]
@@ -21,11 +23,12 @@ struct QuantizeArgs {
     const void *ring_k, *ring_v;// [streams][ring_cap][D] (kv dtype)
     int64_t ring_cap;
     int64_t n_old;
-    int64_t group_begin, group_end;
+    int64_t block_begin, block_end;
     int32_t streams;
     int32_t is_f32;             // kv dtype: 0 fp16, 1 fp32
     int32_t bits;               // 2, 4 or 8
-    int32_t kinds;              // 1: key groups, 2: value groups, 3: both
+    int32_t gt;                 // blocks per key group: G / 32 (1, 2 or 4)
+    int32_t kinds;              // 1: key groups, 2: value blocks, 3: both
     int64_t v_limit;            // value codes / side data of tokens >= v_limit are written 0
 };
 

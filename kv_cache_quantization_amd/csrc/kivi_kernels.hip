@@ -198,26 +198,70 @@ __device__ __forceinline__ V reduce_quad(V v) {
     return MAX ? __builtin_elementwise_maximum(v, o) : __builtin_elementwise_minimum(v, o);
 }
 
+// Key groups: the lane's in-lane minimum / maximum of its 8 channels over
+// the tile's rows it holds, merged over the G / 32 tiles of a group, then
+// reduced over the four lanes c, c+16, c+32, c+48 that hold the other rows.
+template <typename T> struct KPart;
+template <> struct KPart<_Float16> { h2 mn[4], mx[4]; };
+template <> struct KPart<float> { float mn[8], mx[8]; };
+
+__device__ __forceinline__ void kpart_add(const Tile<_Float16> &t, KPart<_Float16> &p, bool first) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        h2 mn = t.v[0][e], mx = t.v[0][e];
+#pragma unroll
+        for (int j = 1; j < 8; j++) { mn = hmin(mn, t.v[j][e]); mx = hmax(mx, t.v[j][e]); }
+        p.mn[e] = first ? mn : hmin(p.mn[e], mn);
+        p.mx[e] = first ? mx : hmax(p.mx[e], mx);
+    }
+}
+__device__ __forceinline__ void kpart_add(const Tile<float> &t, KPart<float> &p, bool first) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        float mn = t.v[0][e], mx = t.v[0][e];
+#pragma unroll
+        for (int j = 1; j < 8; j++) { mn = fmin_(mn, t.v[j][e]); mx = fmax_(mx, t.v[j][e]); }
+        p.mn[e] = first ? mn : fmin_(p.mn[e], mn);
+        p.mx[e] = first ? mx : fmax_(p.mx[e], mx);
+    }
+}
+__device__ __forceinline__ void kpart_finish(KPart<_Float16> &p, float (&lo)[8], float (&hi)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const h2 mn = reduce_q<false>(p.mn[e]), mx = reduce_q<true>(p.mx[e]);
+        lo[2 * e] = (float)mn[0]; lo[2 * e + 1] = (float)mn[1];
+        hi[2 * e] = (float)mx[0]; hi[2 * e + 1] = (float)mx[1];
+    }
+}
+__device__ __forceinline__ void kpart_finish(KPart<float> &p, float (&lo)[8], float (&hi)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        lo[e] = reduce_q<false>(p.mn[e]);
+        hi[e] = reduce_q<true>(p.mx[e]);
+    }
+}
+
+// Value groups of 32 * GT channels: after the quad (32 channels), the lanes
+// c ^ 4 (64 channels) and c ^ 8 (128 channels) of the same row.
+template <int GT, bool MAX, typename V>
+__device__ __forceinline__ V reduce_span(V v) {
+#pragma unroll
+    for (int x = 4; x < 4 * GT; x <<= 1) {
+        const V o = from_f<V>(__shfl_xor(as_f(v), x));
+        v = MAX ? __builtin_elementwise_maximum(v, o) : __builtin_elementwise_minimum(v, o);
+    }
+    return v;
+}
+
 // Per-group minimum and maximum for the lane's 8 groups (k = 0..7: channel
-// 8c + k for keys, row j = k for values).
-template <bool IS_V>
+// 8c + k for keys, row j = k for values) of one tile.
+template <bool IS_V, int GT>
 __device__ __forceinline__ void group_minmax(const Tile<_Float16> &t, float (&lo)[8],
                                              float (&hi)[8]) {
     if (!IS_V) {
-        h2 mn[4], mx[4];
-#pragma unroll
-        for (int p = 0; p < 4; p++) mn[p] = mx[p] = t.v[0][p];
-#pragma unroll
-        for (int j = 1; j < 8; j++)
-#pragma unroll
-            for (int p = 0; p < 4; p++) { mn[p] = hmin(mn[p], t.v[j][p]); mx[p] = hmax(mx[p], t.v[j][p]); }
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            mn[p] = reduce_q<false>(mn[p]);
-            mx[p] = reduce_q<true>(mx[p]);
-            lo[2 * p] = (float)mn[p][0]; lo[2 * p + 1] = (float)mn[p][1];
-            hi[2 * p] = (float)mx[p][0]; hi[2 * p + 1] = (float)mx[p][1];
-        }
+        KPart<_Float16> p;
+        kpart_add(t, p, true);
+        kpart_finish(p, lo, hi);
     } else {
 #pragma unroll
         for (int jp = 0; jp < 4; jp++) {
@@ -231,34 +275,29 @@ __device__ __forceinline__ void group_minmax(const Tile<_Float16> &t, float (&lo
             // (row 2jp, row 2jp+1) pairs
             h2 mn = hmin((h2){a[0][0], a[1][0]}, (h2){a[0][1], a[1][1]});
             h2 mx = hmax((h2){b[0][0], b[1][0]}, (h2){b[0][1], b[1][1]});
-            mn = reduce_quad<false>(mn);
-            mx = reduce_quad<true>(mx);
+            mn = reduce_span<GT, false>(reduce_quad<false>(mn));
+            mx = reduce_span<GT, true>(reduce_quad<true>(mx));
             lo[2 * jp] = (float)mn[0]; lo[2 * jp + 1] = (float)mn[1];
             hi[2 * jp] = (float)mx[0]; hi[2 * jp + 1] = (float)mx[1];
         }
     }
 }
 
-template <bool IS_V>
+template <bool IS_V, int GT>
 __device__ __forceinline__ void group_minmax(const Tile<float> &t, float (&lo)[8],
                                              float (&hi)[8]) {
     if (!IS_V) {
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            float mn = t.v[0][e], mx = t.v[0][e];
-#pragma unroll
-            for (int j = 1; j < 8; j++) { mn = fmin_(mn, t.v[j][e]); mx = fmax_(mx, t.v[j][e]); }
-            lo[e] = reduce_q<false>(mn);
-            hi[e] = reduce_q<true>(mx);
-        }
+        KPart<float> p;
+        kpart_add(t, p, true);
+        kpart_finish(p, lo, hi);
     } else {
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             float mn = t.v[j][0], mx = t.v[j][0];
 #pragma unroll
             for (int e = 1; e < 8; e++) { mn = fmin_(mn, t.v[j][e]); mx = fmax_(mx, t.v[j][e]); }
-            lo[j] = reduce_quad<false>(mn);
-            hi[j] = reduce_quad<true>(mx);
+            lo[j] = reduce_span<GT, false>(reduce_quad<false>(mn));
+            hi[j] = reduce_span<GT, true>(reduce_quad<true>(mx));
         }
     }
 }
@@ -377,8 +416,35 @@ __device__ __forceinline__ void quantize_pack8(const QuantizeArgs &a, const TT &
         *(uint4 *)&dst[w4 * 256 + 4 * l] = *(const uint4 *)&tr[l * DPL + 4 * w4];
 }
 
-template <int BITS, bool IS_V, bool RING, typename T>
-__device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t stream, int64_t g,
+// The lane's 8 rows x 8 channels of block g of a stream.
+template <bool IS_V, bool RING, typename T>
+__device__ __forceinline__ void load_tile(const QuantizeArgs &a, int64_t stream, int64_t g,
+                                          Tile<T> &t) {
+    const int l = threadIdx.x;
+    const int q = l >> 4, c = l & 15;
+    const RowSource<T> src(a, IS_V ? a.ring_v : a.ring_k, IS_V ? a.in_v : a.in_k, stream, g * G);
+    if (!RING) {
+        const T *base = src.in + 8 * c;
+#pragma unroll
+        for (int j = 0; j < 8; j++) load_row(t, j, base + tile_row<IS_V>(j, q) * D);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int r = tile_row<IS_V>(j, q);
+            // value rows at or past v_limit are not quantized (they need
+            // not exist yet): zeros in, codes 0 out
+            if (IS_V && g * G + r >= a.v_limit) zero_row(t, j);
+            else load_row(t, j, src.row(r) + 8 * c);
+        }
+    }
+}
+
+// One task: a key group (GT consecutive blocks starting at block g0: the
+// statistics span all of them, and each block is then coded and stored with
+// the group's zero / scale), or the values of block g0 (groups of 32 * GT
+// channels per token).
+template <int BITS, bool IS_V, bool RING, typename T, int GT>
+__device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t stream, int64_t g0,
                                               uint32_t *tr) {
 #pragma clang fp contract(off)
     constexpr float L = (float)((1 << BITS) - 1);
@@ -386,26 +452,20 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
     const int q = l >> 4, c = l & 15;
 
     Tile<T> t;
-    {
-        const RowSource<T> src(a, IS_V ? a.ring_v : a.ring_k, IS_V ? a.in_v : a.in_k, stream, g * G);
-        if (!RING) {
-            const T *base = src.in + 8 * c;
-#pragma unroll
-            for (int j = 0; j < 8; j++) load_row(t, j, base + tile_row<IS_V>(j, q) * D);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int r = tile_row<IS_V>(j, q);
-                // value rows at or past v_limit are not quantized (they need
-                // not exist yet): zeros in, codes 0 out
-                if (IS_V && g * G + r >= a.v_limit) zero_row(t, j);
-                else load_row(t, j, src.row(r) + 8 * c);
-            }
-        }
-    }
-
     float lo[8], hi[8];
-    group_minmax<IS_V>(t, lo, hi);
+    if constexpr (!IS_V && GT > 1) {
+        // the last block stays in registers for the first store below
+        KPart<T> part;
+#pragma unroll 1
+        for (int tt = 0; tt < GT; tt++) {
+            load_tile<IS_V, RING>(a, stream, g0 + tt, t);
+            kpart_add(t, part, tt == 0);
+        }
+        kpart_finish(part, lo, hi);
+    } else {
+        load_tile<IS_V, RING>(a, stream, g0, t);
+        group_minmax<IS_V, GT>(t, lo, hi);
+    }
     float mn[8], s[8], y[8], cz[8];
     float smin = INFINITY, smax = 0.0f, czmax = 0.0f;
 #pragma unroll
@@ -424,6 +484,8 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
     // 2^-14 + ... for t <= 256.  The margin below is about 4x that.
     const float near_tie = 0.5f - ((BITS == 8 ? 0x1p-12f : 0x1p-16f) + 0x1p-22f * czmax);
 
+    // codes, zero / scale of block g (whose rows are in t)
+    auto store_block = [&](int64_t g) {
     uint8_t *blk = a.blocks + (stream * a.max_groups + g) * a.block_bytes;
     constexpr int cbytes = BITS * G * D / 8;
     _Float16 *side = (_Float16 *)(blk + 2 * cbytes);   // kscale, kzero, vscale, vzero
@@ -538,24 +600,51 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
     for (int w4 = 0; w4 < DPL / 4; w4++)
         *(uint4 *)&dst[w4 * 256 + 4 * l] =
             (uint4){outw[4 * w4], outw[4 * w4 + 1], outw[4 * w4 + 2], outw[4 * w4 + 3]};
+    };
+
+    if constexpr (IS_V || GT == 1) {
+        store_block(g0);
+    } else {
+        store_block(g0 + GT - 1);
+#pragma unroll 1
+        for (int tt = GT - 2; tt >= 0; tt--) {
+            load_tile<IS_V, RING>(a, stream, g0 + tt, t);
+            __syncthreads();            // the previous block's LDS transpose is read
+            store_block(g0 + tt);
+        }
+    }
 }
 
 // RING: the groups [group_begin, group_end) hold tokens appended earlier
 // (read, at least in part, from the ring); otherwise every row comes from
 // the new chunk.
-// kinds = 3: task 2i is the key group and 2i + 1 the value group of pair i;
-// kinds = 1 / 2: every task is a key / value group.
-template <int BITS, typename T, bool RING>
+// kinds = 3: per key group (GT blocks), task (1 + GT) i is the key group and
+// the next GT tasks are the value blocks of the same tokens; kinds = 1 / 2:
+// every task is a key group / a value block.
+template <int BITS, typename T, bool RING, int GT>
 __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
     __shared__ uint32_t tr[64 * 2 * BITS];
-    const uint32_t ngr = (uint32_t)(a.group_end - a.group_begin);
     const uint32_t task = blockIdx.x;
-    const uint32_t rest = a.kinds == 3 ? task >> 1 : task;
-    const bool is_v = a.kinds == 3 ? (task & 1) != 0 : a.kinds == 2;
-    const int64_t stream = rest / ngr;
-    const int64_t g = a.group_begin + rest % ngr;
-    if (is_v) quantize_task<BITS, true, RING, T>(a, stream, g, tr);
-    else quantize_task<BITS, false, RING, T>(a, stream, g, tr);
+    const uint32_t nb = (uint32_t)(a.block_end - a.block_begin);
+    int64_t stream, g;
+    bool is_v;
+    if (a.kinds == 3) {
+        const uint32_t ngr = nb / GT, rest = task / (1 + GT), sub = task % (1 + GT);
+        stream = rest / ngr;
+        is_v = sub != 0;
+        g = a.block_begin + (int64_t)(rest % ngr) * GT + (is_v ? sub - 1 : 0);
+    } else if (a.kinds == 1) {
+        const uint32_t ngr = nb / GT;
+        stream = task / ngr;
+        is_v = false;
+        g = a.block_begin + (int64_t)(task % ngr) * GT;
+    } else {
+        stream = task / nb;
+        is_v = true;
+        g = a.block_begin + task % nb;
+    }
+    if (is_v) quantize_task<BITS, true, RING, T, GT>(a, stream, g, tr);
+    else quantize_task<BITS, false, RING, T, GT>(a, stream, g, tr);
 }
 // ===========================================================================
 // Residual ring append: copy rows [tok_begin, tok_end) of the chunk into
@@ -1888,40 +1977,59 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
 // ===========================================================================
 // Launchers
 // ===========================================================================
-template <int BITS, typename T>
+template <int BITS, typename T, int GT>
 static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
-    const int per = a.kinds == 3 ? 2 : 1;
-    // Groups that start before n_old read rows from the ring; so does a group
+    // tasks per launched block range: key groups of GT blocks and / or blocks
+    auto tasks_of = [&](int64_t nb) {
+        return a.kinds == 3 ? nb / GT * (1 + GT) : a.kinds == 1 ? nb / GT : nb;
+    };
+    const int64_t align = a.kinds == 2 ? 1 : GT;
+    // Blocks with tokens before n_old read rows from the ring; so does a block
     // whose value rows stop at v_limit (only that instance checks the limit).
-    int64_t ring_groups_end = (a.n_old + G - 1) / G;
-    if (a.kinds != 1 && a.v_limit < a.group_end * G) ring_groups_end = a.group_end;
-    int64_t split = ring_groups_end < a.group_begin ? a.group_begin : ring_groups_end;
-    if (split > a.group_end) split = a.group_end;
-    if (split > a.group_begin) {
+    int64_t ring_end = (a.n_old + G - 1) / G;
+    if (a.kinds != 1 && a.v_limit < a.block_end * G) ring_end = a.block_end;
+    int64_t split = ring_end < a.block_begin ? a.block_begin : ring_end;
+    split = a.block_begin + (split - a.block_begin + align - 1) / align * align;
+    if (split > a.block_end) split = a.block_end;
+    if (split > a.block_begin) {
         QuantizeArgs r = a;
-        r.group_end = split;
-        const int64_t tasks = (int64_t)a.streams * (split - a.group_begin) * per;
-        hipLaunchKernelGGL((quantize_kernel<BITS, T, true>), dim3((unsigned)tasks), dim3(64), 0, s, r);
+        r.block_end = split;
+        const int64_t tasks = (int64_t)a.streams * tasks_of(split - a.block_begin);
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, true, GT>), dim3((unsigned)tasks), dim3(64), 0,
+                           s, r);
     }
-    if (a.group_end > split) {
+    if (a.block_end > split) {
         QuantizeArgs n = a;
-        n.group_begin = split;
-        const int64_t tasks = (int64_t)a.streams * (a.group_end - split) * per;
-        hipLaunchKernelGGL((quantize_kernel<BITS, T, false>), dim3((unsigned)tasks), dim3(64), 0, s, n);
+        n.block_begin = split;
+        const int64_t tasks = (int64_t)a.streams * tasks_of(a.block_end - split);
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, false, GT>), dim3((unsigned)tasks), dim3(64), 0,
+                           s, n);
     }
     return hipGetLastError();
 }
 
+template <int BITS, typename T>
+static hipError_t launch_quantize_g(const QuantizeArgs &a, hipStream_t s) {
+    if (a.gt == 1) return launch_quantize_t<BITS, T, 1>(a, s);
+    if (a.gt == 2) return launch_quantize_t<BITS, T, 2>(a, s);
+    return launch_quantize_t<BITS, T, 4>(a, s);
+}
+
 hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
-    if (a.group_end <= a.group_begin || a.streams <= 0) return hipSuccess;
+    if (a.block_end <= a.block_begin || a.streams <= 0) return hipSuccess;
     if (a.kinds < 1 || a.kinds > 3) return hipErrorInvalidValue;
-    // every value row the kernel reads must exist: rows >= v_limit are skipped
-    if (a.kinds != 1 && a.v_limit < a.group_end * G && a.v_limit <= (a.group_end - 1) * G)
+    if (a.gt != 1 && a.gt != 2 && a.gt != 4) return hipErrorInvalidValue;
+    // key tasks cover whole groups of gt blocks
+    if (a.kinds != 2 && (a.block_begin % a.gt != 0 || a.block_end % a.gt != 0))
         return hipErrorInvalidValue;
-    if ((int64_t)a.streams * (a.group_end - a.group_begin) * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (a.bits == 2) return a.is_f32 ? launch_quantize_t<2, float>(a, s) : launch_quantize_t<2, _Float16>(a, s);
-    if (a.bits == 8) return a.is_f32 ? launch_quantize_t<8, float>(a, s) : launch_quantize_t<8, _Float16>(a, s);
-    return a.is_f32 ? launch_quantize_t<4, float>(a, s) : launch_quantize_t<4, _Float16>(a, s);
+    // every value row the kernel reads must exist: rows >= v_limit are skipped,
+    // and only the last block may stop early
+    if (a.kinds != 1 && a.v_limit < a.block_end * G && a.v_limit <= (a.block_end - 1) * G)
+        return hipErrorInvalidValue;
+    if ((int64_t)a.streams * (a.block_end - a.block_begin) * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (a.bits == 2) return a.is_f32 ? launch_quantize_g<2, float>(a, s) : launch_quantize_g<2, _Float16>(a, s);
+    if (a.bits == 8) return a.is_f32 ? launch_quantize_g<8, float>(a, s) : launch_quantize_g<8, _Float16>(a, s);
+    return a.is_f32 ? launch_quantize_g<4, float>(a, s) : launch_quantize_g<4, _Float16>(a, s);
 }
 
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {

@@ -17,9 +17,9 @@ def torch_dtype(np_dtype):
     return torch.float16 if np_dtype == np.float16 else torch.float32
 
 
-def new_cache(B, H, Hq, max_tokens, bits=2, R=128, dtype=np.float16, policy=0):
+def new_cache(B, H, Hq, max_tokens, bits=2, R=128, dtype=np.float16, policy=0, group=32):
     from kv_cache_quantization_amd import KiviCache
-    return KiviCache(B, H, Hq, max_tokens, bits=bits, residual=R,
+    return KiviCache(B, H, Hq, max_tokens, bits=bits, group=group, residual=R,
                      kv_dtype=torch_dtype(dtype), device="cuda", policy=policy)
 
 
@@ -57,7 +57,7 @@ def check_cache(orc, cache, k, v, streams=None, label=""):
     assert lo.n_tokens == n, (label, lo.n_tokens, n)
     assert (lo.n_quantized, lo.n_vquantized) == (qk, qv), (label, lo.n_quantized,
                                                          lo.n_vquantized, qk, qv)
-    ngk, ngv = qk // G, -(-qv // G)
+    ngk, ngv = qk // 32, -(-qv // 32)           # 32-token blocks
     ng = max(ngk, ngv)
     if ng:
         want = orc.pack_blocks(ref, ng)
@@ -98,6 +98,7 @@ def rel_err(out, ref):
 
 
 def oracle_decode(orc, k, v, q, bits, G, R, sm_scale=None, policy=0):
+    """The oracle's decode attention over the cache built from k, v (group G)."""
     ref = orc.build_cache(k, v, bits, G, R, policy)
     kh, vh = orc.dequant_cache(k, v, ref)
     return orc.decode_attn(q, kh, vh, sm_scale)

@@ -64,7 +64,8 @@ BAD = [
     (dict(policy=2), kivi.KIVI_ERR_INVALID_ARG),
     (dict(policy=1, residual=0), kivi.KIVI_ERR_INVALID_ARG),        # paper policy: r = n mod R
     (dict(head_dim=64), kivi.KIVI_ERR_UNSUPPORTED),
-    (dict(group=64), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(group=16, bits=4), kivi.KIVI_ERR_UNSUPPORTED),          # valid KIVI, G < 32 not built
+    (dict(group=64, residual=96), kivi.KIVI_ERR_INVALID_ARG),      # R not a multiple of G
     (dict(n_q_heads=64, n_kv_heads=8), kivi.KIVI_ERR_UNSUPPORTED),   # GQA 8
     (dict(n_q_heads=24, n_kv_heads=8), kivi.KIVI_ERR_UNSUPPORTED),   # GQA 3
 ]
@@ -140,6 +141,28 @@ def test_sizes_and_layout(L, orc, B, H, Hq, bits, R, T, dt, esize):
         assert kivi.kivi_decode_plan(h) == (0, 1)
         ws = kivi.kivi_decode_workspace_bytes(h)
         assert ws > 0 and ws % (B * Hq * (D + 2) * 4) == 0
+    finally:
+        kivi.kivi_cache_destroy(h)
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_group_sizes_layout(L, orc, G):
+    """G = 64 and 128 keep 32-token blocks (the same block bytes as G = 32:
+    each block carries its key group's zero / scale) and a ring of R + G
+    tokens; the window policy's prefix moves in multiples of G."""
+    D, R, T = 128, 128, 1024
+    cfg = kivi.make_config(2, 8, 32, bits=2, group=G, residual=R, max_tokens=T)
+    h = kivi.kivi_cache_create(cfg, FAKE_DEV, kivi.kivi_cache_bytes(cfg))
+    try:
+        lo = kivi.kivi_get_layout(h)
+        assert lo.block_bytes == orc.block_bytes(2) and lo.code_bytes == 2 * 32 * D // 8
+        assert lo.max_groups == T // 32 and lo.ring_capacity == R + G
+        for n in range(0, T + 1, 7):
+            p = kivi.kivi_plan_append(h, n)
+            qk, qv = orc.quantized_prefix(n, G, R)
+            assert p.q_new == qk == qv and qk % G == 0
+            assert (p.ring_token_begin, p.ring_token_end) == (qk, n)
+            assert n - qk < R + G
     finally:
         kivi.kivi_cache_destroy(h)
 

@@ -27,11 +27,11 @@ def _gpu():
 
 
 def _run(orc, B, H, Hq, n, T, bits, R, causal, seed, chunks=None, q_dtype=np.float16,
-         label=""):
+         label="", G=32):
     from kv_cache_quantization_amd import synth, kivi
     k, v = synth.kv_host(seed, B, H, n)
     q = synth.queries_multi_host(seed, B, Hq, T, dtype=q_dtype)
-    cache = new_cache(B, H, Hq, max_tokens=n + 64, bits=bits, R=R)
+    cache = new_cache(B, H, Hq, max_tokens=n + 64, bits=bits, R=R, group=G)
     pos = 0
     for c in (chunks or [n]):
         cache.append(to_dev(k[:, :, pos:pos + c]), to_dev(v[:, :, pos:pos + c]))
@@ -40,7 +40,7 @@ def _run(orc, B, H, Hq, n, T, bits, R, causal, seed, chunks=None, q_dtype=np.flo
     log("case %s: B=%d H=%d Hq=%d n=%d T=%d bits=%d R=%d causal=%d plan(qblocks, splits, "
         "gps)=%s" % (label, B, H, Hq, n, T, bits, R, causal, plan))
     out = cache.attn(to_dev(q), causal=causal).cpu().numpy()
-    ref_cache = orc.build_cache(k, v, bits, 32, R)
+    ref_cache = orc.build_cache(k, v, bits, G, R)
     kh, vh = orc.dequant_cache(k, v, ref_cache)
     ref = orc.attn_queries(q, kh, vh, causal)
     e = rel_err(out, ref)
@@ -129,3 +129,9 @@ def test_attn_errors():
     with pytest.raises(kivi.KiviError) as e:
         c32.attn(q)
     assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("G,bits,causal", [(64, 2, 1), (128, 4, 0)])
+def test_group_sizes(orc, G, bits, causal):
+    """G = 64 and 128: the 32-token blocks carry their group's zero / scale."""
+    _run(orc, 2, 2, 8, 1111, 100, bits, 128, causal, seed=G + bits, label="attn-G%d" % G, G=G)

@@ -21,13 +21,16 @@ def _gpu():
     kivi.lib()   # fail loudly if the HIP library is missing
 
 
-def _run(orc, B, H, Hq, n, bits, R, dtype, seed, chunks=None, q_dtype=np.float16, label=""):
+def _run(orc, B, H, Hq, n, bits, R, dtype, seed, chunks=None, q_dtype=np.float16, label="",
+         G=32, policy=0):
     from kv_cache_quantization_amd import synth
-    log("case %s: B=%d H=%d Hq=%d n=%d bits=%d R=%d %s chunks=%s" %
-        (label, B, H, Hq, n, bits, R, np.dtype(dtype).name, chunks))
+    log("case %s: B=%d H=%d Hq=%d n=%d bits=%d G=%d R=%d %s policy=%d chunks=%s" %
+        (label, B, H, Hq, n, bits, G, R, np.dtype(dtype).name, policy,
+         chunks if chunks is None or len(chunks) < 12 else "%d chunks" % len(chunks)))
     k, v = synth.kv_host(seed, B, H, n, dtype=dtype)
     q = synth.queries_host(seed, B, Hq, dtype=q_dtype)
-    cache = new_cache(B, H, Hq, max_tokens=max(n, 1) + 64, bits=bits, R=R, dtype=dtype)
+    cache = new_cache(B, H, Hq, max_tokens=max(n, 1) + 64, bits=bits, R=R, dtype=dtype,
+                      group=G, policy=policy)
     pos = 0
     for c in (chunks or [n]):
         cache.append(to_dev(k[:, :, pos:pos + c]), to_dev(v[:, :, pos:pos + c]))
@@ -37,7 +40,7 @@ def _run(orc, B, H, Hq, n, bits, R, dtype, seed, chunks=None, q_dtype=np.float16
     if n == 0:
         return
     out = cache.decode(to_dev(q)).cpu().numpy()
-    ref = oracle_decode(orc, k, v, q, bits, 32, R)
+    ref = oracle_decode(orc, k, v, q, bits, G, R, policy=policy)
     e = rel_err(out, ref)
     log("  decode rel err %.3g" % e)
     assert e <= TOL, (label, e)
@@ -259,3 +262,33 @@ def test_deferred_flush(orc):
         e = rel_err(out, oracle_decode(orc, k, v, synth.queries_host(21, B, Hq), bits, 32, R))
         log("  decode rel err %.3g" % e)
         assert e <= TOL
+
+
+@pytest.mark.parametrize("n,bits,G,R,gq,policy", [
+    (1000, 2, 64, 64, 4, 0),     # G = 64, R = 64: the ablation's other group size
+    (1000, 4, 128, 128, 2, 0),   # G = 128: one value group per token
+    (300, 8, 64, 128, 1, 0),     # 8-bit codes, G = 64
+    (129, 2, 64, 0, 4, 0),       # R = 0: two groups plus one token
+    (1000, 2, 64, 128, 4, 1),    # paper policy with G = 64 (keys flush R = 2G at once)
+])
+def test_group_sizes(orc, n, bits, G, R, gq, policy):
+    """[RV] Table 6's group-size ablation (G = 32, 64, 128): key groups span
+    G tokens and value groups G channels; 32-token blocks carry their group's
+    zero / scale."""
+    _run(orc, 2, 3, 3 * gq, n, bits, R, np.float16, seed=n + G, label="G%d-%d" % (G, n),
+         G=G, policy=policy)
+
+
+def test_group_sizes_streaming_and_fp32(orc):
+    """G = 64 streamed in uneven chunks equals the one-shot cache; G = 128 with
+    float32 rows and queries."""
+    rng = np.random.default_rng(5)
+    n = 700
+    chunks = [200] + [1] * 70 + [int(x) for x in rng.integers(1, 50, 8)]
+    chunks.append(n - sum(chunks))
+    assert chunks[-1] > 0
+    for policy in (0, 1):
+        _run(orc, 2, 2, 8, n, 2, 128, np.float16, seed=77, chunks=chunks,
+             label="G64-stream-%d" % policy, G=64, policy=policy)
+    _run(orc, 1, 2, 8, 600, 4, 128, np.float32, seed=78, q_dtype=np.float32, label="G128-fp32",
+         G=128)
