@@ -58,7 +58,7 @@ typedef enum { KIVI_F16 = 0, KIVI_F32 = 1 } kivi_dtype;
    up to Q_V(n) = max(0, n - R) ("[Paper review] KIVI ...", 3.2.2 and the
    prefill / decoding phases of Algorithm 1 in 3.2.3: the key residual is
    quantized R tokens at once when it fills up, the oldest value of the
-   residual one token per step).  In the group holding Q_V the value codes
+   residual one token per step).  In the 32-token block holding Q_V the value codes
    and side data of tokens >= Q_V are 0.  kivi_attn supports only the window
    policy. */
 typedef enum { KIVI_FLUSH_WINDOW = 0, KIVI_FLUSH_PAPER = 1 } kivi_flush_policy;
@@ -79,7 +79,8 @@ typedef struct {
     int32_t n_q_heads;    /* Hq: a multiple of H; Hq / H in {1, 2, 4}         */
     int32_t head_dim;     /* D: 128                                           */
     int32_t bits;         /* b: 2, 4 or 8                                     */
-    int32_t group;        /* G: 32                                            */
+    int32_t group;        /* G: 32, 64 or 128 (key groups of G tokens, value  */
+                          /* groups of G channels)                            */
     int32_t residual;     /* R >= 0, a multiple of G                          */
     int32_t kv_dtype;     /* kivi_dtype of the K/V rows handed to append      */
     int32_t policy;       /* kivi_flush_policy                                */
@@ -91,9 +92,12 @@ typedef struct kivi_cache kivi_cache;   /* opaque host-side handle */
 
 /* Where everything sits inside the caller's device buffer (byte offsets from
    its start).  Packed blocks: [B*H][max_groups][block_bytes], block j of a
-   stream holding tokens [jG, jG+G).  Inside a block (offsets below are from
-   the block start): K codes, V codes (code_bytes = b*G*D/8 each), then fp16
-   K scale[D], K zero[D], V scale[D/G][G], V zero[D/G][G].  The bit order of
+   stream holding tokens [32j, 32j+32) whatever G is.  Inside a block
+   (offsets below are from the block start): K codes, V codes (code_bytes =
+   b*32*D/8 each), then fp16 K scale[D], K zero[D] of the key group the
+   block lies in (repeated in each of a group's G/32 blocks), V scale[4][32],
+   V zero[4][32]: slot cg of token t holds the parameters of the value group
+   containing channels 32cg .. 32cg+31 (repeated when G > 32).  The bit order of
    the codes is described in the kernel source (it follows the matrix-core
    operand layout).  Ring: [B*H][ring_capacity][D] in kv_dtype for K and for
    V; token t of a stream lives in slot t mod ring_capacity while it is in
