@@ -153,11 +153,11 @@ def attn_measure(cache, B, Hq, n, T, stream, evict, evict_out, do_evict):
 
 
 def streaming_measure(policy, do_evict, evict, evict_out, steps=512, prefill=8192, B=8, R=128,
-                      bits=2):
+                      bits=2, fused=False):
     """The streaming workload: batch 8, 8 KV / 32 query heads, a one-shot
     prefill of 8192 tokens, then `steps` decode steps that each append one
     token (K, V ~ N(0, 1) fp16, outlier key channels) and run decode
-    attention with a fresh query.
+    attention with a fresh query (fused: both in one kivi_append_decode call).
 
     warm: the steps' per-step working set (about 55 MB) stays in the 256 MB
     Infinity Cache, as in a real serving loop.  All steps are captured once
@@ -199,12 +199,19 @@ def streaming_measure(policy, do_evict, evict, evict_out, steps=512, prefill=819
         qk, qv = nqk, nqv
         total += B * H * 2 * D * 2 * 2 + quant + decode_bytes_kv(B, H, Hq, n, qk, qv, bits)
     res = {"policy": "window" if policy == kivi.KIVI_FLUSH_WINDOW else "paper",
+           "calls": "kivi_append_decode" if fused else "kivi_append + kivi_decode_attn",
            "steps": steps, "bytes": int(total), "key_flushes": int(flushes)}
+
+    def one_step(s):
+        if fused:
+            cache.append_decode(*rows[s], qs[s], out=outs[s])
+        else:
+            cache.append(*rows[s])
+            cache.decode(qs[s], out=outs[s])
 
     def run_steps():
         for s in range(steps):
-            cache.append(*rows[s])
-            cache.decode(qs[s], out=outs[s])
+            one_step(s)
 
     # warm: capture all steps once, replay from the restored post-prefill cache
     g = torch.cuda.CUDAGraph()
@@ -238,8 +245,7 @@ def streaming_measure(policy, do_evict, evict, evict_out, steps=512, prefill=819
             torch.amax(evict, dim=0, out=evict_out)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            cache.append(*rows[s])
-            cache.decode(qs[s], out=outs[s])
+            one_step(s)
             e1.record(stream)
             per.append((e0, e1))
         torch.cuda.synchronize()
@@ -421,8 +427,10 @@ def main():
                         "residual 128: prefill 8192 tokens, then %d steps of (append one token, "
                         "decode attention)" % args.stream_steps,
             "policies": [streaming_measure(pol, not args.no_evict, evict, evict_out,
-                                           steps=args.stream_steps)
-                         for pol in (kivi.KIVI_FLUSH_WINDOW, kivi.KIVI_FLUSH_PAPER)],
+                                           steps=args.stream_steps, fused=fu)
+                         for pol, fu in ((kivi.KIVI_FLUSH_WINDOW, False),
+                                         (kivi.KIVI_FLUSH_WINDOW, True),
+                                         (kivi.KIVI_FLUSH_PAPER, False))],
         }
     if args.cpu_sample > 0:
         k0, v0 = chunks[0]

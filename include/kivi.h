@@ -189,6 +189,25 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype,
                              float softmax_scale, float *out, void *workspace,
                              size_t ws_bytes, hipStream_t stream);
 
+/* kivi_append(c, k, v, n_new, 0, stream) followed by kivi_decode_attn(c, q,
+   q_dtype, softmax_scale, out, workspace, ws_bytes, stream), with the same
+   results bit for bit, for a serving loop's decode step ("[Paper review]
+   KIVI ...", 1.3: append the new K/V, then attend).  When the append
+   quantizes nothing (window policy, no group ages out: 31 of 32 single-token
+   steps at G = 32), the new rows are not copied into the ring by a kernel
+   of their own: the decode's residual items read them from k / v and write
+   them into the ring, so k / v must stay valid until the decode finishes.
+   Otherwise the call enqueues exactly what the two calls would.  Arguments
+   as for the two calls (n_new >= 0; k, v may be NULL when n_new == 0).
+   Everything is validated before anything is enqueued.  Errors: those of
+   kivi_append (KIVI_DEFER_FLUSH is not accepted here) and of
+   kivi_decode_attn; STATE also when a deferred flush is pending before the
+   call. */
+kivi_status kivi_append_decode(kivi_cache *c, const void *k, const void *v, int64_t n_new,
+                               const void *q, int32_t q_dtype, float softmax_scale,
+                               float *out, void *workspace, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* Attention of T queries per (batch, query head) over all n cached tokens
    (the dequantized groups followed by the full-precision residual):
    out[b][hq][t][:] = softmax(scale * q[b][hq][t] . K_hat^T + mask) V_hat, the

@@ -117,6 +117,34 @@ class KiviCache:
                             ws.data_ptr(), ws.numel(), _stream_handle(self.device))
         return out
 
+    def append_decode(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
+                      softmax_scale: float = 0.0, out: torch.Tensor | None = None) -> torch.Tensor:
+        """append(k, v) then decode(q) in one call (kivi_append_decode): when
+        nothing ages out of the residual the new rows reach the ring through
+        the decode launch itself."""
+        c = self.cfg
+        shape = (c.batch, c.n_kv_heads, k.shape[2], c.head_dim)
+        for t in (k, v):
+            if tuple(t.shape) != shape or t.dtype != self.kv_dtype or not t.is_contiguous() \
+                    or t.device != self.device:
+                raise ValueError("append_decode expects contiguous %s %s on %s" %
+                                 (self.kv_dtype, shape, self.device))
+        if tuple(q.shape) != (c.batch, c.n_q_heads, c.head_dim) or not q.is_contiguous() \
+                or q.dtype not in (torch.float16, torch.float32) or q.device != self.device:
+            raise ValueError("append_decode expects contiguous fp16/fp32 q of shape %s" %
+                             ((c.batch, c.n_q_heads, c.head_dim),))
+        if out is None:
+            out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32,
+                              device=self.device)
+        ws = self.workspace()
+        n_new = k.shape[2]
+        qd = _k.KIVI_F16 if q.dtype == torch.float16 else _k.KIVI_F32
+        _k.kivi_append_decode(self.handle, k.data_ptr() if n_new else None,
+                              v.data_ptr() if n_new else None, n_new, q.data_ptr(), qd,
+                              float(softmax_scale), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream_handle(self.device))
+        return out
+
     def attn(self, q: torch.Tensor, causal: bool = False, softmax_scale: float = 0.0,
              out: torch.Tensor | None = None) -> torch.Tensor:
         """T queries per head over every cached token; q: [B, Hq, T, D].

@@ -422,12 +422,25 @@ kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits, int32_t *gps)
     return KIVI_OK;
 }
 
-kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, float softmax_scale,
-                             float *out, void *workspace, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+kivi_status check_decode_args(const kivi_cache *c, const void *q, int32_t q_dtype,
+                              const float *out, const void *workspace, size_t ws_bytes) {
     if (!c || !q || !out || !workspace) return KIVI_ERR_INVALID_ARG;
     if (q_dtype != KIVI_F16 && q_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
-    if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
     if (ws_bytes < kivi_decode_workspace_bytes(c)) return KIVI_ERR_BUFFER_TOO_SMALL;
+    return KIVI_OK;
+}
+
+// The decode launches over the cache's current (canonical) state.  Tokens
+// t >= in_from (in_from = n - in_n) were appended by the same call and are
+// still only in in_k / in_v: the residual items read them there and copy
+// them into the ring.
+kivi_status enqueue_decode(kivi_cache *c, const void *q, int32_t q_dtype, float softmax_scale,
+                           float *out, void *workspace, hipStream_t stream, const void *in_k,
+                           const void *in_v, int64_t in_n, int64_t in_from) {
     DecodeArgs a;
     // groups [0, nq / G): key and value codes (split items); [nq, q): key
     // codes, value codes below qv (paper policy only); [q, n): the residual
@@ -470,8 +483,52 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, floa
     a.items = (int32_t)items;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)c->cfg.head_dim);
     a.sm_log2 = scale * 1.4426950408889634f;
+    a.in_k = in_k;
+    a.in_v = in_v;
+    a.in_n = in_n;
+    a.in_from = in_from;
     if (launch_decode(a, stream) != hipSuccess) return KIVI_ERR_HIP;
     return KIVI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype, float softmax_scale,
+                             float *out, void *workspace, size_t ws_bytes, hipStream_t stream) {
+    kivi_status st = check_decode_args(c, q, q_dtype, out, workspace, ws_bytes);
+    if (st != KIVI_OK) return st;
+    if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
+    return enqueue_decode(c, q, q_dtype, softmax_scale, out, workspace, stream, nullptr, nullptr,
+                          0, INT64_MAX);
+}
+
+kivi_status kivi_append_decode(kivi_cache *c, const void *k, const void *v, int64_t n_new,
+                               const void *q, int32_t q_dtype, float softmax_scale, float *out,
+                               void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!c || n_new < 0 || (n_new > 0 && (!k || !v))) return KIVI_ERR_INVALID_ARG;
+    kivi_status st = check_decode_args(c, q, q_dtype, out, workspace, ws_bytes);
+    if (st != KIVI_OK) return st;
+    if (!canonical(c)) return KIVI_ERR_STATE;
+    kivi_append_plan p;
+    st = kivi_plan_append(c, n_new, &p);
+    if (st != KIVI_OK) return st;
+    if (p.n_new_total == 0) return KIVI_ERR_STATE;
+    const bool quantizes = p.flush_token_end > p.flush_token_begin ||
+                           p.v_flush_token_end > p.v_flush_token_begin;
+    if (n_new == 0 || quantizes || c->cfg.policy != KIVI_FLUSH_WINDOW) {
+        // the append's own launches, then the decode over the ring
+        st = kivi_append(c, k, v, n_new, 0, stream);
+        if (st != KIVI_OK) return st;
+        return enqueue_decode(c, q, q_dtype, softmax_scale, out, workspace, stream, nullptr,
+                              nullptr, 0, INT64_MAX);
+    }
+    // nothing ages out: every new row lands in the residual, and the decode's
+    // residual items take it from k / v and write it into the ring
+    c->n = p.n_new_total;
+    return enqueue_decode(c, q, q_dtype, softmax_scale, out, workspace, stream, k, v, n_new,
+                          p.n_old);
 }
 
 size_t kivi_attn_workspace_bytes(const kivi_cache *c, int64_t T) {

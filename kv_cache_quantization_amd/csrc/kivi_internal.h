@@ -73,6 +73,12 @@ struct DecodeArgs {
     int32_t tail_chunk_step;    //   consecutive chunks)
     int32_t items;              // partials per (batch, query head): splits, residual, mixed
     float sm_log2;              // softmax scale * log2(e)
+    // Rows appended by the same call (append + decode in one launch): tokens
+    // t >= in_from are read from in_k / in_v ([streams][in_n][D], kv dtype)
+    // instead of the ring, and the residual items also write them into the
+    // ring.  in_from = INT64_MAX when every residual row is in the ring.
+    const void *in_k, *in_v;
+    int64_t in_n, in_from;
 };
 
 // Attention of T queries per (batch, query head) over the cache.  One

@@ -986,17 +986,46 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, int ti, uint8_t
             return s2 >= cap ? s2 - cap : s2;
         };
         lds_sync_wave();   // the previous chunk's LDS reads are done
+        const int cslot0 = slot0;
+        // rows of tokens appended by this call come from the caller's buffer
+        const int64_t tok0 = a.n_tail + (int64_t)G * chunk;
+        const bool has_new = tok0 + cnt > a.in_from;                   // uniform
+        auto new_row = [&](const void *base, int r) {
+            const int rr = r < cnt ? r : cnt - 1;
+            return (const char *)base + ((int64_t)stream * a.in_n + (tok0 + rr - a.in_from)) * D * 2;
+        };
         // V rows -> LDS [32][D] fp16: copy i covers rows 4i .. 4i+3
 #pragma unroll
-        for (int i = 0; i < G / 4; i++)
-            dma_1k((const uint8_t *)rvb + (uint32_t)(slot(4 * i + Gl) * D * 2 + 16 * j),
-                   __builtin_amdgcn_readfirstlane(vbase + 1024u * i));
+        for (int i = 0; i < G / 4; i++) {
+            const int r = 4 * i + Gl;
+            const uint8_t *src = (const uint8_t *)rvb + (uint32_t)(slot(r) * D * 2 + 16 * j);
+            if (has_new && tok0 + (r < cnt ? r : cnt - 1) >= a.in_from)
+                src = (const uint8_t *)new_row(a.in_v, r) + 16 * j;
+            dma_1k(src, __builtin_amdgcn_readfirstlane(vbase + 1024u * i));
+        }
         uint4 kr[2][4];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            const uint32_t off = (uint32_t)(slot(16 * t + j) * D + 8 * Gl) * 2u;
+            const int r = 16 * t + j;
+            const uint32_t off = (uint32_t)(slot(r) * D + 8 * Gl) * 2u;
+            const char *kp = rkb + off;
+            if (has_new && tok0 + (r < cnt ? r : cnt - 1) >= a.in_from)
+                kp = new_row(a.in_k, r) + 16 * Gl;
 #pragma unroll
-            for (int s2 = 0; s2 < 4; s2++) kr[t][s2] = *(const uint4 *)(rkb + off + 64u * s2);
+            for (int s2 = 0; s2 < 4; s2++) kr[t][s2] = *(const uint4 *)(kp + 64u * s2);
+        }
+        if (has_new) {
+            // the appended rows' keys into the ring (lanes of rows >= in_from)
+            char *rkw = (char *)rkb;
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int r = 16 * t + j;
+                if (r < cnt && tok0 + r >= a.in_from) {
+                    char *dst = rkw + (uint32_t)(slot(r) * D + 8 * Gl) * 2u;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; s2++) *(uint4 *)(dst + 64u * s2) = kr[t][s2];
+                }
+            }
         }
         slot0 = slot0 + G >= cap ? slot0 + G - cap : slot0 + G;
         f4 S[2];
@@ -1030,6 +1059,18 @@ __device__ void decode_tail_f16(const DecodeArgs &a, int stream, int ti, uint8_t
         ls = xsum_rows(ls);
         wait_vm<0>();      // V copies landed
         lds_sync_wave();
+        if (has_new) {
+            // the appended rows' values into the ring, from LDS: 16 lanes per
+            // row (slot0 already points at the next chunk: this chunk's slots
+            // start at cslot0)
+            const int r_first = a.in_from > tok0 ? (int)(a.in_from - tok0) : 0;
+            char *rvw = (char *)rvb;
+            for (int r = r_first + Gl; r < cnt; r += 4) {
+                const int sr = cslot0 + r >= cap ? cslot0 + r - cap : cslot0 + r;
+                *(uint4 *)(rvw + (uint32_t)(sr * D * 2 + 16 * j)) =
+                    *(const uint4 *)(lds + r * D * 2 + 16 * j);
+            }
+        }
         // the lane's two channels of every row, then one accumulation chain per head
         const h2 *vl = (const h2 *)lds;
         h2 vr[G];
@@ -1098,7 +1139,18 @@ __device__ void decode_tail_f32(const DecodeArgs &a, int stream, int ti) {
     for (int64_t t = t_begin; t < t_end; t++) {
         const int64_t row = (int64_t)slot * D + 2 * l;
         slot = slot + 1 == cap ? 0 : slot + 1;
-        const float k0 = rk[row], k1 = rk[row + 1], v0 = rv[row], v1 = rv[row + 1];
+        float k0, k1, v0, v1;
+        if (t >= a.in_from) {
+            // a row appended by this call: from the caller's buffer, and into the ring
+            const int64_t src = ((int64_t)stream * a.in_n + (t - a.in_from)) * D + 2 * l;
+            const float2 kk = *(const float2 *)((const float *)a.in_k + src);
+            const float2 vv = *(const float2 *)((const float *)a.in_v + src);
+            *(float2 *)((float *)rk + row) = kk;
+            *(float2 *)((float *)rv + row) = vv;
+            k0 = kk.x; k1 = kk.y; v0 = vv.x; v1 = vv.y;
+        } else {
+            k0 = rk[row]; k1 = rk[row + 1]; v0 = rv[row]; v1 = rv[row + 1];
+        }
 #pragma unroll
         for (int h = 0; h < GQ; h++) {
             float s = wave_sum(__builtin_fmaf(q0[h], k0, q1[h] * k1)) * a.sm_log2;

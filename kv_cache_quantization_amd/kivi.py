@@ -31,7 +31,8 @@ KIVI_DEFER_FLUSH = 1
 EXPORTED = (
     "kivi_cache_bytes", "kivi_cache_create", "kivi_cache_destroy", "kivi_append",
     "kivi_flush", "kivi_plan_append", "kivi_decode_workspace_bytes",
-    "kivi_decode_plan", "kivi_decode_attn", "kivi_attn", "kivi_attn_workspace_bytes",
+    "kivi_decode_plan", "kivi_decode_attn", "kivi_append_decode", "kivi_attn",
+    "kivi_attn_workspace_bytes",
     "kivi_attn_plan", "kivi_get_layout", "kivi_status_string",
 )
 
@@ -100,6 +101,8 @@ def lib():
         L.kivi_decode_plan.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kivi_decode_attn.restype = i32
         L.kivi_decode_attn.argtypes = [P, P, i32, ctypes.c_float, P, P, sz, P]
+        L.kivi_append_decode.restype = i32
+        L.kivi_append_decode.argtypes = [P, P, P, i64, P, i32, ctypes.c_float, P, P, sz, P]
         L.kivi_attn.restype = i32
         L.kivi_attn.argtypes = [P, P, i32, i64, i32, ctypes.c_float, P, P, sz, P]
         L.kivi_attn_workspace_bytes.restype = sz
@@ -170,6 +173,13 @@ def kivi_decode_attn(handle: int, q: int, q_dtype: int, softmax_scale: float, ou
                      workspace: int, ws_bytes: int, stream: int) -> None:
     _check(lib().kivi_decode_attn(handle, q, q_dtype, softmax_scale, out, workspace,
                                   ws_bytes, stream), "kivi_decode_attn")
+
+
+def kivi_append_decode(handle: int, k: int, v: int, n_new: int, q: int, q_dtype: int,
+                       softmax_scale: float, out: int, workspace: int, ws_bytes: int,
+                       stream: int) -> None:
+    _check(lib().kivi_append_decode(handle, k, v, n_new, q, q_dtype, softmax_scale, out,
+                                    workspace, ws_bytes, stream), "kivi_append_decode")
 
 
 def kivi_attn(handle: int, q: int, q_dtype: int, T: int, causal: int, softmax_scale: float,

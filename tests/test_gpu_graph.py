@@ -1,10 +1,10 @@
 """Decode steps captured in a HIP graph (as the streaming benchmark replays
 them) give the eager results: single-token appends followed by decode
-attention are captured once, then the graph is replayed several times from a
-restored post-prefill cache, with the program's own eager work and
-synchronizations between the replays.  Every replay's decode outputs must
-equal the eager run's bit for bit, and its final cache must match the oracle
-bit for bit, under both flush policies."""
+attention (two calls, or one kivi_append_decode) are captured once, then the
+graph is replayed several times from a restored post-prefill cache, with the
+program's own eager work and synchronizations between the replays.  Every
+replay's decode outputs must equal the eager run's bit for bit, and its final
+cache must match the oracle bit for bit, under both flush policies."""
 import numpy as np
 import pytest
 
@@ -22,12 +22,12 @@ def _gpu():
     kivi.lib()
 
 
-@pytest.mark.parametrize("policy", [0, 1])
-def test_graph_replays_equal_eager(orc, policy):
+@pytest.mark.parametrize("policy,fused", [(0, False), (1, False), (0, True)])
+def test_graph_replays_equal_eager(orc, policy, fused):
     import torch
     from kv_cache_quantization_amd import synth
     B, H, Hq, R, bits, P, S = 2, 2, 8, 64, 2, 300, 70
-    log("case graph policy=%d prefill=%d steps=%d" % (policy, P, S))
+    log("case graph policy=%d fused=%d prefill=%d steps=%d" % (policy, fused, P, S))
     k, v = synth.kv_host(71, B, H, P + S)
     kd, vd = to_dev(k), to_dev(v)
     rows = [(kd[:, :, P + s:P + s + 1].contiguous(), vd[:, :, P + s:P + s + 1].contiguous())
@@ -44,8 +44,11 @@ def test_graph_replays_equal_eager(orc, policy):
 
     def run_steps():
         for s in range(S):
-            cache.append(*rows[s])
-            cache.decode(qs[s], out=outs[s])
+            if fused:
+                cache.append_decode(*rows[s], qs[s], out=outs[s])
+            else:
+                cache.append(*rows[s])
+                cache.decode(qs[s], out=outs[s])
 
     prefill()
     run_steps()
