@@ -66,6 +66,10 @@ def lib():
         L.oracle_pack_blocks.argtypes = [i32, i32, i64, i32, i64, P, P, P, P, P, P, P]
         L.oracle_pack_blocks_kv.argtypes = [i32, i32, i32, i64, i64, i32, i64, P, P, P, P, P, P, P]
         L.oracle_code_position.argtypes = [i32, i32, i32, i32, P, P]
+        L.oracle_key_outliers.argtypes = [P, i32, i32, i32, i64, i32, i32, i64, i32,
+                                          P, P, P, P, P]
+        L.oracle_apply_key_outliers.argtypes = [i32, i32, i64, i32, i32, i64, i32, P, P, P]
+        L.oracle_pack_outlier_records.argtypes = [i32, i32, i64, i32, i64, P, P, P]
         L.oracle_fake_quant_2d.argtypes = [P, i32, i32, i32, i32, i32, i32, P]
         L.oracle_f16_to_f32_array.argtypes = [P, P, i64]
         L.oracle_f32_to_f16_array.argtypes = [P, P, i64]
@@ -134,8 +138,11 @@ def quantized_prefix(n: int, group: int, residual: int, policy: int = POLICY_WIN
 # whole-cache views
 # --------------------------------------------------------------------------
 def build_cache(k, v, bits: int, group: int, residual: int,
-                policy: int = POLICY_WINDOW) -> dict:
-    """Logical KIVI cache of K, V ([B, H, n, D], float16 or float32)."""
+                policy: int = POLICY_WINDOW, key_outliers: int = 0) -> dict:
+    """Logical KIVI cache of K, V ([B, H, n, D], float16 or float32).
+    key_outliers > 0: per key group, that many channels kept in fp16
+    (oracle_key_outliers): kout_idx [B, H, qk/G, n], kout_val fp16 bits
+    [B, H, qk/G, n, G]."""
     kk, dt = _kv(k)
     vv, dt2 = _kv(v)
     assert dt == dt2 and kk.shape == vv.shape
@@ -154,6 +161,13 @@ def build_cache(k, v, bits: int, group: int, residual: int,
     lib().oracle_build_cache(_p(kk), _p(vv), dt, B, H, n, D, group, bits, qk, qv,
                              _p(c["kcodes"]), _p(c["kzero16"]), _p(c["kscale16"]),
                              _p(c["vcodes"]), _p(c["vzero16"]), _p(c["vscale16"]))
+    c["key_outliers"] = key_outliers
+    if key_outliers > 0:
+        c["kout_idx"] = np.zeros((B, H, qk // group, key_outliers), np.int32)
+        c["kout_val"] = np.zeros((B, H, qk // group, key_outliers, group), np.uint16)
+        lib().oracle_key_outliers(_p(kk), dt, B, H, n, D, group, qk, key_outliers,
+                                  _p(c["kcodes"]), _p(c["kzero16"]), _p(c["kscale16"]),
+                                  _p(c["kout_idx"]), _p(c["kout_val"]))
     # the full-precision residual, verbatim in the input dtype
     c["k_resid"] = np.ascontiguousarray(np.asarray(k)[:, :, qk:, :])
     c["v_resid"] = np.ascontiguousarray(np.asarray(v)[:, :, qv:, :])
@@ -172,6 +186,9 @@ def dequant_cache(k, v, cache: dict):
         _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
         _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
         _p(khat), _p(vhat))
+    if cache.get("key_outliers", 0) > 0:
+        lib().oracle_apply_key_outliers(B, H, n, D, cache["G"], cache["qk"], cache["key_outliers"],
+                                        _p(cache["kout_idx"]), _p(cache["kout_val"]), _p(khat))
     return khat, vhat
 
 
@@ -233,6 +250,19 @@ def pack_blocks(cache: dict, max_groups: int | None = None) -> np.ndarray:
                                 _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
                                 _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
                                 _p(out))
+    return out
+
+
+def pack_outlier_records(cache: dict, max_groups: int | None = None) -> np.ndarray:
+    """Outlier records [B*H, max_groups, 256] (u8) of a cache built with
+    key_outliers > 0 at G = 32 (see oracle_pack_outlier_records)."""
+    assert cache["G"] == 32 and cache["key_outliers"] > 0
+    B, H, qk = cache["B"], cache["H"], cache["qk"]
+    if max_groups is None:
+        max_groups = qk // 32
+    out = np.zeros((B * H, max_groups, 256), np.uint8)
+    lib().oracle_pack_outlier_records(B, H, qk, cache["key_outliers"], max_groups,
+                                      _p(cache["kout_idx"]), _p(cache["kout_val"]), _p(out))
     return out
 
 

@@ -230,6 +230,81 @@ void oracle_build_cache(const void *k, const void *v, int dtype,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Outlier-aware keys ([NB] "Exercises" item 2: keep the top 1% of K         */
+/* channels at fp16 and quantize the rest).  Reading taken here: within each */
+/* key group (G tokens of a stream), the n_out channels with the largest     */
+/* max |K| over the group's tokens (ties: the lower channel index) keep      */
+/* their values, rounded to fp16; their codes, zero and scale are stored as  */
+/* 0, so that code * scale + zero contributes nothing.  Selection per group  */
+/* keeps the cache independent of how the tokens were chunked.  Applied to   */
+/* the arrays oracle_build_cache wrote for the same inputs and qk.           */
+/*   kout_idx [B*H][qk/G][n_out]  int32, ascending channel indices           */
+/*   kout_val [B*H][qk/G][n_out][G] fp16 bits                                */
+/* ------------------------------------------------------------------------ */
+void oracle_key_outliers(const void *k, int dtype, int B, int H, int64_t n, int D, int G,
+                         int64_t qk, int n_out, uint8_t *kcodes, uint16_t *kzero16,
+                         uint16_t *kscale16, int32_t *kout_idx, uint16_t *kout_val)
+{
+    float *score = (float *)malloc(sizeof(float) * (size_t)D);
+    int *chosen = (int *)malloc(sizeof(int) * (size_t)D);
+    for (int64_t s = 0; s < (int64_t)B * H; s++) {
+        int64_t base = s * n * D;
+        for (int64_t j = 0; j < qk / G; j++) {
+            /* max |K| of every channel over the group's tokens */
+            for (int c = 0; c < D; c++) {
+                float m = 0.0f;
+                for (int i = 0; i < G; i++) {
+                    float a = fabsf(load_elem(k, dtype, base + (j * G + i) * D + c));
+                    if (a > m) m = a;
+                }
+                score[c] = m;
+                chosen[c] = 0;
+            }
+            /* the n_out largest, one at a time (strictly larger wins: ties
+               keep the lower channel index) */
+            for (int o = 0; o < n_out; o++) {
+                int best = -1;
+                for (int c = 0; c < D; c++)
+                    if (!chosen[c] && (best < 0 || score[c] > score[best])) best = c;
+                chosen[best] = 1;
+            }
+            int o = 0;
+            for (int c = 0; c < D; c++) {
+                if (!chosen[c]) continue;
+                int64_t g = s * (qk / G) + j;
+                kout_idx[g * n_out + o] = c;
+                for (int i = 0; i < G; i++) {
+                    float x = load_elem(k, dtype, base + (j * G + i) * D + c);
+                    kout_val[(g * n_out + o) * G + i] = oracle_f32_to_f16(x);
+                    kcodes[(s * qk + j * G + i) * D + c] = 0;
+                }
+                kzero16[g * D + c] = 0;
+                kscale16[g * D + c] = 0;
+                o++;
+            }
+        }
+    }
+    free(score);
+    free(chosen);
+}
+
+/* K-hat of the outlier channels: their stored fp16 values (the other
+   channels keep what oracle_dequant_cache wrote).  khat [B][H][n][D]. */
+void oracle_apply_key_outliers(int B, int H, int64_t n, int D, int G, int64_t qk, int n_out,
+                               const int32_t *kout_idx, const uint16_t *kout_val, float *khat)
+{
+    for (int64_t s = 0; s < (int64_t)B * H; s++)
+        for (int64_t j = 0; j < qk / G; j++)
+            for (int o = 0; o < n_out; o++) {
+                int64_t g = s * (qk / G) + j;
+                int c = kout_idx[g * n_out + o];
+                for (int i = 0; i < G; i++)
+                    khat[(s * n + j * G + i) * D + c] =
+                        oracle_f16_to_f32(kout_val[(g * n_out + o) * G + i]);
+            }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantized view of the whole cache ([RV] 1.1 X' = Q(X) s + z; tokens in  */
 /* the full-precision residual are taken as they are, converted to float).   */
 /* khat, vhat: [B][H][n][D] float32.                                         */
@@ -499,6 +574,30 @@ void oracle_pack_blocks(int B, int H, int64_t nq, int bits, int64_t max_groups,
 {
     oracle_pack_blocks_kv(B, H, 32, nq, nq, bits, max_groups, kcodes, kzero16, kscale16,
                           vcodes, vzero16, vscale16, out);
+}
+
+/* Outlier records of the packed cache, one per 32-token key group (G = 32):
+   256 bytes = uint16 channel[3] (ascending; 0xFFFF when unused), 10 bytes of
+   zeros, then fp16 values [3][32] at byte 16 + 64 o (0 when unused).  out
+   [B*H][max_groups][256]; groups past nk / 32 are left as they are. */
+void oracle_pack_outlier_records(int B, int H, int64_t nk, int n_out, int64_t max_groups,
+                                 const int32_t *kout_idx, const uint16_t *kout_val,
+                                 uint8_t *out)
+{
+    const int T = 32;
+    for (int64_t s = 0; s < (int64_t)B * H; s++)
+        for (int64_t j = 0; j < nk / T; j++) {
+            uint8_t *rec = out + (s * max_groups + j) * 256;
+            uint16_t *idx = (uint16_t *)rec;
+            uint16_t *val = (uint16_t *)(rec + 16);
+            memset(rec, 0, 256);
+            for (int o = 0; o < 3; o++) idx[o] = 0xFFFF;
+            for (int o = 0; o < n_out; o++) {
+                int64_t g = s * (nk / T) + j;
+                idx[o] = (uint16_t)kout_idx[g * n_out + o];
+                for (int i = 0; i < T; i++) val[o * T + i] = kout_val[(g * n_out + o) * T + i];
+            }
+        }
 }
 
 /* Position of one code in the packed area (exported for the layout tests). */
