@@ -268,6 +268,8 @@ def main():
     ap.add_argument("--context", type=int, default=32768)
     ap.add_argument("--residual", type=int, default=128)
     ap.add_argument("--group", type=int, default=32, choices=(32, 64, 128))
+    ap.add_argument("--key-outliers", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="key channels kept in fp16 per 32-token key group (outlier-aware keys)")
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk (0: one shot)")
     ap.add_argument("--cpu-sample", type=int, default=2, help="batch entries timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-evict", action="store_true")
@@ -301,7 +303,8 @@ def main():
         chunks.append(synth.kv_device(3, B, H, cn, D, chunk=ci // chunk, device=dev))
     q = synth.queries_device(3, B, Hq, D, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    cache = KiviCache(B, H, Hq, n, bits=bits, group=G, residual=R, device=dev)
+    n_out = args.key_outliers
+    cache = KiviCache(B, H, Hq, n, bits=bits, group=G, residual=R, device=dev, key_outliers=n_out)
     cache.workspace()
     evict = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
     evict_out = torch.empty((), dtype=torch.float32, device=dev)
@@ -356,12 +359,19 @@ def main():
     Q = lo.n_quantized
     dbytes = decode_bytes(B, H, Hq, n, Q, bits, G=G)
     abytes = append_bytes(B, H, n, Q, bits, G=G)
+    if n_out:
+        # the kept channels' fp16 values (2 bytes per token and channel) and
+        # their indices (2 bytes per channel and group), read by the decode
+        # and written by the append
+        extra = B * H * (Q // 32) * n_out * (32 * 2 + 2)
+        dbytes += extra
+        abytes += extra
     dec_gbps = dbytes / t_dec / 1e9
     app_gbps = abytes / t_app / 1e9
     splits, gps = cache.decode_plan()
     traffic, traffic_src = (None, "workload without a counter summary")
     atraffic = None
-    if (B, n, R, bits, chunk, G) == (16, 32768, 128, 2, 32768, 32):
+    if (B, n, R, bits, chunk, G, n_out) == (16, 32768, 128, 2, 32768, 32, 0):
         traffic, traffic_src = counter_traffic("decode_b16_ctx32768_2bit_counters.txt")
         atraffic, _ = counter_traffic("decode_b16_ctx32768_2bit_counters.txt",
                                       "append_traffic_bytes_per_launch")
@@ -382,8 +392,9 @@ def main():
                 "q ~ N(0,1) fp16, seeded torch generator on the device",
         "config": {
             "workload": "KIVI %d-bit decode over a one-shot prefill: batch %d, 8 KV heads, "
-                        "32 query heads, head_dim 128, context %d, group %d, residual %d%s"
-                        % (bits, B, n, G, R, "" if chunk == n else ", prefill in %d-token chunks" % chunk),
+                        "32 query heads, head_dim 128, context %d, group %d, residual %d%s%s"
+                        % (bits, B, n, G, R, "" if chunk == n else ", prefill in %d-token chunks" % chunk,
+                           "" if not n_out else ", %d fp16 key channels per key group" % n_out),
             "batch": B, "kv_heads": H, "q_heads": Hq, "head_dim": D, "context": n,
             "group": G, "residual": R, "bits": bits, "quantized_tokens": Q,
             "decode_splits_per_stream": splits, "groups_per_split": gps,
@@ -417,7 +428,7 @@ def main():
                   " 1 GiB eviction read before each phase (outside the phase events)"
                   if not args.no_evict else "HIP events, no eviction (warm)",
     }
-    if args.attn_queries > 0:
+    if args.attn_queries > 0 and n_out == 0:
         rec["attn"] = attn_measure(cache, B, Hq, n, args.attn_queries, stream, evict, evict_out,
                                    not args.no_evict)
     if args.stream_steps > 0:
@@ -434,7 +445,7 @@ def main():
         }
     if args.cpu_sample > 0:
         k0, v0 = chunks[0]
-        if chunk == n and G == 32:
+        if chunk == n and G == 32 and n_out == 0:
             rec["cpu_baseline"] = cpu_baseline(k0, v0, q, bits, R, H, Hq, args.cpu_sample)
     print(json.dumps(rec), flush=True)
 

@@ -84,7 +84,10 @@ typedef struct {
     int32_t residual;     /* R >= 0, a multiple of G                          */
     int32_t kv_dtype;     /* kivi_dtype of the K/V rows handed to append      */
     int32_t policy;       /* kivi_flush_policy                                */
-    int32_t reserved;     /* must be 0                                        */
+    int32_t key_outliers; /* 0..3: per 32-token key group, this many channels  */
+                          /* (the largest max |K|) kept in fp16; 2 is the    */
+                          /* notebook's "top 1%" of 128.  > 0 needs G = 32   */
+                          /* and the window policy, and decode only          */
     int64_t max_tokens;   /* capacity per stream, >= 1                        */
 } kivi_config;
 
@@ -97,7 +100,14 @@ typedef struct kivi_cache kivi_cache;   /* opaque host-side handle */
    b*32*D/8 each), then fp16 K scale[D], K zero[D] of the key group the
    block lies in (repeated in each of a group's G/32 blocks), V scale[4][32],
    V zero[4][32]: slot cg of token t holds the parameters of the value group
-   containing channels 32cg .. 32cg+31 (repeated when G > 32).  The bit order of
+   containing channels 32cg .. 32cg+31 (repeated when G > 32).  With
+   key_outliers = n > 0 (outlier-aware keys, the cookbook notebook's
+   "Exercises" item 2, read per key group), the n channels of each key
+   group with the largest max |K| over its tokens (ties: lower channel)
+   keep their values in fp16: their codes, K scale and K zero in the block
+   are 0, and the block's 256-byte record holds uint16 channel[3]
+   (ascending, 0xFFFF unused), 10 zero bytes, then fp16 values [3][32] at
+   byte 16 + 64 o (0 unused).  The bit order of
    the codes is described in the kernel source (it follows the matrix-core
    operand layout).  Ring: [B*H][ring_capacity][D] in kv_dtype for K and for
    V; token t of a stream lives in slot t mod ring_capacity while it is in
@@ -112,6 +122,8 @@ typedef struct {
     int64_t n_tokens;                   /* n                                  */
     int64_t n_quantized;                /* key tokens quantized: Q(n) / Q_K(n) */
     int64_t n_vquantized;               /* value tokens quantized: Q(n) / Q_V(n) */
+    size_t outliers;                    /* key_outliers > 0: offset of the    */
+                                        /* records [B*H][max_groups][256]     */
 } kivi_layout;
 
 /* What an append of n_new tokens will do (pure host computation). */

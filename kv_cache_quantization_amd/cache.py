@@ -20,7 +20,7 @@ class KiviCache:
     def __init__(self, batch: int, n_kv_heads: int, n_q_heads: int, max_tokens: int,
                  bits: int = 2, group: int = 32, residual: int = 128, head_dim: int = 128,
                  kv_dtype: torch.dtype = torch.float16, device="cuda",
-                 policy: int = _k.KIVI_FLUSH_WINDOW):
+                 policy: int = _k.KIVI_FLUSH_WINDOW, key_outliers: int = 0):
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
@@ -30,7 +30,7 @@ class KiviCache:
         if kv_dtype not in (torch.float16, torch.float32):
             raise TypeError("kv_dtype must be float16 or float32")
         self.cfg = _k.make_config(batch, n_kv_heads, n_q_heads, head_dim, bits, group,
-                                  residual, max_tokens, dt, policy)
+                                  residual, max_tokens, dt, policy, key_outliers)
         nbytes = _k.kivi_cache_bytes(self.cfg)
         if nbytes == 0:
             raise _k.KiviError(_k.KIVI_ERR_INVALID_ARG, "kivi_cache_bytes")
@@ -177,6 +177,12 @@ class KiviCache:
         nbytes = self.streams * lo.max_groups * lo.block_bytes
         return self.buffer[lo.blocks:lo.blocks + nbytes].view(
             self.streams, lo.max_groups, lo.block_bytes)
+
+    def outlier_records_view(self) -> torch.Tensor:
+        """[streams, max_groups, 256] bytes of the outlier records (key_outliers > 0)."""
+        lo = self.layout()
+        nbytes = self.streams * lo.max_groups * 256
+        return self.buffer[lo.outliers:lo.outliers + nbytes].view(self.streams, lo.max_groups, 256)
 
     def ring_views(self):
         lo = self.layout()

@@ -30,7 +30,7 @@ struct kivi_cache {
     kivi_config cfg;
     uint8_t *base;
     size_t bytes;
-    size_t off_blocks, off_ring_k, off_ring_v;
+    size_t off_blocks, off_ring_k, off_ring_v, off_outliers;
     int64_t max_groups;
     int64_t block_bytes, code_bytes;
     int64_t ring_cap;
@@ -67,13 +67,16 @@ kivi_status validate(const kivi_config *c) {
     if (c->kv_dtype != KIVI_F16 && c->kv_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
     if (c->policy != KIVI_FLUSH_WINDOW && c->policy != KIVI_FLUSH_PAPER) return KIVI_ERR_INVALID_ARG;
     if (c->policy == KIVI_FLUSH_PAPER && c->residual == 0) return KIVI_ERR_INVALID_ARG;
-    if (c->reserved != 0) return KIVI_ERR_INVALID_ARG;
+    if (c->key_outliers < 0 || c->key_outliers > kMaxKeyOutliers) return KIVI_ERR_INVALID_ARG;
     // Shapes the kernels are built for.
     if (c->head_dim != kHeadDim) return KIVI_ERR_UNSUPPORTED;
     if (c->group != kGroup && c->group != 2 * kGroup && c->group != 4 * kGroup)
         return KIVI_ERR_UNSUPPORTED;
     const int gq = c->n_q_heads / c->n_kv_heads;
     if (gq != 1 && gq != 2 && gq != 4) return KIVI_ERR_UNSUPPORTED;
+    // outlier-aware keys: built for 32-token key groups under the window policy
+    if (c->key_outliers > 0 && (c->group != kGroup || c->policy != KIVI_FLUSH_WINDOW))
+        return KIVI_ERR_UNSUPPORTED;
     if ((int64_t)c->batch * c->n_kv_heads > (1LL << 24)) return KIVI_ERR_UNSUPPORTED;
     return KIVI_OK;
 }
@@ -81,7 +84,7 @@ kivi_status validate(const kivi_config *c) {
 struct Sizes {
     int64_t max_groups, block_bytes, code_bytes, ring_cap;
     int esize;
-    size_t off_blocks, off_ring_k, off_ring_v, total;
+    size_t off_blocks, off_ring_k, off_ring_v, off_outliers, total;
 };
 
 Sizes sizes_of(const kivi_config *c) {
@@ -96,7 +99,10 @@ Sizes sizes_of(const kivi_config *c) {
     s.off_ring_k = align_up((size_t)(streams * s.max_groups * s.block_bytes));
     const size_t ring_bytes = align_up((size_t)(streams * s.ring_cap * c->head_dim * s.esize));
     s.off_ring_v = s.off_ring_k + ring_bytes;
-    s.total = s.off_ring_v + ring_bytes;
+    s.off_outliers = s.off_ring_v + ring_bytes;
+    s.total = s.off_outliers;
+    if (c->key_outliers > 0)
+        s.total += align_up((size_t)(streams * s.max_groups * kOutlierRecordBytes));
     return s;
 }
 
@@ -245,6 +251,7 @@ kivi_status kivi_cache_create(const kivi_config *cfg, void *dev_mem, size_t dev_
     c->off_blocks = s.off_blocks;
     c->off_ring_k = s.off_ring_k;
     c->off_ring_v = s.off_ring_v;
+    c->off_outliers = s.off_outliers;
     c->max_groups = s.max_groups;
     c->block_bytes = s.block_bytes;
     c->code_bytes = s.code_bytes;
@@ -308,6 +315,8 @@ kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const voi
     a.block_begin = block_begin;
     a.block_end = block_end;
     a.gt = c->cfg.group / kGroup;
+    a.n_out = c->cfg.key_outliers;
+    a.outliers = c->cfg.key_outliers > 0 ? c->base + c->off_outliers : nullptr;
     a.streams = c->cfg.batch * c->cfg.n_kv_heads;
     a.is_f32 = c->cfg.kv_dtype == KIVI_F32;
     a.bits = c->cfg.bits;
@@ -483,6 +492,8 @@ kivi_status enqueue_decode(kivi_cache *c, const void *q, int32_t q_dtype, float 
     a.items = (int32_t)items;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)c->cfg.head_dim);
     a.sm_log2 = scale * 1.4426950408889634f;
+    a.n_out = c->cfg.key_outliers;
+    a.outliers = c->cfg.key_outliers > 0 ? c->base + c->off_outliers : nullptr;
     a.in_k = in_k;
     a.in_v = in_v;
     a.in_n = in_n;
@@ -547,7 +558,7 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     if (causal != 0 && causal != 1) return KIVI_ERR_INVALID_ARG;
     if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
     if (causal && T > c->n) return KIVI_ERR_INVALID_ARG;
-    if (c->cfg.policy == KIVI_FLUSH_PAPER) return KIVI_ERR_UNSUPPORTED;
+    if (c->cfg.policy == KIVI_FLUSH_PAPER || c->cfg.key_outliers > 0) return KIVI_ERR_UNSUPPORTED;
     if (c->cfg.kv_dtype != KIVI_F16 && c->n > c->q) return KIVI_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)c->cfg.batch * c->cfg.n_q_heads * T;
     if (rows > 0x7FFFFFFF) return KIVI_ERR_UNSUPPORTED;
@@ -609,6 +620,7 @@ kivi_status kivi_get_layout(const kivi_cache *c, kivi_layout *o) {
     o->n_tokens = c->n;
     o->n_quantized = c->q;
     o->n_vquantized = c->qv;
+    o->outliers = c->cfg.key_outliers > 0 ? c->off_outliers : 0;
     return KIVI_OK;
 }
 

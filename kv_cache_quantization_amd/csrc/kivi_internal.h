@@ -7,7 +7,9 @@
 namespace kivi {
 
 constexpr int kHeadDim = 128;   // D: channels per head
-constexpr int kGroup = 32;      // G: tokens per key group / channels per value group
+constexpr int kGroup = 32;      // tokens per block (G: 32, 64 or 128 per key / value group)
+constexpr int kMaxKeyOutliers = 3;        // fp16 key channels per key group at most
+constexpr int kOutlierRecordBytes = 256;  // per block: uint16 channel[3], pad, fp16 [3][32]
 
 // Quantize the 32-token blocks [block_begin, block_end) of every stream.  A
 // key group spans gt = G / 32 blocks (block_begin and block_end are then
@@ -28,6 +30,8 @@ struct QuantizeArgs {
     int32_t is_f32;             // kv dtype: 0 fp16, 1 fp32
     int32_t bits;               // 2, 4 or 8
     int32_t gt;                 // blocks per key group: G / 32 (1, 2 or 4)
+    int32_t n_out;              // fp16 key channels per key group (0: none)
+    uint8_t *outliers;          // [streams][max_groups][kOutlierRecordBytes]
     int32_t kinds;              // 1: key groups, 2: value blocks, 3: both
     int64_t v_limit;            // value codes / side data of tokens >= v_limit are written 0
 };
@@ -58,6 +62,8 @@ struct DecodeArgs {
     float *part_ml;             // [B*Hq][n_items_per_stream][2]  (m log2, l)
     int32_t batch, kv_heads, q_heads;
     int32_t bits;
+    int32_t n_out;              // fp16 key channels per group (0: none)
+    const uint8_t *outliers;    // [streams][max_groups][kOutlierRecordBytes]
     int64_t n_tokens;           // n
     int64_t n_quant;            // groups [0, n_quant / G) hold key and value codes
     int64_t n_tail;             // fp16 keys and values from here to n (the residual)

@@ -352,7 +352,7 @@ __device__ __forceinline__ void quantize_pack8(const QuantizeArgs &a, const TT &
                                                const float (&mn)[8], const float (&s)[8],
                                                const float (&y)[8], const float (&cz)[8],
                                                float near_tie, bool fast_ok, uint8_t *blk,
-                                               uint32_t *tr) {
+                                               uint32_t *tr, uint32_t omask) {
 #pragma clang fp contract(off)
     constexpr float L = 255.0f;
     constexpr int DPL = 16;
@@ -376,6 +376,11 @@ __device__ __forceinline__ void quantize_pack8(const QuantizeArgs &a, const TT &
                 const float x = IS_V ? t.at(kk, u) : t.at(u, kk);
                 cd[kk] = exact_code(x, mn[kk], s[kk], L);
             }
+        }
+        if (!IS_V) {
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++)          // key channels kept in fp16
+                if ((omask >> kk) & 1u) cd[kk] = 0.0f;
         }
 #pragma unroll
         for (int p = 0; p < 2; p++) {
@@ -443,7 +448,19 @@ __device__ __forceinline__ void load_tile(const QuantizeArgs &a, int64_t stream,
 // statistics span all of them, and each block is then coded and stored with
 // the group's zero / scale), or the values of block g0 (groups of 32 * GT
 // channels per token).
-template <int BITS, bool IS_V, bool RING, typename T, int GT>
+// Outlier-aware keys (OUT): a 64-bit key per channel orders channels by the
+// group's max |K| (its fp32 bits, monotone for non-negative floats), ties to
+// the lower channel; +1 keeps every key above the 0 of "no candidate".
+__device__ __forceinline__ uint64_t outlier_key(float lo, float hi, int ch) {
+    const float sc = fmaxf(fabsf(lo), fabsf(hi));
+    return (((uint64_t)__builtin_bit_cast(uint32_t, sc) << 8) | (uint32_t)(127 - ch)) + 1u;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    const uint32_t lo = __shfl_xor((int)(uint32_t)v, m), hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int BITS, bool IS_V, bool RING, typename T, int GT, bool OUT = false>
 __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t stream, int64_t g0,
                                               uint32_t *tr) {
 #pragma clang fp contract(off)
@@ -465,6 +482,37 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
     } else {
         load_tile<IS_V, RING>(a, stream, g0, t);
         group_minmax<IS_V, GT>(t, lo, hi);
+    }
+    // outlier-aware keys: the a.n_out channels with the largest max |K| of
+    // the group (bit k of omask: channel 8c + k), in ascending order in och
+    uint32_t omask = 0;
+    int och[kMaxKeyOutliers] = {0xFFFF, 0xFFFF, 0xFFFF};
+    if constexpr (OUT && !IS_V) {
+        uint64_t key[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) key[k] = outlier_key(lo[k], hi[k], 8 * c + k);
+#pragma unroll
+        for (int o = 0; o < kMaxKeyOutliers; o++) {
+            if (o < a.n_out) {                  // (unrolled: och stays in registers)
+                uint64_t best = 0;
+#pragma unroll
+                for (int k = 0; k < 8; k++)
+                    if (!((omask >> k) & 1u) && key[k] > best) best = key[k];
+                // over the 16 channel chunks of a row (the four rows agree)
+#pragma unroll
+                for (int x = 1; x < 16; x <<= 1) {
+                    const uint64_t other = shfl_xor_u64(best, x);
+                    best = other > best ? other : best;
+                }
+                const int ch = 127 - (int)((best - 1u) & 0xFFu);
+                och[o] = ch;
+                if ((ch >> 3) == c) omask |= 1u << (ch & 7);
+            }
+        }
+        // ascending channel order (at most three)
+        if (och[1] < och[0]) { const int x = och[0]; och[0] = och[1]; och[1] = x; }
+        if (och[2] < och[1]) { const int x = och[1]; och[1] = och[2]; och[2] = x; }
+        if (och[1] < och[0]) { const int x = och[0]; och[0] = och[1]; och[1] = x; }
     }
     float mn[8], s[8], y[8], cz[8];
     float smin = INFINITY, smax = 0.0f, czmax = 0.0f;
@@ -492,13 +540,55 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
 
     // zero / scale as fp16
     if (!IS_V) {
-        // channels 8c..8c+7: lanes q = 0 store the scales, q = 1 the zeros.
+        // channels 8c..8c+7: lanes q = 0 store the scales, q = 1 the zeros
+        // (0 and 0 for channels kept in fp16).
         if (q < 2) {
+            float sk[8], zk[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                const bool kept = OUT && ((omask >> k) & 1u);
+                sk[k] = kept ? 0.0f : s[k];
+                zk[k] = kept ? 0.0f : mn[k];
+            }
             uint32_t w[4];
 #pragma unroll
             for (int p = 0; p < 4; p++)
-                w[p] = q == 0 ? pack_f16(s[2 * p], s[2 * p + 1]) : pack_f16(mn[2 * p], mn[2 * p + 1]);
+                w[p] = q == 0 ? pack_f16(sk[2 * p], sk[2 * p + 1]) : pack_f16(zk[2 * p], zk[2 * p + 1]);
             *(uint4 *)(side + q * D + 8 * c) = (uint4){w[0], w[1], w[2], w[3]};
+        }
+        if constexpr (OUT) {
+            // the block's outlier record: header (lane 0), each kept channel's
+            // 32 fp16 values (the four lanes of its chunk, 8 rows each), zeros
+            // in the unused slots (lanes 4o .. 4o + 3); no two stores overlap
+            uint8_t *rec = a.outliers + (stream * a.max_groups + g) * kOutlierRecordBytes;
+            if (l == 0)
+                *(uint4 *)rec = (uint4){(uint32_t)och[0] | ((uint32_t)och[1] << 16),
+                                        (uint32_t)och[2], 0u, 0u};
+#pragma unroll
+            for (int o = 0; o < kMaxKeyOutliers; o++) {
+                if (o < a.n_out) {
+                    if ((och[o] >> 3) == c) {
+                        const int e = och[o] & 7;
+                        _Float16 *dst = (_Float16 *)(rec + 16 + 64 * o);
+#pragma unroll
+                        for (int j = 0; j < 8; j++) {
+                            // (a lane-dependent index into the 32-register tile
+                            // would move it to scratch; into 8 copies it stays
+                            // in registers)
+                            float row[8];
+#pragma unroll
+                            for (int e2 = 0; e2 < 8; e2++) row[e2] = t.at(j, e2);
+                            dst[tile_row<false>(j, q)] = (_Float16)row[e];
+                        }
+                    }
+                } else if (l >= 4 * o && l < 4 * o + 4) {
+                    *(uint4 *)(rec + 16 + 64 * o + 16 * (l - 4 * o)) = (uint4){0u, 0u, 0u, 0u};
+                }
+            }
+            // the record's last 48 bytes (after the third slot) are zero too
+            constexpr int kTail = 16 + 64 * kMaxKeyOutliers;
+            if (l >= 12 && l < 12 + (kOutlierRecordBytes - kTail) / 16)
+                *(uint4 *)(rec + kTail + 16 * (l - 12)) = (uint4){0u, 0u, 0u, 0u};
         }
     } else {
         // rows 4q..4q+3 (j < 4) and 16+4q.. (j >= 4) of value group c/4; the
@@ -522,7 +612,7 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
     // Units u = 0..7 (key row j = u over channels kk; value channel e = u over
     // rows kk), parameters indexed by kk for keys and values alike.
     if constexpr (BITS == 8) {
-        quantize_pack8<IS_V>(a, t, mn, s, y, cz, near_tie, fast_ok, blk, tr);
+        quantize_pack8<IS_V>(a, t, mn, s, y, cz, near_tie, fast_ok, blk, tr, OUT ? omask : 0u);
         return;
     }
     uint32_t unit[8];
@@ -532,8 +622,9 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
 #pragma unroll
         for (int kk = 0; kk < 8; kk++) {
             const float tq = IS_V ? t.fma(kk, u, y[kk], cz[kk]) : t.fma(u, kk, y[kk], cz[kk]);
-            const float cd = __builtin_rintf(tq);
+            float cd = __builtin_rintf(tq);
             rmax = fmaxf(rmax, fabsf(tq - cd));
+            if (OUT && !IS_V && ((omask >> kk) & 1u)) cd = 0.0f;    // kept in fp16
             if (kk < (BITS == 4 ? 2 : 1)) (kk ? acc1 : acc0) = cd;   // weight 1
             else if (BITS == 4 && (kk & 1)) acc1 = __builtin_fmaf(cd, unit_weight<BITS>(kk), acc1);
             else acc0 = __builtin_fmaf(cd, unit_weight<BITS>(kk), acc0);
@@ -542,7 +633,8 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
 #pragma unroll
             for (int kk = 0; kk < 8; kk++) {
                 const float x = IS_V ? t.at(kk, u) : t.at(u, kk);
-                const float cd = exact_code(x, mn[kk], s[kk], L);
+                float cd = exact_code(x, mn[kk], s[kk], L);
+                if (OUT && !IS_V && ((omask >> kk) & 1u)) cd = 0.0f;
                 if (kk < (BITS == 4 ? 2 : 1)) (kk ? acc1 : acc0) = cd;
                 else if (BITS == 4 && (kk & 1)) acc1 = __builtin_fmaf(cd, unit_weight<BITS>(kk), acc1);
                 else acc0 = __builtin_fmaf(cd, unit_weight<BITS>(kk), acc0);
@@ -621,7 +713,7 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
 // kinds = 3: per key group (GT blocks), task (1 + GT) i is the key group and
 // the next GT tasks are the value blocks of the same tokens; kinds = 1 / 2:
 // every task is a key group / a value block.
-template <int BITS, typename T, bool RING, int GT>
+template <int BITS, typename T, bool RING, int GT, bool OUT>
 __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
     __shared__ uint32_t tr[64 * 2 * BITS];
     const uint32_t task = blockIdx.x;
@@ -643,8 +735,8 @@ __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
         is_v = true;
         g = a.block_begin + task % nb;
     }
-    if (is_v) quantize_task<BITS, true, RING, T, GT>(a, stream, g, tr);
-    else quantize_task<BITS, false, RING, T, GT>(a, stream, g, tr);
+    if (is_v) quantize_task<BITS, true, RING, T, GT, OUT>(a, stream, g, tr);
+    else quantize_task<BITS, false, RING, T, GT, OUT>(a, stream, g, tr);
 }
 // ===========================================================================
 // Residual ring append: copy rows [tok_begin, tok_end) of the chunk into
@@ -1190,28 +1282,47 @@ struct Pipe {
     static constexpr int NST = BITS == 2 ? 3 : 2;       // stages (8 bits: 9 KiB groups)
 };
 
-template <int BITS>
-__device__ __forceinline__ void issue_group(const uint8_t *blk, uint32_t stage, int l) {
+// LDS bytes of one pipeline stage: the block, and with outlier-aware keys
+// (OUT) the block's 256-byte outlier record after it.
+template <int BITS, bool OUT>
+__device__ __forceinline__ constexpr int stage_bytes() {
+    return Pipe<BITS>::BB + (OUT ? kOutlierRecordBytes : 0);
+}
+
+// 64 lanes x 4 bytes from global memory straight into LDS (M0 + 4 * lane).
+__device__ __forceinline__ void dma_256(const uint8_t *src_lane, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src_lane), "s"(lds_dst)
+                 : "memory", "m0");
+}
+
+template <int BITS, bool OUT = false>
+__device__ __forceinline__ void issue_group(const uint8_t *blk, const uint8_t *rec, uint32_t stage,
+                                            int l) {
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // prior reads of the stage done
 #pragma unroll
     for (int c = 0; c < Pipe<BITS>::DPG; c++)
         dma_1k(blk + c * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(stage + c * 1024));
+    if constexpr (OUT)
+        dma_256(rec + 4 * l, __builtin_amdgcn_readfirstlane(stage + Pipe<BITS>::BB));
 }
 
 // Wait until at most `r` groups (issued after the one needed) are in flight.
-template <int BITS>
+template <int BITS, bool OUT = false>
 __device__ __forceinline__ void wait_groups_after(int r) {
-    constexpr int P = Pipe<BITS>::DPG;
+    constexpr int P = Pipe<BITS>::DPG + (OUT ? 1 : 0);
     if (r >= 3) wait_vm<3 * P>();
     else if (r == 2) wait_vm<2 * P>();
     else if (r == 1) wait_vm<P>();
     else wait_vm<0>();
 }
 
-template <int BITS, int GQ, bool QF32>
+template <int BITS, int GQ, bool QF32, bool OUT = false>
 __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *pipe,
                              uint4 *q_lds) {
     using PP = Pipe<BITS>;
+    constexpr int SB = stage_bytes<BITS, OUT>();
     constexpr int DPL = 2 * BITS;              // code dwords per lane
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
@@ -1226,6 +1337,8 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int n_g = (int)(g1 - g0);             // groups of this split
 
     const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
+    const uint8_t *srec = OUT ? a.outliers + ((int64_t)stream * a.max_groups + g0) * kOutlierRecordBytes
+                              : nullptr;
     const uint32_t pbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)pipe;
     // q of the lane's head in B-operand order, and the unscaled fp16 q of the
     // GQ heads for LDS (16 bytes per lane, head (l/16) % GQ, channels
@@ -1252,7 +1365,9 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     // stage ring: `is` is the stage the next copy goes to, `rs` the stage read
     int issued = 0, is = 0, rs = 0;
     for (; issued < PP::NST - 1 && issued < n_g; issued++) {
-        issue_group<BITS>(sblk + (int64_t)issued * PP::BB, pbase + (uint32_t)is * PP::BB, l);
+        issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
+                               OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                               pbase + (uint32_t)is * SB, l);
         is = is + 1 == PP::NST ? 0 : is + 1;
     }
     // first uses of q: after the copies above (volatile asm keeps the order)
@@ -1280,12 +1395,14 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
 
     for (int g = 0; g < n_g; g++) {
         if (issued < n_g) {
-            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, pbase + (uint32_t)is * PP::BB, l);
+            issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
+                                   OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                                   pbase + (uint32_t)is * SB, l);
             is = is + 1 == PP::NST ? 0 : is + 1;
             issued++;
         }
-        wait_groups_after<BITS>(issued - 1 - g);
-        const uint8_t *stg = pipe + rs * PP::BB;
+        wait_groups_after<BITS, OUT>(issued - 1 - g);
+        const uint8_t *stg = pipe + rs * SB;
         rs = rs + 1 == PP::NST ? 0 : rs + 1;
         const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
         uint32_t kc[DPL], vc[DPL];
@@ -1326,6 +1443,29 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
             S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, S1, 0, 0, 0);
             S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, S0, 0, 0, 0);
             S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1, 0, 0, 0);
+        }
+        if constexpr (OUT) {
+            // key channels kept in fp16: their codes, scale and zero are 0, so
+            // add q . K over them from the record (exact fp16 products; the
+            // scores here are in units of 2^24)
+            const uint2 idx = *(const uint2 *)(stg + PP::BB);    // channel[0..2]
+            const int ch[kMaxKeyOutliers] = {(int)(idx.x & 0xFFFFu), (int)(idx.x >> 16),
+                                             (int)(idx.y & 0xFFFFu)};
+            const _Float16 *rval = (const _Float16 *)(stg + PP::BB + 16);
+            const _Float16 *q16 = (const _Float16 *)q_lds;      // [head][channel]
+#pragma unroll
+            for (int o = 0; o < kMaxKeyOutliers; o++) {
+                if (o < a.n_out) {
+                    const float qo = (float)q16[h * D + ch[o]] * kTwoM24;
+                    const h2 *v0 = (const h2 *)(rval + G * o + 4 * Gl);        // tokens 4Gl + e
+                    const h2 *v1 = (const h2 *)(rval + G * o + 16 + 4 * Gl);   // 16 + 4Gl + e
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        S0[e] = __builtin_fmaf(qo, (float)v0[e >> 1][e & 1], S0[e]);
+                        S1[e] = __builtin_fmaf(qo, (float)v1[e >> 1][e & 1], S1[e]);
+                    }
+                }
+            }
         }
         h2 P[4];
         softmax_step<BITS>(S0, S1, cs, Sk[0] * a.sm_log2, m_run, m_thr, nm, Lsum, vb, accV, P);
@@ -1579,9 +1719,9 @@ __global__ __launch_bounds__(64) void decode_mixed_kernel(DecodeArgs a) {
     }
 }
 
-template <int BITS, int GQ>
+template <int BITS, int GQ, bool OUT = false>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t pipe[Pipe<BITS>::NST * Pipe<BITS>::BB];
+    __shared__ __attribute__((aligned(16))) uint8_t pipe[Pipe<BITS>::NST * stage_bytes<BITS, OUT>()];
     __shared__ uint4 q_lds[64];
     const int64_t item = blockIdx.x;
     const int64_t streams = (int64_t)a.batch * a.kv_heads;
@@ -1596,9 +1736,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     // meet at a control-flow join, where the compiler would wait for them)
     const int64_t it = item - streams * a.tail_items;
     if (a.q_is_f32)
-        decode_split<BITS, GQ, true>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
+        decode_split<BITS, GQ, true, OUT>(a, (int)(it / a.splits), (int)(it % a.splits), pipe,
+                                          q_lds);
     else
-        decode_split<BITS, GQ, false>(a, (int)(it / a.splits), (int)(it % a.splits), pipe, q_lds);
+        decode_split<BITS, GQ, false, OUT>(a, (int)(it / a.splits), (int)(it % a.splits), pipe,
+                                           q_lds);
 }
 
 // Merge the partials of one output row (a (batch, query head) of the decode
@@ -1764,7 +1906,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
     int issued = 0, is = 0, rs = 0;
     if (w == 0) {
         for (; issued < PP::NST - 1 && issued < n_g; issued++) {
-            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, rbase + (uint32_t)is * PP::BB, l);
+            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, nullptr, rbase + (uint32_t)is * PP::BB,
+                              l);
             is = is + 1 == PP::NST ? 0 : is + 1;
         }
     }
@@ -1816,7 +1959,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
         if (w == 0) wait_groups_after<BITS>(issued - 1 - g);
         __syncthreads();            // group g landed; every wave is done with g - 1
         if (w == 0 && issued < n_g) {
-            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, rbase + (uint32_t)is * PP::BB, l);
+            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, nullptr, rbase + (uint32_t)is * PP::BB,
+                              l);
             is = is + 1 == PP::NST ? 0 : is + 1;
             issued++;
         }
@@ -2029,7 +2173,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
 // ===========================================================================
 // Launchers
 // ===========================================================================
-template <int BITS, typename T, int GT>
+template <int BITS, typename T, int GT, bool OUT = false>
 static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
     // tasks per launched block range: key groups of GT blocks and / or blocks
     auto tasks_of = [&](int64_t nb) {
@@ -2047,21 +2191,22 @@ static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
         QuantizeArgs r = a;
         r.block_end = split;
         const int64_t tasks = (int64_t)a.streams * tasks_of(split - a.block_begin);
-        hipLaunchKernelGGL((quantize_kernel<BITS, T, true, GT>), dim3((unsigned)tasks), dim3(64), 0,
-                           s, r);
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, true, GT, OUT>), dim3((unsigned)tasks), dim3(64),
+                           0, s, r);
     }
     if (a.block_end > split) {
         QuantizeArgs n = a;
         n.block_begin = split;
         const int64_t tasks = (int64_t)a.streams * tasks_of(a.block_end - split);
-        hipLaunchKernelGGL((quantize_kernel<BITS, T, false, GT>), dim3((unsigned)tasks), dim3(64), 0,
-                           s, n);
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, false, GT, OUT>), dim3((unsigned)tasks), dim3(64),
+                           0, s, n);
     }
     return hipGetLastError();
 }
 
 template <int BITS, typename T>
 static hipError_t launch_quantize_g(const QuantizeArgs &a, hipStream_t s) {
+    if (a.n_out > 0) return launch_quantize_t<BITS, T, 1, true>(a, s);
     if (a.gt == 1) return launch_quantize_t<BITS, T, 1>(a, s);
     if (a.gt == 2) return launch_quantize_t<BITS, T, 2>(a, s);
     return launch_quantize_t<BITS, T, 4>(a, s);
@@ -2071,6 +2216,8 @@ hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
     if (a.block_end <= a.block_begin || a.streams <= 0) return hipSuccess;
     if (a.kinds < 1 || a.kinds > 3) return hipErrorInvalidValue;
     if (a.gt != 1 && a.gt != 2 && a.gt != 4) return hipErrorInvalidValue;
+    if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && (a.gt != 1 || !a.outliers)))
+        return hipErrorInvalidValue;
     // key tasks cover whole groups of gt blocks
     if (a.kinds != 2 && (a.block_begin % a.gt != 0 || a.block_end % a.gt != 0))
         return hipErrorInvalidValue;
@@ -2095,11 +2242,11 @@ hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, bool OUT = false>
 static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
-    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4>), grid, dim3(64), 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<BITS, 1>), grid, dim3(64), 0, s, a);
+    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4, OUT>), grid, dim3(64), 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2, OUT>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<BITS, 1, OUT>), grid, dim3(64), 0, s, a);
 }
 
 template <int BITS>
@@ -2135,7 +2282,14 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     dim3 grid((unsigned)items);
-    if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
+    if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && !a.outliers))
+        return hipErrorInvalidValue;
+    if (a.n_out > 0 && a.mixed_groups > 0) return hipErrorInvalidValue;   // window policy only
+    if (a.n_out > 0) {
+        if (a.bits == 2) launch_decode_bits<2, true>(a, gq, grid, s);
+        else if (a.bits == 8) launch_decode_bits<8, true>(a, gq, grid, s);
+        else launch_decode_bits<4, true>(a, gq, grid, s);
+    } else if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
     else if (a.bits == 8) launch_decode_bits<8>(a, gq, grid, s);
     else launch_decode_bits<4>(a, gq, grid, s);
     hipError_t e = hipGetLastError();

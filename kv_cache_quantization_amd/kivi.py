@@ -43,7 +43,7 @@ class kivi_config(ctypes.Structure):
         ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
         ("residual", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-        ("policy", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("policy", ctypes.c_int32), ("key_outliers", ctypes.c_int32),
         ("max_tokens", ctypes.c_int64),
     ]
 
@@ -54,7 +54,7 @@ class kivi_layout(ctypes.Structure):
         "off_vcode", "off_kscale", "off_kzero", "off_vscale", "off_vzero")] + [
         ("max_groups", ctypes.c_int64), ("ring_capacity", ctypes.c_int64),
         ("n_tokens", ctypes.c_int64), ("n_quantized", ctypes.c_int64),
-        ("n_vquantized", ctypes.c_int64)]
+        ("n_vquantized", ctypes.c_int64), ("outliers", ctypes.c_size_t)]
 
 
 class kivi_append_plan(ctypes.Structure):
@@ -206,6 +206,7 @@ def kivi_get_layout(handle: int) -> kivi_layout:
 
 
 def make_config(batch, n_kv_heads, n_q_heads, head_dim=128, bits=2, group=32, residual=128,
-                max_tokens=4096, kv_dtype=KIVI_F16, policy=KIVI_FLUSH_WINDOW) -> kivi_config:
+                max_tokens=4096, kv_dtype=KIVI_F16, policy=KIVI_FLUSH_WINDOW,
+                key_outliers=0) -> kivi_config:
     return kivi_config(batch, n_kv_heads, n_q_heads, head_dim, bits, group, residual,
-                       kv_dtype, policy, 0, max_tokens)
+                       kv_dtype, policy, key_outliers, max_tokens)

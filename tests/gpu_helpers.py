@@ -17,10 +17,12 @@ def torch_dtype(np_dtype):
     return torch.float16 if np_dtype == np.float16 else torch.float32
 
 
-def new_cache(B, H, Hq, max_tokens, bits=2, R=128, dtype=np.float16, policy=0, group=32):
+def new_cache(B, H, Hq, max_tokens, bits=2, R=128, dtype=np.float16, policy=0, group=32,
+              key_outliers=0):
     from kv_cache_quantization_amd import KiviCache
     return KiviCache(B, H, Hq, max_tokens, bits=bits, group=group, residual=R,
-                     kv_dtype=torch_dtype(dtype), device="cuda", policy=policy)
+                     kv_dtype=torch_dtype(dtype), device="cuda", policy=policy,
+                     key_outliers=key_outliers)
 
 
 def to_dev(x):
@@ -52,7 +54,7 @@ def check_cache(orc, cache, k, v, streams=None, label=""):
         kk, vv = k[None], v[None]     # [1, S, n, D]: the sampled streams as one batch row
     n = kk.shape[2]
     G = c.group
-    ref = orc.build_cache(kk, vv, c.bits, G, c.residual, c.policy)
+    ref = orc.build_cache(kk, vv, c.bits, G, c.residual, c.policy, c.key_outliers)
     qk, qv = ref["qk"], ref["qv"]
     assert lo.n_tokens == n, (label, lo.n_tokens, n)
     assert (lo.n_quantized, lo.n_vquantized) == (qk, qv), (label, lo.n_quantized,
@@ -73,6 +75,16 @@ def check_cache(orc, cache, k, v, streams=None, label=""):
         if len(bad):
             raise AssertionError("%s: %d packed bytes differ, first (stream, group, byte) %s" %
                                  (label, len(bad), bad[:5].tolist()))
+    if c.key_outliers > 0 and ngk:
+        want = orc.pack_outlier_records(ref, ngk)
+        import torch
+        torch.cuda.synchronize()
+        got = cache.outlier_records_view()
+        got = (got if streams is None else got[list(streams)])[:, :ngk].cpu().numpy()
+        bad = np.argwhere(want != got)
+        if len(bad):
+            raise AssertionError("%s: %d outlier-record bytes differ, first (stream, group, byte) %s"
+                                 % (label, len(bad), bad[:5].tolist()))
     # ring: key tokens [Q_K, n) and value tokens [Q_V, n) in slot t % C, verbatim
     rk, rv = cache.ring_views()
     rk = rk.reshape(-1, lo.ring_capacity, c.head_dim).cpu().numpy()
@@ -97,8 +109,8 @@ def rel_err(out, ref):
     return float((np.abs(out - ref).max(1) / np.abs(ref).max(1)).max())
 
 
-def oracle_decode(orc, k, v, q, bits, G, R, sm_scale=None, policy=0):
+def oracle_decode(orc, k, v, q, bits, G, R, sm_scale=None, policy=0, key_outliers=0):
     """The oracle's decode attention over the cache built from k, v (group G)."""
-    ref = orc.build_cache(k, v, bits, G, R, policy)
+    ref = orc.build_cache(k, v, bits, G, R, policy, key_outliers)
     kh, vh = orc.dequant_cache(k, v, ref)
     return orc.decode_attn(q, kh, vh, sm_scale)

@@ -76,21 +76,32 @@ def test_invalid_configs(L, over, status):
     args = dict(batch=2, n_kv_heads=8, n_q_heads=32, bits=2, residual=128, max_tokens=4096)
     args.update(over)
     cfg = kivi.make_config(**args)
-    if "reserved" in over:
-        cfg.reserved = over["reserved"]
+    if "key_outliers" in over:
+        cfg.key_outliers = over["key_outliers"]
     assert kivi.kivi_cache_bytes(cfg) == 0
     h = ctypes.c_void_p()
     assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV, 1 << 40, ctypes.byref(h)) == status
     assert h.value is None
 
 
-def test_reserved_and_null_arguments(L):
+def test_key_outliers_field_and_null_arguments(L):
     cfg = kivi.make_config(1, 1, 1)
-    cfg.reserved = 1
     h = ctypes.c_void_p()
+    for bad in (-1, 4):
+        cfg.key_outliers = bad
+        assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV, 1 << 40,
+                                   ctypes.byref(h)) == kivi.KIVI_ERR_INVALID_ARG
+    cfg.key_outliers = 2
+    cfg.group = 64
+    cfg.residual = 128
     assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV, 1 << 40,
-                               ctypes.byref(h)) == kivi.KIVI_ERR_INVALID_ARG
-    cfg.reserved = 0
+                               ctypes.byref(h)) == kivi.KIVI_ERR_UNSUPPORTED
+    cfg.group = 32
+    cfg.policy = kivi.KIVI_FLUSH_PAPER
+    assert L.kivi_cache_create(ctypes.byref(cfg), FAKE_DEV, 1 << 40,
+                               ctypes.byref(h)) == kivi.KIVI_ERR_UNSUPPORTED
+    cfg.policy = kivi.KIVI_FLUSH_WINDOW
+    cfg.key_outliers = 0
     assert L.kivi_cache_create(None, FAKE_DEV, 1 << 40, ctypes.byref(h)) == kivi.KIVI_ERR_INVALID_ARG
     assert L.kivi_cache_create(ctypes.byref(cfg), None, 1 << 40,
                                ctypes.byref(h)) == kivi.KIVI_ERR_INVALID_ARG
