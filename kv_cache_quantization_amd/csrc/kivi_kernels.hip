@@ -1288,6 +1288,20 @@ template <int BITS, bool OUT>
 __device__ __forceinline__ constexpr int stage_bytes() {
     return Pipe<BITS>::BB + (OUT ? kOutlierRecordBytes : 0);
 }
+// Stages of the decode pipeline: with records, two at 2 bits as well, so
+// that a wavefront's LDS stays within 10 KiB (16 per compute unit).
+template <int BITS, bool OUT>
+__device__ __forceinline__ constexpr int decode_stages() {
+    return OUT ? 2 : Pipe<BITS>::NST;
+}
+// LDS of a decode wavefront besides q: the stages, and at least what a
+// residual item uses (32 fp16 value rows, then p of 4 heads x 32 tokens).
+template <int BITS, bool OUT>
+__device__ __forceinline__ constexpr int decode_lds_bytes() {
+    constexpr int st = decode_stages<BITS, OUT>() * stage_bytes<BITS, OUT>();
+    constexpr int tail = G * D * 2 + 4 * G * 4;
+    return st > tail ? st : tail;
+}
 
 // 64 lanes x 4 bytes from global memory straight into LDS (M0 + 4 * lane).
 __device__ __forceinline__ void dma_256(const uint8_t *src_lane, uint32_t lds_dst) {
@@ -1323,6 +1337,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
                              uint4 *q_lds) {
     using PP = Pipe<BITS>;
     constexpr int SB = stage_bytes<BITS, OUT>();
+    constexpr int NST = decode_stages<BITS, OUT>();
     constexpr int DPL = 2 * BITS;              // code dwords per lane
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
@@ -1364,11 +1379,11 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     }
     // stage ring: `is` is the stage the next copy goes to, `rs` the stage read
     int issued = 0, is = 0, rs = 0;
-    for (; issued < PP::NST - 1 && issued < n_g; issued++) {
+    for (; issued < NST - 1 && issued < n_g; issued++) {
         issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
                                OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
                                pbase + (uint32_t)is * SB, l);
-        is = is + 1 == PP::NST ? 0 : is + 1;
+        is = is + 1 == NST ? 0 : is + 1;
     }
     // first uses of q: after the copies above (volatile asm keeps the order)
 #pragma unroll
@@ -1398,12 +1413,12 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
             issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
                                    OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
                                    pbase + (uint32_t)is * SB, l);
-            is = is + 1 == PP::NST ? 0 : is + 1;
+            is = is + 1 == NST ? 0 : is + 1;
             issued++;
         }
         wait_groups_after<BITS, OUT>(issued - 1 - g);
         const uint8_t *stg = pipe + rs * SB;
-        rs = rs + 1 == PP::NST ? 0 : rs + 1;
+        rs = rs + 1 == NST ? 0 : rs + 1;
         const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
         uint32_t kc[DPL], vc[DPL];
 #pragma unroll
@@ -1721,7 +1736,7 @@ __global__ __launch_bounds__(64) void decode_mixed_kernel(DecodeArgs a) {
 
 template <int BITS, int GQ, bool OUT = false>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t pipe[Pipe<BITS>::NST * stage_bytes<BITS, OUT>()];
+    __shared__ __attribute__((aligned(16))) uint8_t pipe[decode_lds_bytes<BITS, OUT>()];
     __shared__ uint4 q_lds[64];
     const int64_t item = blockIdx.x;
     const int64_t streams = (int64_t)a.batch * a.kv_heads;
