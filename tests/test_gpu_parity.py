@@ -292,3 +292,30 @@ def test_group_sizes_streaming_and_fp32(orc):
              label="G64-stream-%d" % policy, G=64, policy=policy)
     _run(orc, 1, 2, 8, 600, 4, 128, np.float32, seed=78, q_dtype=np.float32, label="G128-fp32",
          G=128)
+
+
+def test_more_streams_than_the_wave_budget(orc):
+    """4160 streams (batch 520 x 8 KV heads) exceed the decode's one-round
+    budget of 4096 wavefronts: one split item per stream.  Sampled streams
+    are checked bit for bit and their query heads within the tolerance."""
+    import torch
+    from kv_cache_quantization_amd import synth
+    B, H, Hq, n, R, bits = 520, 8, 32, 200, 32, 2
+    log("case many-streams: B=%d H=%d n=%d" % (B, H, n))
+    k, v = synth.kv_host(13, B, H, n)
+    q = synth.queries_host(13, B, Hq)
+    cache = new_cache(B, H, Hq, n, bits=bits, R=R)
+    cache.append(to_dev(k), to_dev(v))
+    assert cache.decode_plan() == (1, 5)
+    out = cache.decode(to_dev(q)).cpu().numpy()
+    sample = [(0, 0), (259, 3), (519, 7)]
+    streams = [b * H + h for b, h in sample]
+    ks = np.stack([k[b, h] for b, h in sample])
+    vs = np.stack([v[b, h] for b, h in sample])
+    check_cache(orc, cache, ks, vs, streams=streams, label="many-streams")
+    for (b, h) in sample:
+        ref = oracle_decode(orc, k[b, h][None, None], v[b, h][None, None],
+                            q[b, 4 * h:4 * h + 4][None], bits, 32, R)
+        e = rel_err(out[b, 4 * h:4 * h + 4], ref[0])
+        log("  stream (%d, %d): decode rel err %.3g" % (b, h, e))
+        assert e <= TOL
