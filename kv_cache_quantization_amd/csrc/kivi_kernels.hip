@@ -1009,6 +1009,14 @@ __device__ __forceinline__ void dma_1k(const uint8_t *src_lane, uint32_t lds_dst
                  : "memory", "m0");
 }
 
+// Wavefront priority (s_setprio takes an immediate, 0..3).
+__device__ __forceinline__ void set_prio(int p) {
+    if (p >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -1408,7 +1416,19 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
 #pragma unroll
     for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
 
+    // The SIMD issues the oldest of its wavefronts first, so with equal
+    // shares the first-dispatched splits finish long before the last ones and
+    // the end of the pass runs with few copies in flight.  Each split lowers
+    // its priority as it advances (3 over its first quarter, down to 0 over
+    // its last): lagging wavefronts are issued first and the splits finish
+    // closer together.  (Results do not depend on it.)
+    int prio = 3;
+    set_prio(prio);
     for (int g = 0; g < n_g; g++) {
+        if (const int want = 3 - (4 * g) / n_g; want != prio) {
+            prio = want;
+            set_prio(want);
+        }
         if (issued < n_g) {
             issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
                                    OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
