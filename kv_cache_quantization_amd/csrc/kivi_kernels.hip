@@ -1009,6 +1009,9 @@ __device__ __forceinline__ void dma_1k(const uint8_t *src_lane, uint32_t lds_dst
                  : "memory", "m0");
 }
 
+// Per-mille weight shift of decode splits between even and odd XCDs.
+constexpr int64_t kXcdSkew = 40;
+
 // Wavefront priority (s_setprio takes an immediate, 0..3).
 __device__ __forceinline__ void set_prio(int p) {
     if (p >= 3) __builtin_amdgcn_s_setprio(3);
@@ -1355,8 +1358,20 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int hq = hk * GQ + h;
     const int items = a.items;
     const int64_t ng = a.n_quant / G;
-    const int64_t g0 = (int64_t)sp * a.groups_per_split;
-    const int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
+    // The stream's ng groups are shared among its splits in proportion to a
+    // weight per split: workgroups go to the eight XCDs in turn (block b to
+    // XCD b mod 8), and on MI355X the odd-numbered XCDs stream 4-10 % slower
+    // than the even ones, so splits whose block is odd get kXcdSkew per mille
+    // less than the average and even ones that much more.  Any weights give
+    // the same groups overall, so results do not depend on them.
+    const int64_t xbase = (int64_t)blockIdx.x - sp;     // block of split 0
+    const int64_t WE = 1000 + kXcdSkew, WO = 1000 - kXcdSkew;
+    auto cum = [&](int64_t k) {                         // weight of splits [0, k)
+        const int64_t odd = (xbase + k) / 2 - xbase / 2;
+        return (k - odd) * WE + odd * WO;
+    };
+    const int64_t wsum = cum(a.splits);
+    const int64_t g0 = ng * cum(sp) / wsum, g1 = ng * cum(sp + 1) / wsum;
     const int n_g = (int)(g1 - g0);             // groups of this split
 
     const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
