@@ -1437,12 +1437,15 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     // its priority as it advances (3 over its first quarter, down to 0 over
     // its last): lagging wavefronts are issued first and the splits finish
     // closer together.  (Results do not depend on it.)
-    int prio = 3;
+    int prio = 3, next_at = (n_g + 3) / 4;     // priority 3 - floor(4 g / n_g)
     set_prio(prio);
     for (int g = 0; g < n_g; g++) {
-        if (const int want = 3 - (4 * g) / n_g; want != prio) {
-            prio = want;
-            set_prio(want);
+        if (g == next_at) {
+            while (prio > 0 && g == next_at) {
+                prio--;
+                next_at = (n_g * (4 - prio) + 3) / 4;
+            }
+            set_prio(prio);
         }
         if (issued < n_g) {
             issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
