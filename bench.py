@@ -428,7 +428,7 @@ def main():
                   " 1 GiB eviction read before each phase (outside the phase events)"
                   if not args.no_evict else "HIP events, no eviction (warm)",
     }
-    if args.attn_queries > 0 and n_out == 0:
+    if args.attn_queries > 0:
         rec["attn"] = attn_measure(cache, B, Hq, n, args.attn_queries, stream, evict, evict_out,
                                    not args.no_evict)
     if args.stream_steps > 0:

@@ -87,7 +87,7 @@ typedef struct {
     int32_t key_outliers; /* 0..3: per 32-token key group, this many channels  */
                           /* (the largest max |K|) kept in fp16; 2 is the    */
                           /* notebook's "top 1%" of 128.  > 0 needs G = 32   */
-                          /* and the window policy, and decode only          */
+                          /* and the window policy                           */
     int64_t max_tokens;   /* capacity per stream, >= 1                        */
 } kivi_config;
 
@@ -228,7 +228,8 @@ kivi_status kivi_append_decode(kivi_cache *c, const void *k, const void *v, int6
    the queries are the last T cached tokens (appended before the call, as in
    [RV] 1.3), so query t sees tokens 0 .. n - T + t; needs T <= n.  T = 1
    without the mask is the decode step.  Query head hq reads KV head
-   hq / (Hq / H).
+   hq / (Hq / H).  With outlier-aware keys, K_hat of a key group's kept
+   channels is their fp16 value from the block's record.
    q: device [B][Hq][T][D] in q_dtype; out: device float32 [B][Hq][T][D];
    softmax_scale <= 0 selects 1/sqrt(D); workspace: device, ws_bytes >=
    kivi_attn_workspace_bytes(c, T) (may be 0, then workspace may be NULL).

@@ -558,7 +558,7 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     if (causal != 0 && causal != 1) return KIVI_ERR_INVALID_ARG;
     if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
     if (causal && T > c->n) return KIVI_ERR_INVALID_ARG;
-    if (c->cfg.policy == KIVI_FLUSH_PAPER || c->cfg.key_outliers > 0) return KIVI_ERR_UNSUPPORTED;
+    if (c->cfg.policy == KIVI_FLUSH_PAPER) return KIVI_ERR_UNSUPPORTED;
     if (c->cfg.kv_dtype != KIVI_F16 && c->n > c->q) return KIVI_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)c->cfg.batch * c->cfg.n_q_heads * T;
     if (rows > 0x7FFFFFFF) return KIVI_ERR_UNSUPPORTED;
@@ -591,6 +591,8 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     a.groups_per_split = gps;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)c->cfg.head_dim);
     a.sm_log2 = scale * 1.4426950408889634f;
+    a.n_out = c->cfg.key_outliers;
+    a.outliers = c->cfg.key_outliers > 0 ? c->base + c->off_outliers : nullptr;
     if (launch_attn(a, stream) != hipSuccess) return KIVI_ERR_HIP;
     return KIVI_OK;
 }

@@ -111,6 +111,8 @@ struct AttnArgs {
     int32_t splits;             // group ranges per (stream, query block)
     int32_t groups_per_split;
     float sm_log2;              // softmax scale * log2(e)
+    int32_t n_out;              // outlier-aware keys: channels per key group kept in fp16
+    const uint8_t *outliers;    // [streams][max_groups][kOutlierRecordBytes] (n_out > 0)
 };
 
 hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s);

@@ -1905,14 +1905,15 @@ __device__ __forceinline__ void mask_scores(f4 &S0, f4 &S1, int64_t tok0, int Gl
     }
 }
 
-template <int BITS, int GQ, bool QF32, int CB>
-__global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
+template <int BITS, int GQ, bool QF32, int CB, bool OUT = false>
+__global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kernel(AttnArgs a) {
     using PP = Pipe<BITS>;
     constexpr int W = kAttnWaves;
     constexpr int QT = 16 / GQ;                 // queries per column block
     constexpr int DPL = 2 * BITS;
     constexpr int VTS = 40;                     // fp16 per transposed value row (80 B)
-    __shared__ __attribute__((aligned(16))) uint8_t ring[PP::NST * PP::BB];
+    constexpr int SB = stage_bytes<BITS, OUT>();   // block (+ outlier record)
+    __shared__ __attribute__((aligned(16))) uint8_t ring[PP::NST * SB];
     __shared__ uint4 qs[W][CB][4][64];          // unscaled fp16 q, B-operand order
     __shared__ __attribute__((aligned(16))) _Float16 vt[D * VTS];
 
@@ -1948,6 +1949,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
     const int n_g = g1 > g0 ? (int)(g1 - g0) : 0;
 
     const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
+    const uint8_t *srec = OUT ? a.outliers + ((int64_t)stream * a.max_groups + g0) * kOutlierRecordBytes
+                              : nullptr;
     const uint32_t rbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
     h2 qB[CB][4][4];
 #pragma unroll
@@ -1959,8 +1962,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
     int issued = 0, is = 0, rs = 0;
     if (w == 0) {
         for (; issued < PP::NST - 1 && issued < n_g; issued++) {
-            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, nullptr, rbase + (uint32_t)is * PP::BB,
-                              l);
+            issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
+                                   OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                                   rbase + (uint32_t)is * SB, l);
             is = is + 1 == PP::NST ? 0 : is + 1;
         }
     }
@@ -2009,15 +2013,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
     const float csq = a.sm_log2 * kTwo24;
 
     for (int g = 0; g < n_g; g++) {
-        if (w == 0) wait_groups_after<BITS>(issued - 1 - g);
+        if (w == 0) wait_groups_after<BITS, OUT>(issued - 1 - g);
         __syncthreads();            // group g landed; every wave is done with g - 1
         if (w == 0 && issued < n_g) {
-            issue_group<BITS>(sblk + (int64_t)issued * PP::BB, nullptr, rbase + (uint32_t)is * PP::BB,
-                              l);
+            issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
+                                   OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                                   rbase + (uint32_t)is * SB, l);
             is = is + 1 == PP::NST ? 0 : is + 1;
             issued++;
         }
-        const uint8_t *stg = ring + rs * PP::BB;
+        const uint8_t *stg = ring + rs * SB;
         rs = rs + 1 == PP::NST ? 0 : rs + 1;
         if (!wave_ok) continue;
         const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
@@ -2065,6 +2070,34 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(AttnArgs a) {
                 S1[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, S1[c], 0, 0, 0);
                 S0[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, S0[c], 0, 0, 0);
                 S1[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S1[c], 0, 0, 0);
+            }
+        }
+        if constexpr (OUT) {
+            // key channels kept in fp16 (codes, scale and zero 0): add q . K
+            // over them from the record, in the scores' units of 2^24.  q of
+            // column j at channel ch sits in the unscaled B operand of step
+            // ch / 32, lane j + 16 ((ch % 32) / 8), element ch % 8.
+            const uint2 idx = *(const uint2 *)(stg + PP::BB);
+            const int ch[kMaxKeyOutliers] = {(int)(idx.x & 0xFFFFu), (int)(idx.x >> 16),
+                                             (int)(idx.y & 0xFFFFu)};
+            const _Float16 *rval = (const _Float16 *)(stg + PP::BB + 16);
+#pragma unroll
+            for (int o = 0; o < kMaxKeyOutliers; o++) {
+                if (o < a.n_out) {
+                    const int co = ch[o];
+                    const int qe = ((co >> 5) * 64 + j + 16 * ((co >> 3) & 3)) * 8 + (co & 7);
+                    const h2 *v0 = (const h2 *)(rval + G * o + 4 * Gl);
+                    const h2 *v1 = (const h2 *)(rval + G * o + 16 + 4 * Gl);
+#pragma unroll
+                    for (int c = 0; c < CB; c++) {
+                        const float qo = (float)((const _Float16 *)&qs[w][c][0][0])[qe] * kTwoM24;
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            S0[c][e] = __builtin_fmaf(qo, (float)v0[e >> 1][e & 1], S0[c][e]);
+                            S1[c][e] = __builtin_fmaf(qo, (float)v1[e >> 1][e & 1], S1[c][e]);
+                        }
+                    }
+                }
             }
         }
         const int64_t tok0 = (g0 + g) * G;
@@ -2352,12 +2385,20 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int BITS, bool QF32, bool OUT>
+static void launch_attn_out(const AttnArgs &a, int gq, dim3 grid, hipStream_t s) {
+    const dim3 block(64 * kAttnWaves);
+    if (gq == 4)
+        hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32, kAttnBlocks, OUT>), grid, block, 0, s, a);
+    else if (gq == 2)
+        hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32, kAttnBlocks, OUT>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32, kAttnBlocks, OUT>), grid, block, 0, s, a);
+}
+
 template <int BITS, bool QF32>
 static void launch_attn_bits(const AttnArgs &a, int gq, dim3 grid, hipStream_t s) {
-    const dim3 block(64 * kAttnWaves);
-    if (gq == 4) hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32, kAttnBlocks>), grid, block, 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32, kAttnBlocks>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32, kAttnBlocks>), grid, block, 0, s, a);
+    if (a.n_out > 0) launch_attn_out<BITS, QF32, true>(a, gq, grid, s);
+    else launch_attn_out<BITS, QF32, false>(a, gq, grid, s);
 }
 
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
@@ -2366,6 +2407,8 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
     const int64_t workgroups = streams * a.qblocks * a.splits;
     const int64_t rows = (int64_t)a.batch * a.q_heads * a.T;
     if (a.splits < 1 || a.splits > kMaxItems || workgroups > 0x7FFFFFFF || rows > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && !a.outliers))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)workgroups);
     if (a.bits == 2) {

@@ -3,8 +3,8 @@ item 2: keep the top 1% of K channels at fp16), read per 32-token key
 group: the n channels with the largest max |K| keep fp16 values in the
 block's record, with codes, zero and scale 0.  Bit-exact against the oracle:
 packed blocks, outlier records, ring, n and Q; decode attention (split items
-add q . K over the kept channels) within 2e-3 of the oracle's attention over
-the same dequantized cache."""
+add q . K over the kept channels) and the attention of T queries within 2e-3
+of the oracle's attention over the same dequantized cache."""
 import numpy as np
 import pytest
 
@@ -93,13 +93,52 @@ def test_outliers_ties_and_notebook(orc):
     assert e <= TOL
 
 
-def test_outliers_attn_unsupported(orc):
-    import torch
+def _attn(orc, B, H, Hq, n, T, bits, R, causal, n_out, seed, q_dtype=np.float16, label=""):
     from kv_cache_quantization_amd import kivi, synth
-    from kv_cache_quantization_amd import KiviError
-    k, v = synth.kv_host(92, 1, 1, 100)
-    cache = new_cache(1, 1, 4, 128, bits=2, R=32, key_outliers=2)
+    k, v = synth.kv_host(seed, B, H, n)
+    q = synth.queries_multi_host(seed, B, Hq, T, dtype=q_dtype)
+    cache = new_cache(B, H, Hq, n + 64, bits=bits, R=R, key_outliers=n_out)
     cache.append(to_dev(k), to_dev(v))
-    with pytest.raises(KiviError) as e:
-        cache.attn(torch.zeros((1, 4, 2, 128), dtype=torch.float16, device="cuda"))
-    assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+    plan = kivi.kivi_attn_plan(cache.handle, T)
+    log("case %s: B=%d H=%d Hq=%d n=%d T=%d bits=%d R=%d causal=%d outliers=%d plan=%s" %
+        (label, B, H, Hq, n, T, bits, R, causal, n_out, plan))
+    out = cache.attn(to_dev(q), causal=causal).cpu().numpy()
+    ref_cache = orc.build_cache(k, v, bits, 32, R, 0, n_out)
+    kh, vh = orc.dequant_cache(k, v, ref_cache)
+    ref = orc.attn_queries(q, kh, vh, causal)
+    e = rel_err(out, ref)
+    log("  attn rel err %.3g" % e)
+    assert np.isfinite(out).all(), label
+    assert e <= TOL, (label, e)
+
+
+@pytest.mark.parametrize("n,T,bits,R,gq,causal,n_out", [
+    (1000, 300, 2, 128, 4, 1, 2),    # causal mask in quantized groups and the residual
+    (4096, 16, 4, 32, 2, 0, 1),      # split ranges + combine
+    (700, 33, 8, 64, 1, 1, 3),       # padding columns, 8-bit codes
+])
+def test_outliers_attn(orc, n, T, bits, R, gq, causal, n_out):
+    """The attention of T queries adds q . K over the kept channels of each
+    key group, per query column."""
+    _attn(orc, 2, 2, 2 * gq, n, T, bits, R, causal, n_out, seed=n + T,
+          label="out-attn-%d-%d" % (n, T))
+
+
+def test_outliers_attn_fp32_queries_notebook(orc):
+    """float32 queries; the notebook's fp32 data (no residual) attended by all
+    1024 of its query rows with two kept channels per key group."""
+    from kv_cache_quantization_amd import synth
+    _attn(orc, 1, 2, 8, 500, 40, 2, 64, 1, 2, seed=93, q_dtype=np.float32,
+          label="out-attn-fp32q")
+    import torch
+    K, V, _ = synth.notebook_inputs()
+    Q = torch.randn(1, 1024, 128, generator=torch.Generator().manual_seed(1)).numpy()
+    Q = Q.reshape(1, 1, 1024, 128).astype(np.float32)
+    cache = new_cache(1, 1, 1, 1024, bits=2, R=0, dtype=np.float32, key_outliers=2)
+    cache.append(to_dev(K), to_dev(V))
+    out = cache.attn(to_dev(Q)).cpu().numpy()
+    ref_cache = orc.build_cache(K, V, 2, 32, 0, 0, 2)
+    kh, vh = orc.dequant_cache(K, V, ref_cache)
+    e = rel_err(out, orc.attn_queries(Q, kh, vh, 0))
+    log("  notebook attn (1024 queries, 2 kept channels) rel err %.3g" % e)
+    assert e <= TOL
