@@ -558,15 +558,18 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     if (causal != 0 && causal != 1) return KIVI_ERR_INVALID_ARG;
     if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
     if (causal && T > c->n) return KIVI_ERR_INVALID_ARG;
-    if (c->cfg.policy == KIVI_FLUSH_PAPER) return KIVI_ERR_UNSUPPORTED;
-    if (c->cfg.kv_dtype != KIVI_F16 && c->n > c->q) return KIVI_ERR_UNSUPPORTED;
+    // a float32 ring is not read by the attention kernel: no residual tokens,
+    // and (paper policy) no groups whose values continue in the ring
+    const int64_t q_full = ring_low(c->cfg, c->qv);     // groups with value codes
+    if (c->cfg.kv_dtype != KIVI_F16 && (c->n > c->q || q_full < c->q))
+        return KIVI_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)c->cfg.batch * c->cfg.n_q_heads * T;
     if (rows > 0x7FFFFFFF) return KIVI_ERR_UNSUPPORTED;
     const size_t need = kivi_attn_workspace_bytes(c, T);
     if (need > 0 && (!workspace || ws_bytes < need)) return KIVI_ERR_BUFFER_TOO_SMALL;
     AttnArgs a;
     int32_t qblocks, splits, gps;
-    attn_plan(c, T, c->q, &qblocks, &splits, &gps);
+    attn_plan(c, T, q_full, &qblocks, &splits, &gps);
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
     a.block_bytes = c->block_bytes;
@@ -584,6 +587,7 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     a.bits = c->cfg.bits;
     a.n_tokens = c->n;
     a.n_quant = c->q;
+    a.n_vquant = c->qv;
     a.T = T;
     a.causal = causal;
     a.qblocks = qblocks;
@@ -600,7 +604,7 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
 kivi_status kivi_attn_plan(const kivi_cache *c, int64_t T, int32_t *qblocks, int32_t *splits,
                            int32_t *groups_per_split) {
     if (!c || T < 1 || !qblocks || !splits || !groups_per_split) return KIVI_ERR_INVALID_ARG;
-    attn_plan(c, T, c->q, qblocks, splits, groups_per_split);
+    attn_plan(c, T, ring_low(c->cfg, c->qv), qblocks, splits, groups_per_split);
     return KIVI_OK;
 }
 

@@ -104,7 +104,8 @@ struct AttnArgs {
     float *part_ml;             // [B*Hq*T][splits][2]  (m log2, l)
     int32_t batch, kv_heads, q_heads;
     int32_t bits;
-    int64_t n_tokens, n_quant;  // n, Q(n)
+    int64_t n_tokens, n_quant;  // n, Q(n) (Q_K under the paper policy)
+    int64_t n_vquant;           // value tokens quantized (Q_V; = n_quant, window policy)
     int64_t T;                  // queries per (batch, query head)
     int32_t causal;             // query t is token n - T + t and sees tokens <= it
     int32_t qblocks;            // query blocks per stream

@@ -1942,9 +1942,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
         pq[c] = a.causal ? n - T + qi[c] : n - 1;             // last token the column sees
     }
 
+    // groups with key and value codes: [0, ngv); under the paper policy the
+    // groups [ngv, ng) have key codes and value codes below n_vquant only
     const int64_t ng = a.n_quant / G;
+    const int64_t ngv = (a.n_vquant < a.n_quant ? a.n_vquant : a.n_quant) / G;
     const int64_t g0 = (int64_t)split * a.groups_per_split;
-    int64_t g1 = g0 + a.groups_per_split < ng ? g0 + a.groups_per_split : ng;
+    int64_t g1 = g0 + a.groups_per_split < ngv ? g0 + a.groups_per_split : ngv;
     if (g1 > pq_wg / G + 1) g1 = pq_wg / G + 1;        // groups past every query
     const int n_g = g1 > g0 ? (int)(g1 - g0) : 0;
 
@@ -2012,32 +2015,18 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
     }
     const float csq = a.sm_log2 * kTwo24;
 
-    for (int g = 0; g < n_g; g++) {
-        if (w == 0) wait_groups_after<BITS, OUT>(issued - 1 - g);
-        __syncthreads();            // group g landed; every wave is done with g - 1
-        if (w == 0 && issued < n_g) {
-            issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
-                                   OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
-                                   rbase + (uint32_t)is * SB, l);
-            is = is + 1 == PP::NST ? 0 : is + 1;
-            issued++;
-        }
-        const uint8_t *stg = ring + rs * SB;
-        rs = rs + 1 == PP::NST ? 0 : rs + 1;
-        if (!wave_ok) continue;
+    // Scores of the 32 tokens of the block at stg against every column:
+    // key-zero bias (every row of a column holds it), the code products (each
+    // key operand unpacked once for all column blocks) and, with outlier-aware
+    // keys, q . K over the kept channels.  Units of 2^-24 (csq converts).
+    auto block_scores = [&](const uint8_t *stg, f4 (&Sk)[CB], f4 (&S0)[CB], f4 (&S1)[CB]) {
         const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
-        const uint2 *s2 = (const uint2 *)side;
-        uint32_t kc[DPL], vc[DPL];
+        uint32_t kc[DPL];
 #pragma unroll
         for (int w4 = 0; w4 < BITS / 2; w4++) {
             const uint4 u = *(const uint4 *)(stg + w4 * 1024 + 16 * l);
-            const uint4 v = *(const uint4 *)(stg + PP::CB + w4 * 1024 + 16 * l);
             kc[4 * w4] = u.x; kc[4 * w4 + 1] = u.y; kc[4 * w4 + 2] = u.z; kc[4 * w4 + 3] = u.w;
-            vc[4 * w4] = v.x; vc[4 * w4 + 1] = v.y; vc[4 * w4 + 2] = v.z; vc[4 * w4 + 3] = v.w;
         }
-        // key-zero bias (every row of a column holds it), then the code
-        // products: each key operand is unpacked once for all column blocks
-        f4 Sk[CB], S0[CB], S1[CB];
 #pragma unroll
         for (int c = 0; c < CB; c++) {
             Sk[c] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -2100,6 +2089,31 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
                 }
             }
         }
+    };
+
+    for (int g = 0; g < n_g; g++) {
+        if (w == 0) wait_groups_after<BITS, OUT>(issued - 1 - g);
+        __syncthreads();            // group g landed; every wave is done with g - 1
+        if (w == 0 && issued < n_g) {
+            issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
+                                   OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                                   rbase + (uint32_t)is * SB, l);
+            is = is + 1 == PP::NST ? 0 : is + 1;
+            issued++;
+        }
+        const uint8_t *stg = ring + rs * SB;
+        rs = rs + 1 == PP::NST ? 0 : rs + 1;
+        if (!wave_ok) continue;
+        const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
+        const uint2 *s2 = (const uint2 *)side;
+        uint32_t vc[DPL];
+#pragma unroll
+        for (int w4 = 0; w4 < BITS / 2; w4++) {
+            const uint4 v = *(const uint4 *)(stg + PP::CB + w4 * 1024 + 16 * l);
+            vc[4 * w4] = v.x; vc[4 * w4 + 1] = v.y; vc[4 * w4 + 2] = v.z; vc[4 * w4 + 3] = v.w;
+        }
+        f4 Sk[CB], S0[CB], S1[CB];
+        block_scores(stg, Sk, S0, S1);
         const int64_t tok0 = (g0 + g) * G;
         const bool masked = tok0 + G - 1 > pq_wave;
         h2 Pc[CB][4];
@@ -2149,6 +2163,72 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
     for (int c = 0; c < CB; c++)
 #pragma unroll
         for (int o = 0; o < 8; o++) accV[c][o] *= kTwo24;
+
+    // Paper policy: the last split walks the groups [ngv, ng), whose keys are
+    // codes but whose values are codes only below n_vquant (in the first of
+    // them; at most 31 tokens) and ring rows from there on.  Per group the
+    // workgroup copies the block into ring stage 0 and stages the 32 value
+    // rows transposed in LDS, the coded ones as fp16 of code * scale + zero
+    // (float32, two roundings, then one to fp16); each wavefront computes the
+    // scores from the key codes as in the loop above and p . V from LDS as in
+    // the residual below.
+    if (split == a.splits - 1 && ng > ngv) {
+        constexpr uint32_t M1 = (1u << BITS) - 1u;
+        const _Float16 *rvh = (const _Float16 *)a.ring_v + (int64_t)stream * a.ring_cap * D;
+        for (int64_t gm = ngv; gm < ng && gm * G <= pq_wg; gm++) {
+            const int64_t tok0 = gm * G;
+            __syncthreads();        // stage 0 and the transposed rows are free
+            const uint4 *blk =
+                (const uint4 *)(a.blocks + ((int64_t)stream * a.max_groups + gm) * a.block_bytes);
+            for (int i = threadIdx.x; i < PP::BB / 16; i += 64 * W) ((uint4 *)ring)[i] = blk[i];
+            __syncthreads();
+            {
+#pragma clang fp contract(off)
+                const uint32_t *vcode = (const uint32_t *)(ring + PP::CB);
+                const _Float16 *sd = (const _Float16 *)(ring + 2 * PP::CB);
+                for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
+                    const int r = idx / D, c = idx % D;
+                    const int64_t t = tok0 + r;
+                    _Float16 v;
+                    if (t < a.n_vquant) {
+                        int dw, bit;
+                        code_pos<BITS>(true, r, c, dw, bit);
+                        const float vs = (float)sd[2 * D + (c / G) * G + r];
+                        const float vz = (float)sd[3 * D + (c / G) * G + r];
+                        v = (_Float16)((float)((vcode[dw] >> bit) & M1) * vs + vz);
+                    } else {
+                        v = rvh[(t % a.ring_cap) * D + c];
+                    }
+                    vt[c * VTS + r] = v;
+                }
+            }
+            __syncthreads();
+            if (!wave_ok) continue;
+            f4 Sk[CB], S0[CB], S1[CB];
+            block_scores(ring, Sk, S0, S1);
+            h8 Bp[CB];
+#pragma unroll
+            for (int c = 0; c < CB; c++) {
+                if (tok0 + G - 1 > pq_wave) mask_scores(S0[c], S1[c], tok0, Gl, G, pq[c]);
+                h2 Ps[4];
+                attn_softmax(S0[c], S1[c], csq, Sk[c][0] * a.sm_log2, m_run[c], m_thr[c], nm[c],
+                             Lsum[c], Vz[c], accV[c], Ps);
+                Bp[c] = pack_h8(Ps);
+                Lsum[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bp[c], Lsum[c], 0, 0, 0);
+            }
+#pragma unroll
+            for (int o = 0; o < 8; o++) {
+                const _Float16 *row = vt + (16 * o + j) * VTS;
+                const uint2 v0 = *(const uint2 *)(row + 4 * Gl);
+                const uint2 v1 = *(const uint2 *)(row + 16 + 4 * Gl);
+                const uint4 vv = {v0.x, v0.y, v1.x, v1.y};
+#pragma unroll
+                for (int c = 0; c < CB; c++)
+                    accV[c][o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, vv),
+                                                                       Bp[c], accV[c][o], 0, 0, 0);
+            }
+        }
+    }
 
     // The last split walks the fp16 residual [Q, n) in 32-token chunks: the
     // workgroup stages the chunk's value rows transposed in LDS (channel
