@@ -1799,53 +1799,71 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 // Merge the partials of one output row (a (batch, query head) of the decode
 // step, or a (batch, query head, query) of the attention of T queries):
 // part_o [rows][items][D], part_ml [rows][items][2].  The weights 2^(m_s - M)
-// are computed once in LDS; each thread then sums one channel.
+// are computed once in LDS.  Thread t sums channel t % D over the items
+// s = t / D (mod kCombineParts), four loads in flight; the parts are added in
+// LDS.  (A row is latency-bound: the parts shorten its chain of loads.)
 constexpr int kMaxItems = 4160;
+constexpr int kCombineParts = 4;
+constexpr int kCombineThreads = D * kCombineParts;
 
-__global__ __launch_bounds__(128) void combine_rows_kernel(const float *part_o,
-                                                           const float *part_ml, float *out,
-                                                           int items) {
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(const float *part_o,
+                                                                       const float *part_ml,
+                                                                       float *out, int items) {
+    constexpr int NW = kCombineThreads / 64;
     __shared__ float w[kMaxItems];
-    __shared__ float red[128];
+    __shared__ float red[NW];
+    __shared__ float acc_s[kCombineThreads];
     const int64_t row = blockIdx.x;
-    const int c = threadIdx.x;
+    const int t = threadIdx.x, wv = t >> 6;
     const float *ml = part_ml + row * items * 2;
     float M = -INFINITY;
-    for (int s = c; s < items; s += 128)
+    for (int s = t; s < items; s += kCombineThreads)
         if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
-    red[c] = M;
+    M = wave_max(M);
+    if ((t & 63) == 0) red[wv] = M;
     __syncthreads();
-    for (int off = 64; off > 0; off >>= 1) {
-        if (c < off) red[c] = fmaxf(red[c], red[c + off]);
-        __syncthreads();
-    }
     M = red[0];
-    __syncthreads();
+#pragma unroll
+    for (int i = 1; i < NW; i++) M = fmaxf(M, red[i]);
+    __syncthreads();                            // red is reused below
     float Lp = 0.f;
-    for (int s = c; s < items; s += 128) {
+    for (int s = t; s < items; s += kCombineThreads) {
         const float ls = ml[2 * s + 1];
         const float ws = ls > 0.f ? __builtin_amdgcn_exp2f(ml[2 * s] - M) : 0.f;
         w[s] = ws;
         Lp = __builtin_fmaf(ls, ws, Lp);
     }
-    red[c] = Lp;
-    __syncthreads();
-    for (int off = 64; off > 0; off >>= 1) {
-        if (c < off) red[c] += red[c + off];
-        __syncthreads();
-    }
-    const float L = red[0];
+    Lp = wave_sum(Lp);
+    if ((t & 63) == 0) red[wv] = Lp;
+    __syncthreads();                            // w and red are complete
+    float L = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; i++) L += red[i];
+    const int c = t % D, part = t / D;
     const float *po = part_o + row * items * D + c;
     float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-    int s = 0;
-    for (; s + 4 <= items; s += 4) {
+    constexpr int P = kCombineParts;
+    int s = part;
+    for (; s + 3 * P < items; s += 4 * P) {
         acc0 = __builtin_fmaf(po[(int64_t)s * D], w[s], acc0);
-        acc1 = __builtin_fmaf(po[(int64_t)(s + 1) * D], w[s + 1], acc1);
-        acc2 = __builtin_fmaf(po[(int64_t)(s + 2) * D], w[s + 2], acc2);
-        acc3 = __builtin_fmaf(po[(int64_t)(s + 3) * D], w[s + 3], acc3);
+        acc1 = __builtin_fmaf(po[(int64_t)(s + P) * D], w[s + P], acc1);
+        acc2 = __builtin_fmaf(po[(int64_t)(s + 2 * P) * D], w[s + 2 * P], acc2);
+        acc3 = __builtin_fmaf(po[(int64_t)(s + 3 * P) * D], w[s + 3 * P], acc3);
     }
-    for (; s < items; s++) acc0 = __builtin_fmaf(po[(int64_t)s * D], w[s], acc0);
-    out[row * D + c] = ((acc0 + acc1) + (acc2 + acc3)) / L;
+    for (; s < items; s += P) acc0 = __builtin_fmaf(po[(int64_t)s * D], w[s], acc0);
+    acc_s[t] = (acc0 + acc1) + (acc2 + acc3);
+    __syncthreads();
+    if (part == 0) {
+        float acc = acc_s[c];
+#pragma unroll
+        for (int i = 1; i < P; i++) acc += acc_s[c + i * D];
+        out[row * D + c] = acc / L;
+    }
 }
 
 // ===========================================================================
@@ -2460,7 +2478,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     else launch_decode_bits<4>(a, gq, grid, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)(a.batch * a.q_heads)), dim3(128), 0,
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)(a.batch * a.q_heads)), dim3(kCombineThreads), 0,
                        s, (const float *)a.part_o, (const float *)a.part_ml, a.out, a.items);
     return hipGetLastError();
 }
@@ -2503,7 +2521,7 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)rows), dim3(128), 0, s,
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0, s,
                        (const float *)a.part_o, (const float *)a.part_ml, a.out, a.splits);
     return hipGetLastError();
 }
