@@ -59,8 +59,7 @@ typedef enum { KIVI_F16 = 0, KIVI_F32 = 1 } kivi_dtype;
    prefill / decoding phases of Algorithm 1 in 3.2.3: the key residual is
    quantized R tokens at once when it fills up, the oldest value of the
    residual one token per step).  In the 32-token block holding Q_V the value codes
-   and side data of tokens >= Q_V are 0.  kivi_attn supports only the window
-   policy. */
+   and side data of tokens >= Q_V are 0. */
 typedef enum { KIVI_FLUSH_WINDOW = 0, KIVI_FLUSH_PAPER = 1 } kivi_flush_policy;
 
 /* kivi_append flags. */
@@ -87,7 +86,6 @@ typedef struct {
     int32_t key_outliers; /* 0..3: per 32-token key group, this many channels  */
                           /* (the largest max |K|) kept in fp16; 2 is the    */
                           /* notebook's "top 1%" of 128.  > 0 needs G = 32   */
-                          /* and the window policy                           */
     int64_t max_tokens;   /* capacity per stream, >= 1                        */
 } kivi_config;
 

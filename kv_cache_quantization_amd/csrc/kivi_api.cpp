@@ -74,9 +74,8 @@ kivi_status validate(const kivi_config *c) {
         return KIVI_ERR_UNSUPPORTED;
     const int gq = c->n_q_heads / c->n_kv_heads;
     if (gq != 1 && gq != 2 && gq != 4) return KIVI_ERR_UNSUPPORTED;
-    // outlier-aware keys: built for 32-token key groups under the window policy
-    if (c->key_outliers > 0 && (c->group != kGroup || c->policy != KIVI_FLUSH_WINDOW))
-        return KIVI_ERR_UNSUPPORTED;
+    // outlier-aware keys: built for 32-token key groups
+    if (c->key_outliers > 0 && c->group != kGroup) return KIVI_ERR_UNSUPPORTED;
     if ((int64_t)c->batch * c->n_kv_heads > (1LL << 24)) return KIVI_ERR_UNSUPPORTED;
     return KIVI_OK;
 }

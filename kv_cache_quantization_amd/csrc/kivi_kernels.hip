@@ -1581,10 +1581,11 @@ __device__ __forceinline__ void code_pos(bool is_v, int t, int c, int &dw, int &
 // item's running state like a residual chunk; p.V runs on the vector ALUs,
 // lane l owning channels 2l, 2l+1, with V-hat = code * scale, then + zero,
 // in float32 for tokens below n_vquant and the ring's rows for the others.
-template <int BITS, int GQ, bool RF32, bool QF32>
+template <int BITS, int GQ, bool RF32, bool QF32, bool OUT>
 __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t *lds,
                                uint4 *q_lds) {
     using PP = Pipe<BITS>;
+    constexpr int SB = stage_bytes<BITS, OUT>();
     constexpr uint32_t M1 = (1u << BITS) - 1u;
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
@@ -1592,7 +1593,7 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * (RF32 ? 4 : 2);
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
-    float *p_lds = (float *)(lds + PP::BB);           // [GQ][G]
+    float *p_lds = (float *)(lds + SB);               // [GQ][G]
     h2 qB[4][4];
     load_q_operand<QF32>(a.q, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
     {
@@ -1632,6 +1633,9 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
 #pragma unroll
         for (int cc = 0; cc < PP::DPG; cc++)
             dma_1k(blk + cc * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(lbase + cc * 1024));
+        if constexpr (OUT)
+            dma_256(a.outliers + ((int64_t)stream * a.max_groups + g) * kOutlierRecordBytes + 4 * l,
+                    __builtin_amdgcn_readfirstlane(lbase + PP::BB));
         // the group's value rows from the ring (slots of tokens below
         // n_vquant may hold other tokens: those rows are not used)
         float2 vr[G];
@@ -1677,6 +1681,28 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
             S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, S[1], 0, 0, 0);
             S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, S[0], 0, 0, 0);
             S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, S[1], 0, 0, 0);
+        }
+        if constexpr (OUT) {
+            // key channels kept in fp16: q . K over them from the record, in
+            // the scores' units of 2^24 (as in decode_split)
+            const uint2 idx = *(const uint2 *)(stg + PP::BB);
+            const int ch[kMaxKeyOutliers] = {(int)(idx.x & 0xFFFFu), (int)(idx.x >> 16),
+                                             (int)(idx.y & 0xFFFFu)};
+            const _Float16 *rval = (const _Float16 *)(stg + PP::BB + 16);
+            const _Float16 *q16 = (const _Float16 *)q_lds;      // [head][channel]
+#pragma unroll
+            for (int o = 0; o < kMaxKeyOutliers; o++) {
+                if (o < a.n_out) {
+                    const float qo = (float)q16[h * D + ch[o]] * kTwoM24;
+                    const h2 *v0 = (const h2 *)(rval + G * o + 4 * Gl);
+                    const h2 *v1 = (const h2 *)(rval + G * o + 16 + 4 * Gl);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        S[0][e] = __builtin_fmaf(qo, (float)v0[e >> 1][e & 1], S[0][e]);
+                        S[1][e] = __builtin_fmaf(qo, (float)v1[e >> 1][e & 1], S[1][e]);
+                    }
+                }
+            }
         }
         // lane (j, Gl) holds tokens 16t + 4Gl + e of column j (head j % GQ),
         // in log2 units after the scale and the key-zero bias
@@ -1757,18 +1783,18 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
 
 // A kernel of its own (one wavefront per (stream, mixed item)), so that its
 // registers do not count against the occupancy of decode_kernel.
-template <int BITS, int GQ>
+template <int BITS, int GQ, bool OUT>
 __global__ __launch_bounds__(64) void decode_mixed_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t blk[Pipe<BITS>::BB + GQ * G * 4];
+    __shared__ __attribute__((aligned(16))) uint8_t blk[stage_bytes<BITS, OUT>() + GQ * G * 4];
     __shared__ uint4 q_lds[64];
     const int streams = a.batch * a.kv_heads;
     const int stream = (int)(blockIdx.x % streams), mi = (int)(blockIdx.x / streams);
     if (a.ring_is_f32) {
-        if (a.q_is_f32) decode_mixed_t<BITS, GQ, true, true>(a, stream, mi, blk, q_lds);
-        else decode_mixed_t<BITS, GQ, true, false>(a, stream, mi, blk, q_lds);
+        if (a.q_is_f32) decode_mixed_t<BITS, GQ, true, true, OUT>(a, stream, mi, blk, q_lds);
+        else decode_mixed_t<BITS, GQ, true, false, OUT>(a, stream, mi, blk, q_lds);
     } else {
-        if (a.q_is_f32) decode_mixed_t<BITS, GQ, false, true>(a, stream, mi, blk, q_lds);
-        else decode_mixed_t<BITS, GQ, false, false>(a, stream, mi, blk, q_lds);
+        if (a.q_is_f32) decode_mixed_t<BITS, GQ, false, true, OUT>(a, stream, mi, blk, q_lds);
+        else decode_mixed_t<BITS, GQ, false, false, OUT>(a, stream, mi, blk, q_lds);
     }
 }
 
@@ -2199,6 +2225,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
             const uint4 *blk =
                 (const uint4 *)(a.blocks + ((int64_t)stream * a.max_groups + gm) * a.block_bytes);
             for (int i = threadIdx.x; i < PP::BB / 16; i += 64 * W) ((uint4 *)ring)[i] = blk[i];
+            if constexpr (OUT) {
+                const uint4 *rec = (const uint4 *)(a.outliers + ((int64_t)stream * a.max_groups + gm) *
+                                                                    kOutlierRecordBytes);
+                if (threadIdx.x < kOutlierRecordBytes / 16)
+                    ((uint4 *)(ring + PP::BB))[threadIdx.x] = rec[threadIdx.x];
+            }
             __syncthreads();
             {
 #pragma clang fp contract(off)
@@ -2433,11 +2465,17 @@ static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream
     else hipLaunchKernelGGL((decode_kernel<BITS, 1, OUT>), grid, dim3(64), 0, s, a);
 }
 
+template <int BITS, bool OUT>
+static void launch_mixed_out(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
+    if (gq == 4) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 4, OUT>), grid, dim3(64), 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 2, OUT>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_mixed_kernel<BITS, 1, OUT>), grid, dim3(64), 0, s, a);
+}
+
 template <int BITS>
 static void launch_mixed_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
-    if (gq == 4) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 4>), grid, dim3(64), 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 2>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((decode_mixed_kernel<BITS, 1>), grid, dim3(64), 0, s, a);
+    if (a.n_out > 0) launch_mixed_out<BITS, true>(a, gq, grid, s);
+    else launch_mixed_out<BITS, false>(a, gq, grid, s);
 }
 
 // decode_kernel: a.tail_items + a.splits items per stream (residual, splits)
@@ -2454,6 +2492,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
         return hipErrorInvalidValue;
     if (a.items != a.splits + a.tail_items + (a.mixed_groups > 0 ? a.mixed_items : 0))
         return hipErrorInvalidValue;
+    if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && !a.outliers))
+        return hipErrorInvalidValue;
     if (a.mixed_groups > 0) {
         if (a.mixed_items < 1 || a.mixed_step < 1 ||
             (int64_t)a.mixed_items * a.mixed_step < a.mixed_groups)
@@ -2466,9 +2506,6 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     dim3 grid((unsigned)items);
-    if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && !a.outliers))
-        return hipErrorInvalidValue;
-    if (a.n_out > 0 && a.mixed_groups > 0) return hipErrorInvalidValue;   // window policy only
     if (a.n_out > 0) {
         if (a.bits == 2) launch_decode_bits<2, true>(a, gq, grid, s);
         else if (a.bits == 8) launch_decode_bits<8, true>(a, gq, grid, s);

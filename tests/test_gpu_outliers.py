@@ -23,7 +23,7 @@ def _gpu():
 
 
 def _run(orc, B, H, Hq, n, bits, R, n_out, seed, chunks=None, dtype=np.float16,
-         q_dtype=np.float16, label="", k=None, v=None, fused=False):
+         q_dtype=np.float16, label="", k=None, v=None, fused=False, policy=0):
     from kv_cache_quantization_amd import synth
     log("case %s: B=%d H=%d Hq=%d n=%d bits=%d R=%d outliers=%d %s chunks=%s" %
         (label, B, H, Hq, n, bits, R, n_out, np.dtype(dtype).name,
@@ -31,7 +31,8 @@ def _run(orc, B, H, Hq, n, bits, R, n_out, seed, chunks=None, dtype=np.float16,
     if k is None:
         k, v = synth.kv_host(seed, B, H, n, dtype=dtype)
     q = synth.queries_host(seed, B, Hq, dtype=q_dtype)
-    cache = new_cache(B, H, Hq, n + 64, bits=bits, R=R, dtype=dtype, key_outliers=n_out)
+    cache = new_cache(B, H, Hq, n + 64, bits=bits, R=R, dtype=dtype, key_outliers=n_out,
+                      policy=policy)
     pos = 0
     chunks = chunks or [n]
     for i, c in enumerate(chunks):
@@ -44,7 +45,7 @@ def _run(orc, B, H, Hq, n, bits, R, n_out, seed, chunks=None, dtype=np.float16,
     check_cache(orc, cache, k, v, label=label)
     if not fused:
         out = cache.decode(to_dev(q)).cpu().numpy()
-    ref = oracle_decode(orc, k, v, q, bits, 32, R, key_outliers=n_out)
+    ref = oracle_decode(orc, k, v, q, bits, 32, R, key_outliers=n_out, policy=policy)
     e = rel_err(out, ref)
     log("  decode rel err %.3g" % e)
     assert e <= TOL, (label, e)
@@ -93,17 +94,18 @@ def test_outliers_ties_and_notebook(orc):
     assert e <= TOL
 
 
-def _attn(orc, B, H, Hq, n, T, bits, R, causal, n_out, seed, q_dtype=np.float16, label=""):
+def _attn(orc, B, H, Hq, n, T, bits, R, causal, n_out, seed, q_dtype=np.float16, label="",
+          policy=0):
     from kv_cache_quantization_amd import kivi, synth
     k, v = synth.kv_host(seed, B, H, n)
     q = synth.queries_multi_host(seed, B, Hq, T, dtype=q_dtype)
-    cache = new_cache(B, H, Hq, n + 64, bits=bits, R=R, key_outliers=n_out)
+    cache = new_cache(B, H, Hq, n + 64, bits=bits, R=R, key_outliers=n_out, policy=policy)
     cache.append(to_dev(k), to_dev(v))
     plan = kivi.kivi_attn_plan(cache.handle, T)
     log("case %s: B=%d H=%d Hq=%d n=%d T=%d bits=%d R=%d causal=%d outliers=%d plan=%s" %
         (label, B, H, Hq, n, T, bits, R, causal, n_out, plan))
     out = cache.attn(to_dev(q), causal=causal).cpu().numpy()
-    ref_cache = orc.build_cache(k, v, bits, 32, R, 0, n_out)
+    ref_cache = orc.build_cache(k, v, bits, 32, R, policy, n_out)
     kh, vh = orc.dequant_cache(k, v, ref_cache)
     ref = orc.attn_queries(q, kh, vh, causal)
     e = rel_err(out, ref)
@@ -142,3 +144,19 @@ def test_outliers_attn_fp32_queries_notebook(orc):
     e = rel_err(out, orc.attn_queries(Q, kh, vh, 0))
     log("  notebook attn (1024 queries, 2 kept channels) rel err %.3g" % e)
     assert e <= TOL
+
+
+PAPER = 1
+
+
+def test_outliers_paper_policy(orc):
+    """Outlier-aware keys under the paper's flush policy: key groups quantized
+    R tokens at a time carry records; the groups whose values continue in the
+    ring take the correction in decode_mixed_kernel and in the attention's
+    mixed pass.  Caches bit-exact, one-shot and streamed across key flushes."""
+    _run(orc, 2, 3, 12, 1000, 2, 128, 2, seed=95, label="out-paper", policy=PAPER)
+    _run(orc, 2, 2, 4, 700, 4, 64, 3, seed=96, chunks=[150] + [1] * 140 + [410],
+         label="out-paper-stream", policy=PAPER)
+    _attn(orc, 2, 2, 8, 2049, 16, 2, 128, 0, 2, seed=97, label="out-paper-attn", policy=PAPER)
+    _attn(orc, 2, 2, 8, 1000, 300, 8, 128, 1, 1, seed=98, label="out-paper-attn-causal",
+          policy=PAPER)
