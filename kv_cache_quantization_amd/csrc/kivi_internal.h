@@ -85,6 +85,7 @@ struct DecodeArgs {
     // ring.  in_from = INT64_MAX when every residual row is in the ring.
     const void *in_k, *in_v;
     int64_t in_n, in_from;
+    int32_t nt;                 // split items copy their blocks as non-temporal lines
 };
 
 // Attention of T queries per (batch, query head) over the cache.  One
