@@ -282,8 +282,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (every (batch, "
+              "KV-head) stream is independent, so sharding by batch or KV head needs no "
+              "communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
