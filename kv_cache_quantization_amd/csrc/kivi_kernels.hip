@@ -1979,7 +1979,10 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
     constexpr int DPL = 2 * BITS;
     constexpr int VTS = 40;                     // fp16 per transposed value row (80 B)
     constexpr int SB = stage_bytes<BITS, OUT>();   // block (+ outlier record)
-    __shared__ __attribute__((aligned(16))) uint8_t ring[PP::NST * SB];
+    // ring stages: the wavefronts meet at one barrier per two groups, with up
+    // to four groups in flight at 2 bits (two at 4 and 8 bits)
+    constexpr int AST = BITS == 2 ? 6 : 4;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[AST * SB];
     __shared__ uint4 qs[W][CB][4][64];          // unscaled fp16 q, B-operand order
     __shared__ __attribute__((aligned(16))) _Float16 vt[D * VTS];
 
@@ -2030,11 +2033,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
     }
     int issued = 0, is = 0, rs = 0;
     if (w == 0) {
-        for (; issued < PP::NST - 1 && issued < n_g; issued++) {
+        for (; issued < AST - 2 && issued < n_g; issued++) {
             issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
                                    OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
                                    rbase + (uint32_t)is * SB, l);
-            is = is + 1 == PP::NST ? 0 : is + 1;
+            is = is + 1 == AST ? 0 : is + 1;
         }
     }
 #pragma unroll
@@ -2158,17 +2161,31 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
     };
 
     for (int g = 0; g < n_g; g++) {
-        if (w == 0) wait_groups_after<BITS, OUT>(issued - 1 - g);
-        __syncthreads();            // group g landed; every wave is done with g - 1
-        if (w == 0 && issued < n_g) {
-            issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
-                                   OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
-                                   rbase + (uint32_t)is * SB, l);
-            is = is + 1 == PP::NST ? 0 : is + 1;
-            issued++;
+        if ((g & 1) == 0) {
+            // groups g and g + 1 landed; every wave is done with g - 1, so the
+            // stages up to group g - 1 + AST are free
+            const int last = g + 1 < n_g ? g + 1 : g;
+            if (w == 0) {
+                constexpr int P = Pipe<BITS>::DPG + (OUT ? 1 : 0);
+                const int r = issued - 1 - last;
+                if (r >= 4) wait_vm<4 * P>();
+                else if (r == 3) wait_vm<3 * P>();
+                else if (r == 2) wait_vm<2 * P>();
+                else if (r == 1) wait_vm<P>();
+                else wait_vm<0>();
+            }
+            __syncthreads();
+            if (w == 0) {
+                for (; issued < n_g && issued <= g + AST - 1; issued++) {
+                    issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
+                                           OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                                           rbase + (uint32_t)is * SB, l);
+                    is = is + 1 == AST ? 0 : is + 1;
+                }
+            }
         }
         const uint8_t *stg = ring + rs * SB;
-        rs = rs + 1 == PP::NST ? 0 : rs + 1;
+        rs = rs + 1 == AST ? 0 : rs + 1;
         if (!wave_ok) continue;
         const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
         const uint2 *s2 = (const uint2 *)side;
