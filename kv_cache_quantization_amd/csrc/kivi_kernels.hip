@@ -1025,7 +1025,7 @@ __device__ __forceinline__ void dma_1k(const uint8_t *src_lane, uint32_t lds_dst
 }
 
 // Per-mille weight shift of decode splits between even and odd XCDs.
-constexpr int64_t kXcdSkew = 40;
+constexpr int64_t kXcdSkew = 20;
 
 // Wavefront priority (s_setprio takes an immediate, 0..3).
 __device__ __forceinline__ void set_prio(int p) {
@@ -1381,8 +1381,9 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int64_t ng = a.n_quant / G;
     // The stream's ng groups are shared among its splits in proportion to a
     // weight per split: workgroups go to the eight XCDs in turn (block b to
-    // XCD b mod 8), and on MI355X the odd-numbered XCDs stream 4-10 % slower
-    // than the even ones, so splits whose block is odd get kXcdSkew per mille
+    // XCD b mod 8), and on MI355X the odd-numbered XCDs stream slower than the
+    // even ones (4-10 % with cached copies, about half that with the
+    // non-temporal ones), so splits whose block is odd get kXcdSkew per mille
     // less than the average and even ones that much more.  Any weights give
     // the same groups overall, so results do not depend on them.
     const int64_t xbase = (int64_t)blockIdx.x - sp;     // block of split 0
