@@ -86,6 +86,7 @@ struct DecodeArgs {
     const void *in_k, *in_v;
     int64_t in_n, in_from;
     int32_t nt;                 // split items copy their blocks as non-temporal lines
+    int32_t deep;               // 4 bits, no outliers: three-stage split items
 };
 
 // Attention of T queries per (batch, query head) over the cache.  One

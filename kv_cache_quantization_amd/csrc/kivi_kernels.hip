@@ -1315,16 +1315,17 @@ __device__ __forceinline__ constexpr int stage_bytes() {
     return Pipe<BITS>::BB + (OUT ? kOutlierRecordBytes : 0);
 }
 // Stages of the decode pipeline: with records, two at 2 bits as well, so
-// that a wavefront's LDS stays within 10 KiB (16 per compute unit).
-template <int BITS, bool OUT>
+// that a wavefront's LDS stays within 10 KiB (16 per compute unit).  DEEP
+// (4 bits, long passes): three, 15 KiB, 10 wavefronts per compute unit.
+template <int BITS, bool OUT, bool DEEP = false>
 __device__ __forceinline__ constexpr int decode_stages() {
-    return OUT ? 2 : Pipe<BITS>::NST;
+    return OUT ? 2 : DEEP ? 3 : Pipe<BITS>::NST;
 }
 // LDS of a decode wavefront besides q: the stages, and at least what a
 // residual item uses (32 fp16 value rows, then p of 4 heads x 32 tokens).
-template <int BITS, bool OUT>
+template <int BITS, bool OUT, bool DEEP = false>
 __device__ __forceinline__ constexpr int decode_lds_bytes() {
-    constexpr int st = decode_stages<BITS, OUT>() * stage_bytes<BITS, OUT>();
+    constexpr int st = decode_stages<BITS, OUT, DEEP>() * stage_bytes<BITS, OUT>();
     constexpr int tail = G * D * 2 + 4 * G * 4;
     return st > tail ? st : tail;
 }
@@ -1364,12 +1365,12 @@ __device__ __forceinline__ void wait_groups_after(int r) {
     else wait_vm<0>();
 }
 
-template <int BITS, int GQ, bool QF32, bool OUT = false>
+template <int BITS, int GQ, bool QF32, bool OUT = false, bool DEEP = false>
 __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *pipe,
                              uint4 *q_lds) {
     using PP = Pipe<BITS>;
     constexpr int SB = stage_bytes<BITS, OUT>();
-    constexpr int NST = decode_stages<BITS, OUT>();
+    constexpr int NST = decode_stages<BITS, OUT, DEEP>();
     constexpr int DPL = 2 * BITS;              // code dwords per lane
     const int l = threadIdx.x & 63;
     const int j = l & 15, Gl = l >> 4;
@@ -1821,9 +1822,9 @@ __global__ __launch_bounds__(64) void decode_mixed_kernel(DecodeArgs a) {
     }
 }
 
-template <int BITS, int GQ, bool OUT = false>
+template <int BITS, int GQ, bool OUT = false, bool DEEP = false>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t pipe[decode_lds_bytes<BITS, OUT>()];
+    __shared__ __attribute__((aligned(16))) uint8_t pipe[decode_lds_bytes<BITS, OUT, DEEP>()];
     __shared__ uint4 q_lds[64];
     const int64_t item = blockIdx.x;
     const int64_t streams = (int64_t)a.batch * a.kv_heads;
@@ -1838,11 +1839,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     // meet at a control-flow join, where the compiler would wait for them)
     const int64_t it = item - streams * a.tail_items;
     if (a.q_is_f32)
-        decode_split<BITS, GQ, true, OUT>(a, (int)(it / a.splits), (int)(it % a.splits), pipe,
-                                          q_lds);
+        decode_split<BITS, GQ, true, OUT, DEEP>(a, (int)(it / a.splits), (int)(it % a.splits),
+                                                pipe, q_lds);
     else
-        decode_split<BITS, GQ, false, OUT>(a, (int)(it / a.splits), (int)(it % a.splits), pipe,
-                                           q_lds);
+        decode_split<BITS, GQ, false, OUT, DEEP>(a, (int)(it / a.splits), (int)(it % a.splits),
+                                                 pipe, q_lds);
 }
 
 // Merge the partials of one output row (a (batch, query head) of the decode
@@ -2498,11 +2499,11 @@ hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BITS, bool OUT = false>
+template <int BITS, bool OUT = false, bool DEEP = false>
 static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
-    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4, OUT>), grid, dim3(64), 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2, OUT>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<BITS, 1, OUT>), grid, dim3(64), 0, s, a);
+    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4, OUT, DEEP>), grid, dim3(64), 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2, OUT, DEEP>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<BITS, 1, OUT, DEEP>), grid, dim3(64), 0, s, a);
 }
 
 template <int BITS, bool OUT>
@@ -2552,6 +2553,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
         else launch_decode_bits<4, true>(a, gq, grid, s);
     } else if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
     else if (a.bits == 8) launch_decode_bits<8>(a, gq, grid, s);
+    else if (a.deep) launch_decode_bits<4, false, true>(a, gq, grid, s);
     else launch_decode_bits<4>(a, gq, grid, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
