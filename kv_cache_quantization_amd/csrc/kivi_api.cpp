@@ -43,13 +43,9 @@ struct kivi_cache {
 namespace {
 
 constexpr size_t kAlign = 256;
-// Decode work items aimed for per launch: 256 compute units x 16 resident
-// wavefronts (4 per SIMD: <= 128 registers per lane and <= 10 KiB of LDS
-// each), i.e. one round.
-#ifndef KIVI_TARGET_WAVES
-#define KIVI_TARGET_WAVES 4096
-#endif
-constexpr int kTargetWaves = KIVI_TARGET_WAVES;
+// Most decode wavefronts resident at once: 256 compute units x 16 (4 per
+// SIMD, <= 128 registers per lane); decode_waves gives the plan's target.
+constexpr int kMaxWaves = 4096;
 
 // A decode pass whose blocks exceed this many bytes copies them as
 // non-temporal lines: they will not stay cached until the next step anyway
@@ -149,7 +145,26 @@ struct DecodePlan {
 // two stages: measured on B32 x 131072 953 -> 868 us, while on B16 x 32768
 // (1020 groups) the two-stage plan is faster (133 against 148 us).
 constexpr int64_t kDeepGroups = 2048;
-constexpr int kDeepWaves = 2560;
+
+// Split items aimed for per decode launch: one round of resident wavefronts.
+// A wavefront's LDS is its copy stages (three at 2 bits or in a deep plan,
+// else two), at least the 8.5 KiB a residual item stages, plus 1 KiB of q;
+// 160 KiB per compute unit, and at most 16 wavefronts (4 per SIMD, <= 128
+// VGPRs): 2 bits 16 per CU, 4 bits 14 (10 deep), 8 bits 8.  Measured against
+// 4096 (two rounds at 8 bits, 1.14 at 4): 4 bits 133 -> 117 us, 8 bits
+// 200 -> 191 us on B16 x 32768.  With outlier records (two stages of block
+// + record) 4096 measured faster at 4 bits (140 against 148 us) and is kept.
+int64_t decode_waves(const kivi_config &cfg, bool deep) {
+    if (cfg.key_outliers > 0) return kMaxWaves;
+    const int64_t block = 2 * (int64_t)cfg.bits * kGroup * cfg.head_dim / 8 + 4 * cfg.head_dim * 2;
+    const int64_t stages = (cfg.bits == 2 || deep) ? 3 : 2;
+    int64_t lds = stages * block;
+    if (lds < 8704) lds = 8704;
+    lds += 1024;
+    int64_t per_cu = (160 * 1024) / lds;
+    if (per_cu > 16) per_cu = 16;
+    return kComputeUnits * per_cu;
+}
 
 // Residual items per stream at most when each chunk is an item of its own.
 constexpr int64_t kMaxTailItems = 64;
@@ -171,7 +186,7 @@ DecodePlan decode_plan_of(const kivi_cache *c, int64_t q, int64_t tail_chunks) {
         return p;
     }
     p.deep = c->cfg.bits == 4 && c->cfg.key_outliers == 0 && ng >= kDeepGroups;
-    const int64_t waves = p.deep ? kDeepWaves : kTargetWaves;
+    const int64_t waves = decode_waves(c->cfg, p.deep);
     for (int pass = 0; pass < 2; pass++) {
         int64_t want = waves / streams - p.tail_items;
         if (want < 1) want = 1;
@@ -426,12 +441,12 @@ kivi_status kivi_flush(kivi_cache *c, hipStream_t stream) {
 
 size_t kivi_decode_workspace_bytes(const kivi_cache *c) {
     if (!c) return 0;
-    // decode_plan_of never makes more than max(1, kTargetWaves / streams - 1)
+    // decode_plan_of never makes more than max(1, kMaxWaves / streams - 1)
     // split items per stream, whatever n is (fewer when the residual takes
     // one item per chunk), plus at most one residual item per chunk, and
     // under the paper policy one item for the groups with partial value codes.
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
-    int64_t splits = kTargetWaves / streams - 1;
+    int64_t splits = kMaxWaves / streams - 1;
     if (splits < 1) splits = 1;
     const int64_t items = splits + max_tail_items(c->cfg) +
                           (c->cfg.policy == KIVI_FLUSH_PAPER ? max_mixed_items(c->cfg) : 0);
