@@ -147,18 +147,21 @@ struct DecodePlan {
 constexpr int64_t kDeepGroups = 2048;
 
 // Split items aimed for per decode launch: one round of resident wavefronts.
-// A wavefront's LDS is its copy stages (three at 2 bits or in a deep plan,
-// else two), at least the 8.5 KiB a residual item stages, plus 1 KiB of q;
-// 160 KiB per compute unit, and at most 16 wavefronts (4 per SIMD, <= 128
-// VGPRs): 2 bits 16 per CU, 4 bits 14 (10 deep), 8 bits 8.  Measured against
-// 4096 (two rounds at 8 bits, 1.14 at 4): 4 bits 133 -> 117 us, 8 bits
-// 200 -> 191 us on B16 x 32768.  With outlier records (two stages of block
-// + record) 4096 measured faster at 4 bits (140 against 148 us) and is kept.
+// A wavefront's LDS (as the decode kernel declares it) is its copy stages
+// (block, plus the 256-byte record with outlier-aware keys; two stages with
+// records, three at 2 bits or in a deep plan, else two), at least the
+// 8.5 KiB a residual item stages, plus 1 KiB of q; 160 KiB per compute unit,
+// and at most 16 wavefronts (4 per SIMD, <= 128 VGPRs): 2 bits 16 per CU,
+// 4 bits 14 (10 deep), 8 bits 8.  Measured against 4096 (two rounds at 8
+// bits, 1.14 at 4) on B16 x 32768: 4 bits 133 -> 117 us, 8 bits 200 -> 191
+// us, 8 bits with records 206 -> 198 us.  At 4 bits with records the one
+// round (3328) measured slower than 4096 (148 against 140 us): 4096 is kept.
 int64_t decode_waves(const kivi_config &cfg, bool deep) {
-    if (cfg.key_outliers > 0) return kMaxWaves;
+    const bool out = cfg.key_outliers > 0;
+    if (out && cfg.bits == 4) return kMaxWaves;
     const int64_t block = 2 * (int64_t)cfg.bits * kGroup * cfg.head_dim / 8 + 4 * cfg.head_dim * 2;
-    const int64_t stages = (cfg.bits == 2 || deep) ? 3 : 2;
-    int64_t lds = stages * block;
+    const int64_t stages = out ? 2 : (cfg.bits == 2 || deep) ? 3 : 2;
+    int64_t lds = stages * (block + (out ? kOutlierRecordBytes : 0));
     if (lds < 8704) lds = 8704;
     lds += 1024;
     int64_t per_cu = (160 * 1024) / lds;
