@@ -146,6 +146,15 @@ struct DecodePlan {
 // (1020 groups) the two-stage plan is faster (133 against 148 us).
 constexpr int64_t kDeepGroups = 2048;
 
+// Short passes (fewer groups per stream than this) aim at no more than
+// kShortWaves: with ~5 groups per split a wavefront's prologue and memory
+// round trips dominate, and twice the groups per split in half the
+// wavefronts measured faster on the streaming workload (8 KV x 8 batch,
+// 262-272 groups per stream): 21.4 -> 20.4 us per fused warm step, 26.2 ->
+// 24.9 cold; 1024, 1536 and 3072 were slower than 2048.
+constexpr int64_t kShortGroups = 512;
+constexpr int64_t kShortWaves = 2048;
+
 // Split items aimed for per decode launch: one round of resident wavefronts.
 // A wavefront's LDS (as the decode kernel declares it) is its copy stages
 // (block, plus the 256-byte record with outlier-aware keys; two stages with
@@ -189,7 +198,8 @@ DecodePlan decode_plan_of(const kivi_cache *c, int64_t q, int64_t tail_chunks) {
         return p;
     }
     p.deep = c->cfg.bits == 4 && c->cfg.key_outliers == 0 && ng >= kDeepGroups;
-    const int64_t waves = decode_waves(c->cfg, p.deep);
+    int64_t waves = decode_waves(c->cfg, p.deep);
+    if (ng < kShortGroups && waves > kShortWaves) waves = kShortWaves;
     for (int pass = 0; pass < 2; pass++) {
         int64_t want = waves / streams - p.tail_items;
         if (want < 1) want = 1;
