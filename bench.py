@@ -271,7 +271,7 @@ def main():
     ap.add_argument("--key-outliers", type=int, default=0, choices=(0, 1, 2, 3),
                     help="key channels kept in fp16 per 32-token key group (outlier-aware keys)")
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk (0: one shot)")
-    ap.add_argument("--cpu-sample", type=int, default=2, help="batch entries timed on the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=6, help="batch entries timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-evict", action="store_true")
     ap.add_argument("--stream-steps", type=int, default=512,
                     help="also time the streaming workload (batch 8, prefill 8192, then this many "

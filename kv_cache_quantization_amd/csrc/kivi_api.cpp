@@ -336,15 +336,36 @@ kivi_status kivi_plan_append(const kivi_cache *c, int64_t n_new, kivi_append_pla
 
 namespace {
 
+// Tokens [begin, end) (all >= n_old) of every stream, copied into the ring.
+RingArgs ring_args(const kivi_cache *c, const void *k, const void *v, int64_t n_new,
+                   int64_t n_old, int64_t begin, int64_t end) {
+    RingArgs r;
+    r.in_k = k;
+    r.in_v = v;
+    r.n_new = n_new;
+    r.n_old = n_old;
+    r.ring_k = c->base + c->off_ring_k;
+    r.ring_v = c->base + c->off_ring_v;
+    r.ring_cap = c->ring_cap;
+    r.tok_begin = begin;
+    r.tok_end = end > begin ? end : begin;
+    r.streams = c->cfg.batch * c->cfg.n_kv_heads;
+    r.esize = c->esize;
+    return r;
+}
+
 // Quantize the 32-token blocks [block_begin, block_end) of every stream:
 // kinds 1 = key groups (G / 32 blocks each), 2 = value blocks, 3 = both;
 // value rows at or past v_limit are left out (codes and side data 0).
 // Tokens t < p.n_old are read from the ring, later ones from k / v.
+// `copy` (optional): ring rows to write once every ring row the quantize
+// work reads has been read, folded into its launch where one reads no ring
+// row (then the copy needs no launch of its own).
 kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const void *k,
                              const void *v, int64_t n_new, int64_t block_begin,
                              int64_t block_end, int kinds, int64_t v_limit,
-                             hipStream_t stream) {
-    if (block_end <= block_begin) return KIVI_OK;
+                             hipStream_t stream, const RingArgs *copy = nullptr) {
+    if (block_end <= block_begin && !copy) return KIVI_OK;
     QuantizeArgs a;
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
@@ -366,6 +387,8 @@ kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const voi
     a.bits = c->cfg.bits;
     a.kinds = kinds;
     a.v_limit = v_limit;
+    a.copy = copy ? *copy : RingArgs{};
+    a.quant_tasks = 0;
     return launch_quantize(a, stream) == hipSuccess ? KIVI_OK : KIVI_ERR_HIP;
 }
 
@@ -375,13 +398,15 @@ kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const voi
 // qv_new): whole blocks, and the block holding qv_new up to that token
 // (re-quantized whole on every append that adds rows to it; its earlier rows
 // come out identical, since values are quantized per token).
+// Window policy: `copy` (optional) is written to the ring by the same launches.
 kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *k, const void *v,
-                          int64_t n_new, hipStream_t stream) {
+                          int64_t n_new, hipStream_t stream, const RingArgs *copy = nullptr) {
     const int64_t G = kGroup;
     constexpr int64_t kNoLimit = INT64_MAX;
     if (c->cfg.policy != KIVI_FLUSH_PAPER)
         return enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
-                                p.flush_token_end / G, 3, kNoLimit, stream);
+                                p.flush_token_end / G, 3, kNoLimit, stream, copy);
+    if (copy) return KIVI_ERR_INVALID_ARG;
     kivi_status st = enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
                                       p.flush_token_end / G, 1, kNoLimit, stream);
     if (st != KIVI_OK || p.v_flush_token_end <= p.v_flush_token_begin) return st;
@@ -395,18 +420,7 @@ kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *
 kivi_status enqueue_ring(kivi_cache *c, const void *k, const void *v, int64_t n_new,
                          int64_t n_old, int64_t begin, int64_t end, hipStream_t stream) {
     if (end <= begin) return KIVI_OK;
-    RingArgs r;
-    r.in_k = k;
-    r.in_v = v;
-    r.n_new = n_new;
-    r.n_old = n_old;
-    r.ring_k = c->base + c->off_ring_k;
-    r.ring_v = c->base + c->off_ring_v;
-    r.ring_cap = c->ring_cap;
-    r.tok_begin = begin;
-    r.tok_end = end;
-    r.streams = c->cfg.batch * c->cfg.n_kv_heads;
-    r.esize = c->esize;
+    const RingArgs r = ring_args(c, k, v, n_new, n_old, begin, end);
     return launch_ring_append(r, stream) == hipSuccess ? KIVI_OK : KIVI_ERR_HIP;
 }
 
@@ -429,9 +443,14 @@ kivi_status kivi_append(kivi_cache *c, const void *k, const void *v, int64_t n_n
         c->n = p.n_new_total;
         return KIVI_OK;
     }
-    st = enqueue_flush(c, p, k, v, n_new, stream);
-    if (st != KIVI_OK) return st;
-    st = enqueue_ring(c, k, v, n_new, p.n_old, p.ring_token_begin, p.ring_token_end, stream);
+    if (c->cfg.policy != KIVI_FLUSH_PAPER) {
+        const RingArgs r = ring_args(c, k, v, n_new, p.n_old, p.ring_token_begin, p.ring_token_end);
+        st = enqueue_flush(c, p, k, v, n_new, stream, &r);
+    } else {
+        st = enqueue_flush(c, p, k, v, n_new, stream);
+        if (st == KIVI_OK)
+            st = enqueue_ring(c, k, v, n_new, p.n_old, p.ring_token_begin, p.ring_token_end, stream);
+    }
     if (st != KIVI_OK) return st;
     c->n = p.n_new_total;
     c->q = p.q_new;

@@ -11,6 +11,18 @@ constexpr int kGroup = 32;      // tokens per block (G: 32, 64 or 128 per key / 
 constexpr int kMaxKeyOutliers = 3;        // fp16 key channels per key group at most
 constexpr int kOutlierRecordBytes = 256;  // per block: uint16 channel[3], pad, fp16 [3][32]
 
+// Copy tokens [tok_begin, tok_end) of every stream from the appended chunk
+// into the ring.
+struct RingArgs {
+    const void *in_k, *in_v;
+    int64_t n_new, n_old;
+    void *ring_k, *ring_v;
+    int64_t ring_cap;
+    int64_t tok_begin, tok_end;
+    int32_t streams;
+    int32_t esize;              // bytes per element (2 or 4)
+};
+
 // Quantize the 32-token blocks [block_begin, block_end) of every stream.  A
 // key group spans gt = G / 32 blocks (block_begin and block_end are then
 // multiples of gt for key tasks); a value group spans 32 * gt channels of one
@@ -34,18 +46,11 @@ struct QuantizeArgs {
     uint8_t *outliers;          // [streams][max_groups][kOutlierRecordBytes]
     int32_t kinds;              // 1: key groups, 2: value blocks, 3: both
     int64_t v_limit;            // value codes / side data of tokens >= v_limit are written 0
-};
-
-// Copy tokens [tok_begin, tok_end) of every stream from the appended chunk
-// into the ring.
-struct RingArgs {
-    const void *in_k, *in_v;
-    int64_t n_new, n_old;
-    void *ring_k, *ring_v;
-    int64_t ring_cap;
-    int64_t tok_begin, tok_end;
-    int32_t streams;
-    int32_t esize;              // bytes per element (2 or 4)
+    // Rows to copy into the ring as well (none when copy.tok_end <= tok_begin).
+    // The launch that reads no ring row does the copy in extra workgroups,
+    // after its quant_tasks workgroups; without one, a ring append follows.
+    RingArgs copy;
+    uint32_t quant_tasks;       // set by the launcher
 };
 
 struct DecodeArgs {

@@ -714,16 +714,71 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
     }
 }
 
+// ===========================================================================
+// Residual ring append: copy rows [tok_begin, tok_end) of the chunk into
+// ring slot t % ring_cap.  16 bytes per thread.
+// ===========================================================================
+// The copy is split into 16-byte pieces of the flattened [streams][tokens]
+// range of row pairs: a row pair (K and V) is 2 * D * esize / 16 pieces.
+// The row's stream, token and slot are computed with 32-bit arithmetic where
+// the range allows.  A ring append workgroup copies kRingThreads pieces, one
+// per thread; the quantize launch that folds the copy in gives each of its
+// copy workgroups the same kRingThreads pieces, kRingThreads / 64 per lane.
+constexpr int kRingThreads = 256;
+
+__device__ __forceinline__ void ring_copy_piece(const RingArgs &a, int64_t piece) {
+    const int row_vec = D * a.esize / 16;                 // 16-byte pieces of one row
+    const int per_row = 2 * row_vec;                      // K and V
+    const int64_t ntok = a.tok_end - a.tok_begin;
+    const int64_t rows = (int64_t)a.streams * ntok;
+    const int64_t r = piece / per_row;
+    if (r >= rows) return;
+    const int e = (int)(piece % per_row);
+    const int which = e >= row_vec;                       // 0: K, 1: V
+    const int v = e - which * row_vec;
+    int64_t stream, t;
+    if (rows <= 0x7FFFFFFF) {
+        const uint32_t r32 = (uint32_t)r, n32 = (uint32_t)ntok;
+        stream = r32 / n32;
+        t = a.tok_begin + (r32 - (uint32_t)stream * n32);
+    } else {
+        stream = r / ntok;
+        t = a.tok_begin + (r - stream * ntok);
+    }
+    const uint32_t slot = a.ring_cap <= 0x7FFFFFFF && t <= 0xFFFFFFFFll
+                              ? (uint32_t)t % (uint32_t)a.ring_cap
+                              : (uint32_t)(t % a.ring_cap);
+    const uint4 *src = (const uint4 *)((const uint8_t *)(which ? a.in_v : a.in_k) +
+                                       (stream * a.n_new + (t - a.n_old)) * D * a.esize);
+    uint4 *dst = (uint4 *)((uint8_t *)(which ? a.ring_v : a.ring_k) +
+                           (stream * a.ring_cap + slot) * D * a.esize);
+    dst[v] = src[v];
+}
+
+__global__ __launch_bounds__(kRingThreads) void ring_append_kernel(RingArgs a) {
+    ring_copy_piece(a, (int64_t)blockIdx.x * kRingThreads + threadIdx.x);
+}
+
 // RING: the groups [group_begin, group_end) hold tokens appended earlier
 // (read, at least in part, from the ring); otherwise every row comes from
 // the new chunk.
 // kinds = 3: per key group (GT blocks), task (1 + GT) i is the key group and
 // the next GT tasks are the value blocks of the same tokens; kinds = 1 / 2:
 // every task is a key group / a value block.
+// Without RING, workgroups from a.quant_tasks on copy a.copy's ring rows.
 template <int BITS, typename T, bool RING, int GT, bool OUT>
 __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
     __shared__ uint32_t tr[64 * 2 * BITS];
     const uint32_t task = blockIdx.x;
+    if constexpr (!RING) {
+        if (task >= a.quant_tasks) {
+            const int64_t first = (int64_t)(task - a.quant_tasks) * kRingThreads;
+#pragma unroll
+            for (int j = 0; j < kRingThreads / 64; j++)
+                ring_copy_piece(a.copy, first + j * 64 + threadIdx.x);
+            return;
+        }
+    }
     const uint32_t nb = (uint32_t)(a.block_end - a.block_begin);
     int64_t stream, g;
     bool is_v;
@@ -744,45 +799,6 @@ __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
     }
     if (is_v) quantize_task<BITS, true, RING, T, GT, OUT>(a, stream, g, tr);
     else quantize_task<BITS, false, RING, T, GT, OUT>(a, stream, g, tr);
-}
-// ===========================================================================
-// Residual ring append: copy rows [tok_begin, tok_end) of the chunk into
-// ring slot t % ring_cap.  16 bytes per thread.
-// ===========================================================================
-// Each workgroup copies kRingRows rows (K and V) of the flattened
-// [streams][tokens] range: a row pair is 2 * D * esize / 16 threads, each
-// moving 16 bytes; the row's stream, token and slot are computed once per
-// thread with 32-bit arithmetic where the range allows.
-constexpr int kRingThreads = 256;
-
-__global__ __launch_bounds__(kRingThreads) void ring_append_kernel(RingArgs a) {
-    const int row_vec = D * a.esize / 16;                 // 16-byte pieces of one row
-    const int per_row = 2 * row_vec;                      // K and V
-    const int rows_per_block = kRingThreads / per_row;
-    const int64_t ntok = a.tok_end - a.tok_begin;
-    const int64_t rows = (int64_t)a.streams * ntok;
-    const int64_t r = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / per_row;
-    if (r >= rows) return;
-    const int e = threadIdx.x % per_row;
-    const int which = e >= row_vec;                       // 0: K, 1: V
-    const int v = e - which * row_vec;
-    int64_t stream, t;
-    if (rows <= 0x7FFFFFFF) {
-        const uint32_t r32 = (uint32_t)r, n32 = (uint32_t)ntok;
-        stream = r32 / n32;
-        t = a.tok_begin + (r32 - (uint32_t)stream * n32);
-    } else {
-        stream = r / ntok;
-        t = a.tok_begin + (r - stream * ntok);
-    }
-    const uint32_t slot = a.ring_cap <= 0x7FFFFFFF && t <= 0xFFFFFFFFll
-                              ? (uint32_t)t % (uint32_t)a.ring_cap
-                              : (uint32_t)(t % a.ring_cap);
-    const uint4 *src = (const uint4 *)((const uint8_t *)(which ? a.in_v : a.in_k) +
-                                       (stream * a.n_new + (t - a.n_old)) * D * a.esize);
-    uint4 *dst = (uint4 *)((uint8_t *)(which ? a.ring_v : a.ring_k) +
-                           (stream * a.ring_cap + slot) * D * a.esize);
-    dst[v] = src[v];
 }
 
 // ===========================================================================
@@ -2430,6 +2446,14 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
 // ===========================================================================
 // Launchers
 // ===========================================================================
+// Workgroups of kRingThreads pieces that copy a ring append's rows.
+static int64_t ring_blocks(const RingArgs &a) {
+    const int64_t ntok = a.tok_end - a.tok_begin;
+    if (ntok <= 0) return 0;
+    const int64_t pieces = (int64_t)a.streams * ntok * (2 * D * a.esize / 16);
+    return (pieces + kRingThreads - 1) / kRingThreads;
+}
+
 template <int BITS, typename T, int GT, bool OUT = false>
 static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
     // tasks per launched block range: key groups of GT blocks and / or blocks
@@ -2455,10 +2479,14 @@ static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
         QuantizeArgs n = a;
         n.block_begin = split;
         const int64_t tasks = (int64_t)a.streams * tasks_of(a.block_end - split);
-        hipLaunchKernelGGL((quantize_kernel<BITS, T, false, GT, OUT>), dim3((unsigned)tasks), dim3(64),
-                           0, s, n);
+        n.quant_tasks = (uint32_t)tasks;
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, false, GT, OUT>),
+                           dim3((unsigned)(tasks + ring_blocks(a.copy))), dim3(64), 0, s, n);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    // every quantized block reads the ring: the copy runs after them
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_ring_append(a.copy, s);
 }
 
 template <int BITS, typename T>
@@ -2470,7 +2498,11 @@ static hipError_t launch_quantize_g(const QuantizeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
-    if (a.block_end <= a.block_begin || a.streams <= 0) return hipSuccess;
+    const bool copy = a.copy.tok_end > a.copy.tok_begin;
+    if (copy && a.copy.esize != 2 && a.copy.esize != 4) return hipErrorInvalidValue;
+    if (copy && ring_blocks(a.copy) > 0x7FFFFFFF - 2 * (int64_t)a.streams * a.max_groups)
+        return hipErrorInvalidValue;
+    if (a.block_end <= a.block_begin || a.streams <= 0) return launch_ring_append(a.copy, s);
     if (a.kinds < 1 || a.kinds > 3) return hipErrorInvalidValue;
     if (a.gt != 1 && a.gt != 2 && a.gt != 4) return hipErrorInvalidValue;
     if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && (a.gt != 1 || !a.outliers)))
@@ -2489,11 +2521,9 @@ hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {
-    const int64_t ntok = a.tok_end - a.tok_begin;
-    if (ntok <= 0) return hipSuccess;
+    if (a.tok_end <= a.tok_begin) return hipSuccess;
     if (a.esize != 2 && a.esize != 4) return hipErrorInvalidValue;
-    const int64_t rows_per_block = kRingThreads / (2 * D * a.esize / 16);
-    const int64_t blocks = ((int64_t)a.streams * ntok + rows_per_block - 1) / rows_per_block;
+    const int64_t blocks = ring_blocks(a);
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)blocks), dim3(kRingThreads), 0, s, a);
     return hipGetLastError();
