@@ -23,11 +23,13 @@
  *        uniform quantization, the half-step error bound, QuantizedCache.
  *
  * Parity status: every function is pinned by tests/test_oracle_pins.py to
- * what the pages print or to closed forms, except the bit order of the
- * packed block (code_position / oracle_pack_blocks): the pages fix the
- * storage cost but not the order, so that order is a layout choice --
- * parity unpinned beyond its bijectivity (and the GPU decode reading it
- * back into the oracle's logical attention).
+ * what the pages print or to closed forms.  The packers (oracle_pack_blocks_kv,
+ * oracle_pack_outlier_records) are pinned by tests/test_oracle_layout_pins.py,
+ * which decodes their output with its own forward reading of the documented
+ * byte layout (never through code_position) back to the pinned logical
+ * arrays, the paper-policy zero rows included.  The bit order itself is a
+ * layout choice of this library: the pages fix the storage cost (b bits per
+ * code and two fp16 per group), not the order.
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fPIC -shared
  * (x86-64 SSE arithmetic: every float operation below is one IEEE-754
