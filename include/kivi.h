@@ -21,8 +21,14 @@
  *  - Pointers named "device" are HIP device addresses; the library never
  *    allocates, frees or synchronizes; all work is enqueued on the caller's
  *    stream in call order.  Host handles are not thread-safe.
- *  - Arguments are validated before anything is enqueued: a call that returns
- *    an error has had no effect on the cache.  Asynchronous kernel faults
+ *  - Arguments are validated before anything is enqueued: a call that fails
+ *    validation has had no effect.  KIVI_ERR_HIP means the runtime refused a
+ *    kernel launch: launches the call enqueued before it stay enqueued, but
+ *    the handle's n and quantized prefixes, the ring and every byte a later
+ *    call reads are as they were before the call (the earlier launches only
+ *    write packed blocks outside the quantized prefixes), so the call may be
+ *    retried.  The one exception is kivi_append_decode when the append part
+ *    needs launches of its own (see there).  Asynchronous kernel faults
  *    surface at the caller's next synchronization.
  *  - Inputs must be finite (NaN / Inf are a precondition violation and are
  *    not checked).
@@ -105,9 +111,19 @@ typedef struct kivi_cache kivi_cache;   /* opaque host-side handle */
    keep their values in fp16: their codes, K scale and K zero in the block
    are 0, and the block's 256-byte record holds uint16 channel[3]
    (ascending, 0xFFFF unused), 10 zero bytes, then fp16 values [3][32] at
-   byte 16 + 64 o (0 unused).  The bit order of
-   the codes is described in the kernel source (it follows the matrix-core
-   operand layout).  Ring: [B*H][ring_capacity][D] in kv_dtype for K and for
+   byte 16 + 64 o (0 unused), then 48 zero bytes.
+   Bit order of a code area (the storage cost, b bits per code and two fp16
+   per group, is the notebook's storage cell; the order is this library's,
+   chosen so that each lane's bytes are its own matrix-core operands): as
+   little-endian uint32 dwords, lane l (0..63) and lane dword w (0..2b-1)
+   name dword (w/4)*256 + 4l + w%4.  Its bits [16h + b i, 16h + b i + b)
+   (half h = 0, 1; slot i = 0 .. 16/b - 1) hold the code at operand o,
+   position kk:  b = 2, 4: o = w*(4/b) + i/4, kk = 2(i%4) + h;
+                 b = 8:    o = w/2,         kk = 4(w%2) + 2i + h.
+   Keys:   token 16(o/4) + l%16, channel 32(o%4) + 8(l/16) + kk.
+   Values: token 4(l/16) + kk%4 + 16(kk/4), channel 16o + l%16.
+   (Tokens are counted from the start of the block.)
+   Ring: [B*H][ring_capacity][D] in kv_dtype for K and for
    V; token t of a stream lives in slot t mod ring_capacity while it is in
    [G * floor(n_vquantized / G), n_tokens), which holds the key residual
    [n_quantized, n_tokens) and the value residual [n_vquantized, n_tokens). */
@@ -138,11 +154,19 @@ typedef struct {
 } kivi_append_plan;
 
 /* Bytes of device memory a cache with this config needs (0 if the config is
-   invalid or unsupported). */
+   invalid or unsupported): the packed blocks of max_tokens / 32 token
+   groups per stream at b bits per code plus two fp16 per key and per value
+   group (the notebook's storage cell: "2 fp16 per group"), and the two
+   full-precision rings of R + G tokens ("KIVI", VeloxQuant-MLX docs, "How it
+   works" item 3). */
 size_t kivi_cache_bytes(const kivi_config *cfg);
 
 /* Validate cfg and bind a host handle to the caller's device buffer
    (dev_mem, dev_bytes >= kivi_cache_bytes(cfg), 256-byte aligned).  The
+   config is the method's: b-bit codes with G-element groups, keys per
+   channel and values per token (notebook, "K (per-channel) and V
+   (per-token) quantisation"; VeloxQuant-MLX docs, "How it works" items 1-2),
+   and R full-precision tokens (item 3).  The
    cache starts empty; the buffer's contents need no initialization.  The
    buffer must outlive the handle.  *out is set only on KIVI_OK. */
 kivi_status kivi_cache_create(const kivi_config *cfg, void *dev_mem,
@@ -151,7 +175,11 @@ kivi_status kivi_cache_create(const kivi_config *cfg, void *dev_mem,
 /* Release the host handle (the device buffer is the caller's). NULL is ok. */
 kivi_status kivi_cache_destroy(kivi_cache *c);
 
-/* Append n_new >= 0 tokens to every stream.  k, v: device, contiguous
+/* Append n_new >= 0 tokens to every stream ("KIVI", VeloxQuant-MLX docs,
+   "How it works" items 3-4: the newest R tokens stay in full precision and
+   older ones are quantized in whole groups of G; under KIVI_FLUSH_PAPER,
+   "[Paper review] KIVI ...", 3.2.3 Algorithm 1, decoding phase).
+   k, v: device, contiguous
    [B][H][n_new][D] in kv_dtype (may be NULL when n_new == 0); they are read
    by kernels enqueued on `stream` and must stay valid until those finish.
    Enqueues, in this order: quantization of the newly aged tokens (see
@@ -167,7 +195,8 @@ kivi_status kivi_append(kivi_cache *c, const void *k, const void *v,
 
 /* Make the cache canonical: quantize the tokens that deferred appends left
    in the ring up to the policy's prefixes (nothing to do after appends
-   without KIVI_DEFER_FLUSH).  Idempotent.  Errors: INVALID_ARG, HIP. */
+   without KIVI_DEFER_FLUSH), in whole groups ("KIVI", VeloxQuant-MLX docs,
+   "How it works" items 3-4).  Idempotent.  Errors: INVALID_ARG, HIP. */
 kivi_status kivi_flush(kivi_cache *c, hipStream_t stream);
 
 /* Host-only: what kivi_append(c, ..., n_new, 0, ...) would enqueue. */
@@ -185,7 +214,9 @@ size_t kivi_decode_workspace_bytes(const kivi_cache *c);
 kivi_status kivi_decode_plan(const kivi_cache *c, int32_t *splits,
                              int32_t *groups_per_split);
 
-/* One decode-attention step over all n cached tokens of every stream:
+/* One decode-attention step over all n cached tokens of every stream
+   ("[Paper review] KIVI ...", 1.3 decoding: A = softmax(q K^T / sqrt(D)),
+   o = A V; 3.2, dequantization fused into the two products):
    out[b][hq][:] = softmax(scale * q[b][hq] . K_hat^T) V_hat, where K_hat and
    V_hat are the dequantized tokens (code * scale + zero) followed by the
    full-precision residual (under the paper policy the key and value
@@ -212,7 +243,10 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype,
    Everything is validated before anything is enqueued.  Errors: those of
    kivi_append (KIVI_DEFER_FLUSH is not accepted here) and of
    kivi_decode_attn; STATE also when a deferred flush is pending before the
-   call. */
+   call.  HIP: if the append enqueues launches of its own (some group ages
+   out, n_new == 0 or the paper policy) and the decode launch is the one
+   refused, the append has taken effect exactly as a successful kivi_append
+   and out is not written; otherwise the call had no effect. */
 kivi_status kivi_append_decode(kivi_cache *c, const void *k, const void *v, int64_t n_new,
                                const void *q, int32_t q_dtype, float softmax_scale,
                                float *out, void *workspace, size_t ws_bytes,
@@ -251,7 +285,9 @@ size_t kivi_attn_workspace_bytes(const kivi_cache *c, int64_t T);
 kivi_status kivi_attn_plan(const kivi_cache *c, int64_t T, int32_t *qblocks,
                            int32_t *splits, int32_t *groups_per_split);
 
-/* Offsets, sizes and the current n / Q(n) (host-only). */
+/* Offsets, sizes and the current n / Q(n) (host-only): where the packed
+   codes and the fp16 zero / scale pairs of the notebook's storage cell, and
+   the full-precision residual, sit in the caller's buffer (layout above). */
 kivi_status kivi_get_layout(const kivi_cache *c, kivi_layout *out);
 
 /* Static string for a status code. */

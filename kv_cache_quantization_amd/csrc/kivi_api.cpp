@@ -428,6 +428,14 @@ kivi_status enqueue_ring(kivi_cache *c, const void *k, const void *v, int64_t n_
 
 extern "C" {
 
+// Host state (n, Q) moves only once every launch of the call was accepted.
+// The launches are ordered so that a refused one leaves the old state valid:
+// the ring is written only by the last launch of an append (the copy
+// workgroups of the chunk-reading quantize launch, or the ring launch after
+// all quantize launches), and the quantize launches before it write only
+// blocks past the old prefixes (under the paper policy also the value rows
+// at or past the old Q_V of the block holding it, which no call reads while
+// Q_V is unchanged).
 kivi_status kivi_append(kivi_cache *c, const void *k, const void *v, int64_t n_new,
                         uint32_t flags, hipStream_t stream) {
     if (!c || (flags & ~(uint32_t)KIVI_DEFER_FLUSH) != 0 || n_new < 0) return KIVI_ERR_INVALID_ARG;
@@ -606,10 +614,14 @@ kivi_status kivi_append_decode(kivi_cache *c, const void *k, const void *v, int6
                               nullptr, 0, INT64_MAX);
     }
     // nothing ages out: every new row lands in the residual, and the decode's
-    // residual items take it from k / v and write it into the ring
+    // residual items take it from k / v and write it into the ring.  The
+    // decode plan is made for the new n; if its launch is refused nothing was
+    // enqueued, and n goes back to its old value.
     c->n = p.n_new_total;
-    return enqueue_decode(c, q, q_dtype, softmax_scale, out, workspace, stream, k, v, n_new,
-                          p.n_old);
+    st = enqueue_decode(c, q, q_dtype, softmax_scale, out, workspace, stream, k, v, n_new,
+                        p.n_old);
+    if (st != KIVI_OK) c->n = p.n_old;
+    return st;
 }
 
 size_t kivi_attn_workspace_bytes(const kivi_cache *c, int64_t T) {

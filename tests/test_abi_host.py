@@ -1,8 +1,11 @@
 """Host-side checks of libkivi's C ABI that need no GPU: the library loads,
 exports every function include/kivi.h declares, validates configurations,
 lays out the device buffer as documented, and plans appends by the window
-flush policy.  Nothing here launches a kernel (every call below returns
-before the library touches the HIP runtime)."""
+flush policy.  Nothing here launches a kernel: every call below returns
+before the library touches the HIP runtime, except in
+test_refused_launches_leave_state, which runs only where no GPU is visible
+(there the HIP runtime refuses every launch, and the test checks what the
+library does with that refusal)."""
 import ctypes
 import os
 import re
@@ -270,3 +273,40 @@ def test_host_error_paths(L):
         assert (lo.n_tokens, lo.n_quantized) == (0, 0)
     finally:
         kivi.kivi_cache_destroy(h)
+
+
+def _no_gpu_visible():
+    import torch
+    return torch.cuda.device_count() == 0       # counting does not initialise a device
+
+
+def test_refused_launches_leave_state(L):
+    """KIVI_ERR_HIP: a call whose launch the runtime refuses leaves the
+    handle's n and quantized prefixes as they were, so it can be retried
+    (include/kivi.h, conventions).  Without a GPU every launch is refused,
+    so each call below fails at its first launch: for kivi_append_decode on
+    the path where the decode itself copies the new rows into the ring, n
+    goes back to its value before the call.  Device pointers are never
+    dereferenced (no launch is accepted)."""
+    if not _no_gpu_visible():
+        pytest.skip("a GPU is visible: launches would run")
+    for policy in (kivi.KIVI_FLUSH_WINDOW, kivi.KIVI_FLUSH_PAPER):
+        cfg = kivi.make_config(2, 8, 32, bits=2, residual=64, max_tokens=4096, policy=policy)
+        h = kivi.kivi_cache_create(cfg, FAKE_DEV, kivi.kivi_cache_bytes(cfg))
+        try:
+            for n_new, flags in ((300, 0), (10, 0), (10, kivi.KIVI_DEFER_FLUSH)):
+                with pytest.raises(kivi.KiviError) as e:
+                    kivi.kivi_append(h, FAKE_DEV, FAKE_DEV, n_new, flags, 0)
+                assert e.value.status == kivi.KIVI_ERR_HIP
+                lo = kivi.kivi_get_layout(h)
+                assert (lo.n_tokens, lo.n_quantized, lo.n_vquantized) == (0, 0, 0)
+            ws = kivi.kivi_decode_workspace_bytes(h)
+            for n_new in (1, 40, 300):        # 1, 40: fused path (window); 300: quantizes
+                with pytest.raises(kivi.KiviError) as e:
+                    kivi.kivi_append_decode(h, FAKE_DEV, FAKE_DEV, n_new, FAKE_DEV, kivi.KIVI_F16,
+                                            0.0, FAKE_DEV, FAKE_DEV, ws, 0)
+                assert e.value.status == kivi.KIVI_ERR_HIP
+                lo = kivi.kivi_get_layout(h)
+                assert (lo.n_tokens, lo.n_quantized, lo.n_vquantized) == (0, 0, 0)
+        finally:
+            kivi.kivi_cache_destroy(h)
