@@ -230,6 +230,28 @@ kivi_status kivi_decode_attn(kivi_cache *c, const void *q, int32_t q_dtype,
                              float softmax_scale, float *out, void *workspace,
                              size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the fixed device array kivi_decode_attn_noalloc keeps its decode
+   partials in (one copy per device, held until the process ends). */
+#define KIVI_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* kivi_decode_attn without a workspace, for callers that cannot allocate
+   device memory (code under HIP graph capture, allocation-free serving
+   loops, harnesses that forbid hipMalloc).  Same arguments, results and
+   kernels as kivi_decode_attn; the split partials go to a fixed device
+   array of KIVI_NOALLOC_SCRATCH_BYTES inside the library instead of a
+   caller workspace.  The call itself allocates nothing (the array's device
+   address is looked up on the first call on each device).  Every call on a
+   device shares that device's array: calls that overlap on one device (on
+   different streams, or from different threads) race and must be ordered
+   by the caller; nothing in the array needs to start at zero.  Errors:
+   those of kivi_decode_attn, and BUFFER_TOO_SMALL when this cache's
+   partials, kivi_decode_workspace_bytes(c), exceed
+   KIVI_NOALLOC_SCRATCH_BYTES (B * Hq * items * (D + 2) * 4 bytes: 9.6 MB
+   at batch 16 and 10.6 MB at batch 32 with 8 KV and 32 query heads,
+   R = 128). */
+kivi_status kivi_decode_attn_noalloc(kivi_cache *c, const void *q, int32_t q_dtype,
+                                     float softmax_scale, float *out, hipStream_t stream);
+
 /* kivi_append(c, k, v, n_new, 0, stream) followed by kivi_decode_attn(c, q,
    q_dtype, softmax_scale, out, workspace, ws_bytes, stream), with the same
    results bit for bit, for a serving loop's decode step ("[Paper review]

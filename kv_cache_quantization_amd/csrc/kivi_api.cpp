@@ -26,6 +26,9 @@
 
 using namespace kivi;
 
+static_assert(KIVI_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes,
+              "kivi.h and the kernels must agree on the fixed scratch size");
+
 struct kivi_cache {
     kivi_config cfg;
     uint8_t *base;
@@ -622,6 +625,18 @@ kivi_status kivi_append_decode(kivi_cache *c, const void *k, const void *v, int6
                         p.n_old);
     if (st != KIVI_OK) c->n = p.n_old;
     return st;
+}
+
+kivi_status kivi_decode_attn_noalloc(kivi_cache *c, const void *q, int32_t q_dtype,
+                                     float softmax_scale, float *out, hipStream_t stream) {
+    if (!c || !q || !out) return KIVI_ERR_INVALID_ARG;
+    if (q_dtype != KIVI_F16 && q_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
+    if (kivi_decode_workspace_bytes(c) > KIVI_NOALLOC_SCRATCH_BYTES) return KIVI_ERR_BUFFER_TOO_SMALL;
+    if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
+    void *ws = nullptr;
+    if (noalloc_scratch(&ws) != hipSuccess) return KIVI_ERR_HIP;
+    return enqueue_decode(c, q, q_dtype, softmax_scale, out, ws, stream, nullptr, nullptr, 0,
+                          INT64_MAX);
 }
 
 size_t kivi_attn_workspace_bytes(const kivi_cache *c, int64_t T) {

@@ -1,6 +1,7 @@
 // Private interface between the C-ABI front end (kivi_api.cpp) and the HIP
 // kernels (kivi_kernels.hip).  Not installed, not part of the ABI.
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -122,6 +123,14 @@ struct AttnArgs {
     int32_t n_out;              // outlier-aware keys: channels per key group kept in fp16
     const uint8_t *outliers;    // [streams][max_groups][kOutlierRecordBytes] (n_out > 0)
 };
+
+// Bytes of the fixed device array that holds the decode partials of
+// kivi_decode_attn_noalloc (KIVI_NOALLOC_SCRATCH_BYTES in kivi.h).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+
+// Device address of that array on the current device (looked up with
+// hipGetSymbolAddress on the first call per device, then cached).
+hipError_t noalloc_scratch(void **ptr);
 
 hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);

@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <atomic>
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -2441,6 +2442,35 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
             }
         }
     }
+}
+
+// ===========================================================================
+// Fixed scratch of kivi_decode_attn_noalloc: the decode partials live in a
+// file-scope device array instead of a caller workspace, for callers that
+// cannot allocate.  Each device holds its own copy until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name
+// stands for a host-side placeholder): its device address is looked up once
+// per device, with that device current, and kept.
+// ===========================================================================
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+hipError_t noalloc_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 // ===========================================================================

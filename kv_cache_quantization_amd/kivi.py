@@ -26,12 +26,14 @@ KIVI_F32 = 1
 KIVI_FLUSH_WINDOW = 0
 KIVI_FLUSH_PAPER = 1
 KIVI_DEFER_FLUSH = 1
+KIVI_NOALLOC_SCRATCH_BYTES = 32 << 20      # fixed decode scratch of kivi_decode_attn_noalloc
 
 # Every symbol include/kivi.h declares.
 EXPORTED = (
     "kivi_cache_bytes", "kivi_cache_create", "kivi_cache_destroy", "kivi_append",
     "kivi_flush", "kivi_plan_append", "kivi_decode_workspace_bytes",
-    "kivi_decode_plan", "kivi_decode_attn", "kivi_append_decode", "kivi_attn",
+    "kivi_decode_plan", "kivi_decode_attn", "kivi_decode_attn_noalloc", "kivi_append_decode",
+    "kivi_attn",
     "kivi_attn_workspace_bytes",
     "kivi_attn_plan", "kivi_get_layout", "kivi_status_string",
 )
@@ -101,6 +103,8 @@ def lib():
         L.kivi_decode_plan.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kivi_decode_attn.restype = i32
         L.kivi_decode_attn.argtypes = [P, P, i32, ctypes.c_float, P, P, sz, P]
+        L.kivi_decode_attn_noalloc.restype = i32
+        L.kivi_decode_attn_noalloc.argtypes = [P, P, i32, ctypes.c_float, P, P]
         L.kivi_append_decode.restype = i32
         L.kivi_append_decode.argtypes = [P, P, P, i64, P, i32, ctypes.c_float, P, P, sz, P]
         L.kivi_attn.restype = i32
@@ -173,6 +177,12 @@ def kivi_decode_attn(handle: int, q: int, q_dtype: int, softmax_scale: float, ou
                      workspace: int, ws_bytes: int, stream: int) -> None:
     _check(lib().kivi_decode_attn(handle, q, q_dtype, softmax_scale, out, workspace,
                                   ws_bytes, stream), "kivi_decode_attn")
+
+
+def kivi_decode_attn_noalloc(handle: int, q: int, q_dtype: int, softmax_scale: float, out: int,
+                             stream: int) -> None:
+    _check(lib().kivi_decode_attn_noalloc(handle, q, q_dtype, softmax_scale, out, stream),
+           "kivi_decode_attn_noalloc")
 
 
 def kivi_append_decode(handle: int, k: int, v: int, n_new: int, q: int, q_dtype: int,

@@ -310,3 +310,24 @@ def test_refused_launches_leave_state(L):
                 assert (lo.n_tokens, lo.n_quantized, lo.n_vquantized) == (0, 0, 0)
         finally:
             kivi.kivi_cache_destroy(h)
+
+
+def test_noalloc_scratch_limit(L):
+    """kivi_decode_attn_noalloc refuses, before touching the device, a cache
+    whose decode partials exceed the library's fixed array; the limit in the
+    binding matches the header's."""
+    hdr = open(HEADER).read()
+    assert re.search(r"#define KIVI_NOALLOC_SCRATCH_BYTES \(\(size_t\)32 << 20\)", hdr)
+    assert kivi.KIVI_NOALLOC_SCRATCH_BYTES == 32 << 20
+    for B, ok in ((32, True), (512, False)):
+        cfg = kivi.make_config(B, 8, 32, bits=2, residual=128, max_tokens=64)
+        h = kivi.kivi_cache_create(cfg, FAKE_DEV, kivi.kivi_cache_bytes(cfg))
+        try:
+            ws = kivi.kivi_decode_workspace_bytes(h)
+            assert (ws <= kivi.KIVI_NOALLOC_SCRATCH_BYTES) == ok, ws
+            with pytest.raises(kivi.KiviError) as e:
+                kivi.kivi_decode_attn_noalloc(h, FAKE_DEV, kivi.KIVI_F16, 0.0, FAKE_DEV, 0)
+            # empty cache: STATE when the partials fit, BUFFER_TOO_SMALL when not
+            assert e.value.status == (kivi.KIVI_ERR_STATE if ok else kivi.KIVI_ERR_BUFFER_TOO_SMALL)
+        finally:
+            kivi.kivi_cache_destroy(h)
