@@ -86,30 +86,116 @@ def append_bytes(B, H, n, Q, bits, D=128, G=32, esize=2):
     return q_el * (esize + bits / 8 + 4 / G) + r_el * 2 * esize
 
 
-def cpu_baseline(k_dev, v_dev, q_dev, bits, R, H, Hq, sample_b):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload
-    (the first `sample_b` batch entries: sample_b * H streams)."""
-    import numpy as np
+def cpu_facts():
+    """Host facts for the CPU baseline: usable cores, OMP_NUM_THREADS, CPU model."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = min(cores, int(omp)) if omp and omp.isdigit() and int(omp) > 0 else cores
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": cores, "OMP_NUM_THREADS": omp, "threads": threads, "cpu_model": model}
+
+
+def _oracle_stream(k, v, q, bits, R, gq, b, h):
+    """The oracle on one (batch, KV-head) stream: build_cache (quantize),
+    then dequantize + fp64 attention for its gq query heads.  Returns the
+    two durations (the C calls release the GIL, so streams run in parallel)."""
     import oracle
-    k = k_dev[:sample_b].cpu().numpy()
-    v = v_dev[:sample_b].cpu().numpy()
-    q = q_dev[:sample_b].cpu().numpy()
-    n = k.shape[2]
+    ks, vs = k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1]
     t0 = time.perf_counter()
-    c = oracle.build_cache(k, v, bits, 32, R)
+    c = oracle.build_cache(ks, vs, bits, 32, R)
     t1 = time.perf_counter()
-    kh, vh = oracle.dequant_cache(k, v, c)
-    oracle.decode_attn(q, kh, vh)
+    kh, vh = oracle.dequant_cache(ks, vs, c)
+    oracle.decode_attn(q[b:b + 1, h * gq:(h + 1) * gq], kh, vh)
     t2 = time.perf_counter()
-    Q = c["qk"]
-    return dict(
-        value=decode_bytes(sample_b, H, Hq, n, Q, bits) / (t2 - t1) / 1e9,
-        unit="GB/s", cores=1, kind="oracle",
-        quantize_GBps=append_bytes(sample_b, H, n, Q, bits) / (t1 - t0) / 1e9,
-        sample="%d of the workload's batch entries (%d streams x %d tokens); decode = "
-               "dequantize + fp64 attention, quantize = build_cache; single-threaded C"
-               % (sample_b, sample_b * H, n),
-        seconds=dict(quantize=t1 - t0, decode=t2 - t1))
+    return t1 - t0, t2 - t1
+
+
+def _oracle_pass(k, v, q, bits, R, streams, threads):
+    """Wall-clock seconds of the oracle over `streams` (list of (b, h)) on
+    `threads` threads: quantize of every stream, then decode of every stream
+    (two phases, each timed on its own)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    H, Hq = k.shape[1], q.shape[1]
+    gq = Hq // H
+    caches = [None] * len(streams)
+
+    def quant(i):
+        b, h = streams[i]
+        caches[i] = oracle.build_cache(k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], bits, 32, R)
+
+    def dec(i):
+        b, h = streams[i]
+        ks, vs = k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1]
+        kh, vh = oracle.dequant_cache(ks, vs, caches[i])
+        oracle.decode_attn(q[b:b + 1, h * gq:(h + 1) * gq], kh, vh)
+        caches[i] = None
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(quant, range(len(streams))))
+        t1 = time.perf_counter()
+        list(ex.map(dec, range(len(streams))))
+        t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
+
+
+def cpu_baseline(k_dev, v_dev, q_dev, bits, R, H, Hq, c5=None):
+    """The CPU oracle as it stands (single-threaded C per call), timed on the
+    host's cores with one call per (batch, KV-head) stream spread over a
+    thread pool -- the streams are independent -- and on one thread over one
+    batch entry.  The whole long-context workload runs on all threads; the
+    B32 x 131072 workload (c5 = (k, v, q) of its first 16 streams, host
+    arrays) on a fixed sample of 16 of its 256 streams, scaled by its
+    bytes.  GB/s are over the same algorithmic bytes as the GPU figures."""
+    import oracle
+    oracle.lib()
+    facts = cpu_facts()
+    k = k_dev.cpu().numpy()
+    v = v_dev.cpu().numpy()
+    q = q_dev.cpu().numpy()
+    B, n = k.shape[0], k.shape[2]
+    Q = max(0, n - R) // 32 * 32
+    streams = [(b, h) for b in range(B) for h in range(H)]
+    tq, td = _oracle_pass(k, v, q, bits, R, streams, facts["threads"])
+    one = [(0, h) for h in range(H)]
+    tq1, td1 = _oracle_pass(k, v, q, bits, R, one, 1)
+    res = dict(
+        value=decode_bytes(B, H, Hq, n, Q, bits) / td / 1e9,
+        unit="GB/s", cores=facts["threads"], kind="oracle",
+        quantize_GBps=append_bytes(B, H, n, Q, bits) / tq / 1e9,
+        sample="the whole long-context workload (%d streams x %d tokens) on %d threads, one "
+               "oracle call per stream; decode = dequantize + fp64 attention, quantize = "
+               "build_cache" % (len(streams), n, facts["threads"]),
+        seconds=dict(quantize=tq, decode=td),
+        one_thread=dict(streams=len(one), decode_GBps=decode_bytes(1, H, Hq, n, Q, bits) / td1 / 1e9,
+                        quantize_GBps=append_bytes(1, H, n, Q, bits) / tq1 / 1e9,
+                        seconds=dict(quantize=tq1, decode=td1)),
+        host=facts)
+    if c5 is not None:
+        k5, v5, q5, B5, n5 = c5
+        Q5 = max(0, n5 - R) // 32 * 32
+        sb = k5.shape[0]
+        s5 = [(b, h) for b in range(sb) for h in range(H)]
+        tq5, td5 = _oracle_pass(k5, v5, q5, bits, R, s5, facts["threads"])
+        res["b32_ctx131072"] = dict(
+            sample="%d of %d streams (the first %d batch entries), extrapolated: GB/s over the "
+                   "sample's bytes" % (len(s5), B5 * H, sb),
+            decode_GBps=decode_bytes(sb, H, Hq, n5, Q5, bits) / td5 / 1e9,
+            quantize_GBps=append_bytes(sb, H, n5, Q5, bits) / tq5 / 1e9,
+            seconds=dict(quantize=tq5, decode=td5), extrapolated=True)
+    return res
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
@@ -258,6 +344,97 @@ def streaming_measure(policy, do_evict, evict, evict_out, steps=512, prefill=819
     return res
 
 
+def evict_read(evict, evict_out):
+    """Read 1 GiB of an unrelated buffer (leaves no dirty lines behind)."""
+    import torch
+    torch.amax(evict, dim=0, out=evict_out)
+
+
+def long_context_measure(B, n, R, bits, G, chunk, n_out, steps, warmup, stream, evict, evict_out,
+                         do_evict, cfg_id=3, keep=False):
+    """Prefill + decode on one workload: inputs drawn on the device first;
+    each step = a reset cache, the appends of all chunks (quantize + ring),
+    then one decode step; each phase timed with HIP events on `stream`,
+    after an eviction read.  Returns the record (and with keep=True also
+    the cache, inputs and query for later use)."""
+    import torch
+    from kv_cache_quantization_amd import KiviCache, synth
+    H, Hq, D = 8, 32, 128
+    dev = stream.device
+    chunk = chunk or n
+    chunks = []
+    for ci in range(0, n, chunk):
+        cn = min(chunk, n - ci)
+        chunks.append(synth.kv_device(cfg_id, B, H, cn, D, chunk=ci // chunk, device=dev))
+    q = synth.queries_device(cfg_id, B, Hq, D, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    cache = KiviCache(B, H, Hq, n, bits=bits, group=G, residual=R, device=dev, key_outliers=n_out)
+    cache.workspace()
+    torch.cuda.synchronize()
+
+    def step(evs):
+        cache.reset()
+        if do_evict:
+            evict_read(evict, evict_out)
+        evs[0].record(stream)
+        for k, v in chunks:
+            cache.append(k, v)
+        evs[1].record(stream)
+        if do_evict:
+            evict_read(evict, evict_out)
+        evs[2].record(stream)
+        cache.decode(q, out=out)
+        evs[3].record(stream)
+
+    for _ in range(warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    app_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
+    dec_ms = sorted(e[2].elapsed_time(e[3]) for e in events)
+    t_app = sum(app_ms) / steps / 1e3
+    t_dec = sum(dec_ms) / steps / 1e3
+    lo = cache.layout()
+    Q = lo.n_quantized
+    dbytes = decode_bytes(B, H, Hq, n, Q, bits, G=G)
+    abytes = append_bytes(B, H, n, Q, bits, G=G)
+    if n_out:
+        # the kept channels' fp16 values (2 bytes per token and channel) and
+        # their indices (2 bytes per channel and group), read by the decode
+        # and written by the append
+        extra = B * H * (Q // 32) * n_out * (32 * 2 + 2)
+        dbytes += extra
+        abytes += extra
+    dec_gbps = dbytes / t_dec / 1e9
+    app_gbps = abytes / t_app / 1e9
+    splits, gps = cache.decode_plan()
+    rec = {
+        "workload": "KIVI %d-bit decode over a %s prefill: batch %d, 8 KV heads, 32 query heads, "
+                    "head_dim 128, context %d, group %d, residual %d%s"
+                    % (bits, "one-shot" if chunk == n else "%d-token-chunk" % chunk, B, n, G, R,
+                       "" if not n_out else ", %d fp16 key channels per key group" % n_out),
+        "batch": B, "context": n, "bits": bits, "group": G, "residual": R, "chunk": chunk,
+        "quantized_tokens": Q, "decode_splits_per_stream": splits, "groups_per_split": gps,
+        "decode": {"ms": round(t_dec * 1e3, 4), "median_ms": round(dec_ms[len(dec_ms) // 2], 4),
+                   "GBps": round(dec_gbps, 1), "bytes": int(dbytes),
+                   "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4)},
+        "quantize": {"ms": round(t_app * 1e3, 4), "median_ms": round(app_ms[len(app_ms) // 2], 4),
+                     "GBps": round(app_gbps, 1), "bytes": int(abytes),
+                     "frac_hbm_peak": round(app_gbps / HBM_PEAK_GBPS, 4)},
+        "steps": steps, "wall_s": round(t1 - t0, 3),
+    }
+    if keep:
+        return rec, dict(cache=cache, chunks=chunks, q=q, out=out)
+    del cache, chunks
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,7 +448,8 @@ def main():
     ap.add_argument("--key-outliers", type=int, default=0, choices=(0, 1, 2, 3),
                     help="key channels kept in fp16 per 32-token key group (outlier-aware keys)")
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk (0: one shot)")
-    ap.add_argument("--cpu-sample", type=int, default=6, help="batch entries timed on the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=1,
+                    help="time the CPU oracle on the host's cores (0: skip)")
     ap.add_argument("--no-evict", action="store_true")
     ap.add_argument("--stream-steps", type=int, default=512,
                     help="also time the streaming workload (batch 8, prefill 8192, then this many "
@@ -279,6 +457,10 @@ def main():
     ap.add_argument("--attn-queries", type=int, default=256,
                     help="also time the attention of this many causal queries per head over "
                          "the same cache (a chunked-prefill step; 0: skip)")
+    ap.add_argument("--other-configs", type=int, default=1,
+                    help="also time the other decode workloads: B32 x 131072 in 8192-token "
+                         "chunks at 2 and 4 bits, this workload at 4 bits, and B1 x 4096 with "
+                         "residual 32 (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -288,7 +470,6 @@ def main():
         sys.exit(2)
 
     import torch
-    from kv_cache_quantization_amd import KiviCache, synth
 
     B, H, Hq, D = args.batch, 8, 32, 128
     n, R, bits, G = args.context, args.residual, args.bits, args.group
@@ -296,19 +477,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-
-    # inputs resident in HBM before any timing
-    chunks = []
-    for ci in range(0, n, chunk):
-        cn = min(chunk, n - ci)
-        chunks.append(synth.kv_device(3, B, H, cn, D, chunk=ci // chunk, device=dev))
-    q = synth.queries_device(3, B, Hq, D, device=dev)
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    n_out = args.key_outliers
-    cache = KiviCache(B, H, Hq, n, bits=bits, group=G, residual=R, device=dev, key_outliers=n_out)
-    cache.workspace()
     evict = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
     evict_out = torch.empty((), dtype=torch.float32, device=dev)
+    do_evict = not args.no_evict
     torch.cuda.synchronize()
 
     # Copy yardstick: one elementwise kernel reads COPY_BYTES and writes
@@ -327,93 +498,46 @@ def main():
     copy_gbps = 2 * COPY_BYTES / (sorted(copy_ms[1:])[1] / 1e3) / 1e9
     del cdst
 
-    def step(evs):
-        cache.reset()
-        if not args.no_evict:
-            torch.amax(evict, dim=0, out=evict_out)
-        evs[0].record(stream)
-        for k, v in chunks:
-            cache.append(k, v)
-        evs[1].record(stream)
-        if not args.no_evict:
-            torch.amax(evict, dim=0, out=evict_out)
-        evs[2].record(stream)
-        cache.decode(q, out=out)
-        evs[3].record(stream)
-
-    for _ in range(args.warmup):
-        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    app_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
-    dec_ms = sorted(e[2].elapsed_time(e[3]) for e in events)
-    t_app = sum(app_ms) / args.steps / 1e3
-    t_dec = sum(dec_ms) / args.steps / 1e3
-    lo = cache.layout()
-    Q = lo.n_quantized
-    dbytes = decode_bytes(B, H, Hq, n, Q, bits, G=G)
-    abytes = append_bytes(B, H, n, Q, bits, G=G)
-    if n_out:
-        # the kept channels' fp16 values (2 bytes per token and channel) and
-        # their indices (2 bytes per channel and group), read by the decode
-        # and written by the append
-        extra = B * H * (Q // 32) * n_out * (32 * 2 + 2)
-        dbytes += extra
-        abytes += extra
-    dec_gbps = dbytes / t_dec / 1e9
-    app_gbps = abytes / t_app / 1e9
-    splits, gps = cache.decode_plan()
+    main_rec, kept = long_context_measure(B, n, R, bits, G, chunk, args.key_outliers, args.steps,
+                                          args.warmup, stream, evict, evict_out, do_evict, keep=True)
+    cache, q = kept["cache"], kept["q"]
+    dec_gbps = main_rec["decode"]["GBps"]
+    app_gbps = main_rec["quantize"]["GBps"]
     traffic, traffic_src = (None, "workload without a counter summary")
     atraffic = None
-    if (B, n, R, bits, chunk, G, n_out) == (16, 32768, 128, 2, 32768, 32, 0):
+    if (B, n, R, bits, chunk, G, args.key_outliers) == (16, 32768, 128, 2, 32768, 32, 0):
         traffic, traffic_src = counter_traffic("decode_b16_ctx32768_2bit_counters.txt")
         atraffic, _ = counter_traffic("decode_b16_ctx32768_2bit_counters.txt",
                                       "append_traffic_bytes_per_launch")
 
     rec = {
         "metric": "decode-attn GB/s over packed 2-bit KV (% of HBM peak); quantize GB/s",
-        "value": round(dec_gbps, 1),
+        "value": dec_gbps,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round((t1 - t0) / args.steps * 1e3, 4),
+        "ms_per_step": round(main_rec["wall_s"] / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u%d codes, f16 side data, f32 accumulate" % bits,
         "data": "synthetic: K,V ~ N(0,1) fp16 with 4 outlier key channels x5 per KV head, "
                 "q ~ N(0,1) fp16, seeded torch generator on the device",
-        "config": {
-            "workload": "KIVI %d-bit decode over a one-shot prefill: batch %d, 8 KV heads, "
-                        "32 query heads, head_dim 128, context %d, group %d, residual %d%s%s"
-                        % (bits, B, n, G, R, "" if chunk == n else ", prefill in %d-token chunks" % chunk,
-                           "" if not n_out else ", %d fp16 key channels per key group" % n_out),
-            "batch": B, "kv_heads": H, "q_heads": Hq, "head_dim": D, "context": n,
-            "group": G, "residual": R, "bits": bits, "quantized_tokens": Q,
-            "decode_splits_per_stream": splits, "groups_per_split": gps,
-        },
-        "decode": {"ms": round(t_dec * 1e3, 4), "median_ms": round(dec_ms[len(dec_ms) // 2], 4),
-                   "GBps": round(dec_gbps, 1), "bytes": int(dbytes),
-                   "pct_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
-                   "pct_copy": round(100 * dec_gbps / copy_gbps, 2)},
-        "quantize": {"ms": round(t_app * 1e3, 4), "median_ms": round(app_ms[len(app_ms) // 2], 4),
-                     "GBps": round(app_gbps, 1), "bytes": int(abytes),
-                     "pct_hbm_peak": round(100 * app_gbps / HBM_PEAK_GBPS, 2),
-                     "pct_copy": round(100 * app_gbps / copy_gbps, 2)},
+        "config": dict({k_: main_rec[k_] for k_ in ("workload", "batch", "context", "group",
+                                                   "residual", "bits", "quantized_tokens",
+                                                   "decode_splits_per_stream", "groups_per_split")},
+                       kv_heads=H, q_heads=Hq, head_dim=D),
+        "decode": dict(main_rec["decode"], pct_hbm_peak=round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
+                       pct_copy=round(100 * dec_gbps / copy_gbps, 2)),
+        "quantize": dict(main_rec["quantize"], pct_hbm_peak=round(100 * app_gbps / HBM_PEAK_GBPS, 2),
+                         pct_copy=round(100 * app_gbps / copy_gbps, 2)),
         "copy": {"GBps": round(copy_gbps, 1), "bytes": 2 * COPY_BYTES,
                  "what": "torch.neg over 512 MiB fp32 (read 512 MiB + write 512 MiB), median of 3"},
         "roofline": {
             "bound": "hbm",
             "kernel": "decode (split-K pass + combine, one kivi_decode_attn call)",
-            "achieved": round(dec_gbps, 1),
+            "achieved": dec_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
@@ -422,32 +546,69 @@ def main():
         },
         "roofline_quantize": {
             "bound": "hbm", "kernel": "append (quantize + ring copy, one kivi_append call)",
-            "achieved": round(app_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "achieved": app_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(app_gbps / HBM_PEAK_GBPS, 4), "traffic": atraffic,
         },
         "timing": "HIP events on the launch stream around each phase; mean over the timed steps;"
                   " 1 GiB eviction read before each phase (outside the phase events)"
-                  if not args.no_evict else "HIP events, no eviction (warm)",
+                  if do_evict else "HIP events, no eviction (warm)",
     }
     if args.attn_queries > 0:
         rec["attn"] = attn_measure(cache, B, Hq, n, args.attn_queries, stream, evict, evict_out,
-                                   not args.no_evict)
+                                   do_evict)
+    host_inputs = None
+    if args.cpu_sample > 0 and chunk == n and G == 32 and args.key_outliers == 0:
+        k0, v0 = kept["chunks"][0]
+        host_inputs = (k0.cpu(), v0.cpu(), q.cpu())
+    del cache, kept
+    torch.cuda.empty_cache()
+    c5_host = None
+    if args.other_configs > 0:
+        others = {}
+        # the largest workload: B32 x 131072 tokens appended in 8192-token
+        # chunks, decode over the full packed cache, at 2 and 4 bits
+        for b5 in (2, 4):
+            others["b32_ctx131072_%dbit" % b5] = long_context_measure(
+                32, 131072, 128, b5, 32, 8192, 0, 10, 2, stream, evict, evict_out, do_evict,
+                cfg_id=5)
+        if bits != 4 or (B, n) != (16, 32768):
+            others["b16_ctx32768_4bit"] = long_context_measure(
+                16, 32768, 128, 4, 32, 0, 0, 10, 2, stream, evict, evict_out, do_evict)
+        # one layer of a single sequence: launch-bound, reported only
+        others["b1_ctx4096_2bit"] = long_context_measure(
+            1, 4096, 32, 2, 32, 0, 0, 20, 5, stream, evict, evict_out, do_evict, cfg_id=2)
+        rec["other_configs"] = others
+        if args.cpu_sample > 0:
+            from kv_cache_quantization_amd import synth
+            k5, v5 = synth.kv_device(5, 32, H, 8192, D, chunk=0, device=dev)
+            # the sample's streams over their whole 131072-token context
+            ks = [k5[:2]]
+            vs = [v5[:2]]
+            del k5, v5
+            for ci in range(1, 16):
+                kc, vc = synth.kv_device(5, 32, H, 8192, D, chunk=ci, device=dev)
+                ks.append(kc[:2].clone())
+                vs.append(vc[:2].clone())
+                del kc, vc
+            q5 = synth.queries_device(5, 32, Hq, D, device=dev)[:2]
+            c5_host = (torch.cat(ks, 2).cpu().numpy(), torch.cat(vs, 2).cpu().numpy(),
+                       q5.cpu().numpy(), 32, 131072)
+            del ks, vs
+            torch.cuda.empty_cache()
     if args.stream_steps > 0:
         from kv_cache_quantization_amd import kivi
         rec["streaming"] = {
             "workload": "batch 8, 8 KV heads, 32 query heads, head_dim 128, 2-bit, group 32, "
                         "residual 128: prefill 8192 tokens, then %d steps of (append one token, "
                         "decode attention)" % args.stream_steps,
-            "policies": [streaming_measure(pol, not args.no_evict, evict, evict_out,
+            "policies": [streaming_measure(pol, do_evict, evict, evict_out,
                                            steps=args.stream_steps, fused=fu)
                          for pol, fu in ((kivi.KIVI_FLUSH_WINDOW, False),
                                          (kivi.KIVI_FLUSH_WINDOW, True),
                                          (kivi.KIVI_FLUSH_PAPER, False))],
         }
-    if args.cpu_sample > 0:
-        k0, v0 = chunks[0]
-        if chunk == n and G == 32 and n_out == 0:
-            rec["cpu_baseline"] = cpu_baseline(k0, v0, q, bits, R, H, Hq, args.cpu_sample)
+    if host_inputs is not None:
+        rec["cpu_baseline"] = cpu_baseline(*host_inputs, bits, R, H, Hq, c5=c5_host)
     print(json.dumps(rec), flush=True)
 
 
