@@ -23,6 +23,7 @@ _LIB = os.path.join(_HERE, "libkivi_oracle.so")
 
 POLICY_WINDOW = 0
 POLICY_PAPER = 1
+POLICY_SEGMENT = 2      # KCVT: one key group per channel and flush segment
 
 _lib = None
 
@@ -59,6 +60,12 @@ def lib():
                                          i64, i64, P, P, P, P, P, P]
         L.oracle_dequant_cache.argtypes = [P, P, i32, i32, i32, i64, i32, i32,
                                            i64, i64, P, P, P, P, P, P, P, P]
+        L.oracle_dequant_cache_kv.argtypes = [P, P, i32, i32, i32, i64, i32, i32, i32,
+                                              i64, i64, P, P, P, P, P, P, P, P]
+        L.oracle_build_cache_segments.argtypes = [P, P, i32, i32, i32, i64, i32, i32, P, i32,
+                                                  P, P, P, P, P, P]
+        L.oracle_pack_blocks_kv2.argtypes = [i32, i32, i32, i32, i64, i64, i32, i64,
+                                             P, P, P, P, P, P, P]
         L.oracle_decode_attn.argtypes = [P, P, P, i32, i32, i32, i64, i32, f64, P]
         L.oracle_attn_queries.argtypes = [P, P, P, i32, i32, i32, i64, i64, i32, f64, i32, P]
         L.oracle_block_bytes.restype = i64
@@ -137,12 +144,37 @@ def quantized_prefix(n: int, group: int, residual: int, policy: int = POLICY_WIN
 # --------------------------------------------------------------------------
 # whole-cache views
 # --------------------------------------------------------------------------
+def segment_ends(appends, residual: int, deferred=()):
+    """Flush segments of the segment (KCVT) policy for a sequence of appends
+    of `appends[i]` tokens each: every append that moves the quantized
+    prefix Q(n) = n - n mod R quantizes the tokens [Q_old, Q_new) as one
+    segment.  `deferred`: indices of appends that only buffer their rows
+    (the next one that does not folds them into its segment).  Returns the
+    list of segment ends."""
+    n, q, ends = 0, 0, []
+    for i, m in enumerate(appends):
+        n += m
+        if i in deferred:
+            continue
+        qn, _ = quantized_prefix(n, 32, residual, POLICY_SEGMENT)
+        if qn > q:
+            ends.append(qn)
+            q = qn
+    return ends
+
+
 def build_cache(k, v, bits: int, group: int, residual: int,
-                policy: int = POLICY_WINDOW, key_outliers: int = 0) -> dict:
+                policy: int = POLICY_WINDOW, key_outliers: int = 0, segments=None) -> dict:
     """Logical KIVI cache of K, V ([B, H, n, D], float16 or float32).
     key_outliers > 0: per key group, that many channels kept in fp16
     (oracle_key_outliers): kout_idx [B, H, qk/G, n], kout_val fp16 bits
-    [B, H, qk/G, n, G]."""
+    [B, H, qk/G, n, G].
+    policy = POLICY_SEGMENT (KCVT): `segments` lists the flush segment ends
+    (segment_ends); keys get one group per (segment, channel), stored per
+    32-token block ("Gk" = 32), values one group per token over all D
+    channels ("Gv" = D; `group` must be D)."""
+    if policy == POLICY_SEGMENT:
+        return _build_cache_segments(k, v, bits, group, residual, segments)
     kk, dt = _kv(k)
     vv, dt2 = _kv(v)
     assert dt == dt2 and kk.shape == vv.shape
@@ -174,6 +206,35 @@ def build_cache(k, v, bits: int, group: int, residual: int,
     return c
 
 
+def _build_cache_segments(k, v, bits, group, residual, segments):
+    kk, dt = _kv(k)
+    vv, dt2 = _kv(v)
+    assert dt == dt2 and kk.shape == vv.shape
+    B, H, n, D = kk.shape
+    assert group == D, "KCVT values: one group over all D channels"
+    ends = np.ascontiguousarray(np.asarray(list(segments or []), dtype=np.int64))
+    assert all(int(e) % 32 == 0 for e in ends) and list(ends) == sorted(set(ends.tolist()))
+    Q = int(ends[-1]) if len(ends) else 0
+    assert Q <= n
+    c = dict(
+        B=B, H=H, n=n, D=D, G=group, Gk=32, Gv=D, bits=bits, R=residual,
+        policy=POLICY_SEGMENT, qk=Q, qv=Q, segments=[int(e) for e in ends],
+        kcodes=np.zeros((B, H, Q, D), np.uint8),
+        kzero16=np.zeros((B, H, Q // 32, D), np.uint16),
+        kscale16=np.zeros((B, H, Q // 32, D), np.uint16),
+        vcodes=np.zeros((B, H, Q, D), np.uint8),
+        vzero16=np.zeros((B, H, Q, 1), np.uint16),
+        vscale16=np.zeros((B, H, Q, 1), np.uint16),
+        key_outliers=0,
+    )
+    lib().oracle_build_cache_segments(_p(kk), _p(vv), dt, B, H, n, D, bits, _p(ends), len(ends),
+                                      _p(c["kcodes"]), _p(c["kzero16"]), _p(c["kscale16"]),
+                                      _p(c["vcodes"]), _p(c["vzero16"]), _p(c["vscale16"]))
+    c["k_resid"] = np.ascontiguousarray(np.asarray(k)[:, :, Q:, :])
+    c["v_resid"] = np.ascontiguousarray(np.asarray(v)[:, :, Q:, :])
+    return c
+
+
 def dequant_cache(k, v, cache: dict):
     """Float32 K_hat, V_hat [B, H, n, D] of the cache built from k, v."""
     kk, dt = _kv(k)
@@ -181,8 +242,9 @@ def dequant_cache(k, v, cache: dict):
     B, H, n, D = kk.shape
     khat = np.empty((B, H, n, D), np.float32)
     vhat = np.empty((B, H, n, D), np.float32)
-    lib().oracle_dequant_cache(
-        _p(kk), _p(vv), dt, B, H, n, D, cache["G"], cache["qk"], cache["qv"],
+    lib().oracle_dequant_cache_kv(
+        _p(kk), _p(vv), dt, B, H, n, D, cache.get("Gk", cache["G"]), cache.get("Gv", cache["G"]),
+        cache["qk"], cache["qv"],
         _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
         _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
         _p(khat), _p(vhat))
@@ -246,7 +308,8 @@ def pack_blocks(cache: dict, max_groups: int | None = None) -> np.ndarray:
         max_groups = ng
     assert max_groups >= ng
     out = np.zeros((B * H, max_groups, block_bytes(bits)), np.uint8)
-    lib().oracle_pack_blocks_kv(B, H, cache["G"], qk, qv, bits, max_groups,
+    lib().oracle_pack_blocks_kv2(B, H, cache.get("Gk", cache["G"]), cache.get("Gv", cache["G"]),
+                                 qk, qv, bits, max_groups,
                                 _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
                                 _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
                                 _p(out))

@@ -21,13 +21,17 @@
  *        split; 3.2.3 Algorithm 1 (prefill / decoding) and its example.
  *  [CQ]  "KV Cache Compression > Cache Quantization" (Language AI Handbook):
  *        uniform quantization, the half-step error bound, QuantizedCache.
+ *  [GR]  GEAR paper review (velog): "KCVT" (KIVI's coarse-grained grouping)
+ *        and "streaming buffer strategy".
  *
  * Parity status: every function is pinned by tests/test_oracle_pins.py to
  * what the pages print or to closed forms.  The packers (oracle_pack_blocks_kv,
  * oracle_pack_outlier_records) are pinned by tests/test_oracle_layout_pins.py,
  * which decodes their output with its own forward reading of the documented
  * byte layout (never through code_position) back to the pinned logical
- * arrays, the paper-policy zero rows included.  The bit order itself is a
+ * arrays, the paper-policy zero rows included.  The KCVT segment builder is
+ * pinned by tests/test_oracle_kcvt_pins.py (reductions to pinned KIVI group
+ * sizes, closed-form statistics, locality, the documented block layout).  The bit order itself is a
  * layout choice of this library: the pages fix the storage cost (b bits per
  * code and two fp16 per group), not the order.
  *
@@ -160,12 +164,18 @@ float oracle_dequant_one(uint8_t code, uint16_t zero16, uint16_t scale16)
 /* tokens in full precision (Q_K = n - r); values keep the newest R          */
 /* (Q_V = max(0, n - R)).                                                    */
 /* ------------------------------------------------------------------------ */
-enum { ORACLE_POLICY_WINDOW = 0, ORACLE_POLICY_PAPER = 1 };
+/* Segment policy (KCVT, the GEAR review's "KCVT" and "streaming buffer     */
+/* strategy" sections): new tokens wait in a full-precision buffer of R      */
+/* tokens and are compressed when it fills, keys and values alike:           */
+/*        Q(n) = n - (n mod R).                                              */
+enum { ORACLE_POLICY_WINDOW = 0, ORACLE_POLICY_PAPER = 1, ORACLE_POLICY_SEGMENT = 2 };
 
 void oracle_quantized_prefix(int64_t n, int group, int residual, int policy,
                              int64_t *qk, int64_t *qv)
 {
-    if (policy == ORACLE_POLICY_PAPER) {
+    if (policy == ORACLE_POLICY_SEGMENT) {
+        *qk = *qv = n - (n % residual);
+    } else if (policy == ORACLE_POLICY_PAPER) {
         /* R > 0 required by the paper's definition r = l mod R. */
         *qk = n - (n % residual);
         *qv = n > residual ? n - residual : 0;
@@ -227,6 +237,66 @@ void oracle_build_cache(const void *k, const void *v, int dtype,
                         vcodes[(((int64_t)b * H + h) * qv + t) * D + j * G + i] = cg[i];
                 }
         }
+    free(grp);
+    free(cg);
+}
+
+/* ------------------------------------------------------------------------ */
+/* KCVT: the coarse-grained grouping of the GEAR review ("KCVT" section).    */
+/* Keys are quantized per channel with one group per channel over all the    */
+/* tokens compressed together, values per token with one group over all D    */
+/* channels.  With the streaming buffer ("streaming buffer strategy"         */
+/* section) the tokens compressed together are those of one flush: the whole */
+/* prompt at prefill, then each buffer of new tokens.  Reading taken here:   */
+/* segment i is tokens [seg_end[i-1], seg_end[i]) (seg_end[-1] = 0), every   */
+/* boundary a multiple of 32; the key group of (segment i, channel c) is     */
+/* K[seg_end[i-1] .. seg_end[i]-1][c].  Q = seg_end[n_seg-1] tokens are      */
+/* quantized.  Outputs:                                                      */
+/*   kcodes [B][H][Q][D] u8; kzero16 / kscale16 [B][H][Q/32][D]: the pair of */
+/*   the segment each 32-token block lies in (repeated over its blocks);     */
+/*   vcodes [B][H][Q][D] u8; vzero16 / vscale16 [B][H][Q][1].                */
+/* ------------------------------------------------------------------------ */
+void oracle_build_cache_segments(const void *k, const void *v, int dtype,
+                                 int B, int H, int64_t n, int D, int bits,
+                                 const int64_t *seg_end, int n_seg,
+                                 uint8_t *kcodes, uint16_t *kzero16, uint16_t *kscale16,
+                                 uint8_t *vcodes, uint16_t *vzero16, uint16_t *vscale16)
+{
+    const int T = 32;
+    int64_t Q = n_seg > 0 ? seg_end[n_seg - 1] : 0;
+    int64_t longest = D;
+    for (int i = 0; i < n_seg; i++) {
+        int64_t a = i ? seg_end[i - 1] : 0;
+        if (seg_end[i] - a > longest) longest = seg_end[i] - a;
+    }
+    float *grp = (float *)malloc(sizeof(float) * (size_t)longest);
+    uint8_t *cg = (uint8_t *)malloc((size_t)longest);
+    for (int64_t s = 0; s < (int64_t)B * H; s++) {
+        int64_t base = s * n * D;
+        /* keys: one group per (segment, channel) */
+        for (int i = 0; i < n_seg; i++) {
+            int64_t a = i ? seg_end[i - 1] : 0, e = seg_end[i];
+            int len = (int)(e - a);
+            for (int c = 0; c < D; c++) {
+                for (int t = 0; t < len; t++)
+                    grp[t] = load_elem(k, dtype, base + (a + t) * D + c);
+                uint16_t z16, s16;
+                oracle_group_quant(grp, len, bits, cg, NULL, NULL, &z16, &s16);
+                for (int t = 0; t < len; t++) kcodes[(s * Q + a + t) * D + c] = cg[t];
+                for (int64_t j = a / T; j < e / T; j++) {
+                    kzero16[(s * (Q / T) + j) * D + c] = z16;
+                    kscale16[(s * (Q / T) + j) * D + c] = s16;
+                }
+            }
+        }
+        /* values: one group per token over all D channels */
+        for (int64_t t = 0; t < Q; t++) {
+            for (int c = 0; c < D; c++) grp[c] = load_elem(v, dtype, base + t * D + c);
+            oracle_group_quant(grp, D, bits, cg, NULL, NULL, &vzero16[s * Q + t],
+                               &vscale16[s * Q + t]);
+            for (int c = 0; c < D; c++) vcodes[(s * Q + t) * D + c] = cg[c];
+        }
+    }
     free(grp);
     free(cg);
 }
@@ -311,6 +381,42 @@ void oracle_apply_key_outliers(int B, int H, int64_t n, int D, int G, int64_t qk
 /* the full-precision residual are taken as they are, converted to float).   */
 /* khat, vhat: [B][H][n][D] float32.                                         */
 /* ------------------------------------------------------------------------ */
+/* Key parameters per Gk tokens, value parameters per Gv channels (the      */
+/* per-group arrays of oracle_build_cache have Gk = Gv = G; those of         */
+/* oracle_build_cache_segments have Gk = 32, Gv = D).                        */
+void oracle_dequant_cache_kv(const void *k, const void *v, int dtype,
+                             int B, int H, int64_t n, int D, int Gk, int Gv,
+                             int64_t qk, int64_t qv,
+                             const uint8_t *kcodes, const uint16_t *kzero16,
+                             const uint16_t *kscale16,
+                             const uint8_t *vcodes, const uint16_t *vzero16,
+                             const uint16_t *vscale16,
+                             float *khat, float *vhat)
+{
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++) {
+            int64_t s = (int64_t)b * H + h;
+            for (int64_t t = 0; t < n; t++)
+                for (int c = 0; c < D; c++) {
+                    int64_t o = (s * n + t) * D + c;
+                    if (t < qk) {
+                        int64_t p = (s * (qk / Gk) + t / Gk) * D + c;
+                        khat[o] = oracle_dequant_one(kcodes[(s * qk + t) * D + c],
+                                                     kzero16[p], kscale16[p]);
+                    } else {
+                        khat[o] = load_elem(k, dtype, o);
+                    }
+                    if (t < qv) {
+                        int64_t p = (s * qv + t) * (D / Gv) + c / Gv;
+                        vhat[o] = oracle_dequant_one(vcodes[(s * qv + t) * D + c],
+                                                     vzero16[p], vscale16[p]);
+                    } else {
+                        vhat[o] = load_elem(v, dtype, o);
+                    }
+                }
+        }
+}
+
 void oracle_dequant_cache(const void *k, const void *v, int dtype,
                           int B, int H, int64_t n, int D, int G,
                           int64_t qk, int64_t qv,
@@ -320,28 +426,8 @@ void oracle_dequant_cache(const void *k, const void *v, int dtype,
                           const uint16_t *vscale16,
                           float *khat, float *vhat)
 {
-    for (int b = 0; b < B; b++)
-        for (int h = 0; h < H; h++) {
-            int64_t s = (int64_t)b * H + h;
-            for (int64_t t = 0; t < n; t++)
-                for (int c = 0; c < D; c++) {
-                    int64_t o = (s * n + t) * D + c;
-                    if (t < qk) {
-                        int64_t p = (s * (qk / G) + t / G) * D + c;
-                        khat[o] = oracle_dequant_one(kcodes[(s * qk + t) * D + c],
-                                                     kzero16[p], kscale16[p]);
-                    } else {
-                        khat[o] = load_elem(k, dtype, o);
-                    }
-                    if (t < qv) {
-                        int64_t p = (s * qv + t) * (D / G) + c / G;
-                        vhat[o] = oracle_dequant_one(vcodes[(s * qv + t) * D + c],
-                                                     vzero16[p], vscale16[p]);
-                    } else {
-                        vhat[o] = load_elem(v, dtype, o);
-                    }
-                }
-        }
+    oracle_dequant_cache_kv(k, v, dtype, B, H, n, D, G, G, qk, qv, kcodes, kzero16, kscale16,
+                            vcodes, vzero16, vscale16, khat, vhat);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -498,12 +584,33 @@ int64_t oracle_block_bytes(int bits)
    entry of a token that is not quantized (a value row at or past nv inside a
    block that holds value rows) is 0; blocks past both prefixes are left as
    they are. */
+void oracle_pack_blocks_kv2(int B, int H, int Gk, int Gv, int64_t nk, int64_t nv, int bits,
+                            int64_t max_groups,
+                            const uint8_t *kcodes, const uint16_t *kzero16,
+                            const uint16_t *kscale16,
+                            const uint8_t *vcodes, const uint16_t *vzero16,
+                            const uint16_t *vscale16, uint8_t *out);
+
 void oracle_pack_blocks_kv(int B, int H, int G, int64_t nk, int64_t nv, int bits,
                            int64_t max_groups,
                            const uint8_t *kcodes, const uint16_t *kzero16,
                            const uint16_t *kscale16,
                            const uint8_t *vcodes, const uint16_t *vzero16,
                            const uint16_t *vscale16, uint8_t *out)
+{
+    oracle_pack_blocks_kv2(B, H, G, G, nk, nv, bits, max_groups, kcodes, kzero16, kscale16,
+                           vcodes, vzero16, vscale16, out);
+}
+
+/* As oracle_pack_blocks_kv, with key parameters per Gk tokens and value
+   parameters per Gv channels (the arrays of oracle_build_cache_segments:
+   Gk = 32, Gv = D). */
+void oracle_pack_blocks_kv2(int B, int H, int Gk, int Gv, int64_t nk, int64_t nv, int bits,
+                            int64_t max_groups,
+                            const uint8_t *kcodes, const uint16_t *kzero16,
+                            const uint16_t *kscale16,
+                            const uint8_t *vcodes, const uint16_t *vzero16,
+                            const uint16_t *vscale16, uint8_t *out)
 {
     const int D = 128, T = 32;      /* channels; tokens per block */
     const int64_t cbytes = bits * T * D / 8;
@@ -531,8 +638,8 @@ void oracle_pack_blocks_kv(int B, int H, int G, int64_t nk, int64_t nv, int bits
             uint16_t *vs = kz + D;
             uint16_t *vz = vs + D;
             if (j < ngk) {
-                /* key group of this block: tokens [jT, jT + T) lie in group jT / G */
-                int64_t kg = (s * (nk / G) + (j * T) / G) * D;
+                /* key group of this block: tokens [jT, jT + T) lie in group jT / Gk */
+                int64_t kg = (s * (nk / Gk) + (j * T) / Gk) * D;
                 memset(kc, 0, (size_t)cbytes);
                 for (int t = 0; t < T; t++)
                     for (int c = 0; c < D; c++) {
@@ -552,9 +659,9 @@ void oracle_pack_blocks_kv(int B, int H, int G, int64_t nk, int64_t nv, int bits
                         uint32_t cv = tok < nv ? vcodes[(s * nv + tok) * D + c] : 0;
                         vc[vd[t * D + c]] |= cv << vb[t * D + c];
                     }
-                    /* slot cg: channels 32cg .. 32cg+31, in value group 32cg / G */
+                    /* slot cg: channels 32cg .. 32cg+31, in value group 32cg / Gv */
                     for (int cg = 0; cg < D / T; cg++) {
-                        int64_t vg = (s * nv + tok) * (D / G) + (cg * T) / G;
+                        int64_t vg = (s * nv + tok) * (D / Gv) + (cg * T) / Gv;
                         vs[cg * T + t] = tok < nv ? vscale16[vg] : 0;
                         vz[cg * T + t] = tok < nv ? vzero16[vg] : 0;
                     }
