@@ -65,8 +65,15 @@ typedef enum { KIVI_F16 = 0, KIVI_F32 = 1 } kivi_dtype;
    prefill / decoding phases of Algorithm 1 in 3.2.3: the key residual is
    quantized R tokens at once when it fills up, the oldest value of the
    residual one token per step).  In the 32-token block holding Q_V the value codes
-   and side data of tokens >= Q_V are 0. */
-typedef enum { KIVI_FLUSH_WINDOW = 0, KIVI_FLUSH_PAPER = 1 } kivi_flush_policy;
+   and side data of tokens >= Q_V are 0.
+   KIVI_FLUSH_SEGMENT (KCVT, the GEAR review's "KCVT" and "streaming buffer
+   strategy" sections; needs R > 0 a multiple of 32, G = head_dim, no
+   key_outliers): new tokens wait in the full-precision buffer of R tokens
+   and keys and values are quantized up to Q(n) = n - (n mod R); each append
+   or flush that moves Q quantizes its tokens [Q_old, Q_new) as one segment,
+   with one zero / scale per key channel over the whole segment (stored in
+   each of its blocks) and one per token over all D value channels. */
+typedef enum { KIVI_FLUSH_WINDOW = 0, KIVI_FLUSH_PAPER = 1, KIVI_FLUSH_SEGMENT = 2 } kivi_flush_policy;
 
 /* kivi_append flags. */
 enum {
@@ -86,7 +93,8 @@ typedef struct {
     int32_t bits;         /* b: 2, 4 or 8                                     */
     int32_t group;        /* G: 32, 64 or 128 (key groups of G tokens, value  */
                           /* groups of G channels)                            */
-    int32_t residual;     /* R >= 0, a multiple of G                          */
+    int32_t residual;     /* R >= 0, a multiple of G (segment policy: R > 0,  */
+                          /* a multiple of 32)                                */
     int32_t kv_dtype;     /* kivi_dtype of the K/V rows handed to append      */
     int32_t policy;       /* kivi_flush_policy                                */
     int32_t key_outliers; /* 0..3: per 32-token key group, this many channels  */

@@ -34,6 +34,8 @@ struct kivi_cache {
     uint8_t *base;
     size_t bytes;
     size_t off_blocks, off_ring_k, off_ring_v, off_outliers;
+    size_t off_seg_partial, off_seg_stats;   // segment policy scratch
+    int32_t seg_chunks;                      // chunks of the longest segment
     int64_t max_groups;
     int64_t block_bytes, code_bytes;
     int64_t ring_cap;
@@ -67,11 +69,20 @@ kivi_status validate(const kivi_config *c) {
         return KIVI_ERR_INVALID_ARG;
     if (c->bits != 2 && c->bits != 4 && c->bits != 8) return KIVI_ERR_INVALID_ARG;
     if (c->group < 1 || c->head_dim < 1 || c->head_dim % c->group != 0) return KIVI_ERR_INVALID_ARG;
-    if (c->residual < 0 || c->residual % c->group != 0) return KIVI_ERR_INVALID_ARG;
+    if (c->policy == KIVI_FLUSH_SEGMENT) {
+        // KCVT: values grouped over the whole head, a buffer of whole blocks
+        if (c->residual <= 0 || c->residual % kGroup != 0 || c->group != c->head_dim)
+            return KIVI_ERR_INVALID_ARG;
+        if (c->key_outliers != 0) return KIVI_ERR_UNSUPPORTED;
+    } else if (c->residual < 0 || c->residual % c->group != 0) {
+        return KIVI_ERR_INVALID_ARG;
+    }
     if ((int64_t)c->group * c->bits % 64 != 0) return KIVI_ERR_INVALID_ARG;
     if (c->n_q_heads % c->n_kv_heads != 0) return KIVI_ERR_INVALID_ARG;
     if (c->kv_dtype != KIVI_F16 && c->kv_dtype != KIVI_F32) return KIVI_ERR_INVALID_ARG;
-    if (c->policy != KIVI_FLUSH_WINDOW && c->policy != KIVI_FLUSH_PAPER) return KIVI_ERR_INVALID_ARG;
+    if (c->policy != KIVI_FLUSH_WINDOW && c->policy != KIVI_FLUSH_PAPER &&
+        c->policy != KIVI_FLUSH_SEGMENT)
+        return KIVI_ERR_INVALID_ARG;
     if (c->policy == KIVI_FLUSH_PAPER && c->residual == 0) return KIVI_ERR_INVALID_ARG;
     if (c->key_outliers < 0 || c->key_outliers > kMaxKeyOutliers) return KIVI_ERR_INVALID_ARG;
     // Shapes the kernels are built for.
@@ -89,7 +100,8 @@ kivi_status validate(const kivi_config *c) {
 struct Sizes {
     int64_t max_groups, block_bytes, code_bytes, ring_cap;
     int esize;
-    size_t off_blocks, off_ring_k, off_ring_v, off_outliers, total;
+    int32_t seg_chunks;
+    size_t off_blocks, off_ring_k, off_ring_v, off_outliers, off_seg_partial, off_seg_stats, total;
 };
 
 Sizes sizes_of(const kivi_config *c) {
@@ -108,6 +120,15 @@ Sizes sizes_of(const kivi_config *c) {
     s.total = s.off_outliers;
     if (c->key_outliers > 0)
         s.total += align_up((size_t)(streams * s.max_groups * kOutlierRecordBytes));
+    // segment policy: per-chunk statistics of the longest possible segment
+    // (every block of a stream) and the per-stream statistics, float32
+    s.seg_chunks = (int32_t)((s.max_groups + kSegChunkBlocks - 1) / kSegChunkBlocks);
+    s.off_seg_partial = s.off_seg_stats = s.total;
+    if (c->policy == KIVI_FLUSH_SEGMENT) {
+        s.off_seg_partial = s.total;
+        s.off_seg_stats = s.off_seg_partial + align_up((size_t)(streams * s.seg_chunks * 256 * 4));
+        s.total = s.off_seg_stats + align_up((size_t)(streams * 256 * 4));
+    }
     return s;
 }
 
@@ -119,6 +140,7 @@ struct Prefix {
 Prefix prefix_of(const kivi_config &c, int64_t n) {
     const int64_t aged = n > c.residual ? n - c.residual : 0;
     if (c.policy == KIVI_FLUSH_PAPER) return {n - n % c.residual, aged};
+    if (c.policy == KIVI_FLUSH_SEGMENT) return {n - n % c.residual, n - n % c.residual};
     const int64_t q = aged / c.group * c.group;
     return {q, q};
 }
@@ -299,6 +321,9 @@ kivi_status kivi_cache_create(const kivi_config *cfg, void *dev_mem, size_t dev_
     c->off_ring_k = s.off_ring_k;
     c->off_ring_v = s.off_ring_v;
     c->off_outliers = s.off_outliers;
+    c->off_seg_partial = s.off_seg_partial;
+    c->off_seg_stats = s.off_seg_stats;
+    c->seg_chunks = s.seg_chunks;
     c->max_groups = s.max_groups;
     c->block_bytes = s.block_bytes;
     c->code_bytes = s.code_bytes;
@@ -392,6 +417,19 @@ kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const voi
     a.v_limit = v_limit;
     a.copy = copy ? *copy : RingArgs{};
     a.quant_tasks = 0;
+    a.seg_stats = nullptr;
+    a.seg_partial = nullptr;
+    a.seg_chunk_blocks = kSegChunkBlocks;
+    a.seg_chunks = 0;
+    if (kinds == 4) {
+        // KCVT: the blocks [block_begin, block_end) are one segment; its key
+        // statistics first, then the pairs of key and value tasks
+        a.seg_stats = (float *)(c->base + c->off_seg_stats);
+        a.seg_partial = (float *)(c->base + c->off_seg_partial);
+        a.seg_chunks = (int32_t)((block_end - block_begin + kSegChunkBlocks - 1) / kSegChunkBlocks);
+        if (block_end > block_begin && launch_segment_stats(a, stream) != hipSuccess)
+            return KIVI_ERR_HIP;
+    }
     return launch_quantize(a, stream) == hipSuccess ? KIVI_OK : KIVI_ERR_HIP;
 }
 
@@ -406,6 +444,9 @@ kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *
                           int64_t n_new, hipStream_t stream, const RingArgs *copy = nullptr) {
     const int64_t G = kGroup;
     constexpr int64_t kNoLimit = INT64_MAX;
+    if (c->cfg.policy == KIVI_FLUSH_SEGMENT)
+        return enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
+                                p.flush_token_end / G, 4, kNoLimit, stream, copy);
     if (c->cfg.policy != KIVI_FLUSH_PAPER)
         return enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
                                 p.flush_token_end / G, 3, kNoLimit, stream, copy);
@@ -455,6 +496,7 @@ kivi_status kivi_append(kivi_cache *c, const void *k, const void *v, int64_t n_n
         return KIVI_OK;
     }
     if (c->cfg.policy != KIVI_FLUSH_PAPER) {
+        // window and segment policies: the ring copy rides on the last launch
         const RingArgs r = ring_args(c, k, v, n_new, p.n_old, p.ring_token_begin, p.ring_token_end);
         st = enqueue_flush(c, p, k, v, n_new, stream, &r);
     } else {

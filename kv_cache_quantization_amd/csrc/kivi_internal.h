@@ -45,14 +45,28 @@ struct QuantizeArgs {
     int32_t gt;                 // blocks per key group: G / 32 (1, 2 or 4)
     int32_t n_out;              // fp16 key channels per key group (0: none)
     uint8_t *outliers;          // [streams][max_groups][kOutlierRecordBytes]
-    int32_t kinds;              // 1: key groups, 2: value blocks, 3: both
+    int32_t kinds;              // 1: key groups, 2: value blocks, 3: both, 4: segment
+                                // pairs (per block a key task with the segment's
+                                // statistics, then a value task)
     int64_t v_limit;            // value codes / side data of tokens >= v_limit are written 0
     // Rows to copy into the ring as well (none when copy.tok_end <= tok_begin).
     // The launch that reads no ring row does the copy in extra workgroups,
     // after its quant_tasks workgroups; without one, a ring append follows.
     RingArgs copy;
     uint32_t quant_tasks;       // set by the launcher
+    // Segment policy (KCVT): the key statistics of the blocks [block_begin,
+    // block_end) taken as one segment: seg_stats [streams][256] = per-channel
+    // minimum [128] and maximum [128] (float32), computed by
+    // launch_segment_stats through seg_partial [streams][seg_chunks][256]
+    // (seg_chunk_blocks blocks per chunk).
+    float *seg_stats;
+    float *seg_partial;
+    int32_t seg_chunk_blocks;
+    int32_t seg_chunks;
 };
+
+// Blocks per wavefront of the segment statistics pass.
+constexpr int kSegChunkBlocks = 16;
 
 struct DecodeArgs {
     const uint8_t *blocks;
@@ -133,6 +147,10 @@ constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 hipError_t noalloc_scratch(void **ptr);
 
 hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s);
+// Per-channel key minimum and maximum over the blocks [block_begin,
+// block_end) of every stream into a.seg_stats (two launches: chunks, then a
+// reduction per stream).
+hipError_t launch_segment_stats(const QuantizeArgs &a, hipStream_t s);
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);

@@ -468,7 +468,7 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-template <int BITS, bool IS_V, bool RING, typename T, int GT, bool OUT = false>
+template <int BITS, bool IS_V, bool RING, typename T, int GT, bool OUT = false, bool KSEG = false>
 __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t stream, int64_t g0,
                                               uint32_t *tr) {
 #pragma clang fp contract(off)
@@ -478,7 +478,18 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
 
     Tile<T> t;
     float lo[8], hi[8];
-    if constexpr (!IS_V && GT > 1) {
+    if constexpr (!IS_V && KSEG) {
+        // segment policy: one block, with the minimum / maximum of its
+        // segment's channels 8c .. 8c+7
+        load_tile<IS_V, RING>(a, stream, g0, t);
+        const float *st = a.seg_stats + stream * 256 + 8 * c;
+        const float4 l0 = *(const float4 *)st, l1 = *(const float4 *)(st + 4);
+        const float4 h0 = *(const float4 *)(st + 128), h1 = *(const float4 *)(st + 132);
+        lo[0] = l0.x; lo[1] = l0.y; lo[2] = l0.z; lo[3] = l0.w;
+        lo[4] = l1.x; lo[5] = l1.y; lo[6] = l1.z; lo[7] = l1.w;
+        hi[0] = h0.x; hi[1] = h0.y; hi[2] = h0.z; hi[3] = h0.w;
+        hi[4] = h1.x; hi[5] = h1.y; hi[6] = h1.z; hi[7] = h1.w;
+    } else if constexpr (!IS_V && GT > 1) {
         // the last block stays in registers for the first store below
         KPart<T> part;
 #pragma unroll 1
@@ -702,7 +713,7 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
             (uint4){outw[4 * w4], outw[4 * w4 + 1], outw[4 * w4 + 2], outw[4 * w4 + 3]};
     };
 
-    if constexpr (IS_V || GT == 1) {
+    if constexpr (IS_V || GT == 1 || KSEG) {
         store_block(g0);
     } else {
         store_block(g0 + GT - 1);
@@ -767,7 +778,10 @@ __global__ __launch_bounds__(kRingThreads) void ring_append_kernel(RingArgs a) {
 // the next GT tasks are the value blocks of the same tokens; kinds = 1 / 2:
 // every task is a key group / a value block.
 // Without RING, workgroups from a.quant_tasks on copy a.copy's ring rows.
-template <int BITS, typename T, bool RING, int GT, bool OUT>
+// kinds = 4 (segment policy, KSEG): task 2i is the key block i with its
+// segment's statistics, task 2i + 1 the value block i (groups of 32 * GT
+// channels).
+template <int BITS, typename T, bool RING, int GT, bool OUT, bool KSEG = false>
 __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
     __shared__ uint32_t tr[64 * 2 * BITS];
     const uint32_t task = blockIdx.x;
@@ -783,7 +797,12 @@ __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
     const uint32_t nb = (uint32_t)(a.block_end - a.block_begin);
     int64_t stream, g;
     bool is_v;
-    if (a.kinds == 3) {
+    if (KSEG) {
+        const uint32_t pair = task >> 1;
+        stream = pair / nb;
+        is_v = task & 1;
+        g = a.block_begin + pair % nb;
+    } else if (a.kinds == 3) {
         const uint32_t ngr = nb / GT, rest = task / (1 + GT), sub = task % (1 + GT);
         stream = rest / ngr;
         is_v = sub != 0;
@@ -799,7 +818,57 @@ __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
         g = a.block_begin + task % nb;
     }
     if (is_v) quantize_task<BITS, true, RING, T, GT, OUT>(a, stream, g, tr);
-    else quantize_task<BITS, false, RING, T, GT, OUT>(a, stream, g, tr);
+    else quantize_task<BITS, false, RING, T, GT, OUT, KSEG>(a, stream, g, tr);
+}
+
+// Segment policy: per-channel key minimum / maximum of the blocks [b0, b0 +
+// seg_chunk_blocks) of one stream (one wavefront per (stream, chunk)), in
+// float32 (exact for fp16 and fp32 inputs), to seg_partial.
+template <typename T>
+__global__ __launch_bounds__(64) void seg_stats_kernel(QuantizeArgs a) {
+    const int64_t task = blockIdx.x;
+    const int64_t stream = task / a.seg_chunks, ch = task % a.seg_chunks;
+    const int64_t b0 = a.block_begin + ch * a.seg_chunk_blocks;
+    const int64_t b1 = b0 + a.seg_chunk_blocks < a.block_end ? b0 + a.seg_chunk_blocks : a.block_end;
+    const int l = threadIdx.x, q = l >> 4, c = l & 15;
+    KPart<T> part;
+    Tile<T> t;
+#pragma unroll 1
+    for (int64_t g = b0; g < b1; g++) {
+        load_tile<false, true>(a, stream, g, t);
+        kpart_add(t, part, g == b0);
+    }
+    float lo[8], hi[8];
+    kpart_finish(part, lo, hi);
+    float *dst = a.seg_partial + (stream * a.seg_chunks + ch) * 256 + 8 * c;
+    if (q == 0) {
+        *(float4 *)dst = (float4){lo[0], lo[1], lo[2], lo[3]};
+        *(float4 *)(dst + 4) = (float4){lo[4], lo[5], lo[6], lo[7]};
+    } else if (q == 1) {
+        *(float4 *)(dst + 128) = (float4){hi[0], hi[1], hi[2], hi[3]};
+        *(float4 *)(dst + 132) = (float4){hi[4], hi[5], hi[6], hi[7]};
+    }
+}
+
+// The segment's statistics of one stream: minimum of the chunk minima and
+// maximum of the chunk maxima (lane l: entries 4l .. 4l+3; minima for l < 32).
+__global__ __launch_bounds__(64) void seg_reduce_kernel(QuantizeArgs a) {
+    const int64_t stream = blockIdx.x;
+    const int l = threadIdx.x;
+    const bool is_max = l >= 32;
+    const float *src = a.seg_partial + stream * a.seg_chunks * 256 + 4 * l;
+    float4 acc = *(const float4 *)src;
+    for (int ch = 1; ch < a.seg_chunks; ch++) {
+        const float4 v = *(const float4 *)(src + ch * 256);
+        if (is_max) {
+            acc.x = fmax_(acc.x, v.x); acc.y = fmax_(acc.y, v.y);
+            acc.z = fmax_(acc.z, v.z); acc.w = fmax_(acc.w, v.w);
+        } else {
+            acc.x = fmin_(acc.x, v.x); acc.y = fmin_(acc.y, v.y);
+            acc.z = fmin_(acc.z, v.z); acc.w = fmin_(acc.w, v.w);
+        }
+    }
+    *(float4 *)(a.seg_stats + stream * 256 + 4 * l) = acc;
 }
 
 // ===========================================================================
@@ -2484,13 +2553,14 @@ static int64_t ring_blocks(const RingArgs &a) {
     return (pieces + kRingThreads - 1) / kRingThreads;
 }
 
-template <int BITS, typename T, int GT, bool OUT = false>
+template <int BITS, typename T, int GT, bool OUT = false, bool KSEG = false>
 static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
     // tasks per launched block range: key groups of GT blocks and / or blocks
+    // (segment pairs: two per block)
     auto tasks_of = [&](int64_t nb) {
-        return a.kinds == 3 ? nb / GT * (1 + GT) : a.kinds == 1 ? nb / GT : nb;
+        return KSEG ? 2 * nb : a.kinds == 3 ? nb / GT * (1 + GT) : a.kinds == 1 ? nb / GT : nb;
     };
-    const int64_t align = a.kinds == 2 ? 1 : GT;
+    const int64_t align = (a.kinds == 2 || KSEG) ? 1 : GT;
     // Blocks with tokens before n_old read rows from the ring; so does a block
     // whose value rows stop at v_limit (only that instance checks the limit).
     int64_t ring_end = (a.n_old + G - 1) / G;
@@ -2502,15 +2572,15 @@ static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
         QuantizeArgs r = a;
         r.block_end = split;
         const int64_t tasks = (int64_t)a.streams * tasks_of(split - a.block_begin);
-        hipLaunchKernelGGL((quantize_kernel<BITS, T, true, GT, OUT>), dim3((unsigned)tasks), dim3(64),
-                           0, s, r);
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, true, GT, OUT, KSEG>), dim3((unsigned)tasks),
+                           dim3(64), 0, s, r);
     }
     if (a.block_end > split) {
         QuantizeArgs n = a;
         n.block_begin = split;
         const int64_t tasks = (int64_t)a.streams * tasks_of(a.block_end - split);
         n.quant_tasks = (uint32_t)tasks;
-        hipLaunchKernelGGL((quantize_kernel<BITS, T, false, GT, OUT>),
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, false, GT, OUT, KSEG>),
                            dim3((unsigned)(tasks + ring_blocks(a.copy))), dim3(64), 0, s, n);
         return hipGetLastError();
     }
@@ -2521,6 +2591,7 @@ static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
 
 template <int BITS, typename T>
 static hipError_t launch_quantize_g(const QuantizeArgs &a, hipStream_t s) {
+    if (a.kinds == 4) return launch_quantize_t<BITS, T, 4, false, true>(a, s);
     if (a.n_out > 0) return launch_quantize_t<BITS, T, 1, true>(a, s);
     if (a.gt == 1) return launch_quantize_t<BITS, T, 1>(a, s);
     if (a.gt == 2) return launch_quantize_t<BITS, T, 2>(a, s);
@@ -2533,12 +2604,14 @@ hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
     if (copy && ring_blocks(a.copy) > 0x7FFFFFFF - 2 * (int64_t)a.streams * a.max_groups)
         return hipErrorInvalidValue;
     if (a.block_end <= a.block_begin || a.streams <= 0) return launch_ring_append(a.copy, s);
-    if (a.kinds < 1 || a.kinds > 3) return hipErrorInvalidValue;
+    if (a.kinds < 1 || a.kinds > 4) return hipErrorInvalidValue;
+    // segment pairs: value groups of 128 channels, statistics from seg_stats
+    if (a.kinds == 4 && (a.gt != 4 || a.n_out != 0 || !a.seg_stats)) return hipErrorInvalidValue;
     if (a.gt != 1 && a.gt != 2 && a.gt != 4) return hipErrorInvalidValue;
     if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && (a.gt != 1 || !a.outliers)))
         return hipErrorInvalidValue;
     // key tasks cover whole groups of gt blocks
-    if (a.kinds != 2 && (a.block_begin % a.gt != 0 || a.block_end % a.gt != 0))
+    if (a.kinds != 2 && a.kinds != 4 && (a.block_begin % a.gt != 0 || a.block_end % a.gt != 0))
         return hipErrorInvalidValue;
     // every value row the kernel reads must exist: rows >= v_limit are skipped,
     // and only the last block may stop early
@@ -2548,6 +2621,25 @@ hipError_t launch_quantize(const QuantizeArgs &a, hipStream_t s) {
     if (a.bits == 2) return a.is_f32 ? launch_quantize_g<2, float>(a, s) : launch_quantize_g<2, _Float16>(a, s);
     if (a.bits == 8) return a.is_f32 ? launch_quantize_g<8, float>(a, s) : launch_quantize_g<8, _Float16>(a, s);
     return a.is_f32 ? launch_quantize_g<4, float>(a, s) : launch_quantize_g<4, _Float16>(a, s);
+}
+
+hipError_t launch_segment_stats(const QuantizeArgs &a, hipStream_t s) {
+    const int64_t nb = a.block_end - a.block_begin;
+    if (nb <= 0 || a.streams <= 0) return hipSuccess;
+    if (!a.seg_stats || !a.seg_partial || a.seg_chunk_blocks < 1 ||
+        (int64_t)a.seg_chunks * a.seg_chunk_blocks < nb ||
+        (int64_t)(a.seg_chunks - 1) * a.seg_chunk_blocks >= nb)
+        return hipErrorInvalidValue;
+    const int64_t tasks = (int64_t)a.streams * a.seg_chunks;
+    if (tasks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (a.is_f32)
+        hipLaunchKernelGGL(seg_stats_kernel<float>, dim3((unsigned)tasks), dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL(seg_stats_kernel<_Float16>, dim3((unsigned)tasks), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(seg_reduce_kernel, dim3((unsigned)a.streams), dim3(64), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {

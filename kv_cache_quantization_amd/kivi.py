@@ -25,6 +25,7 @@ KIVI_F16 = 0
 KIVI_F32 = 1
 KIVI_FLUSH_WINDOW = 0
 KIVI_FLUSH_PAPER = 1
+KIVI_FLUSH_SEGMENT = 2      # KCVT: one key group per channel and flush segment
 KIVI_DEFER_FLUSH = 1
 KIVI_NOALLOC_SCRATCH_BYTES = 32 << 20      # fixed decode scratch of kivi_decode_attn_noalloc
 

@@ -39,7 +39,7 @@ def gpu_blocks(cache, n_groups, streams=None):
     return blk[:, :n_groups].cpu().numpy()
 
 
-def check_cache(orc, cache, k, v, streams=None, label=""):
+def check_cache(orc, cache, k, v, streams=None, label="", segments=None):
     """Bit-exact check of packed blocks, ring contents and (n, Q_K, Q_V)
     against the oracle built from the full K, V ([B, H, n, D] numpy, or only
     the streams listed in `streams`, given as [len(streams), n, D] arrays in
@@ -54,7 +54,8 @@ def check_cache(orc, cache, k, v, streams=None, label=""):
         kk, vv = k[None], v[None]     # [1, S, n, D]: the sampled streams as one batch row
     n = kk.shape[2]
     G = c.group
-    ref = orc.build_cache(kk, vv, c.bits, G, c.residual, c.policy, c.key_outliers)
+    ref = orc.build_cache(kk, vv, c.bits, G, c.residual, c.policy, c.key_outliers,
+                          segments=segments)
     qk, qv = ref["qk"], ref["qv"]
     assert lo.n_tokens == n, (label, lo.n_tokens, n)
     assert (lo.n_quantized, lo.n_vquantized) == (qk, qv), (label, lo.n_quantized,
@@ -109,8 +110,10 @@ def rel_err(out, ref):
     return float((np.abs(out - ref).max(1) / np.abs(ref).max(1)).max())
 
 
-def oracle_decode(orc, k, v, q, bits, G, R, sm_scale=None, policy=0, key_outliers=0):
-    """The oracle's decode attention over the cache built from k, v (group G)."""
-    ref = orc.build_cache(k, v, bits, G, R, policy, key_outliers)
+def oracle_decode(orc, k, v, q, bits, G, R, sm_scale=None, policy=0, key_outliers=0,
+                  segments=None):
+    """The oracle's decode attention over the cache built from k, v (group G;
+    segments: the flush segment ends under the segment policy)."""
+    ref = orc.build_cache(k, v, bits, G, R, policy, key_outliers, segments=segments)
     kh, vh = orc.dequant_cache(k, v, ref)
     return orc.decode_attn(q, kh, vh, sm_scale)

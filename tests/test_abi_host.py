@@ -245,6 +245,64 @@ def test_plan_append_matches_paper_policy(L, orc, R):
         kivi.kivi_cache_destroy(h)
 
 
+@pytest.mark.parametrize("R", [32, 96, 128])
+def test_plan_append_matches_segment_policy(L, orc, R):
+    """Segment policy (KCVT, GEAR review "KCVT" and "streaming buffer
+    strategy"): keys and values quantized up to n - (n mod R), compared with
+    the oracle's prefix for every n of a first append; the buffer (ring)
+    holds the fewer than R newest tokens.  The layout adds the per-chunk and
+    per-stream statistics scratch after the rings."""
+    T = 700
+    cfg = kivi.make_config(2, 2, 8, bits=2, group=128, residual=R, max_tokens=T,
+                           policy=kivi.KIVI_FLUSH_SEGMENT)
+    nbytes = kivi.kivi_cache_bytes(cfg)
+    assert nbytes > 0
+    h = kivi.kivi_cache_create(cfg, FAKE_DEV, nbytes)
+    try:
+        for n in range(0, T + 1):
+            p = kivi.kivi_plan_append(h, n)
+            qk, qv = orc.quantized_prefix(n, 128, R, orc.POLICY_SEGMENT)
+            assert qk == qv == n - n % R
+            assert (p.q_new, p.v_flush_token_end) == (qk, qv), (n, qk, qv)
+            assert (p.flush_token_begin, p.flush_token_end) == (0, qk)
+            assert (p.ring_token_begin, p.ring_token_end) == (qk, n)
+            assert p.ring_token_end - p.ring_token_begin < R
+        lo = kivi.kivi_get_layout(h)
+        assert lo.ring_capacity == R + 128
+        streams, groups = 4, T // 32
+        chunks = -(-groups // 16)
+        scratch = -(-streams * chunks * 1024 // 256) * 256 + -(-streams * 1024 // 256) * 256
+        assert nbytes >= lo.ring_v + scratch
+    finally:
+        kivi.kivi_cache_destroy(h)
+
+
+def test_segment_policy_validation(L):
+    """The segment policy needs R > 0 a multiple of 32 (not of G), G = the
+    head dimension (values grouped over the whole head), and no fp16 key
+    channels."""
+    ok = dict(bits=2, group=128, residual=96, max_tokens=1024, policy=kivi.KIVI_FLUSH_SEGMENT)
+    assert kivi.kivi_cache_bytes(kivi.make_config(1, 8, 32, **ok)) > 0
+    for over, status in ((dict(residual=0), kivi.KIVI_ERR_INVALID_ARG),
+                         (dict(residual=48), kivi.KIVI_ERR_INVALID_ARG),
+                         (dict(group=32), kivi.KIVI_ERR_INVALID_ARG),
+                         (dict(group=64, residual=64), kivi.KIVI_ERR_INVALID_ARG),
+                         (dict(policy=3), kivi.KIVI_ERR_INVALID_ARG)):
+        args = dict(ok)
+        args.update(over)
+        cfg = kivi.make_config(1, 8, 32, **args)
+        assert kivi.kivi_cache_bytes(cfg) == 0
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.kivi_cache_create(cfg, FAKE_DEV, 1 << 30)
+        assert e.value.status == status, over
+    cfg = kivi.make_config(1, 8, 32, **ok)
+    cfg.key_outliers = 2
+    assert kivi.kivi_cache_bytes(cfg) == 0
+    with pytest.raises(kivi.KiviError) as e:
+        kivi.kivi_cache_create(cfg, FAKE_DEV, 1 << 30)
+    assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+
+
 def test_host_error_paths(L):
     """Errors that the front end returns before any device work: the cache
     is left unchanged."""
