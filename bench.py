@@ -77,6 +77,22 @@ def decode_bytes_kv(B, H, Hq, n, qk, qv, bits, D=128, G=32):
     return B * H * (k + v) + B * Hq * D * (2 + 4)
 
 
+def kcvt_decode_bytes(B, H, Hq, n, Q, bits, segments, D=128):
+    """Decode bytes under the segment policy (KCVT): the codes, one fp16 pair
+    per token for its 128 value channels, one fp16 pair per key channel and
+    segment, the fp16 buffer, q and out."""
+    per_stream = Q * D * 2 * bits / 8 + Q * 4 + segments * D * 4 + (n - Q) * D * 2 * 2
+    return B * H * per_stream + B * Hq * D * (2 + 4)
+
+
+def kcvt_append_bytes(B, H, n, Q, bits, segments, D=128, esize=2):
+    """A segment-policy append: read K and V, write codes, one value pair per
+    token and one key pair per channel and segment, copy the buffer rows."""
+    q_el = B * H * Q * D * 2
+    return (q_el * (esize + bits / 8) + B * H * (Q * 4 + segments * D * 4)
+            + B * H * (n - Q) * D * 2 * 2 * esize)
+
+
 def append_bytes(B, H, n, Q, bits, D=128, G=32, esize=2):
     """One-shot append of n tokens: read K and V (esize B per element), write
     codes (b/8 B) and zero/scale (4/G B) for the Q quantized tokens, copy the
@@ -351,7 +367,7 @@ def evict_read(evict, evict_out):
 
 
 def long_context_measure(B, n, R, bits, G, chunk, n_out, steps, warmup, stream, evict, evict_out,
-                         do_evict, cfg_id=3, keep=False):
+                         do_evict, cfg_id=3, keep=False, policy=0):
     """Prefill + decode on one workload: inputs drawn on the device first;
     each step = a reset cache, the appends of all chunks (quantize + ring),
     then one decode step; each phase timed with HIP events on `stream`,
@@ -368,7 +384,8 @@ def long_context_measure(B, n, R, bits, G, chunk, n_out, steps, warmup, stream, 
         chunks.append(synth.kv_device(cfg_id, B, H, cn, D, chunk=ci // chunk, device=dev))
     q = synth.queries_device(cfg_id, B, Hq, D, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    cache = KiviCache(B, H, Hq, n, bits=bits, group=G, residual=R, device=dev, key_outliers=n_out)
+    cache = KiviCache(B, H, Hq, n, bits=bits, group=G, residual=R, device=dev, key_outliers=n_out,
+                      policy=policy)
     cache.workspace()
     torch.cuda.synchronize()
 
@@ -401,8 +418,14 @@ def long_context_measure(B, n, R, bits, G, chunk, n_out, steps, warmup, stream, 
     t_dec = sum(dec_ms) / steps / 1e3
     lo = cache.layout()
     Q = lo.n_quantized
-    dbytes = decode_bytes(B, H, Hq, n, Q, bits, G=G)
-    abytes = append_bytes(B, H, n, Q, bits, G=G)
+    if policy == 2:
+        # KCVT: one segment per flush (every chunk append moves Q here)
+        segs = len(chunks)
+        dbytes = kcvt_decode_bytes(B, H, Hq, n, Q, bits, segs)
+        abytes = kcvt_append_bytes(B, H, n, Q, bits, segs)
+    else:
+        dbytes = decode_bytes(B, H, Hq, n, Q, bits, G=G)
+        abytes = append_bytes(B, H, n, Q, bits, G=G)
     if n_out:
         # the kept channels' fp16 values (2 bytes per token and channel) and
         # their indices (2 bytes per channel and group), read by the decode
@@ -414,9 +437,11 @@ def long_context_measure(B, n, R, bits, G, chunk, n_out, steps, warmup, stream, 
     app_gbps = abytes / t_app / 1e9
     splits, gps = cache.decode_plan()
     rec = {
-        "workload": "KIVI %d-bit decode over a %s prefill: batch %d, 8 KV heads, 32 query heads, "
+        "workload": "%s %d-bit decode over a %s prefill: batch %d, 8 KV heads, 32 query heads, "
                     "head_dim 128, context %d, group %d, residual %d%s"
-                    % (bits, "one-shot" if chunk == n else "%d-token-chunk" % chunk, B, n, G, R,
+                    % ("KCVT (one key group per channel and flush segment)" if policy == 2
+                       else "KIVI", bits,
+                       "one-shot" if chunk == n else "%d-token-chunk" % chunk, B, n, G, R,
                        "" if not n_out else ", %d fp16 key channels per key group" % n_out),
         "batch": B, "context": n, "bits": bits, "group": G, "residual": R, "chunk": chunk,
         "quantized_tokens": Q, "decode_splits_per_stream": splits, "groups_per_split": gps,
@@ -574,9 +599,18 @@ def main():
         if bits != 4 or (B, n) != (16, 32768):
             others["b16_ctx32768_4bit"] = long_context_measure(
                 16, 32768, 128, 4, 32, 0, 0, 10, 2, stream, evict, evict_out, do_evict)
+        # KCVT at 4 bits (the GEAR review's backbone at that width): one key
+        # segment over the whole prompt, values grouped over all 128 channels
+        others["b16_ctx32768_kcvt_4bit"] = long_context_measure(
+            16, 32768, 128, 4, 128, 0, 0, 10, 2, stream, evict, evict_out, do_evict, policy=2)
         # one layer of a single sequence: launch-bound, reported only
         others["b1_ctx4096_2bit"] = long_context_measure(
             1, 4096, 32, 2, 32, 0, 0, 20, 5, stream, evict, evict_out, do_evict, cfg_id=2)
+        # HBM traffic from the committed counter summary (while the kernel
+        # sources still match it)
+        t5, src5 = counter_traffic("decode_b32_ctx131072_2bit_counters.txt")
+        others["b32_ctx131072_2bit"]["decode"]["traffic"] = t5
+        others["b32_ctx131072_2bit"]["decode"]["traffic_source"] = src5
         rec["other_configs"] = others
         if args.cpu_sample > 0:
             from kv_cache_quantization_amd import synth
