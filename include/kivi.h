@@ -297,10 +297,11 @@ kivi_status kivi_append_decode(kivi_cache *c, const void *k, const void *v, int6
    kivi_attn_workspace_bytes(c, T) (may be 0, then workspace may be NULL).
    Errors: INVALID_ARG (null pointers, T < 1, bad q_dtype or causal, causal
    with T > n), STATE (n == 0 or a deferred flush pending), UNSUPPORTED
-   (float32 cache with residual tokens, or under the paper policy with value
-   rows of coded key groups still in the ring; B * Hq * T >= 2^31),
-   BUFFER_TOO_SMALL, HIP.  Under the paper policy keys are the codes below
-   Q_K and values the codes below Q_V, the ring's rows above each. */
+   (B * Hq * T >= 2^31), BUFFER_TOO_SMALL, HIP.  Under the paper policy keys
+   are the codes below Q_K and values the codes below Q_V, the ring's rows
+   above each.  The products run on fp16 operands: rows of a float32 ring
+   enter them rounded to nearest fp16 (finite up to 65504 in magnitude, as
+   the fp16 zero / scale of the coded groups are). */
 kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T,
                       int32_t causal, float softmax_scale, float *out,
                       void *workspace, size_t ws_bytes, hipStream_t stream);

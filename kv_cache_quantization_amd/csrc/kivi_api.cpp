@@ -697,11 +697,7 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     if (causal != 0 && causal != 1) return KIVI_ERR_INVALID_ARG;
     if (c->n == 0 || !canonical(c)) return KIVI_ERR_STATE;
     if (causal && T > c->n) return KIVI_ERR_INVALID_ARG;
-    // a float32 ring is not read by the attention kernel: no residual tokens,
-    // and (paper policy) no groups whose values continue in the ring
     const int64_t q_full = ring_low(c->cfg, c->qv);     // groups with value codes
-    if (c->cfg.kv_dtype != KIVI_F16 && (c->n > c->q || q_full < c->q))
-        return KIVI_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)c->cfg.batch * c->cfg.n_q_heads * T;
     if (rows > 0x7FFFFFFF) return KIVI_ERR_UNSUPPORTED;
     const size_t need = kivi_attn_workspace_bytes(c, T);
@@ -715,6 +711,7 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     a.ring_k = c->base + c->off_ring_k;
     a.ring_v = c->base + c->off_ring_v;
     a.ring_cap = c->ring_cap;
+    a.ring_f32 = c->cfg.kv_dtype == KIVI_F32;
     a.q = q;
     a.q_is_f32 = q_dtype == KIVI_F32;
     a.out = out;

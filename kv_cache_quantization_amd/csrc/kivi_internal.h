@@ -117,8 +117,9 @@ struct AttnArgs {
     const uint8_t *blocks;
     int64_t max_groups;
     int64_t block_bytes;
-    const void *ring_k, *ring_v;  // fp16 ring
+    const void *ring_k, *ring_v;  // ring rows, fp16 or (ring_f32) float32
     int64_t ring_cap;
+    int32_t ring_f32;
     const void *q;              // [B][Hq][T][D]
     int32_t q_is_f32;
     float *out;                 // [B][Hq][T][D] float32

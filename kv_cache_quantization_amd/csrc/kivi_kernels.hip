@@ -2346,6 +2346,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
     if (split == a.splits - 1 && ng > ngv) {
         constexpr uint32_t M1 = (1u << BITS) - 1u;
         const _Float16 *rvh = (const _Float16 *)a.ring_v + (int64_t)stream * a.ring_cap * D;
+        const float *rvf = (const float *)a.ring_v + (int64_t)stream * a.ring_cap * D;
         for (int64_t gm = ngv; gm < ng && gm * G <= pq_wg; gm++) {
             const int64_t tok0 = gm * G;
             __syncthreads();        // stage 0 and the transposed rows are free
@@ -2374,7 +2375,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
                         const float vz = (float)sd[3 * D + (c / G) * G + r];
                         v = (_Float16)((float)((vcode[dw] >> bit) & M1) * vs + vz);
                     } else {
-                        v = rvh[(t % a.ring_cap) * D + c];
+                        const int64_t ri = (t % a.ring_cap) * D + c;
+                        v = a.ring_f32 ? (_Float16)rvf[ri] : rvh[ri];
                     }
                     vt[c * VTS + r] = v;
                 }
@@ -2407,14 +2409,16 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
         }
     }
 
-    // The last split walks the fp16 residual [Q, n) in 32-token chunks: the
+    // The last split walks the residual [Q, n) in 32-token chunks: the
     // workgroup stages the chunk's value rows transposed in LDS (channel
-    // rows), each wavefront reads its K rows straight from the ring.
+    // rows), each wavefront reads its K rows straight from the ring.  Rows
+    // of a float32 ring enter the fp16 products rounded to nearest fp16.
     if (split == a.splits - 1 && n > a.n_quant) {
         const int64_t nres = n - a.n_quant;
         const int cap = (int)a.ring_cap;
-        const char *rkb = (const char *)a.ring_k + (int64_t)stream * a.ring_cap * D * 2;
-        const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * 2;
+        const int rb = a.ring_f32 ? 4 : 2;              // bytes per ring element
+        const char *rkb = (const char *)a.ring_k + (int64_t)stream * a.ring_cap * D * rb;
+        const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * rb;
         const int slot_q = (int)(a.n_quant % a.ring_cap);
         for (int64_t c0 = 0; c0 < nres && a.n_quant + c0 <= pq_wg; c0 += G) {
             const int cnt = nres - c0 < G ? (int)(nres - c0) : G;
@@ -2426,9 +2430,17 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
             __syncthreads();        // the previous chunk's transposed rows are read
             for (int idx = threadIdx.x; idx < G * (D / 8); idx += 64 * W) {
                 const int r = idx >> 4, piece = idx & 15;
-                const uint4 v16 = *(const uint4 *)(rvb + (int64_t)slot(r) * D * 2 + 16 * piece);
+                const char *src = rvb + ((int64_t)slot(r) * D + 8 * piece) * rb;
                 h2 hv[4];
-                split4(v16, hv);
+                if (a.ring_f32) {
+                    const float4 x0 = *(const float4 *)src, x1 = *(const float4 *)(src + 16);
+                    hv[0] = (h2){(_Float16)x0.x, (_Float16)x0.y};
+                    hv[1] = (h2){(_Float16)x0.z, (_Float16)x0.w};
+                    hv[2] = (h2){(_Float16)x1.x, (_Float16)x1.y};
+                    hv[3] = (h2){(_Float16)x1.z, (_Float16)x1.w};
+                } else {
+                    split4(*(const uint4 *)src, hv);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     vt[(8 * piece + 2 * i) * VTS + r] = hv[i][0];
@@ -2442,10 +2454,19 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
             for (int c = 0; c < CB; c++) S[c][0] = S[c][1] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < 2; t++) {
-                const char *krow = rkb + (int64_t)slot(16 * t + j) * D * 2 + 16 * Gl;
+                // lane (j, Gl) takes channels 32s + 8Gl .. + 7 of row 16t + j
+                const char *krow = rkb + ((int64_t)slot(16 * t + j) * D + 8 * Gl) * rb;
 #pragma unroll
                 for (int s = 0; s < 4; s++) {
-                    const h8 kk = __builtin_bit_cast(h8, *(const uint4 *)(krow + 64 * s));
+                    h8 kk;
+                    if (a.ring_f32) {
+                        const float4 x0 = *(const float4 *)(krow + 128 * s);
+                        const float4 x1 = *(const float4 *)(krow + 128 * s + 16);
+                        kk = (h8){(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
+                                  (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+                    } else {
+                        kk = __builtin_bit_cast(h8, *(const uint4 *)(krow + 64 * s));
+                    }
 #pragma unroll
                     for (int c = 0; c < CB; c++)
                         S[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(

@@ -151,11 +151,12 @@ def test_deferred_flush(orc):
     assert e <= TOL
 
 
-def _attn(orc, B, H, Hq, n, T, bits, R, causal, seed, chunks=None, label=""):
+def _attn(orc, B, H, Hq, n, T, bits, R, causal, seed, chunks=None, label="",
+          dtype=np.float16):
     from kv_cache_quantization_amd import kivi, synth
-    k, v = synth.kv_host(seed, B, H, n)
+    k, v = synth.kv_host(seed, B, H, n, dtype=dtype)
     q = synth.queries_multi_host(seed, B, Hq, T)
-    cache = new_cache(B, H, Hq, max_tokens=n + 64, bits=bits, R=R, policy=PAPER)
+    cache = new_cache(B, H, Hq, max_tokens=n + 64, bits=bits, R=R, policy=PAPER, dtype=dtype)
     pos = 0
     for c in (chunks or [n]):
         cache.append(to_dev(k[:, :, pos:pos + c]), to_dev(v[:, :, pos:pos + c]))
@@ -190,15 +191,11 @@ def test_attn_queries(orc, n, T, bits, R, gq, causal):
 
 def test_attn_queries_streamed_and_fp32(orc):
     """A streamed paper-policy cache (one-token appends across a key flush);
-    a float32 cache is refused while groups continue in its ring."""
-    import torch
-    from kv_cache_quantization_amd import kivi, synth
-    from kv_cache_quantization_amd import KiviError
+    float32 caches whose mixed groups take their value rows from the ring,
+    one-shot and streamed."""
     _attn(orc, 1, 2, 8, 300, 40, 2, 64, 1, seed=71, chunks=[200] + [1] * 100,
           label="paper-attn-stream")
-    k, v = synth.kv_host(72, 1, 1, 200)
-    c32 = new_cache(1, 1, 4, 256, bits=2, R=64, dtype=np.float32, policy=PAPER)
-    c32.append(to_dev(k.astype(np.float32)), to_dev(v.astype(np.float32)))
-    with pytest.raises(KiviError) as e:
-        c32.attn(torch.zeros((1, 4, 2, 128), dtype=torch.float16, device="cuda"))
-    assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED
+    _attn(orc, 1, 2, 8, 1000, 300, 2, 128, 1, seed=72, dtype=np.float32,
+          label="paper-attn-fp32")
+    _attn(orc, 1, 2, 8, 300, 40, 4, 64, 0, seed=73, chunks=[200] + [1] * 100,
+          dtype=np.float32, label="paper-attn-fp32-stream")
