@@ -1005,50 +1005,70 @@ __device__ __forceinline__ constexpr int pair_shift(int m) {
     return kScaleLog2<SB>(m) + kSlack;
 }
 
-// One step over the 8 scores a lane holds (two 16-token tiles).  Returns p as
-// fp16 pairs in value-operand order, pair m pre-divided by 2^pair_shift(m)
-// (kScaleLog2<SB>(m) + kSlack).  The unscaled sum of p runs on the matrix
-// core: A holds the weights 2^pair_shift(m) in every row, so each row of
-// Lsum carries the running sum of its column.  nm[m] caches
-// -m_run - pair_shift(m).
-template <int SB>
+// ds_swizzle in bitmask mode (the LDS crossbar, no memory access): within
+// each 32-lane half, lane i reads lane ((i & AND) | OR) ^ XOR.
+template <int AND, int OR, int XOR>
+__device__ __forceinline__ uint32_t swizzle(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, AND | (OR << 5) | (XOR << 10));
+}
+template <int XOR>
+__device__ __forceinline__ float swizzle_xor(float v) {
+    return __builtin_bit_cast(float, swizzle<31, 0, XOR>(__builtin_bit_cast(uint32_t, v)));
+}
+
+// One step over the 8 scores of a lane's column (two 16-token tiles): pair m
+// holds tile m / 2, rows 2(m % 2), +1.  The 16 columns are GQ heads, each
+// repeated 16 / GQ times, so the lanes h + GQ * m' (m' = 0..3) of a row hold
+// the same scores: lane (j, row) computes p of pair own = (j / GQ) % 4 only,
+// pre-divided by 2^pair_shift(own) (kScaleLog2<SB>(own) + kSlack), two
+// exponentials instead of eight, and gathers the four pairs from those lanes.
+// Returns p as fp16 pairs in value-operand order.  The unscaled sum of p runs
+// on the matrix core: A holds the weights 2^pair_shift(m) in every row, so
+// each row of Lsum carries the running sum of its column.  b0, b1: bits 0
+// and 1 of own as masks of all ones or zeros; ps_own = pair_shift(own);
+// nm_own caches -m_run - ps_own.
+// (a & m) | (b & ~m): one v_bfi_b32, a lane-wise select by a mask of all ones
+// or zeros that cannot become a branch.
+__device__ __forceinline__ float bitsel(uint32_t m, float a, float b) {
+    return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, a) & m) |
+                                         (__builtin_bit_cast(uint32_t, b) & ~m));
+}
+
+template <int SB, int GQ>
 __device__ __forceinline__ void softmax_step(const f4 &S0, const f4 &S1, float cs, float kbl,
-                                             float &m_run, float &m_thr, float (&nm)[4],
-                                             f4 &Lsum, float (&vb)[4], f4 (&accV)[8],
-                                             h2 (&P)[4]) {
-    float mt = vmax(vmax(vmax(S0[0], S0[1]), vmax(S0[2], S0[3])),
-                    vmax(vmax(S1[0], S1[1]), vmax(S1[2], S1[3])));
-    mt = __builtin_fmaf(mt, cs, kbl);               // this lane's maximum, log2 units
+                                             uint32_t b0, uint32_t b1, float ps_own,
+                                             float &m_run, float &m_thr, float &nm_own, f4 &Lsum,
+                                             float (&vb)[4], f4 (&accV)[8], h2 (&P)[4]) {
+    const float y = bitsel(b1, bitsel(b0, S1[2], S1[0]), bitsel(b0, S0[2], S0[0]));
+    const float z = bitsel(b1, bitsel(b0, S1[3], S1[1]), bitsel(b0, S0[3], S0[1]));
+    float mt = __builtin_fmaf(vmax(y, z), cs, kbl);   // this lane's maximum, log2 units
     if (__any(mt > m_thr)) {
+        // the column's maximum: over the pair lanes of the row, then the rows
+        mt = vmax(mt, swizzle_xor<GQ>(mt));
+        mt = vmax(mt, swizzle_xor<2 * GQ>(mt));
         const float m_new = vmax(m_run, xmax_rows(mt));
         const float al = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
         for (int o = 0; o < 8; o++) accV[o] *= al;
         Lsum *= al;
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            vb[m] *= al;
-            nm[m] = -m_new - (float)pair_shift<SB>(m);
-        }
+        for (int m = 0; m < 4; m++) vb[m] *= al;
+        nm_own = -m_new - ps_own;
         m_run = m_new;
         m_thr = m_new + (float)kSlack;
     }
-    float nk[4];
-#pragma unroll
-    for (int m = 0; m < 4; m++) nk[m] = nm[m] + kbl;
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S0[e], cs, nk[e >> 1]));
-        p[4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S1[e], cs, nk[2 + (e >> 1)]));
-    }
+    const float nk = nm_own + kbl;
+    const h2 d = {(_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(y, cs, nk)),
+                  (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z, cs, nk))};
+    const uint32_t du = __builtin_bit_cast(uint32_t, d);
+    constexpr int AND = 16 | (GQ - 1);          // keep the head bits and the row parity
+    P[0] = __builtin_bit_cast(h2, swizzle<AND, 0 * GQ, 0>(du));
+    P[1] = __builtin_bit_cast(h2, swizzle<AND, 1 * GQ, 0>(du));
+    P[2] = __builtin_bit_cast(h2, swizzle<AND, 2 * GQ, 0>(du));
+    P[3] = __builtin_bit_cast(h2, swizzle<AND, 3 * GQ, 0>(du));
     h8 W;
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-        P[m][0] = (_Float16)p[2 * m];
-        P[m][1] = (_Float16)p[2 * m + 1];
-        W[2 * m] = W[2 * m + 1] = (_Float16)(float)(1 << pair_shift<SB>(m));
-    }
+    for (int m = 0; m < 4; m++) W[2 * m] = W[2 * m + 1] = (_Float16)(float)(1 << pair_shift<SB>(m));
     Lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(W, pack_h8(P), Lsum, 0, 0, 0);
 }
 
@@ -1536,7 +1556,10 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
 
     float m_run = -INFINITY, m_thr = -INFINITY;
     f4 Lsum = (f4){0.f, 0.f, 0.f, 0.f};
-    float nm[4] = {INFINITY, INFINITY, INFINITY, INFINITY}, vb[4] = {0.f, 0.f, 0.f, 0.f};
+    float nm_own = INFINITY, vb[4] = {0.f, 0.f, 0.f, 0.f};
+    const int own = (j / GQ) & 3;               // the pair of p this lane computes
+    const uint32_t ob0 = (own & 1) ? ~0u : 0u, ob1 = (own & 2) ? ~0u : 0u;
+    const float ps_own = (float)(kScaleLog2<BITS>(own) + kSlack);
     f4 accV[8];
 #pragma unroll
     for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -1631,7 +1654,8 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
             }
         }
         h2 P[4];
-        softmax_step<BITS>(S0, S1, cs, Sk[0] * a.sm_log2, m_run, m_thr, nm, Lsum, vb, accV, P);
+        softmax_step<BITS, GQ>(S0, S1, cs, Sk[0] * a.sm_log2, ob0, ob1, ps_own, m_run, m_thr,
+                               nm_own, Lsum, vb, accV, P);
         h2 vs[4], vz[4], ps[4];
         {
             const uint2 *s2 = (const uint2 *)side;
