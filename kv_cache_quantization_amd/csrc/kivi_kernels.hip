@@ -1133,6 +1133,19 @@ __device__ __forceinline__ void dma_1k(const uint8_t *src_lane, uint32_t lds_dst
 // Per-mille weight shift of decode splits between even and odd XCDs.
 constexpr int64_t kXcdSkew = 20;
 
+// Split items of the decode pass, in launch order: the grid's split items are
+// cut into four quarters (quarter r holds (splits + 3 - r) / 4 splits of
+// every stream, stream by stream, a stream's splits adjacent), so that each
+// stream has splits in every quarter.  The quarters reach the compute units in
+// turn, and a SIMD issues the wavefronts it received first ahead of the later
+// ones: splits of earlier quarters get a larger share of their stream's
+// groups (per mille of the average).
+constexpr int64_t kQuarterWeight[4] = {1060, 1020, 980, 940};
+
+__device__ __forceinline__ int64_t quarter_splits(int64_t splits, int r) {
+    return (splits + 3 - r) / 4;
+}
+
 // Wavefront priority (s_setprio takes an immediate, 0..3).
 __device__ __forceinline__ void set_prio(int p) {
     if (p >= 3) __builtin_amdgcn_s_setprio(3);
@@ -1487,17 +1500,30 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int items = a.items;
     const int64_t ng = a.n_quant / G;
     // The stream's ng groups are shared among its splits in proportion to a
-    // weight per split: workgroups go to the eight XCDs in turn (block b to
-    // XCD b mod 8), and on MI355X the odd-numbered XCDs stream slower than the
-    // even ones (4-10 % with cached copies, about half that with the
-    // non-temporal ones), so splits whose block is odd get kXcdSkew per mille
-    // less than the average and even ones that much more.  Any weights give
-    // the same groups overall, so results do not depend on them.
-    const int64_t xbase = (int64_t)blockIdx.x - sp;     // block of split 0
+    // weight per split: the weight of the split's quarter of the grid
+    // (kQuarterWeight) times an XCD factor.  Workgroups go to the eight XCDs
+    // in turn (block b to XCD b mod 8), and on MI355X the odd-numbered XCDs
+    // stream slower than the even ones (4-10 % with cached copies, about half
+    // that with the non-temporal ones), so splits whose block is odd get
+    // kXcdSkew per mille less than the average and even ones that much more.
+    // Any weights give the same groups overall, so results do not depend on
+    // them.  Split k of quarter r is block tail + streams * (splits before
+    // quarter r) + stream * (quarter's splits) + (k - splits before r).
     const int64_t WE = 1000 + kXcdSkew, WO = 1000 - kXcdSkew;
+    const int64_t streams = (int64_t)a.batch * a.kv_heads;
+    const int64_t tail_blocks = streams * a.tail_items;
     auto cum = [&](int64_t k) {                         // weight of splits [0, k)
-        const int64_t odd = (xbase + k) / 2 - xbase / 2;
-        return (k - odd) * WE + odd * WO;
+        int64_t c = 0, k0 = 0;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t u = quarter_splits(a.splits, r);
+            const int64_t m = k - k0 < 0 ? 0 : k - k0 > u ? u : k - k0;
+            const int64_t base = tail_blocks + streams * k0 + stream * u;
+            const int64_t odd = (base + m) / 2 - base / 2;
+            c += kQuarterWeight[r] * ((m - odd) * WE + odd * WO);
+            k0 += u;
+        }
+        return c;
     };
     const int64_t wsum = cum(a.splits);
     const int64_t g0 = ng * cum(sp) / wsum, g1 = ng * cum(sp + 1) / wsum;
@@ -1947,13 +1973,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     }
     // (q's dtype selects an instantiation: the prologue's loads must not
     // meet at a control-flow join, where the compiler would wait for them)
+    // split item it: quarter r, then stream, then split (kQuarterWeight)
     const int64_t it = item - streams * a.tail_items;
+    int64_t k0 = 0;
+    int r = 0;
+    for (; r < 3 && it >= streams * (k0 + quarter_splits(a.splits, r)); r++)
+        k0 += quarter_splits(a.splits, r);
+    const int64_t u = quarter_splits(a.splits, r);
+    const int64_t rem = it - streams * k0;
+    const int stream = (int)(rem / u), sp = (int)(k0 + rem % u);
     if (a.q_is_f32)
-        decode_split<BITS, GQ, true, OUT, DEEP>(a, (int)(it / a.splits), (int)(it % a.splits),
-                                                pipe, q_lds);
+        decode_split<BITS, GQ, true, OUT, DEEP>(a, stream, sp, pipe, q_lds);
     else
-        decode_split<BITS, GQ, false, OUT, DEEP>(a, (int)(it / a.splits), (int)(it % a.splits),
-                                                 pipe, q_lds);
+        decode_split<BITS, GQ, false, OUT, DEEP>(a, stream, sp, pipe, q_lds);
 }
 
 // Merge the partials of one output row (a (batch, query head) of the decode
