@@ -107,12 +107,11 @@ typedef struct kivi_cache kivi_cache;   /* opaque host-side handle */
 
 /* Where everything sits inside the caller's device buffer (byte offsets from
    its start).  Packed blocks: [B*H][max_groups][block_bytes], block j of a
-   stream holding tokens [32j, 32j+32) whatever G is.  Inside a block
-   (offsets below are from the block start): K codes, V codes (code_bytes =
-   b*32*D/8 each), then fp16 K scale[D], K zero[D] of the key group the
-   block lies in (repeated in each of a group's G/32 blocks), V scale[4][32],
-   V zero[4][32]: slot cg of token t holds the parameters of the value group
-   containing channels 32cg .. 32cg+31 (repeated when G > 32).  With
+   stream holding tokens [32j, 32j+32) whatever G is.  At G = 32, inside a
+   block (offsets below are from the block start): K codes, V codes
+   (code_bytes = b*32*D/8 each), then fp16 K scale[D], K zero[D] of the key
+   group, V scale[4][32], V zero[4][32]: slot cg of token t holds the
+   parameters of the value group of channels 32cg .. 32cg+31.  With
    key_outliers = n > 0 (outlier-aware keys, the cookbook notebook's
    "Exercises" item 2, read per key group), the n channels of each key
    group with the largest max |K| over its tokens (ties: lower channel)
@@ -131,6 +130,16 @@ typedef struct kivi_cache kivi_cache;   /* opaque host-side handle */
    Keys:   token 16(o/4) + l%16, channel 32(o%4) + 8(l/16) + kk.
    Values: token 4(l/16) + kk%4 + 16(kk/4), channel 16o + l%16.
    (Tokens are counted from the start of the block.)
+   Split layout (G = 64 or 128, and the segment policy, whose value groups
+   span all D channels): a block holds K codes, V codes, then fp16 V
+   scale[D/G][32] and V zero[D/G][32] only (slot gv of token t: value group
+   gv; off_vscale / off_vzero give the offsets), and the key zero / scale
+   live once per key unit in the region at `kside`: [B*H][max_kside_units]
+   units of fp16 K scale[D] then K zero[D] (off_kscale, off_kzero are the
+   offsets inside a unit), unit u holding key group u (kside_unit_tokens =
+   G tokens; the segment policy: one unit per 32-token block, the pair of
+   the segment the block lies in).  The packed bytes are then exactly b bits
+   per code and two fp16 per group ([NB] storage cell).
    Ring: [B*H][ring_capacity][D] in kv_dtype for K and for
    V; token t of a stream lives in slot t mod ring_capacity while it is in
    [G * floor(n_vquantized / G), n_tokens), which holds the key residual
@@ -146,6 +155,10 @@ typedef struct {
     int64_t n_vquantized;               /* value tokens quantized: Q(n) / Q_V(n) */
     size_t outliers;                    /* key_outliers > 0: offset of the    */
                                         /* records [B*H][max_groups][256]     */
+    size_t kside;                       /* split layout: offset of the key    */
+                                        /*   units (0 otherwise)              */
+    int64_t kside_unit_tokens;          /* tokens per key unit (0: in-block)  */
+    int64_t max_kside_units;            /* key units per stream               */
 } kivi_layout;
 
 /* What an append of n_new tokens will do (pure host computation). */

@@ -178,6 +178,17 @@ class KiviCache:
         return self.buffer[lo.blocks:lo.blocks + nbytes].view(
             self.streams, lo.max_groups, lo.block_bytes)
 
+    def kside_view(self):
+        """[streams, max_kside_units, 2, D] fp16 key units of the split layout
+        (G > 32: K scale, K zero of each key group), or None at G = 32."""
+        lo = self.layout()
+        if lo.kside_unit_tokens == 0:
+            return None
+        D = self.cfg.head_dim
+        nbytes = self.streams * lo.max_kside_units * 4 * D
+        return self.buffer[lo.kside:lo.kside + nbytes].view(torch.float16).view(
+            self.streams, lo.max_kside_units, 2, D)
+
     def outlier_records_view(self) -> torch.Tensor:
         """[streams, max_groups, 256] bytes of the outlier records (key_outliers > 0)."""
         lo = self.layout()

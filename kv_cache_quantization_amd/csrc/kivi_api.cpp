@@ -34,6 +34,9 @@ struct kivi_cache {
     uint8_t *base;
     size_t bytes;
     size_t off_blocks, off_ring_k, off_ring_v, off_outliers;
+    size_t off_kside;                        // split layout: key units
+    int64_t max_kunits, kunit_blocks;        //   per stream; blocks per unit
+    bool split;                              // G > 32: the split layout
     size_t off_seg_partial, off_seg_stats;   // segment policy scratch
     int32_t seg_chunks;                      // chunks of the longest segment
     int64_t max_groups;
@@ -101,19 +104,34 @@ struct Sizes {
     int64_t max_groups, block_bytes, code_bytes, ring_cap;
     int esize;
     int32_t seg_chunks;
-    size_t off_blocks, off_ring_k, off_ring_v, off_outliers, off_seg_partial, off_seg_stats, total;
+    bool split;
+    int64_t max_kunits, kunit_blocks;
+    size_t off_blocks, off_kside, off_ring_k, off_ring_v, off_outliers, off_seg_partial,
+        off_seg_stats, total;
 };
 
+// Block layouts.  G = 32: a block carries its key group's zero / scale and
+// four value slots per token.  G > 32 (and the segment policy, whose value
+// groups span all D channels), the split layout: a block carries the codes
+// and its tokens' D / G value pairs only, and each key unit (a key group;
+// under the segment policy one 32-token block) has its zero / scale once, in
+// a region of its own, so the cache holds b bits per code and two fp16 per
+// group ([NB] storage cell) and the decode reads only those bytes.
 Sizes sizes_of(const kivi_config *c) {
     Sizes s;
     const int64_t streams = (int64_t)c->batch * c->n_kv_heads;
     s.max_groups = c->max_tokens / kGroup;     // 32-token blocks
     s.code_bytes = (int64_t)c->bits * kGroup * c->head_dim / 8;
-    s.block_bytes = 2 * s.code_bytes + 4 * (int64_t)c->head_dim * 2;
+    s.split = c->group > kGroup;
+    s.block_bytes = s.split ? 2 * s.code_bytes + 2 * 2 * (int64_t)kGroup * (c->head_dim / c->group)
+                            : 2 * s.code_bytes + 4 * (int64_t)c->head_dim * 2;
+    s.kunit_blocks = c->policy == KIVI_FLUSH_SEGMENT ? 1 : c->group / kGroup;
+    s.max_kunits = s.split ? (s.max_groups + s.kunit_blocks - 1) / s.kunit_blocks : 0;
     s.ring_cap = (int64_t)c->residual + c->group;
     s.esize = c->kv_dtype == KIVI_F32 ? 4 : 2;
     s.off_blocks = 0;
-    s.off_ring_k = align_up((size_t)(streams * s.max_groups * s.block_bytes));
+    s.off_kside = align_up((size_t)(streams * s.max_groups * s.block_bytes));
+    s.off_ring_k = s.off_kside + align_up((size_t)(streams * s.max_kunits * 4 * c->head_dim));
     const size_t ring_bytes = align_up((size_t)(streams * s.ring_cap * c->head_dim * s.esize));
     s.off_ring_v = s.off_ring_k + ring_bytes;
     s.off_outliers = s.off_ring_v + ring_bytes;
@@ -152,6 +170,22 @@ int64_t ring_low(const kivi_config &, int64_t qv) { return qv / kGroup * kGroup;
 bool canonical(const kivi_cache *c) {
     const Prefix p = prefix_of(c->cfg, c->n);
     return c->q == p.k && c->qv == p.v;
+}
+
+// Where the decode and attention kernels find zero / scale.
+void set_side_args(const kivi_cache *c, SideArgs &sa) {
+    sa.split = c->split;
+    sa.kside = c->base + c->off_kside;
+    sa.max_kunits = c->max_kunits;
+    int shift = 0;
+    while ((1 << shift) < c->kunit_blocks) shift++;
+    sa.kunit_shift = shift;
+    // value slot of the 32-channel group cg: cg >> vsh of nvs slots per token
+    const int gt = c->cfg.group / kGroup;
+    int vsh = 0;
+    while ((1 << vsh) < gt) vsh++;
+    sa.vsh = c->split ? vsh : 0;
+    sa.nvs = c->split ? c->cfg.head_dim / c->cfg.group : 4;
 }
 
 // G-token chunks of the residual [Q, n) (walked by one item per stream).
@@ -321,6 +355,10 @@ kivi_status kivi_cache_create(const kivi_config *cfg, void *dev_mem, size_t dev_
     c->off_ring_k = s.off_ring_k;
     c->off_ring_v = s.off_ring_v;
     c->off_outliers = s.off_outliers;
+    c->off_kside = s.off_kside;
+    c->max_kunits = s.max_kunits;
+    c->kunit_blocks = s.kunit_blocks;
+    c->split = s.split;
     c->off_seg_partial = s.off_seg_partial;
     c->off_seg_stats = s.off_seg_stats;
     c->seg_chunks = s.seg_chunks;
@@ -398,6 +436,8 @@ kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const voi
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
     a.block_bytes = c->block_bytes;
+    a.kside = c->base + c->off_kside;
+    a.max_kunits = c->max_kunits;
     a.in_k = k;
     a.in_v = v;
     a.n_new = n_new;
@@ -580,6 +620,7 @@ kivi_status enqueue_decode(kivi_cache *c, const void *q, int32_t q_dtype, float 
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
     a.block_bytes = c->block_bytes;
+    set_side_args(c, a.side);
     a.ring_k = c->base + c->off_ring_k;
     a.ring_v = c->base + c->off_ring_v;
     a.ring_cap = c->ring_cap;
@@ -708,6 +749,7 @@ kivi_status kivi_attn(kivi_cache *c, const void *q, int32_t q_dtype, int64_t T, 
     a.blocks = c->base + c->off_blocks;
     a.max_groups = c->max_groups;
     a.block_bytes = c->block_bytes;
+    set_side_args(c, a.side);
     a.ring_k = c->base + c->off_ring_k;
     a.ring_v = c->base + c->off_ring_v;
     a.ring_cap = c->ring_cap;
@@ -753,10 +795,21 @@ kivi_status kivi_get_layout(const kivi_cache *c, kivi_layout *o) {
     o->code_bytes = (size_t)c->code_bytes;
     o->off_kcode = 0;
     o->off_vcode = (size_t)c->code_bytes;
-    o->off_kscale = 2 * (size_t)c->code_bytes;
-    o->off_kzero = o->off_kscale + 2 * (size_t)c->cfg.head_dim;
-    o->off_vscale = o->off_kzero + 2 * (size_t)c->cfg.head_dim;
-    o->off_vzero = o->off_vscale + 2 * (size_t)c->cfg.head_dim;
+    if (c->split) {
+        // key zero / scale inside a key unit; value pairs after the codes
+        o->off_kscale = 0;
+        o->off_kzero = 2 * (size_t)c->cfg.head_dim;
+        o->off_vscale = 2 * (size_t)c->code_bytes;
+        o->off_vzero = o->off_vscale + 2 * (size_t)kGroup * (c->cfg.head_dim / c->cfg.group);
+    } else {
+        o->off_kscale = 2 * (size_t)c->code_bytes;
+        o->off_kzero = o->off_kscale + 2 * (size_t)c->cfg.head_dim;
+        o->off_vscale = o->off_kzero + 2 * (size_t)c->cfg.head_dim;
+        o->off_vzero = o->off_vscale + 2 * (size_t)c->cfg.head_dim;
+    }
+    o->kside = c->split ? c->off_kside : 0;
+    o->kside_unit_tokens = c->split ? c->kunit_blocks * kGroup : 0;
+    o->max_kside_units = c->max_kunits;
     o->max_groups = c->max_groups;
     o->ring_capacity = c->ring_cap;
     o->n_tokens = c->n;

@@ -33,6 +33,11 @@ struct QuantizeArgs {
     uint8_t *blocks;            // [streams][max_groups][block_bytes]
     int64_t max_groups;
     int64_t block_bytes;
+    // Split layout (G > 32): key units [streams][max_kunits][2][D] fp16, one
+    // per key group (segment policy: per block); blocks carry the codes and
+    // D / G value pairs per token.
+    uint8_t *kside;
+    int64_t max_kunits;
     const void *in_k, *in_v;    // [streams][n_new][D] chunk (kv dtype)
     int64_t n_new;
     const void *ring_k, *ring_v;// [streams][ring_cap][D] (kv dtype)
@@ -68,10 +73,24 @@ struct QuantizeArgs {
 // Blocks per wavefront of the segment statistics pass.
 constexpr int kSegChunkBlocks = 16;
 
+// Where the decode and attention kernels find zero / scale.  G = 32: in
+// every block (kscale, kzero, then four value slots per token).  Split
+// layout (split = 1): key units of 2 x D fp16 in kside (unit = block >>
+// kunit_shift), nvs value slots per token after the block's codes.  The
+// 32-channel group cg reads value slot cg >> vsh of nvs.
+struct SideArgs {
+    int32_t split;
+    const uint8_t *kside;       // [streams][max_kunits][2][D] fp16
+    int64_t max_kunits;
+    int32_t kunit_shift;
+    int32_t vsh, nvs;
+};
+
 struct DecodeArgs {
     const uint8_t *blocks;
     int64_t max_groups;
     int64_t block_bytes;
+    SideArgs side;
     const void *ring_k, *ring_v;
     int64_t ring_cap;
     int32_t ring_is_f32;
@@ -117,6 +136,7 @@ struct AttnArgs {
     const uint8_t *blocks;
     int64_t max_groups;
     int64_t block_bytes;
+    SideArgs side;
     const void *ring_k, *ring_v;  // ring rows, fp16 or (ring_f32) float32
     int64_t ring_cap;
     int32_t ring_f32;

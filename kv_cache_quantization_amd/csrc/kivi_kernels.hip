@@ -551,11 +551,18 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
     // 2^-14 + ... for t <= 256.  The margin below is about 4x that.
     const float near_tie = 0.5f - ((BITS == 8 ? 0x1p-12f : 0x1p-16f) + 0x1p-22f * czmax);
 
-    // codes, zero / scale of block g (whose rows are in t)
+    // codes, zero / scale of block g (whose rows are in t).  G = 32 (GT = 1):
+    // the block's side area is kscale, kzero, vscale[4][32], vzero[4][32].
+    // G > 32 (the split layout): it is vscale[NVG][32], vzero[NVG][32], and
+    // the key zero / scale go to the key unit of the group (under the
+    // segment policy: of the block), written by its first block only.
+    constexpr bool SPLIT = GT > 1;
+    constexpr int NVG = 4 / GT;                         // value groups per token
+    constexpr int KUB = KSEG ? 1 : GT;                  // blocks per key unit
     auto store_block = [&](int64_t g) {
     uint8_t *blk = a.blocks + (stream * a.max_groups + g) * a.block_bytes;
     constexpr int cbytes = BITS * G * D / 8;
-    _Float16 *side = (_Float16 *)(blk + 2 * cbytes);   // kscale, kzero, vscale, vzero
+    _Float16 *side = (_Float16 *)(blk + 2 * cbytes);
 
     // zero / scale as fp16
     if (!IS_V) {
@@ -573,7 +580,14 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
 #pragma unroll
             for (int p = 0; p < 4; p++)
                 w[p] = q == 0 ? pack_f16(sk[2 * p], sk[2 * p + 1]) : pack_f16(zk[2 * p], zk[2 * p + 1]);
-            *(uint4 *)(side + q * D + 8 * c) = (uint4){w[0], w[1], w[2], w[3]};
+            if constexpr (SPLIT) {
+                if (g % KUB == 0) {
+                    _Float16 *ku = (_Float16 *)(a.kside + (stream * a.max_kunits + g / KUB) * (4 * D));
+                    *(uint4 *)(ku + q * D + 8 * c) = (uint4){w[0], w[1], w[2], w[3]};
+                }
+            } else {
+                *(uint4 *)(side + q * D + 8 * c) = (uint4){w[0], w[1], w[2], w[3]};
+            }
         }
         if constexpr (OUT) {
             // the block's outlier record: header (lane 0), each kept channel's
@@ -625,7 +639,14 @@ __device__ __forceinline__ void quantize_task(const QuantizeArgs &a, int64_t str
         const uint32_t z45 = pack_f16(mn[4], mn[5]), z67 = pack_f16(mn[6], mn[7]);
         const uint32_t w0 = part == 0 ? s01 : part == 1 ? s45 : part == 2 ? z01 : z45;
         const uint32_t w1 = part == 0 ? s23 : part == 1 ? s67 : part == 2 ? z23 : z67;
-        *(uint2 *)(side + (2 + (part >> 1)) * D + (c >> 2) * G + 16 * jh + 4 * q) = (uint2){w0, w1};
+        if constexpr (SPLIT) {
+            // slot gv of the value group of channels 32 (c / 4) ..: the quads
+            // of one group hold the same pairs and store the same words
+            *(uint2 *)(side + (part >> 1) * (NVG * G) + ((c >> 2) / GT) * G + 16 * jh + 4 * q) =
+                (uint2){w0, w1};
+        } else {
+            *(uint2 *)(side + (2 + (part >> 1)) * D + (c >> 2) * G + 16 * jh + 4 * q) = (uint2){w0, w1};
+        }
     }
 
     // Units u = 0..7 (key row j = u over channels kk; value channel e = u over
@@ -1463,28 +1484,46 @@ __device__ __forceinline__ void dma_256(const uint8_t *src_lane, uint32_t lds_ds
                      : "memory", "m0");
 }
 
-template <int BITS, bool OUT = false>
+// One group into an LDS stage.  G = 32: the whole block (and with OUT its
+// outlier record after it).  Split layout (SPLIT): the block's codes, then
+// its key unit ku (512 bytes) at the offset where a G = 32 block has its key
+// scale and zero, then its value pairs (vbytes = 128 * value slots per
+// token: lanes past them copy the first ones again, into LDS the stage does
+// not use), so that the stage reads the same way in both layouts.
+template <int BITS, bool OUT = false, bool SPLIT = false>
 __device__ __forceinline__ void issue_group(const uint8_t *blk, const uint8_t *rec, uint32_t stage,
-                                            int l, bool nt = false) {
+                                            int l, bool nt = false, const uint8_t *ku = nullptr,
+                                            int vlanes = 64) {
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // prior reads of the stage done
+    if constexpr (SPLIT) {
+        constexpr int CB2 = 2 * Pipe<BITS>::CB;
 #pragma unroll
-    for (int c = 0; c < Pipe<BITS>::DPG; c++)
-        dma_1k(blk + c * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(stage + c * 1024), nt);
-    if constexpr (OUT)
-        dma_256(rec + 4 * l, __builtin_amdgcn_readfirstlane(stage + Pipe<BITS>::BB), nt);
+        for (int c = 0; c < CB2 / 1024; c++)
+            dma_1k(blk + c * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(stage + c * 1024), nt);
+        dma_256(ku + 4 * l, __builtin_amdgcn_readfirstlane(stage + CB2), nt);
+        dma_256(ku + 256 + 4 * l, __builtin_amdgcn_readfirstlane(stage + CB2 + 256), nt);
+        dma_256(blk + CB2 + 4 * (l & (vlanes - 1)), __builtin_amdgcn_readfirstlane(stage + CB2 + 512),
+                nt);
+    } else {
+#pragma unroll
+        for (int c = 0; c < Pipe<BITS>::DPG; c++)
+            dma_1k(blk + c * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(stage + c * 1024), nt);
+        if constexpr (OUT)
+            dma_256(rec + 4 * l, __builtin_amdgcn_readfirstlane(stage + Pipe<BITS>::BB), nt);
+    }
 }
 
 // Wait until at most `r` groups (issued after the one needed) are in flight.
-template <int BITS, bool OUT = false>
+template <int BITS, bool OUT = false, bool SPLIT = false>
 __device__ __forceinline__ void wait_groups_after(int r) {
-    constexpr int P = Pipe<BITS>::DPG + (OUT ? 1 : 0);
+    constexpr int P = SPLIT ? 2 * Pipe<BITS>::CB / 1024 + 3 : Pipe<BITS>::DPG + (OUT ? 1 : 0);
     if (r >= 3) wait_vm<3 * P>();
     else if (r == 2) wait_vm<2 * P>();
     else if (r == 1) wait_vm<P>();
     else wait_vm<0>();
 }
 
-template <int BITS, int GQ, bool QF32, bool OUT = false, bool DEEP = false>
+template <int BITS, int GQ, bool QF32, bool OUT = false, bool DEEP = false, bool SPLIT = false>
 __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *pipe,
                              uint4 *q_lds) {
     using PP = Pipe<BITS>;
@@ -1532,6 +1571,11 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
     const uint8_t *srec = OUT ? a.outliers + ((int64_t)stream * a.max_groups + g0) * kOutlierRecordBytes
                               : nullptr;
+    const int64_t bstride = SPLIT ? a.block_bytes : PP::BB;
+    // split layout: the key unit of group g0 + i, and the value-pair lanes
+    const uint8_t *skside = a.side.kside + (int64_t)stream * a.side.max_kunits * (4 * D);
+    auto kunit = [&](int i) { return skside + ((g0 + i) >> a.side.kunit_shift) * (4 * D); };
+    const int vlanes = 32 * a.side.nvs;
     const uint32_t pbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)pipe;
     const bool nt = a.nt != 0;                  // the pass streams more than the caches keep
     // q of the lane's head in B-operand order, and the unscaled fp16 q of the
@@ -1559,9 +1603,10 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     // stage ring: `is` is the stage the next copy goes to, `rs` the stage read
     int issued = 0, is = 0, rs = 0;
     for (; issued < NST - 1 && issued < n_g; issued++) {
-        issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
-                               OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
-                               pbase + (uint32_t)is * SB, l, nt);
+        issue_group<BITS, OUT, SPLIT>(sblk + (int64_t)issued * bstride,
+                                      OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                                      pbase + (uint32_t)is * SB, l, nt,
+                                      SPLIT ? kunit(issued) : nullptr, vlanes);
         is = is + 1 == NST ? 0 : is + 1;
     }
     // first uses of q: after the copies above (volatile asm keeps the order)
@@ -1586,6 +1631,10 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     const int own = (j / GQ) & 3;               // the pair of p this lane computes
     const uint32_t ob0 = (own & 1) ? ~0u : 0u, ob1 = (own & 2) ? ~0u : 0u;
     const float ps_own = (float)(kScaleLog2<BITS>(own) + kSlack);
+    // value pairs of the lane's channel group cg, in 8-byte units from the
+    // side area: slot cg >> vsh of nvs (tokens 4 Gl .., +4 for 16 + 4 Gl ..)
+    const int vsi = 64 + 8 * (cg >> (SPLIT ? a.side.vsh : 0)) + Gl;
+    const int vzi = vsi + 8 * (SPLIT ? a.side.nvs : 4);
     f4 accV[8];
 #pragma unroll
     for (int o = 0; o < 8; o++) accV[o] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -1607,13 +1656,14 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
             set_prio(prio);
         }
         if (issued < n_g) {
-            issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
-                                   OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
-                                   pbase + (uint32_t)is * SB, l, nt);
+            issue_group<BITS, OUT, SPLIT>(sblk + (int64_t)issued * bstride,
+                                          OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                                          pbase + (uint32_t)is * SB, l, nt,
+                                          SPLIT ? kunit(issued) : nullptr, vlanes);
             is = is + 1 == NST ? 0 : is + 1;
             issued++;
         }
-        wait_groups_after<BITS, OUT>(issued - 1 - g);
+        wait_groups_after<BITS, OUT, SPLIT>(issued - 1 - g);
         const uint8_t *stg = pipe + rs * SB;
         rs = rs + 1 == NST ? 0 : rs + 1;
         const uint4 *side = (const uint4 *)(stg + 2 * PP::CB);
@@ -1685,8 +1735,8 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
         h2 vs[4], vz[4], ps[4];
         {
             const uint2 *s2 = (const uint2 *)side;
-            const uint2 a0 = s2[64 + 8 * cg + Gl], a1 = s2[64 + 8 * cg + Gl + 4];
-            const uint2 z0 = s2[96 + 8 * cg + Gl], z1 = s2[96 + 8 * cg + Gl + 4];
+            const uint2 a0 = s2[vsi], a1 = s2[vsi + 4];
+            const uint2 z0 = s2[vzi], z1 = s2[vzi + 4];
             vs[0] = __builtin_bit_cast(h2, a0.x); vs[1] = __builtin_bit_cast(h2, a0.y);
             vs[2] = __builtin_bit_cast(h2, a1.x); vs[3] = __builtin_bit_cast(h2, a1.y);
             vz[0] = __builtin_bit_cast(h2, z0.x); vz[1] = __builtin_bit_cast(h2, z0.y);
@@ -1741,7 +1791,7 @@ __device__ __forceinline__ void code_pos(bool is_v, int t, int c, int &dw, int &
 // item's running state like a residual chunk; p.V runs on the vector ALUs,
 // lane l owning channels 2l, 2l+1, with V-hat = code * scale, then + zero,
 // in float32 for tokens below n_vquant and the ring's rows for the others.
-template <int BITS, int GQ, bool RF32, bool QF32, bool OUT>
+template <int BITS, int GQ, bool RF32, bool QF32, bool OUT, bool SPLIT = false>
 __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t *lds,
                                uint4 *q_lds) {
     using PP = Pipe<BITS>;
@@ -1783,6 +1833,8 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
 #pragma unroll
     for (int hh = 0; hh < GQ; hh++) { Mr[hh] = -INFINITY; Lr[hh] = 0.f; O0[hh] = O1[hh] = 0.f; }
     const int c0 = 2 * l, cgv = c0 / G;
+    // value pairs of channel group cgv (fp16 index from the side area)
+    const int vsf = 2 * D + G * (cgv >> a.side.vsh), vzf = vsf + G * a.side.nvs;
     const int g_begin = mi * a.mixed_step;
     const int g_end = g_begin + a.mixed_step < a.mixed_groups ? g_begin + a.mixed_step
                                                                : a.mixed_groups;
@@ -1790,12 +1842,11 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
         const int64_t g = a.n_quant / G + gi;
         const uint8_t *blk = a.blocks + ((int64_t)stream * a.max_groups + g) * a.block_bytes;
         lds_sync_wave();            // the previous group's LDS reads are done
-#pragma unroll
-        for (int cc = 0; cc < PP::DPG; cc++)
-            dma_1k(blk + cc * 1024 + 16 * l, __builtin_amdgcn_readfirstlane(lbase + cc * 1024));
-        if constexpr (OUT)
-            dma_256(a.outliers + ((int64_t)stream * a.max_groups + g) * kOutlierRecordBytes + 4 * l,
-                    __builtin_amdgcn_readfirstlane(lbase + PP::BB));
+        issue_group<BITS, OUT, SPLIT>(
+            blk, OUT ? a.outliers + ((int64_t)stream * a.max_groups + g) * kOutlierRecordBytes : nullptr,
+            lbase, l, false,
+            a.side.kside + ((int64_t)stream * a.side.max_kunits + (g >> a.side.kunit_shift)) * (4 * D),
+            32 * a.side.nvs);
         // the group's value rows from the ring (slots of tokens below
         // n_vquant may hold other tokens: those rows are not used)
         float2 vr[G];
@@ -1898,8 +1949,8 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
                     int dv0, bv0, dv1, bv1;
                     code_pos<BITS>(true, r, c0, dv0, bv0);
                     code_pos<BITS>(true, r, c0 + 1, dv1, bv1);
-                    const float vs = (float)sd[2 * D + cgv * G + r];
-                    const float vz = (float)sd[3 * D + cgv * G + r];
+                    const float vs = (float)sd[vsf + r];
+                    const float vz = (float)sd[vzf + r];
                     vr[r].x = (float)((vcode[dv0] >> bv0) & M1) * vs + vz;
                     vr[r].y = (float)((vcode[dv1] >> bv1) & M1) * vs + vz;
                 }
@@ -1943,22 +1994,22 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
 
 // A kernel of its own (one wavefront per (stream, mixed item)), so that its
 // registers do not count against the occupancy of decode_kernel.
-template <int BITS, int GQ, bool OUT>
+template <int BITS, int GQ, bool OUT, bool SPLIT = false>
 __global__ __launch_bounds__(64) void decode_mixed_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t blk[stage_bytes<BITS, OUT>() + GQ * G * 4];
     __shared__ uint4 q_lds[64];
     const int streams = a.batch * a.kv_heads;
     const int stream = (int)(blockIdx.x % streams), mi = (int)(blockIdx.x / streams);
     if (a.ring_is_f32) {
-        if (a.q_is_f32) decode_mixed_t<BITS, GQ, true, true, OUT>(a, stream, mi, blk, q_lds);
-        else decode_mixed_t<BITS, GQ, true, false, OUT>(a, stream, mi, blk, q_lds);
+        if (a.q_is_f32) decode_mixed_t<BITS, GQ, true, true, OUT, SPLIT>(a, stream, mi, blk, q_lds);
+        else decode_mixed_t<BITS, GQ, true, false, OUT, SPLIT>(a, stream, mi, blk, q_lds);
     } else {
-        if (a.q_is_f32) decode_mixed_t<BITS, GQ, false, true, OUT>(a, stream, mi, blk, q_lds);
-        else decode_mixed_t<BITS, GQ, false, false, OUT>(a, stream, mi, blk, q_lds);
+        if (a.q_is_f32) decode_mixed_t<BITS, GQ, false, true, OUT, SPLIT>(a, stream, mi, blk, q_lds);
+        else decode_mixed_t<BITS, GQ, false, false, OUT, SPLIT>(a, stream, mi, blk, q_lds);
     }
 }
 
-template <int BITS, int GQ, bool OUT = false, bool DEEP = false>
+template <int BITS, int GQ, bool OUT = false, bool DEEP = false, bool SPLIT = false>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t pipe[decode_lds_bytes<BITS, OUT, DEEP>()];
     __shared__ uint4 q_lds[64];
@@ -1983,9 +2034,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int64_t rem = it - streams * k0;
     const int stream = (int)(rem / u), sp = (int)(k0 + rem % u);
     if (a.q_is_f32)
-        decode_split<BITS, GQ, true, OUT, DEEP>(a, stream, sp, pipe, q_lds);
+        decode_split<BITS, GQ, true, OUT, DEEP, SPLIT>(a, stream, sp, pipe, q_lds);
     else
-        decode_split<BITS, GQ, false, OUT, DEEP>(a, stream, sp, pipe, q_lds);
+        decode_split<BITS, GQ, false, OUT, DEEP, SPLIT>(a, stream, sp, pipe, q_lds);
 }
 
 // Merge the partials of one output row (a (batch, query head) of the decode
@@ -2115,7 +2166,7 @@ __device__ __forceinline__ void mask_scores(f4 &S0, f4 &S1, int64_t tok0, int Gl
     }
 }
 
-template <int BITS, int GQ, bool QF32, int CB, bool OUT = false>
+template <int BITS, int GQ, bool QF32, int CB, bool OUT = false, bool SPLIT = false>
 __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kernel(AttnArgs a) {
     using PP = Pipe<BITS>;
     constexpr int W = kAttnWaves;
@@ -2167,6 +2218,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
     const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
     const uint8_t *srec = OUT ? a.outliers + ((int64_t)stream * a.max_groups + g0) * kOutlierRecordBytes
                               : nullptr;
+    const int64_t bstride = SPLIT ? a.block_bytes : PP::BB;
+    // split layout: key unit of group gi, value slots (cg >> vsh of nvs)
+    const uint8_t *skside = a.side.kside + (int64_t)stream * a.side.max_kunits * (4 * D);
+    auto kunit = [&](int64_t gi) { return skside + (gi >> a.side.kunit_shift) * (4 * D); };
+    const int vsh = SPLIT ? a.side.vsh : 0, nvs = SPLIT ? a.side.nvs : 4;
     const uint32_t rbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
     h2 qB[CB][4][4];
 #pragma unroll
@@ -2178,9 +2234,10 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
     int issued = 0, is = 0, rs = 0;
     if (w == 0) {
         for (; issued < AST - 2 && issued < n_g; issued++) {
-            issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
-                                   OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
-                                   rbase + (uint32_t)is * SB, l);
+            issue_group<BITS, OUT, SPLIT>(sblk + (int64_t)issued * bstride,
+                                          OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                                          rbase + (uint32_t)is * SB, l, false,
+                                          SPLIT ? kunit(g0 + issued) : nullptr, 32 * nvs);
             is = is + 1 == AST ? 0 : is + 1;
         }
     }
@@ -2310,7 +2367,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
             // stages up to group g - 1 + AST are free
             const int last = g + 1 < n_g ? g + 1 : g;
             if (w == 0) {
-                constexpr int P = Pipe<BITS>::DPG + (OUT ? 1 : 0);
+                constexpr int P = SPLIT ? 2 * Pipe<BITS>::CB / 1024 + 3 : Pipe<BITS>::DPG + (OUT ? 1 : 0);
                 const int r = issued - 1 - last;
                 if (r >= 4) wait_vm<4 * P>();
                 else if (r == 3) wait_vm<3 * P>();
@@ -2321,9 +2378,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
             __syncthreads();
             if (w == 0) {
                 for (; issued < n_g && issued <= g + AST - 1; issued++) {
-                    issue_group<BITS, OUT>(sblk + (int64_t)issued * PP::BB,
-                                           OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
-                                           rbase + (uint32_t)is * SB, l);
+                    issue_group<BITS, OUT, SPLIT>(
+                        sblk + (int64_t)issued * bstride,
+                        OUT ? srec + (int64_t)issued * kOutlierRecordBytes : nullptr,
+                        rbase + (uint32_t)is * SB, l, false, SPLIT ? kunit(g0 + issued) : nullptr,
+                        32 * nvs);
                     is = is + 1 == AST ? 0 : is + 1;
                 }
             }
@@ -2345,7 +2404,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
         const bool masked = tok0 + G - 1 > pq_wave;
         h2 Pc[CB][4];
         const int cz = j & 3;
-        const uint2 z0 = s2[96 + 8 * cz + Gl], z1 = s2[96 + 8 * cz + Gl + 4];
+        const int zi = 64 + 8 * nvs + 8 * (cz >> vsh) + Gl;
+        const uint2 z0 = s2[zi], z1 = s2[zi + 4];
         const uint4 zz = {z0.x, z0.y, z1.x, z1.y};
 #pragma unroll
         for (int c = 0; c < CB; c++) {
@@ -2366,7 +2426,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
         }
 #pragma unroll
         for (int cg = 0; cg < 4; cg++) {
-            const uint2 a0 = s2[64 + 8 * cg + Gl], a1 = s2[64 + 8 * cg + Gl + 4];
+            const int si = 64 + 8 * (cg >> vsh) + Gl;
+            const uint2 a0 = s2[si], a1 = s2[si + 4];
             const h2 v0 = __builtin_bit_cast(h2, a0.x), v1 = __builtin_bit_cast(h2, a0.y);
             const h2 v2 = __builtin_bit_cast(h2, a1.x), v3 = __builtin_bit_cast(h2, a1.y);
             const h8 U0 = unpack_operand<BITS>(vc, 2 * cg), U1 = unpack_operand<BITS>(vc, 2 * cg + 1);
@@ -2408,7 +2469,16 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
             __syncthreads();        // stage 0 and the transposed rows are free
             const uint4 *blk =
                 (const uint4 *)(a.blocks + ((int64_t)stream * a.max_groups + gm) * a.block_bytes);
-            for (int i = threadIdx.x; i < PP::BB / 16; i += 64 * W) ((uint4 *)ring)[i] = blk[i];
+            if constexpr (SPLIT) {
+                // codes, the key unit where a G = 32 block has its key scale
+                // and zero, then the value pairs
+                const uint4 *ku = (const uint4 *)kunit(gm);
+                constexpr int C16 = 2 * PP::CB / 16;
+                for (int i = threadIdx.x; i < C16 + 32 + 8 * nvs; i += 64 * W)
+                    ((uint4 *)ring)[i] = i < C16 ? blk[i] : i < C16 + 32 ? ku[i - C16] : blk[i - 32];
+            } else {
+                for (int i = threadIdx.x; i < PP::BB / 16; i += 64 * W) ((uint4 *)ring)[i] = blk[i];
+            }
             if constexpr (OUT) {
                 const uint4 *rec = (const uint4 *)(a.outliers + ((int64_t)stream * a.max_groups + gm) *
                                                                     kOutlierRecordBytes);
@@ -2427,8 +2497,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
                     if (t < a.n_vquant) {
                         int dw, bit;
                         code_pos<BITS>(true, r, c, dw, bit);
-                        const float vs = (float)sd[2 * D + (c / G) * G + r];
-                        const float vz = (float)sd[3 * D + (c / G) * G + r];
+                        const float vs = (float)sd[2 * D + G * ((c / G) >> vsh) + r];
+                        const float vz = (float)sd[2 * D + G * (nvs + ((c / G) >> vsh)) + r];
                         v = (_Float16)((float)((vcode[dw] >> bit) & M1) * vs + vz);
                     } else {
                         const int64_t ri = (t % a.ring_cap) * D + c;
@@ -2728,23 +2798,33 @@ hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BITS, bool OUT = false, bool DEEP = false>
-static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
-    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4, OUT, DEEP>), grid, dim3(64), 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2, OUT, DEEP>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<BITS, 1, OUT, DEEP>), grid, dim3(64), 0, s, a);
+// The layouts the kernels read: G = 32 (four value slots, no shift) or the
+// split layout (1 or 2 value slots per token, unit shift 0..2, no outlier
+// records).
+static bool side_args_ok(const SideArgs &sa, int n_out) {
+    if (!sa.split) return sa.vsh == 0 && sa.nvs == 4;
+    return n_out == 0 && sa.kside && (sa.nvs == 1 || sa.nvs == 2) && sa.vsh >= 1 && sa.vsh <= 2 &&
+           (4 >> sa.vsh) == sa.nvs && sa.kunit_shift >= 0 && sa.kunit_shift <= 2;
 }
 
-template <int BITS, bool OUT>
+template <int BITS, bool OUT = false, bool DEEP = false, bool SPLIT = false>
+static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
+    if (gq == 4) hipLaunchKernelGGL((decode_kernel<BITS, 4, OUT, DEEP, SPLIT>), grid, dim3(64), 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((decode_kernel<BITS, 2, OUT, DEEP, SPLIT>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<BITS, 1, OUT, DEEP, SPLIT>), grid, dim3(64), 0, s, a);
+}
+
+template <int BITS, bool OUT, bool SPLIT = false>
 static void launch_mixed_out(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
-    if (gq == 4) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 4, OUT>), grid, dim3(64), 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 2, OUT>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((decode_mixed_kernel<BITS, 1, OUT>), grid, dim3(64), 0, s, a);
+    if (gq == 4) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 4, OUT, SPLIT>), grid, dim3(64), 0, s, a);
+    else if (gq == 2) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 2, OUT, SPLIT>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_mixed_kernel<BITS, 1, OUT, SPLIT>), grid, dim3(64), 0, s, a);
 }
 
 template <int BITS>
 static void launch_mixed_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
     if (a.n_out > 0) launch_mixed_out<BITS, true>(a, gq, grid, s);
+    else if (a.side.split) launch_mixed_out<BITS, false, true>(a, gq, grid, s);
     else launch_mixed_out<BITS, false>(a, gq, grid, s);
 }
 
@@ -2764,6 +2844,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
         return hipErrorInvalidValue;
     if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && !a.outliers))
         return hipErrorInvalidValue;
+    if (!side_args_ok(a.side, a.n_out)) return hipErrorInvalidValue;
     if (a.mixed_groups > 0) {
         if (a.mixed_items < 1 || a.mixed_step < 1 ||
             (int64_t)a.mixed_items * a.mixed_step < a.mixed_groups)
@@ -2780,6 +2861,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
         if (a.bits == 2) launch_decode_bits<2, true>(a, gq, grid, s);
         else if (a.bits == 8) launch_decode_bits<8, true>(a, gq, grid, s);
         else launch_decode_bits<4, true>(a, gq, grid, s);
+    } else if (a.side.split) {
+        if (a.bits == 2) launch_decode_bits<2, false, false, true>(a, gq, grid, s);
+        else if (a.bits == 8) launch_decode_bits<8, false, false, true>(a, gq, grid, s);
+        else if (a.deep) launch_decode_bits<4, false, true, true>(a, gq, grid, s);
+        else launch_decode_bits<4, false, false, true>(a, gq, grid, s);
     } else if (a.bits == 2) launch_decode_bits<2>(a, gq, grid, s);
     else if (a.bits == 8) launch_decode_bits<8>(a, gq, grid, s);
     else if (a.deep) launch_decode_bits<4, false, true>(a, gq, grid, s);
@@ -2791,19 +2877,20 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BITS, bool QF32, bool OUT>
+template <int BITS, bool QF32, bool OUT, bool SPLIT = false>
 static void launch_attn_out(const AttnArgs &a, int gq, dim3 grid, hipStream_t s) {
     const dim3 block(64 * kAttnWaves);
     if (gq == 4)
-        hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32, kAttnBlocks, OUT>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32, kAttnBlocks, OUT, SPLIT>), grid, block, 0, s, a);
     else if (gq == 2)
-        hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32, kAttnBlocks, OUT>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32, kAttnBlocks, OUT>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32, kAttnBlocks, OUT, SPLIT>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32, kAttnBlocks, OUT, SPLIT>), grid, block, 0, s, a);
 }
 
 template <int BITS, bool QF32>
 static void launch_attn_bits(const AttnArgs &a, int gq, dim3 grid, hipStream_t s) {
     if (a.n_out > 0) launch_attn_out<BITS, QF32, true>(a, gq, grid, s);
+    else if (a.side.split) launch_attn_out<BITS, QF32, false, true>(a, gq, grid, s);
     else launch_attn_out<BITS, QF32, false>(a, gq, grid, s);
 }
 
@@ -2816,6 +2903,7 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
         return hipErrorInvalidValue;
     if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && !a.outliers))
         return hipErrorInvalidValue;
+    if (!side_args_ok(a.side, a.n_out)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)workgroups);
     if (a.bits == 2) {
         if (a.q_is_f32) launch_attn_bits<2, true>(a, gq, grid, s);

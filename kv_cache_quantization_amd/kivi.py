@@ -57,7 +57,9 @@ class kivi_layout(ctypes.Structure):
         "off_vcode", "off_kscale", "off_kzero", "off_vscale", "off_vzero")] + [
         ("max_groups", ctypes.c_int64), ("ring_capacity", ctypes.c_int64),
         ("n_tokens", ctypes.c_int64), ("n_quantized", ctypes.c_int64),
-        ("n_vquantized", ctypes.c_int64), ("outliers", ctypes.c_size_t)]
+        ("n_vquantized", ctypes.c_int64), ("outliers", ctypes.c_size_t),
+        ("kside", ctypes.c_size_t), ("kside_unit_tokens", ctypes.c_int64),
+        ("max_kside_units", ctypes.c_int64)]
 
 
 class kivi_append_plan(ctypes.Structure):

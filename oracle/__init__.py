@@ -64,14 +64,17 @@ def lib():
                                               i64, i64, P, P, P, P, P, P, P, P]
         L.oracle_build_cache_segments.argtypes = [P, P, i32, i32, i32, i64, i32, i32, P, i32,
                                                   P, P, P, P, P, P]
-        L.oracle_pack_blocks_kv2.argtypes = [i32, i32, i32, i32, i64, i64, i32, i64,
-                                             P, P, P, P, P, P, P]
+        L.oracle_pack_blocks_kv2.argtypes = [i32, i32, i32, i32, i64, i64, i32, i64, i64,
+                                             P, P, P, P, P, P, P, P]
         L.oracle_decode_attn.argtypes = [P, P, P, i32, i32, i32, i64, i32, f64, P]
         L.oracle_attn_queries.argtypes = [P, P, P, i32, i32, i32, i64, i64, i32, f64, i32, P]
         L.oracle_block_bytes.restype = i64
         L.oracle_block_bytes.argtypes = [i32]
+        L.oracle_block_bytes_g.restype = i64
+        L.oracle_block_bytes_g.argtypes = [i32, i32]
         L.oracle_pack_blocks.argtypes = [i32, i32, i64, i32, i64, P, P, P, P, P, P, P]
-        L.oracle_pack_blocks_kv.argtypes = [i32, i32, i32, i64, i64, i32, i64, P, P, P, P, P, P, P]
+        L.oracle_pack_blocks_kv.argtypes = [i32, i32, i32, i64, i64, i32, i64, i64,
+                                            P, P, P, P, P, P, P, P]
         L.oracle_code_position.argtypes = [i32, i32, i32, i32, P, P]
         L.oracle_key_outliers.argtypes = [P, i32, i32, i32, i64, i32, i32, i64, i32,
                                           P, P, P, P, P]
@@ -291,29 +294,55 @@ def attn_queries(q, khat, vhat, causal: bool = False, sm_scale: float | None = N
     return out
 
 
-def block_bytes(bits: int) -> int:
-    return int(lib().oracle_block_bytes(bits))
+def block_bytes(bits: int, Gv: int = 32) -> int:
+    """Bytes of one 32-token block when value groups span Gv channels (the
+    split layout when Gv > 32; see oracle_block_bytes_g)."""
+    return int(lib().oracle_block_bytes_g(bits, Gv))
 
 
-def pack_blocks(cache: dict, max_groups: int | None = None) -> np.ndarray:
-    """Packed 32-token blocks [B*H, max_groups, block_bytes] (u8) of the
-    quantized tokens: keys of the first qk, values of the first qv (a value
-    row at or past qv inside a block that holds value rows packs as 0); each
-    block carries the zero / scale of its key group and of its tokens' value
-    groups (repeated when G > 32)."""
+def is_split(cache: dict) -> bool:
+    """The split layout (key zero / scale once per key group in a separate
+    array) is used when value groups span more than 32 channels."""
+    return cache.get("Gv", cache["G"]) > 32
+
+
+def kunit_tokens(cache: dict) -> int:
+    """Tokens per key unit of the split layout: the key group size."""
+    return cache.get("Gk", cache["G"])
+
+
+def pack_cache(cache: dict, max_groups: int | None = None, max_kunits: int | None = None):
+    """(blocks, kside): the packed 32-token blocks [B*H, max_groups,
+    block_bytes] (u8) of the quantized tokens -- keys of the first qk,
+    values of the first qv (a value row at or past qv inside a block that
+    holds value rows packs as 0) -- and, in the split layout, the key units
+    [B*H, max_kunits, 2, D] (fp16 bits: K scale, K zero of each key group),
+    else None.  See oracle_pack_blocks_kv2 for the two layouts."""
     assert cache["D"] == 128 and cache["G"] in (32, 64, 128)
     B, H, qk, qv, bits = cache["B"], cache["H"], cache["qk"], cache["qv"], cache["bits"]
+    Gk, Gv = kunit_tokens(cache), cache.get("Gv", cache["G"])
     ng = max(qk // 32, -(-qv // 32))
     if max_groups is None:
         max_groups = ng
     assert max_groups >= ng
-    out = np.zeros((B * H, max_groups, block_bytes(bits)), np.uint8)
-    lib().oracle_pack_blocks_kv2(B, H, cache.get("Gk", cache["G"]), cache.get("Gv", cache["G"]),
-                                 qk, qv, bits, max_groups,
-                                _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
-                                _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
-                                _p(out))
-    return out
+    out = np.zeros((B * H, max_groups, block_bytes(bits, Gv)), np.uint8)
+    kside = None
+    if is_split(cache):
+        if max_kunits is None:
+            max_kunits = qk // Gk
+        assert max_kunits >= qk // Gk
+        kside = np.zeros((B * H, max_kunits, 2, 128), np.uint16)
+    lib().oracle_pack_blocks_kv2(B, H, Gk, Gv, qk, qv, bits, max_groups,
+                                 max_kunits or 0,
+                                 _p(cache["kcodes"]), _p(cache["kzero16"]), _p(cache["kscale16"]),
+                                 _p(cache["vcodes"]), _p(cache["vzero16"]), _p(cache["vscale16"]),
+                                 _p(out), _p(kside) if kside is not None else None)
+    return out, kside
+
+
+def pack_blocks(cache: dict, max_groups: int | None = None) -> np.ndarray:
+    """The packed blocks of pack_cache (without the key units)."""
+    return pack_cache(cache, max_groups)[0]
 
 
 def pack_outlier_records(cache: dict, max_groups: int | None = None) -> np.ndarray:

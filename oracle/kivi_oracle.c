@@ -25,7 +25,8 @@
  *        and "streaming buffer strategy".
  *
  * Parity status: every function is pinned by tests/test_oracle_pins.py to
- * what the pages print or to closed forms.  The packers (oracle_pack_blocks_kv,
+ * what the pages print or to closed forms.  The packers (oracle_pack_blocks_kv
+ * in both layouts, with the key units of the split layout,
  * oracle_pack_outlier_records) are pinned by tests/test_oracle_layout_pins.py,
  * which decodes their output with its own forward reading of the documented
  * byte layout (never through code_position) back to the pinned logical
@@ -572,49 +573,67 @@ int64_t oracle_block_bytes(int bits)
     return 2 * (int64_t)(bits * G * D / 8) + 4 * (int64_t)D * 2;
 }
 
+/* Bytes of one 32-token block when value groups span Gv channels: with
+   Gv = 32 the block carries its key group's zero / scale and four value
+   slots per token (oracle_block_bytes); with Gv > 32 (the split layout) it
+   carries only the codes and its tokens' D / Gv value pairs, and the key
+   zero / scale live once per key group in a separate array. */
+int64_t oracle_block_bytes_g(int bits, int Gv)
+{
+    const int D = 128, T = 32;
+    if (Gv == T) return oracle_block_bytes(bits);
+    return 2 * (int64_t)(bits * T * D / 8) + 2 * 2 * (int64_t)T * (D / Gv);
+}
+
 /* Pack the quantized tokens of each stream into 32-token blocks:
-   out [B*H][max_blocks][block_bytes].  Keys of the first nk tokens (nk a
-   multiple of the group size G, G in {32, 64, 128}) and values of the first
-   nv tokens, from the logical arrays of oracle_build_cache for the same
-   (nk, nv, G): kcodes [B*H][nk][D], kzero16 / kscale16 [B*H][nk/G][D],
-   vcodes [B*H][nv][D], vzero16 / vscale16 [B*H][nv][D/G].  A block holds the
-   zero / scale of the key group it belongs to, and value slot cg (channels
-   32cg .. 32cg+31) of a token holds the zero / scale of the value group
-   containing those channels (both repeated when G > 32).  Every code or side
-   entry of a token that is not quantized (a value row at or past nv inside a
-   block that holds value rows) is 0; blocks past both prefixes are left as
-   they are. */
+   out [B*H][max_groups][oracle_block_bytes_g(bits, Gv)].  Keys of the first
+   nk tokens (nk a multiple of Gk) and values of the first nv tokens, from
+   the logical arrays of oracle_build_cache (Gk = Gv = G, G in {32, 64, 128})
+   or oracle_build_cache_segments (Gk = 32, Gv = D): kcodes [B*H][nk][D],
+   kzero16 / kscale16 [B*H][nk/Gk][D], vcodes [B*H][nv][D], vzero16 /
+   vscale16 [B*H][nv][D/Gv].
+   Gv = 32: a block holds K codes, V codes, then fp16 K scale[D], K zero[D]
+   of the key group it lies in, V scale[4][32], V zero[4][32] (slot cg of
+   token t: the value group of channels 32cg .. 32cg+31).
+   Gv > 32 (split layout, two fp16 per group as the notebook's storage cell
+   counts them): a block holds K codes, V codes, then fp16 V scale[D/Gv][32],
+   V zero[D/Gv][32] (slot gv of token t: value group gv); key unit u (the
+   key group of tokens [u Gk, u Gk + Gk)) of stream s is kside [B*H]
+   [max_kunits][2][D]: K scale[D], then K zero[D].
+   Every code or side entry of a token that is not quantized (a value row
+   at or past nv inside a block that holds value rows) is 0; blocks and key
+   units past the prefixes are left as they are.  kside may be NULL when
+   Gv = 32. */
 void oracle_pack_blocks_kv2(int B, int H, int Gk, int Gv, int64_t nk, int64_t nv, int bits,
-                            int64_t max_groups,
+                            int64_t max_groups, int64_t max_kunits,
                             const uint8_t *kcodes, const uint16_t *kzero16,
                             const uint16_t *kscale16,
                             const uint8_t *vcodes, const uint16_t *vzero16,
-                            const uint16_t *vscale16, uint8_t *out);
+                            const uint16_t *vscale16, uint8_t *out, uint16_t *kside);
 
 void oracle_pack_blocks_kv(int B, int H, int G, int64_t nk, int64_t nv, int bits,
-                           int64_t max_groups,
+                           int64_t max_groups, int64_t max_kunits,
                            const uint8_t *kcodes, const uint16_t *kzero16,
                            const uint16_t *kscale16,
                            const uint8_t *vcodes, const uint16_t *vzero16,
-                           const uint16_t *vscale16, uint8_t *out)
+                           const uint16_t *vscale16, uint8_t *out, uint16_t *kside)
 {
-    oracle_pack_blocks_kv2(B, H, G, G, nk, nv, bits, max_groups, kcodes, kzero16, kscale16,
-                           vcodes, vzero16, vscale16, out);
+    oracle_pack_blocks_kv2(B, H, G, G, nk, nv, bits, max_groups, max_kunits, kcodes, kzero16,
+                           kscale16, vcodes, vzero16, vscale16, out, kside);
 }
 
-/* As oracle_pack_blocks_kv, with key parameters per Gk tokens and value
-   parameters per Gv channels (the arrays of oracle_build_cache_segments:
-   Gk = 32, Gv = D). */
 void oracle_pack_blocks_kv2(int B, int H, int Gk, int Gv, int64_t nk, int64_t nv, int bits,
-                            int64_t max_groups,
+                            int64_t max_groups, int64_t max_kunits,
                             const uint8_t *kcodes, const uint16_t *kzero16,
                             const uint16_t *kscale16,
                             const uint8_t *vcodes, const uint16_t *vzero16,
-                            const uint16_t *vscale16, uint8_t *out)
+                            const uint16_t *vscale16, uint8_t *out, uint16_t *kside)
 {
     const int D = 128, T = 32;      /* channels; tokens per block */
+    const int split = Gv > T;
+    const int nvg = D / Gv;         /* value groups per token */
     const int64_t cbytes = bits * T * D / 8;
-    const int64_t bb = oracle_block_bytes(bits);
+    const int64_t bb = oracle_block_bytes_g(bits, Gv);
     /* position tables for one tile, computed by the search above */
     int64_t *kd = (int64_t *)malloc(sizeof(int64_t) * T * D);
     int64_t *vd = (int64_t *)malloc(sizeof(int64_t) * T * D);
@@ -628,15 +647,14 @@ void oracle_pack_blocks_kv2(int B, int H, int Gk, int Gv, int64_t nk, int64_t nv
     int64_t ngk = nk / T;             /* blocks with key codes */
     int64_t ngv = (nv + T - 1) / T;   /* blocks with value rows */
     int64_t ng = ngk > ngv ? ngk : ngv;
-    for (int64_t s = 0; s < (int64_t)B * H; s++)
+    for (int64_t s = 0; s < (int64_t)B * H; s++) {
         for (int64_t j = 0; j < ng; j++) {
             uint8_t *blk = out + (s * max_groups + j) * bb;
             uint32_t *kc = (uint32_t *)blk;
             uint32_t *vc = (uint32_t *)(blk + cbytes);
-            uint16_t *ks = (uint16_t *)(blk + 2 * cbytes);
-            uint16_t *kz = ks + D;
-            uint16_t *vs = kz + D;
-            uint16_t *vz = vs + D;
+            uint16_t *side = (uint16_t *)(blk + 2 * cbytes);
+            uint16_t *vs = split ? side : side + 2 * D;
+            uint16_t *vz = vs + (split ? nvg : D / T) * T;
             if (j < ngk) {
                 /* key group of this block: tokens [jT, jT + T) lie in group jT / Gk */
                 int64_t kg = (s * (nk / Gk) + (j * T) / Gk) * D;
@@ -646,10 +664,11 @@ void oracle_pack_blocks_kv2(int B, int H, int Gk, int Gv, int64_t nk, int64_t nv
                         uint32_t ck = kcodes[(s * nk + j * T + t) * D + c];
                         kc[kd[t * D + c]] |= ck << kb[t * D + c];
                     }
-                for (int c = 0; c < D; c++) {
-                    ks[c] = kscale16[kg + c];
-                    kz[c] = kzero16[kg + c];
-                }
+                if (!split)
+                    for (int c = 0; c < D; c++) {
+                        side[c] = kscale16[kg + c];
+                        side[D + c] = kzero16[kg + c];
+                    }
             }
             if (j < ngv) {
                 memset(vc, 0, (size_t)cbytes);
@@ -659,15 +678,35 @@ void oracle_pack_blocks_kv2(int B, int H, int Gk, int Gv, int64_t nk, int64_t nv
                         uint32_t cv = tok < nv ? vcodes[(s * nv + tok) * D + c] : 0;
                         vc[vd[t * D + c]] |= cv << vb[t * D + c];
                     }
-                    /* slot cg: channels 32cg .. 32cg+31, in value group 32cg / Gv */
-                    for (int cg = 0; cg < D / T; cg++) {
-                        int64_t vg = (s * nv + tok) * (D / Gv) + (cg * T) / Gv;
-                        vs[cg * T + t] = tok < nv ? vscale16[vg] : 0;
-                        vz[cg * T + t] = tok < nv ? vzero16[vg] : 0;
+                    if (split) {
+                        /* slot gv: value group gv */
+                        for (int gv = 0; gv < nvg; gv++) {
+                            int64_t vg = (s * nv + tok) * nvg + gv;
+                            vs[gv * T + t] = tok < nv ? vscale16[vg] : 0;
+                            vz[gv * T + t] = tok < nv ? vzero16[vg] : 0;
+                        }
+                    } else {
+                        /* slot cg: channels 32cg .. 32cg+31, in value group 32cg / Gv */
+                        for (int cg = 0; cg < D / T; cg++) {
+                            int64_t vg = (s * nv + tok) * (D / Gv) + (cg * T) / Gv;
+                            vs[cg * T + t] = tok < nv ? vscale16[vg] : 0;
+                            vz[cg * T + t] = tok < nv ? vzero16[vg] : 0;
+                        }
                     }
                 }
             }
         }
+        /* split layout: one key unit per key group */
+        if (split && kside)
+            for (int64_t u = 0; u < nk / Gk; u++) {
+                uint16_t *ku = kside + (s * max_kunits + u) * 2 * D;
+                int64_t kg = (s * (nk / Gk) + u) * D;
+                for (int c = 0; c < D; c++) {
+                    ku[c] = kscale16[kg + c];
+                    ku[D + c] = kzero16[kg + c];
+                }
+            }
+    }
     free(kd);
     free(vd);
     free(kb);
@@ -681,8 +720,8 @@ void oracle_pack_blocks(int B, int H, int64_t nq, int bits, int64_t max_groups,
                         const uint8_t *vcodes, const uint16_t *vzero16,
                         const uint16_t *vscale16, uint8_t *out)
 {
-    oracle_pack_blocks_kv(B, H, 32, nq, nq, bits, max_groups, kcodes, kzero16, kscale16,
-                          vcodes, vzero16, vscale16, out);
+    oracle_pack_blocks_kv(B, H, 32, nq, nq, bits, max_groups, 0, kcodes, kzero16, kscale16,
+                          vcodes, vzero16, vscale16, out, NULL);
 }
 
 /* Outlier records of the packed cache, one per 32-token key group (G = 32):

@@ -40,8 +40,8 @@ def gpu_blocks(cache, n_groups, streams=None):
 
 
 def check_cache(orc, cache, k, v, streams=None, label="", segments=None):
-    """Bit-exact check of packed blocks, ring contents and (n, Q_K, Q_V)
-    against the oracle built from the full K, V ([B, H, n, D] numpy, or only
+    """Bit-exact check of packed blocks (and, in the split layout, the key
+    units below Q_K), ring contents and (n, Q_K, Q_V) against the oracle built from the full K, V ([B, H, n, D] numpy, or only
     the streams listed in `streams`, given as [len(streams), n, D] arrays in
     k, v) under the cache's flush policy.  Key parts (codes, scale, zero) are
     compared for the groups below Q_K, value parts for the groups that hold
@@ -62,13 +62,15 @@ def check_cache(orc, cache, k, v, streams=None, label="", segments=None):
                                                          lo.n_vquantized, qk, qv)
     ngk, ngv = qk // 32, -(-qv // 32)           # 32-token blocks
     ng = max(ngk, ngv)
+    split = lo.kside_unit_tokens > 0
     if ng:
-        want = orc.pack_blocks(ref, ng)
+        want, want_ks = orc.pack_cache(ref, ng)
         got = gpu_blocks(cache, ng, streams)
         cb = lo.code_bytes
         kpart = np.zeros(lo.block_bytes, bool)
         kpart[:cb] = True
-        kpart[2 * cb:2 * cb + 4 * c.head_dim] = True        # K scale, K zero
+        if not split:
+            kpart[2 * cb:2 * cb + 4 * c.head_dim] = True    # K scale, K zero
         mask = np.zeros(want.shape, bool)
         mask[:, :ngk, :] |= kpart
         mask[:, :ngv, :] |= ~kpart
@@ -76,6 +78,18 @@ def check_cache(orc, cache, k, v, streams=None, label="", segments=None):
         if len(bad):
             raise AssertionError("%s: %d packed bytes differ, first (stream, group, byte) %s" %
                                  (label, len(bad), bad[:5].tolist()))
+        nku = qk // lo.kside_unit_tokens if split else 0
+        assert (want_ks is not None) == split, label
+        if nku:
+            import torch
+            torch.cuda.synchronize()
+            ks = cache.kside_view()
+            ks = (ks if streams is None else ks[list(streams)])[:, :nku].cpu().numpy()
+            bad = np.argwhere(want_ks[:, :nku] != ks.view(np.uint16))
+            if len(bad):
+                raise AssertionError("%s: %d key-unit entries differ, first (stream, unit, "
+                                     "scale/zero, channel) %s" % (label, len(bad),
+                                                                   bad[:5].tolist()))
     if c.key_outliers > 0 and ngk:
         want = orc.pack_outlier_records(ref, ngk)
         import torch

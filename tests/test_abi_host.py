@@ -152,6 +152,7 @@ def test_sizes_and_layout(L, orc, B, H, Hq, bits, R, T, dt, esize):
         assert (lo.off_kcode, lo.off_vcode, lo.off_kscale, lo.off_kzero, lo.off_vscale,
                 lo.off_vzero) == (0, cb, 2 * cb, 2 * cb + 2 * D, 2 * cb + 4 * D, 2 * cb + 6 * D)
         assert lo.max_groups == T // G and lo.ring_capacity == R + G
+        assert (lo.kside, lo.kside_unit_tokens, lo.max_kside_units) == (0, 0, 0)
         assert (lo.n_tokens, lo.n_quantized) == (0, 0)
         assert kivi.kivi_decode_plan(h) == (0, 1)
         ws = kivi.kivi_decode_workspace_bytes(h)
@@ -160,17 +161,33 @@ def test_sizes_and_layout(L, orc, B, H, Hq, bits, R, T, dt, esize):
         kivi.kivi_cache_destroy(h)
 
 
-@pytest.mark.parametrize("G", [64, 128])
-def test_group_sizes_layout(L, orc, G):
-    """G = 64 and 128 keep 32-token blocks (the same block bytes as G = 32:
-    each block carries its key group's zero / scale) and a ring of R + G
-    tokens; the window policy's prefix moves in multiples of G."""
+@pytest.mark.parametrize("G,bits", [(64, 2), (128, 2), (64, 4), (128, 8)])
+def test_group_sizes_layout(L, orc, G, bits):
+    """G = 64 and 128 (the split layout) keep 32-token blocks of codes and
+    D / G value pairs per token (the oracle's block size), the key zero /
+    scale once per key group in the key-unit region after the blocks, and a
+    ring of R + G tokens; the window policy's prefix moves in multiples of
+    G."""
     D, R, T = 128, 128, 1024
-    cfg = kivi.make_config(2, 8, 32, bits=2, group=G, residual=R, max_tokens=T)
-    h = kivi.kivi_cache_create(cfg, FAKE_DEV, kivi.kivi_cache_bytes(cfg))
+    cfg = kivi.make_config(2, 8, 32, bits=bits, group=G, residual=R, max_tokens=T)
+    nbytes = kivi.kivi_cache_bytes(cfg)
+    h = kivi.kivi_cache_create(cfg, FAKE_DEV, nbytes)
     try:
         lo = kivi.kivi_get_layout(h)
-        assert lo.block_bytes == orc.block_bytes(2) and lo.code_bytes == 2 * 32 * D // 8
+        cb = bits * 32 * D // 8
+        nvg = D // G
+        assert lo.block_bytes == orc.block_bytes(bits, G) == 2 * cb + 2 * 2 * 32 * nvg
+        assert lo.code_bytes == cb
+        assert (lo.off_kcode, lo.off_vcode, lo.off_vscale, lo.off_vzero) == \
+            (0, cb, 2 * cb, 2 * cb + 2 * 32 * nvg)
+        assert (lo.off_kscale, lo.off_kzero) == (0, 2 * D)         # inside a key unit
+        S = 2 * 8
+        blocks = align(S * (T // 32) * lo.block_bytes)
+        assert (lo.kside, lo.kside_unit_tokens, lo.max_kside_units) == (blocks, G, T // G)
+        kside = align(S * (T // G) * 4 * D)
+        ring = align(S * (R + G) * D * 2)
+        assert (lo.ring_k, lo.ring_v, nbytes) == (blocks + kside, blocks + kside + ring,
+                                                 blocks + kside + 2 * ring)
         assert lo.max_groups == T // 32 and lo.ring_capacity == R + G
         for n in range(0, T + 1, 7):
             p = kivi.kivi_plan_append(h, n)
@@ -269,6 +286,9 @@ def test_plan_append_matches_segment_policy(L, orc, R):
             assert p.ring_token_end - p.ring_token_begin < R
         lo = kivi.kivi_get_layout(h)
         assert lo.ring_capacity == R + 128
+        # the split layout with one key unit per 32-token block
+        assert lo.block_bytes == orc.block_bytes(2, 128)
+        assert (lo.kside_unit_tokens, lo.max_kside_units) == (32, T // 32)
         streams, groups = 4, T // 32
         chunks = -(-groups // 16)
         scratch = -(-streams * chunks * 1024 // 256) * 256 + -(-streams * 1024 // 256) * 256

@@ -63,6 +63,8 @@ class StreamSnapshot:
         self._lo = cache.layout()
         self._blocks = cache.blocks_view()[s:s + 1].cpu()
         self._rec = cache.outlier_records_view()[s:s + 1].cpu() if cache.cfg.key_outliers else None
+        ks = cache.kside_view()
+        self._ks = ks[s:s + 1].cpu() if ks is not None else None
         rk, rv = cache.ring_views()
         self._ring = (rk[b:b + 1, h:h + 1].cpu(), rv[b:b + 1, h:h + 1].cpu())
 
@@ -74,6 +76,9 @@ class StreamSnapshot:
 
     def outlier_records_view(self):
         return self._rec
+
+    def kside_view(self):
+        return self._ks
 
     def ring_views(self):
         return self._ring

@@ -18,7 +18,7 @@ group, and decode the packed blocks by the layout include/kivi.h documents.
 import numpy as np
 import pytest
 
-from test_oracle_layout_pins import decode_block, documented_code_slots
+from test_oracle_layout_pins import decode_block_split, decode_kunit, documented_code_slots
 
 D, T = 128, 32
 
@@ -123,30 +123,32 @@ def test_segment_locality(orc):
 
 
 def test_packed_blocks_carry_their_segment(orc):
-    """Packed by the layout include/kivi.h documents: each 32-token block
-    holds its tokens' key codes and the fp16 pair of the segment it lies in,
-    and all four value slots of a token hold its one (all-channel) pair."""
+    """Packed by the layout include/kivi.h documents (the split layout: value
+    groups span all 128 channels): each 32-token block holds its tokens' key
+    codes and their one value pair each, and the block's key unit (one per
+    32 tokens) holds the fp16 pair of the segment the block lies in."""
     B, H, n = 1, 2, 300
     k, v = _kv(31, B, H, n)
     segs = [128, 192, 256]
     c = orc.build_cache(k, v, 2, D, 64, orc.POLICY_SEGMENT, segments=segs)
-    blocks = orc.pack_blocks(c)
+    blocks, kside = orc.pack_cache(c)
+    assert kside.shape == (B * H, 256 // T, 2, D)
     slots = documented_code_slots(2)
     for s in range(B * H):
         b, h = divmod(s, H)
         for j in range(256 // T):
-            kc, vc, ks, kz, vs, vz = decode_block(blocks[s, j], 2, slots)
+            kc, vc, vs, vz = decode_block_split(blocks[s, j], 2, slots, 1)
             toks = slice(T * j, T * j + T)
             assert np.array_equal(kc, c["kcodes"][b, h, toks])
             assert np.array_equal(vc, c["vcodes"][b, h, toks])
             seg0 = [0] + segs
             i = next(i for i in range(len(segs)) if T * j < segs[i])
             first = seg0[i] // T             # the segment's first block shares the pair
+            ks, kz = decode_kunit(kside[s, j])
             assert np.array_equal(ks, c["kscale16"][b, h, first])
             assert np.array_equal(kz, c["kzero16"][b, h, first])
-            for cg in range(4):
-                assert np.array_equal(vs[cg], c["vscale16"][b, h, toks, 0])
-                assert np.array_equal(vz[cg], c["vzero16"][b, h, toks, 0])
+            assert np.array_equal(vs[0], c["vscale16"][b, h, toks, 0])
+            assert np.array_equal(vz[0], c["vzero16"][b, h, toks, 0])
 
 
 def test_kcvt_attention_close_to_full_precision(orc):

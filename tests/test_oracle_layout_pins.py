@@ -1,5 +1,6 @@
-"""Pins of the oracle's packers (oracle_pack_blocks_kv, oracle_pack_outlier_records)
-against the byte layout that include/kivi.h documents.
+"""Pins of the oracle's packers (oracle_pack_blocks_kv in both layouts with
+the split layout's key units, oracle_pack_outlier_records) against the byte
+layout that include/kivi.h documents.
 
 The decoders below are written from that documented layout alone, in the
 forward direction (from a dword, a bit and a lane to the logical token and
@@ -70,6 +71,27 @@ def decode_block(blk, bits, slots):
         side[3 * D:].reshape(4, T)
 
 
+def decode_block_split(blk, bits, slots, nvg):
+    """(kcodes, vcodes, vscale[nvg][32], vzero[nvg][32]) of one block of the
+    split layout (value groups of 128 / nvg channels > 32), by the
+    documented offsets: K codes, V codes, then fp16 V scale[nvg][32], V
+    zero[nvg][32] (slot gv of token t: value group gv)."""
+    cb = bits * T * D // 8
+    kc = decode_code_area(blk[:cb], bits, False, slots)
+    vc = decode_code_area(blk[cb:2 * cb], bits, True, slots)
+    side = np.frombuffer(blk[2 * cb:].tobytes(), dtype="<u2")
+    assert side.size == 2 * nvg * T
+    return kc, vc, side[:nvg * T].reshape(nvg, T), side[nvg * T:].reshape(nvg, T)
+
+
+def decode_kunit(unit):
+    """(kscale[128], kzero[128]) of one key unit of the split layout: fp16
+    K scale[D], then K zero[D] (unit given as 512 bytes or [2][D] uint16)."""
+    u = np.frombuffer(np.ascontiguousarray(unit).tobytes(), dtype="<u2")
+    assert u.size == 2 * D
+    return u[:D], u[D:]
+
+
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_documented_layout_covers_every_code_once(bits):
     """The documented formula alone: every (token, channel) of a tile gets
@@ -88,9 +110,12 @@ def test_documented_layout_covers_every_code_once(bits):
                                     (8, 128)])
 def test_pack_blocks_decode_to_logical_cache(orc, bits, G):
     """Window policy: every block decodes (documented formula and offsets) to
-    the logical codes of its 32 tokens, the fp16 zero / scale of the key
-    group it lies in, and per value slot cg the zero / scale of the value
-    group holding channels 32cg .. 32cg + 31."""
+    the logical codes of its 32 tokens.  G = 32: the block carries the fp16
+    zero / scale of its key group and, per value slot cg, the zero / scale
+    of the value group holding channels 32cg .. 32cg + 31.  G = 64, 128 (the
+    split layout): the block carries its tokens' 128 / G value pairs, slot gv
+    of token t the pair of value group gv, and key unit u the zero / scale
+    of key group u, once."""
     rng = np.random.default_rng(100 + bits + G)
     B, H, n, R = 1, 2, 5 * 64 + 17, G
     k = rng.standard_normal((B, H, n, D)).astype(np.float16)
@@ -99,21 +124,56 @@ def test_pack_blocks_decode_to_logical_cache(orc, bits, G):
     c = orc.build_cache(k, v, bits, G, R)
     q = c["qk"]
     assert q == c["qv"] and q % G == 0 and q > 0
-    blocks = orc.pack_blocks(c)
-    assert blocks.shape == (B * H, q // T, 2 * bits * T * D // 8 + 4 * D * 2)
+    blocks, kside = orc.pack_cache(c)
+    nvg = D // G
+    side_bytes = 4 * D * 2 if G == 32 else 2 * 2 * T * nvg
+    assert blocks.shape == (B * H, q // T, 2 * bits * T * D // 8 + side_bytes)
+    assert (kside is None) == (G == 32)
+    if G > 32:
+        assert kside.shape == (B * H, q // G, 2, D)
     slots = documented_code_slots(bits)
     for s in range(B * H):
         b, h = divmod(s, H)
         for j in range(q // T):
-            kc, vc, ks, kz, vs, vz = decode_block(blocks[s, j], bits, slots)
             toks = slice(T * j, T * j + T)
+            if G == 32:
+                kc, vc, ks, kz, vs, vz = decode_block(blocks[s, j], bits, slots)
+                assert np.array_equal(ks, c["kscale16"][b, h, j])
+                assert np.array_equal(kz, c["kzero16"][b, h, j])
+                for cg in range(4):
+                    assert np.array_equal(vs[cg], c["vscale16"][b, h, toks, cg])
+                    assert np.array_equal(vz[cg], c["vzero16"][b, h, toks, cg])
+            else:
+                kc, vc, vs, vz = decode_block_split(blocks[s, j], bits, slots, nvg)
+                for gv in range(nvg):
+                    assert np.array_equal(vs[gv], c["vscale16"][b, h, toks, gv])
+                    assert np.array_equal(vz[gv], c["vzero16"][b, h, toks, gv])
             assert np.array_equal(kc, c["kcodes"][b, h, toks])
             assert np.array_equal(vc, c["vcodes"][b, h, toks])
-            assert np.array_equal(ks, c["kscale16"][b, h, T * j // G])
-            assert np.array_equal(kz, c["kzero16"][b, h, T * j // G])
-            for cg in range(4):
-                assert np.array_equal(vs[cg], c["vscale16"][b, h, toks, T * cg // G])
-                assert np.array_equal(vz[cg], c["vzero16"][b, h, toks, T * cg // G])
+        if G > 32:
+            for u in range(q // G):
+                ks, kz = decode_kunit(kside[s, u])
+                assert np.array_equal(ks, c["kscale16"][b, h, u])
+                assert np.array_equal(kz, c["kzero16"][b, h, u])
+
+
+@pytest.mark.parametrize("bits,G", [(2, 32), (2, 64), (4, 128), (8, 64)])
+def test_packed_bytes_are_the_storage_cost(orc, bits, G):
+    """The notebook's storage cell counts b bits per code and two fp16 per
+    group.  In the split layout (G > 32) the packed bytes of Q tokens are
+    exactly that, keys and values: Q*D*b/8 * 2 + 2*2*(Q/G*D + Q*D/G).  At
+    G = 32 too (key groups per 32 tokens, value groups per 32 channels)."""
+    rng = np.random.default_rng(5 + G + bits)
+    n = 4 * 128 + 40
+    k = rng.standard_normal((1, 1, n, D)).astype(np.float16)
+    v = rng.standard_normal((1, 1, n, D)).astype(np.float16)
+    c = orc.build_cache(k, v, bits, G, 0)
+    Q = c["qk"]
+    blocks, kside = orc.pack_cache(c)
+    total = blocks.nbytes + (kside.nbytes if kside is not None else 0)
+    codes = Q * D * bits // 8 * 2
+    groups = Q // G * D + Q * D // G         # key groups + value groups
+    assert total == codes + 2 * 2 * groups
 
 
 def _pack_prefilled(orc, c, fill):
@@ -121,12 +181,16 @@ def _pack_prefilled(orc, c, fill):
     bytes the packer must leave alone can be seen."""
     B, H, qk, qv, bits = c["B"], c["H"], c["qk"], c["qv"], c["bits"]
     ng = max(qk // T, -(-qv // T))
-    out = np.full((B * H, ng, orc.block_bytes(bits)), fill, np.uint8)
-    orc.lib().oracle_pack_blocks_kv(B, H, c["G"], qk, qv, bits, ng,
+    G = c["G"]
+    out = np.full((B * H, ng, orc.block_bytes(bits, G)), fill, np.uint8)
+    nku = qk // G + 1
+    kside = np.full((B * H, nku, 2, D), fill * 0x101, np.uint16) if G > 32 else None
+    orc.lib().oracle_pack_blocks_kv(B, H, G, qk, qv, bits, ng, nku if G > 32 else 0,
                                     orc._p(c["kcodes"]), orc._p(c["kzero16"]),
                                     orc._p(c["kscale16"]), orc._p(c["vcodes"]),
-                                    orc._p(c["vzero16"]), orc._p(c["vscale16"]), orc._p(out))
-    return out
+                                    orc._p(c["vzero16"]), orc._p(c["vscale16"]), orc._p(out),
+                                    orc._p(kside) if kside is not None else None)
+    return (out, kside) if G > 32 else out
 
 
 @pytest.mark.parametrize("bits", [2, 4])
@@ -170,6 +234,44 @@ def test_pack_blocks_paper_policy_partial_value_block(orc, bits):
     # a fully quantized cache are not all-zero
     full = orc.build_cache(k, v, bits, G, 0, policy=orc.POLICY_WINDOW)
     assert (full["vcodes"][:, :, 86:96] != 0).any()
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_pack_blocks_paper_policy_split_layout(orc, bits):
+    """The paper policy at G = 64 (split layout): keys quantized up to Q_K =
+    n - n mod R, values up to Q_V = n - R (R4: rows at or past Q_V inside
+    the block holding it pack as code 0 with zero / scale 0; blocks past
+    the value prefix keep their value area, key units past Q_K / G stay
+    untouched)."""
+    rng = np.random.default_rng(70 + bits)
+    B, H, R, G = 1, 2, 64, 64
+    n = 230                                  # Q_K = 192, Q_V = 166: block 5 holds rows 160..191
+    k = rng.standard_normal((B, H, n, D)).astype(np.float16)
+    v = rng.standard_normal((B, H, n, D)).astype(np.float16)
+    c = orc.build_cache(k, v, bits, G, R, policy=orc.POLICY_PAPER)
+    assert (c["qk"], c["qv"]) == (192, 166)
+    out, kside = _pack_prefilled(orc, c, 0xAB)
+    assert out.shape[1] == 6 and kside.shape[1] == 4
+    slots = documented_code_slots(bits)
+    nvg = D // G
+    for s in range(B * H):
+        b, h = divmod(s, H)
+        for j in range(6):
+            kc, vc, vs, vz = decode_block_split(out[s, j], bits, slots, nvg)
+            toks = slice(T * j, T * j + T)
+            assert np.array_equal(kc, c["kcodes"][b, h, toks])
+            lim = min(T, c["qv"] - T * j)       # 32 ... 32, then 6
+            assert np.array_equal(vc[:lim], c["vcodes"][b, h, T * j:T * j + lim])
+            assert (vc[lim:] == 0).all()
+            for gv in range(nvg):
+                assert np.array_equal(vs[gv, :lim], c["vscale16"][b, h, T * j:T * j + lim, gv])
+                assert np.array_equal(vz[gv, :lim], c["vzero16"][b, h, T * j:T * j + lim, gv])
+                assert (vs[gv, lim:] == 0).all() and (vz[gv, lim:] == 0).all()
+        for u in range(3):
+            ks, kz = decode_kunit(kside[s, u])
+            assert np.array_equal(ks, c["kscale16"][b, h, u])
+            assert np.array_equal(kz, c["kzero16"][b, h, u])
+        assert (kside[s, 3] == 0xABAB).all()
 
 
 @pytest.mark.parametrize("n_out", [1, 2, 3])

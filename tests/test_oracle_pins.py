@@ -406,37 +406,39 @@ def test_pack_layout_is_bijective(orc, bits):
 
 @pytest.mark.parametrize("G", [64, 128])
 def test_pack_blocks_group_sizes(orc, G):
-    """Blocks stay 32 tokens for G = 64 and 128: every block unpacks (through
-    the pinned code positions) to its tokens' logical codes, carries the
-    zero / scale of the key group it lies in, and value slot cg of a token
-    carries the zero / scale of the value group holding channels 32cg .. 32cg
-    + 31."""
+    """Blocks stay 32 tokens for G = 64 and 128 (the split layout): every
+    block unpacks (through the pinned code positions) to its tokens' logical
+    codes and carries its tokens' 128 / G value zero / scale pairs; the key
+    zero / scale of each key group is stored once, in its key unit."""
     rng = np.random.default_rng(11)
     n, D, bits = 256, 128, 2
     k = rng.standard_normal((1, 1, n, D)).astype(np.float16)
     v = rng.standard_normal((1, 1, n, D)).astype(np.float16)
     c = orc.build_cache(k, v, bits, G, 0)
-    blk = orc.pack_blocks(c)[0]
+    blocks, kside = orc.pack_cache(c)
+    blk, ku = blocks[0], kside[0]
     cb = bits * 32 * D // 8
+    nvg = D // G
     pos = {(isv, t, ch): orc.code_position(bits, isv, t, ch)
            for isv in (0, 1) for t in range(32) for ch in range(D)}
     for j in range(n // 32):
         words = blk[j, :2 * cb].view(np.uint32)
         side = blk[j, 2 * cb:].view(np.uint16)
+        assert side.size == 2 * 32 * nvg
         for t in range(0, 32, 7):
             for ch in range(0, D, 5):
                 for isv, codes in ((0, c["kcodes"]), (1, c["vcodes"])):
                     d, b = pos[(isv, t, ch)]
                     got = (int(words[isv * cb // 4 + d]) >> b) & ((1 << bits) - 1)
                     assert got == codes[0, 0, 32 * j + t, ch]
-        assert np.array_equal(side[:D], c["kscale16"][0, 0, 32 * j // G])
-        assert np.array_equal(side[D:2 * D], c["kzero16"][0, 0, 32 * j // G])
-        for cg in range(4):
+        for gv in range(nvg):
             toks = slice(32 * j, 32 * j + 32)
-            assert np.array_equal(side[2 * D + 32 * cg:2 * D + 32 * cg + 32],
-                                  c["vscale16"][0, 0, toks, 32 * cg // G])
-            assert np.array_equal(side[3 * D + 32 * cg:3 * D + 32 * cg + 32],
-                                  c["vzero16"][0, 0, toks, 32 * cg // G])
+            assert np.array_equal(side[32 * gv:32 * gv + 32], c["vscale16"][0, 0, toks, gv])
+            assert np.array_equal(side[32 * nvg + 32 * gv:32 * nvg + 32 * gv + 32],
+                                  c["vzero16"][0, 0, toks, gv])
+    for u in range(n // G):
+        assert np.array_equal(ku[u, 0], c["kscale16"][0, 0, u])
+        assert np.array_equal(ku[u, 1], c["kzero16"][0, 0, u])
 
 
 # ---------------------------------------------------------------------------
