@@ -28,11 +28,12 @@ def _gpu():
 
 
 def _run(orc, B, H, Hq, n, T, bits, R, causal, seed, chunks=None, q_dtype=np.float16,
-         label="", G=32, dtype=np.float16):
+         label="", G=32, dtype=np.float16, policy=0):
     from kv_cache_quantization_amd import synth, kivi
     k, v = synth.kv_host(seed, B, H, n, dtype=dtype)
     q = synth.queries_multi_host(seed, B, Hq, T, dtype=q_dtype)
-    cache = new_cache(B, H, Hq, max_tokens=n + 64, bits=bits, R=R, group=G, dtype=dtype)
+    cache = new_cache(B, H, Hq, max_tokens=n + 64, bits=bits, R=R, group=G, dtype=dtype,
+                      policy=policy)
     pos = 0
     for c in (chunks or [n]):
         cache.append(to_dev(k[:, :, pos:pos + c]), to_dev(v[:, :, pos:pos + c]))
@@ -41,7 +42,7 @@ def _run(orc, B, H, Hq, n, T, bits, R, causal, seed, chunks=None, q_dtype=np.flo
     log("case %s: B=%d H=%d Hq=%d n=%d T=%d bits=%d R=%d causal=%d plan(qblocks, splits, "
         "gps)=%s" % (label, B, H, Hq, n, T, bits, R, causal, plan))
     out = cache.attn(to_dev(q), causal=causal).cpu().numpy()
-    ref_cache = orc.build_cache(k, v, bits, G, R)
+    ref_cache = orc.build_cache(k, v, bits, G, R, policy)
     kh, vh = orc.dequant_cache(k, v, ref_cache)
     ref = orc.attn_queries(q, kh, vh, causal)
     e = rel_err(out, ref)
@@ -143,5 +144,17 @@ def test_attn_errors():
 
 @pytest.mark.parametrize("G,bits,causal", [(64, 2, 1), (128, 4, 0)])
 def test_group_sizes(orc, G, bits, causal):
-    """G = 64 and 128: the 32-token blocks carry their group's zero / scale."""
+    """G = 64 and 128 (the split layout): the stages take each block's codes,
+    its key unit (one per key group) and its value pairs."""
     _run(orc, 2, 2, 8, 1111, 100, bits, 128, causal, seed=G + bits, label="attn-G%d" % G, G=G)
+
+
+@pytest.mark.parametrize("G,causal", [(64, 1), (128, 0)])
+def test_group_sizes_paper_policy(orc, G, causal):
+    """The paper policy in the split layout: the last split's pass over the
+    groups whose value codes stop at Q_V copies codes, key unit and value
+    pairs into its stage (one-shot, and streamed across key flushes)."""
+    _run(orc, 2, 2, 8, 1000, 300, 2, 128, causal, seed=G + 5, label="attn-paper-G%d" % G,
+         G=G, policy=1)
+    _run(orc, 1, 2, 8, 700, 40, 4, 128, causal, seed=G + 6, chunks=[500] + [1] * 200,
+         label="attn-paper-stream-G%d" % G, G=G, policy=1)

@@ -9,7 +9,8 @@ runs on a thread pool (its C calls release the interpreter lock).
 
   * long context: batch 16 x 8 KV heads x 32 query heads, context 32768,
     residual 128, one-shot prefill, one decode step -- at 2, 4 and 8 bits,
-    and at 2 bits with two fp16 key channels per key group;
+    at 2 bits with two fp16 key channels per key group, and in the split
+    layout at G = 64 (2-bit) and G = 128 (4-bit);
   * streaming: batch 8, prefill 8192, then 512 single-token appends each
     followed by a decode step, under the window policy and under the review's
     Algorithm-1 policy (key flushes every 128 steps); the final cache equals
@@ -84,7 +85,8 @@ class StreamSnapshot:
         return self._ring
 
 
-def _check_streams(orc, cache, ks, vs, q, out, sample, bits, R, label, policy=0, n_out=0):
+def _check_streams(orc, cache, ks, vs, q, out, sample, bits, R, label, policy=0, n_out=0,
+                   group=G):
     """ks, vs: {(b, h): [n, D] host arrays}; q, out: host [B, Hq, D]."""
     snaps = {s: StreamSnapshot(cache, *s) for s in sample}
 
@@ -93,7 +95,7 @@ def _check_streams(orc, cache, ks, vs, q, out, sample, bits, R, label, policy=0,
         k, v = ks[s][None], vs[s][None]
         check_cache(orc, snaps[s], k, v, streams=[0], label="%s (%d, %d)" % (label, b, h))
         qs = q[b, GQ * h:GQ * (h + 1)][None]
-        ref = oracle_decode(orc, k[None], v[None], qs, bits, G, R, policy=policy,
+        ref = oracle_decode(orc, k[None], v[None], qs, bits, group, R, policy=policy,
                             key_outliers=n_out)
         return rel_err(out[b, GQ * h:GQ * (h + 1)], ref[0])
 
@@ -105,16 +107,20 @@ def _check_streams(orc, cache, ks, vs, q, out, sample, bits, R, label, policy=0,
         assert e <= TOL, (label, s, e)
 
 
-@pytest.mark.parametrize("bits,n_out", [(2, 0), (4, 0), (8, 0), (2, 2)])
-def test_long_context_b16(bits, n_out):
+@pytest.mark.parametrize("bits,n_out,group", [(2, 0, 32), (4, 0, 32), (8, 0, 32), (2, 2, 32),
+                                              (2, 0, 64), (4, 0, 128)])
+def test_long_context_b16(bits, n_out, group):
+    """G = 64 and 128 run the split layout (key units once per group): the
+    key units of the sampled streams are compared bit for bit too."""
     import torch
     from kv_cache_quantization_amd import KiviCache, synth
     import oracle as orc
     B, n, R = 16, 32768, 128
-    log("case long-context B=%d n=%d bits=%d key_outliers=%d" % (B, n, bits, n_out))
+    log("case long-context B=%d n=%d bits=%d key_outliers=%d G=%d" % (B, n, bits, n_out, group))
     k, v = synth.kv_device(3, B, H, n)
     q = synth.queries_device(3, B, HQ)
-    cache = KiviCache(B, H, HQ, n, bits=bits, residual=R, device="cuda:0", key_outliers=n_out)
+    cache = KiviCache(B, H, HQ, n, bits=bits, group=group, residual=R, device="cuda:0",
+                      key_outliers=n_out)
     cache.append(k, v)
     out = cache.decode(q).cpu().numpy()
     sample = spread_sample(B)
@@ -122,8 +128,9 @@ def test_long_context_b16(bits, n_out):
     vs = {s: v[s].cpu().numpy() for s in sample}
     del k, v
     _check_streams(orc, cache, ks, vs, q.cpu().numpy(), out, sample, bits, R,
-                   "long-context %d-bit%s" % (bits, "" if not n_out else ", %d kept" % n_out),
-                   n_out=n_out)
+                   "long-context %d-bit G=%d%s" % (bits, group, "" if not n_out else
+                                                    ", %d kept" % n_out),
+                   n_out=n_out, group=group)
     del cache
     torch.cuda.empty_cache()
 
