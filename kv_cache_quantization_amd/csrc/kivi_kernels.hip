@@ -2109,6 +2109,81 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(const flo
     }
 }
 
+// Rows of at most kFewItems partials: every thread issues all of its loads
+// at once (items s = part + kCombineParts * k, its channel t % D of each and
+// their (m, l)), so the row costs a single memory round trip; the weights
+// 2^(m_s - M) and both sums come from registers, and the parts meet in LDS.
+constexpr int kFewPerPart = 16;
+constexpr int kFewItems = kCombineParts * kFewPerPart;
+__global__ __launch_bounds__(kCombineThreads) void combine_rows_few_kernel(const float *part_o,
+                                                                           const float *part_ml,
+                                                                           float *out, int items) {
+    constexpr int NW = kCombineThreads / 64;
+    constexpr int P = kCombineParts;
+    __shared__ float red[NW];
+    __shared__ float acc_s[kCombineThreads];
+    __shared__ float l_s[P];
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x, wv = t >> 6;
+    const int c = t % D, part = t / D;          // a wavefront lies within one part
+    const float *ml = part_ml + row * items * 2;
+    const float *po = part_o + row * items * D + c;
+    float o[kFewPerPart], m[kFewPerPart], lw[kFewPerPart];
+#pragma unroll
+    for (int k = 0; k < kFewPerPart; k++) {
+        const int sidx = part + P * k;
+        if (sidx < items) {
+            o[k] = po[(int64_t)sidx * D];
+            const float2 x = *(const float2 *)(ml + 2 * sidx);
+            m[k] = x.x;
+            lw[k] = x.y;
+        } else {
+            o[k] = 0.f;
+            m[k] = -INFINITY;
+            lw[k] = 0.f;
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kFewPerPart; k++)
+        if (lw[k] > 0.f) M = fmaxf(M, m[k]);
+    if ((t & 63) == 0) red[wv] = M;
+    __syncthreads();
+    M = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; i++) M = fmaxf(M, red[i]);
+    float acc = 0.f, L = 0.f;
+#pragma unroll
+    for (int k = 0; k < kFewPerPart; k++) {
+        const float w = lw[k] > 0.f ? __builtin_amdgcn_exp2f(m[k] - M) : 0.f;
+        acc = __builtin_fmaf(o[k], w, acc);
+        L = __builtin_fmaf(lw[k], w, L);
+    }
+    acc_s[t] = acc;
+    if (c == 0) l_s[part] = L;
+    __syncthreads();
+    if (part == 0) {
+        float a = acc_s[c], Lt = l_s[0];
+#pragma unroll
+        for (int i = 1; i < P; i++) {
+            a += acc_s[c + i * D];
+            Lt += l_s[i];
+        }
+        out[row * D + c] = a / Lt;
+    }
+}
+
+// Merge `rows` rows of `items` partials each.
+static void launch_combine(const float *part_o, const float *part_ml, float *out, int64_t rows,
+                           int items, hipStream_t s) {
+    if (items <= kFewItems)
+        hipLaunchKernelGGL(combine_rows_few_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0, s,
+                           part_o, part_ml, out, items);
+    else
+        hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0, s,
+                           part_o, part_ml, out, items);
+}
+
 // ===========================================================================
 // Attention of T queries per (batch, query head) over the packed cache
 // ===========================================================================
@@ -2872,8 +2947,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     else launch_decode_bits<4>(a, gq, grid, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)(a.batch * a.q_heads)), dim3(kCombineThreads), 0,
-                       s, (const float *)a.part_o, (const float *)a.part_ml, a.out, a.items);
+    launch_combine((const float *)a.part_o, (const float *)a.part_ml, a.out,
+                   (int64_t)a.batch * a.q_heads, a.items, s);
     return hipGetLastError();
 }
 
@@ -2917,8 +2992,7 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0, s,
-                       (const float *)a.part_o, (const float *)a.part_ml, a.out, a.splits);
+    launch_combine((const float *)a.part_o, (const float *)a.part_ml, a.out, rows, a.splits, s);
     return hipGetLastError();
 }
 

@@ -294,6 +294,19 @@ def test_group_sizes_streaming_and_fp32(orc):
          G=128)
 
 
+@pytest.mark.parametrize("B,n,few", [(16, 2000, True), (1, 3000, False)])
+def test_combine_row_lengths(orc, B, n, few):
+    """The combine merges a row of at most 64 partials with all of its loads
+    in flight at once, and a longer row with a loop over its partials: both
+    checked on every output row (batch 16: ~15 partials per row; batch 1:
+    ~94)."""
+    cache, _ = _run(orc, B, 8, 32, n, 2, 128, np.float16, 60 + B, label="combine B=%d" % B)
+    splits, _ = cache.decode_plan()
+    log("  split items per stream: %d" % splits)
+    # the residual adds at most 5 items per stream here (fewer than 160 tokens)
+    assert (splits + 5 <= 64) if few else (splits > 64)
+
+
 def test_more_streams_than_the_wave_budget(orc):
     """4160 streams (batch 520 x 8 KV heads) exceed the decode's one-round
     budget of 4096 wavefronts: one split item per stream.  Sampled streams
