@@ -479,7 +479,7 @@ kivi_status enqueue_quantize(kivi_cache *c, const kivi_append_plan &p, const voi
 // qv_new): whole blocks, and the block holding qv_new up to that token
 // (re-quantized whole on every append that adds rows to it; its earlier rows
 // come out identical, since values are quantized per token).
-// Window policy: `copy` (optional) is written to the ring by the same launches.
+// `copy` (optional) is written to the ring by the last of these launches.
 kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *k, const void *v,
                           int64_t n_new, hipStream_t stream, const RingArgs *copy = nullptr) {
     const int64_t G = kGroup;
@@ -490,14 +490,21 @@ kivi_status enqueue_flush(kivi_cache *c, const kivi_append_plan &p, const void *
     if (c->cfg.policy != KIVI_FLUSH_PAPER)
         return enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
                                 p.flush_token_end / G, 3, kNoLimit, stream, copy);
-    if (copy) return KIVI_ERR_INVALID_ARG;
-    kivi_status st = enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
-                                      p.flush_token_end / G, 1, kNoLimit, stream);
-    if (st != KIVI_OK || p.v_flush_token_end <= p.v_flush_token_begin) return st;
+    // paper policy: the key groups, the whole value blocks, then the value
+    // block holding Q_V; the copy rides on the last of them
+    const bool vflush = p.v_flush_token_end > p.v_flush_token_begin;
     const int64_t g0 = p.v_flush_token_begin / G, gw = p.v_flush_token_end / G;
-    st = enqueue_quantize(c, p, k, v, n_new, g0, gw, 2, kNoLimit, stream);
-    if (st != KIVI_OK || p.v_flush_token_end % G == 0) return st;
-    return enqueue_quantize(c, p, k, v, n_new, gw, gw + 1, 2, p.v_flush_token_end, stream);
+    const bool vwhole = vflush && gw > g0, vpart = vflush && p.v_flush_token_end % G != 0;
+    kivi_status st = enqueue_quantize(c, p, k, v, n_new, p.flush_token_begin / G,
+                                      p.flush_token_end / G, 1, kNoLimit, stream,
+                                      vwhole || vpart ? nullptr : copy);
+    if (st != KIVI_OK) return st;
+    if (vwhole) {
+        st = enqueue_quantize(c, p, k, v, n_new, g0, gw, 2, kNoLimit, stream, vpart ? nullptr : copy);
+        if (st != KIVI_OK) return st;
+    }
+    if (vpart) st = enqueue_quantize(c, p, k, v, n_new, gw, gw + 1, 2, p.v_flush_token_end, stream, copy);
+    return st;
 }
 
 // Copy tokens [begin, end) (all >= n_old) of every stream into the ring.
@@ -514,9 +521,9 @@ extern "C" {
 
 // Host state (n, Q) moves only once every launch of the call was accepted.
 // The launches are ordered so that a refused one leaves the old state valid:
-// the ring is written only by the last launch of an append (the copy
-// workgroups of the chunk-reading quantize launch, or the ring launch after
-// all quantize launches), and the quantize launches before it write only
+// the ring is written only by the last launch of an append (copy
+// workgroups riding on the last quantize launch, or a ring launch after all
+// quantize launches), and the quantize launches before it write only
 // blocks past the old prefixes (under the paper policy also the value rows
 // at or past the old Q_V of the block holding it, which no call reads while
 // Q_V is unchanged).
@@ -535,14 +542,10 @@ kivi_status kivi_append(kivi_cache *c, const void *k, const void *v, int64_t n_n
         c->n = p.n_new_total;
         return KIVI_OK;
     }
-    if (c->cfg.policy != KIVI_FLUSH_PAPER) {
-        // window and segment policies: the ring copy rides on the last launch
+    {
+        // the ring copy rides on the last launch
         const RingArgs r = ring_args(c, k, v, n_new, p.n_old, p.ring_token_begin, p.ring_token_end);
         st = enqueue_flush(c, p, k, v, n_new, stream, &r);
-    } else {
-        st = enqueue_flush(c, p, k, v, n_new, stream);
-        if (st == KIVI_OK)
-            st = enqueue_ring(c, k, v, n_new, p.n_old, p.ring_token_begin, p.ring_token_end, stream);
     }
     if (st != KIVI_OK) return st;
     c->n = p.n_new_total;

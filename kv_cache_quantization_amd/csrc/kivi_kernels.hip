@@ -806,14 +806,12 @@ template <int BITS, typename T, bool RING, int GT, bool OUT, bool KSEG = false>
 __global__ __launch_bounds__(64) void quantize_kernel(QuantizeArgs a) {
     __shared__ uint32_t tr[64 * 2 * BITS];
     const uint32_t task = blockIdx.x;
-    if constexpr (!RING) {
-        if (task >= a.quant_tasks) {
-            const int64_t first = (int64_t)(task - a.quant_tasks) * kRingThreads;
+    if (task >= a.quant_tasks) {
+        const int64_t first = (int64_t)(task - a.quant_tasks) * kRingThreads;
 #pragma unroll
-            for (int j = 0; j < kRingThreads / 64; j++)
-                ring_copy_piece(a.copy, first + j * 64 + threadIdx.x);
-            return;
-        }
+        for (int j = 0; j < kRingThreads / 64; j++)
+            ring_copy_piece(a.copy, first + j * 64 + threadIdx.x);
+        return;
     }
     const uint32_t nb = (uint32_t)(a.block_end - a.block_begin);
     int64_t stream, g;
@@ -2790,12 +2788,22 @@ static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
     int64_t split = ring_end < a.block_begin ? a.block_begin : ring_end;
     split = a.block_begin + (split - a.block_begin + align - 1) / align * align;
     if (split > a.block_end) split = a.block_end;
+    // The ring copy (a.copy) rides on the instance that reads no ring row.
+    // When every block reads the ring, it rides on that instance instead if
+    // none of the slots it writes holds a row the instance reads: the rows
+    // read lie in [block_begin * G, n_old) and the rows written below
+    // copy.tok_end, so that holds when the two ranges span less than the ring.
+    const bool copy = a.copy.tok_end > a.copy.tok_begin;
+    const bool ring_carries = copy && a.block_end <= split &&
+                              a.copy.tok_end - 1 - a.block_begin * G < a.ring_cap;
     if (split > a.block_begin) {
         QuantizeArgs r = a;
         r.block_end = split;
         const int64_t tasks = (int64_t)a.streams * tasks_of(split - a.block_begin);
-        hipLaunchKernelGGL((quantize_kernel<BITS, T, true, GT, OUT, KSEG>), dim3((unsigned)tasks),
-                           dim3(64), 0, s, r);
+        r.quant_tasks = (uint32_t)tasks;
+        hipLaunchKernelGGL((quantize_kernel<BITS, T, true, GT, OUT, KSEG>),
+                           dim3((unsigned)(tasks + (ring_carries ? ring_blocks(a.copy) : 0))), dim3(64),
+                           0, s, r);
     }
     if (a.block_end > split) {
         QuantizeArgs n = a;
@@ -2806,9 +2814,10 @@ static hipError_t launch_quantize_t(const QuantizeArgs &a, hipStream_t s) {
                            dim3((unsigned)(tasks + ring_blocks(a.copy))), dim3(64), 0, s, n);
         return hipGetLastError();
     }
-    // every quantized block reads the ring: the copy runs after them
+    // every quantized block reads the ring: unless it rode along, the copy
+    // runs after them
     const hipError_t e = hipGetLastError();
-    return e != hipSuccess ? e : launch_ring_append(a.copy, s);
+    return e != hipSuccess || ring_carries ? e : launch_ring_append(a.copy, s);
 }
 
 template <int BITS, typename T>

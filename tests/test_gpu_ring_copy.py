@@ -1,12 +1,16 @@
-"""The copy of the newest rows into the residual ring takes one of three
+"""The copy of the newest rows into the residual ring takes one of four
 routes under the window policy, and every route must leave the same ring
 (and cache) as the oracle, bit for bit:
 
 - folded into the quantize launch that reads only the appended chunk (a
-  one-shot prefill; a chunk whose flush also quantizes groups that start in
-  the ring, which run in a launch of their own before it);
-- a ring-append launch after a quantize launch whose groups all read the ring
-  (a single-token step that flushes a group);
+  one-shot prefill, the chunks of 700, 300 and 257; a chunk whose flush also
+  quantizes groups that start in the ring, which run in a launch of their own
+  before it);
+- folded into a quantize launch whose groups all read the ring, when the rows
+  it reads and the rows the copy writes span less than the ring, so no slot
+  is both (the last single-token step, which flushes a group);
+- a ring-append launch after such a quantize launch when they span more (the
+  chunk of 33);
 - a ring-append launch alone (an append that quantizes nothing).
 
 fp16 and fp32 rows (32 and 64 16-byte pieces per row pair), several streams
