@@ -1802,30 +1802,13 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
     const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * (RF32 ? 4 : 2);
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
     float *p_lds = (float *)(lds + SB);               // [GQ][G]
+    // q of the lane's head is loaded here, the unscaled q for LDS after the
+    // first group's copies and value-row loads; both are first used after
+    // those, so the item waits one memory round trip for all of them (loads
+    // complete in order)
     h2 qB[4][4];
     load_q_operand<QF32>(a.q, ((int64_t)b * a.q_heads + hk * GQ + h) * D, Gl, qB);
-    {
-        const int64_t qoff = ((int64_t)b * a.q_heads + hk * GQ + (l >> 4) % GQ) * D + 8 * (l & 15);
-        uint4 uq;
-        if constexpr (QF32) {
-            const float *qf = (const float *)a.q + qoff;
-            const float4 x0 = *(const float4 *)qf, x1 = *(const float4 *)(qf + 4);
-            h2 t0 = {(_Float16)x0.x, (_Float16)x0.y}, t1 = {(_Float16)x0.z, (_Float16)x0.w};
-            h2 t2 = {(_Float16)x1.x, (_Float16)x1.y}, t3 = {(_Float16)x1.z, (_Float16)x1.w};
-            uq.x = __builtin_bit_cast(uint32_t, t0); uq.y = __builtin_bit_cast(uint32_t, t1);
-            uq.z = __builtin_bit_cast(uint32_t, t2); uq.w = __builtin_bit_cast(uint32_t, t3);
-        } else {
-            uq = *(const uint4 *)((const _Float16 *)a.q + qoff);
-        }
-        q_lds[l] = uq;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-        const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
-        const h2 d2 = {dn, dn};
-#pragma unroll
-        for (int s2 = 0; s2 < 4; s2++) qB[s2][m] = qB[s2][m] * d2;
-    }
+    const int64_t qoff = ((int64_t)b * a.q_heads + hk * GQ + (l >> 4) % GQ) * D + 8 * (l & 15);
     const float cs = a.sm_log2 * kTwo24;
     float Mr[GQ], Lr[GQ], O0[GQ], O1[GQ];
 #pragma unroll
@@ -1847,15 +1830,45 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
             32 * a.side.nvs);
         // the group's value rows from the ring (slots of tokens below
         // n_vquant may hold other tokens: those rows are not used)
+        // (one modulo per group: the ring holds more than G slots, so the
+        // group's rows wrap around it at most once)
+        const int64_t slot0 = (g * G) % a.ring_cap;
         float2 vr[G];
 #pragma unroll
         for (int r = 0; r < G; r++) {
-            const int64_t slot = (g * G + r) % a.ring_cap;
+            const int64_t slot = slot0 + r < a.ring_cap ? slot0 + r : slot0 + r - a.ring_cap;
             if constexpr (RF32) {
                 vr[r] = *(const float2 *)(rvb + (slot * D + c0) * 4);
             } else {
                 const h2 hv = *(const h2 *)(rvb + (slot * D + c0) * 2);
                 vr[r] = (float2){(float)hv[0], (float)hv[1]};
+            }
+        }
+        if (gi == g_begin) {
+            uint4 uq;
+            if constexpr (QF32) {
+                const float *qf = (const float *)a.q + qoff;
+                const float4 x0 = *(const float4 *)qf, x1 = *(const float4 *)(qf + 4);
+                h2 t0 = {(_Float16)x0.x, (_Float16)x0.y}, t1 = {(_Float16)x0.z, (_Float16)x0.w};
+                h2 t2 = {(_Float16)x1.x, (_Float16)x1.y}, t3 = {(_Float16)x1.z, (_Float16)x1.w};
+                uq.x = __builtin_bit_cast(uint32_t, t0); uq.y = __builtin_bit_cast(uint32_t, t1);
+                uq.z = __builtin_bit_cast(uint32_t, t2); uq.w = __builtin_bit_cast(uint32_t, t3);
+            } else {
+                uq = *(const uint4 *)((const _Float16 *)a.q + qoff);
+            }
+            // first uses of q: after the copies and loads above (volatile asm
+            // keeps the order; q is not touched before this point)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; s2++)
+#pragma unroll
+                for (int m = 0; m < 4; m++) asm volatile("" : "+v"(qB[s2][m]));
+            q_lds[l] = uq;
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const _Float16 dn = (_Float16)(1.0f / (float)(1 << kScaleLog2<BITS>(m)));
+                const h2 d2 = {dn, dn};
+#pragma unroll
+                for (int s2 = 0; s2 < 4; s2++) qB[s2][m] = qB[s2][m] * d2;
             }
         }
         wait_vm<0>();
@@ -2563,6 +2576,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
 #pragma clang fp contract(off)
                 const uint32_t *vcode = (const uint32_t *)(ring + PP::CB);
                 const _Float16 *sd = (const _Float16 *)(ring + 2 * PP::CB);
+                // the group's rows wrap around the ring (more than G slots) at most once
+                const int64_t slot0 = tok0 % a.ring_cap;
                 for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
                     const int r = idx / D, c = idx % D;
                     const int64_t t = tok0 + r;
@@ -2574,7 +2589,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kerne
                         const float vz = (float)sd[2 * D + G * (nvs + ((c / G) >> vsh)) + r];
                         v = (_Float16)((float)((vcode[dw] >> bit) & M1) * vs + vz);
                     } else {
-                        const int64_t ri = (t % a.ring_cap) * D + c;
+                        const int64_t sl = slot0 + r < a.ring_cap ? slot0 + r : slot0 + r - a.ring_cap;
+                        const int64_t ri = sl * D + c;
                         v = a.ring_f32 ? (_Float16)rvf[ri] : rvh[ri];
                     }
                     vt[c * VTS + r] = v;
