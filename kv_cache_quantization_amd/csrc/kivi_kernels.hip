@@ -1546,24 +1546,34 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     // Any weights give the same groups overall, so results do not depend on
     // them.  Split k of quarter r is block tail + streams * (splits before
     // quarter r) + stream * (quarter's splits) + (k - splits before r).
-    const int64_t WE = 1000 + kXcdSkew, WO = 1000 - kXcdSkew;
-    const int64_t streams = (int64_t)a.batch * a.kv_heads;
-    const int64_t tail_blocks = streams * a.tail_items;
-    auto cum = [&](int64_t k) {                         // weight of splits [0, k)
-        int64_t c = 0, k0 = 0;
+    // (Block numbers stay below 2^31, the launch checks it, so the parities
+    // are taken in 32 bits; a split's share and the weights in 64.  The
+    // shares' quotients are IEEE double divisions of integers below 2^53,
+    // which truncate to the integer quotient: the rounding error, at most
+    // quotient * 2^-53, is smaller than 1 / wsum, the least distance of a
+    // fraction with that denominator from an integer.  A scalar 64-bit
+    // division costs over a hundred instructions, and a compute unit's
+    // scalar unit serves its 16 wavefronts' prologues in turn.)
+    constexpr int WE = 1000 + (int)kXcdSkew, WO = 1000 - (int)kXcdSkew;
+    const int streams32 = a.batch * a.kv_heads;
+    const int tail_blocks = streams32 * a.tail_items;
+    auto cum = [&](int k) {                             // weight of splits [0, k)
+        int64_t c = 0;
+        int k0 = 0;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int64_t u = quarter_splits(a.splits, r);
-            const int64_t m = k - k0 < 0 ? 0 : k - k0 > u ? u : k - k0;
-            const int64_t base = tail_blocks + streams * k0 + stream * u;
-            const int64_t odd = (base + m) / 2 - base / 2;
-            c += kQuarterWeight[r] * ((m - odd) * WE + odd * WO);
+            const int u = (a.splits + 3 - r) >> 2;      // quarter_splits
+            const int m = k - k0 < 0 ? 0 : k - k0 > u ? u : k - k0;
+            const int base = tail_blocks + streams32 * k0 + stream * u;
+            const int odd = ((base + m) >> 1) - (base >> 1);
+            c += kQuarterWeight[r] * (int64_t)((m - odd) * WE + odd * WO);
             k0 += u;
         }
         return c;
     };
-    const int64_t wsum = cum(a.splits);
-    const int64_t g0 = ng * cum(sp) / wsum, g1 = ng * cum(sp + 1) / wsum;
+    const double wsum = (double)cum(a.splits);
+    const int64_t g0 = (int64_t)((double)(ng * cum(sp)) / wsum);
+    const int64_t g1 = (int64_t)((double)(ng * cum(sp + 1)) / wsum);
     const int n_g = (int)(g1 - g0);             // groups of this split
 
     const uint8_t *sblk = a.blocks + ((int64_t)stream * a.max_groups + g0) * a.block_bytes;
@@ -2036,14 +2046,15 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     // (q's dtype selects an instantiation: the prologue's loads must not
     // meet at a control-flow join, where the compiler would wait for them)
     // split item it: quarter r, then stream, then split (kQuarterWeight)
-    const int64_t it = item - streams * a.tail_items;
-    int64_t k0 = 0;
+    // (in 32 bits: the launch keeps every block number below 2^31)
+    const uint32_t it = (uint32_t)(item - streams * a.tail_items), st = (uint32_t)streams;
+    uint32_t k0 = 0;
     int r = 0;
-    for (; r < 3 && it >= streams * (k0 + quarter_splits(a.splits, r)); r++)
-        k0 += quarter_splits(a.splits, r);
-    const int64_t u = quarter_splits(a.splits, r);
-    const int64_t rem = it - streams * k0;
-    const int stream = (int)(rem / u), sp = (int)(k0 + rem % u);
+    for (; r < 3 && it >= st * (k0 + (uint32_t)quarter_splits(a.splits, r)); r++)
+        k0 += (uint32_t)quarter_splits(a.splits, r);
+    const uint32_t u = (uint32_t)quarter_splits(a.splits, r);
+    const uint32_t rem = it - st * k0, sq = rem / u;
+    const int stream = (int)sq, sp = (int)(k0 + (rem - sq * u));
     if (a.q_is_f32)
         decode_split<BITS, GQ, true, OUT, DEEP, SPLIT>(a, stream, sp, pipe, q_lds);
     else
