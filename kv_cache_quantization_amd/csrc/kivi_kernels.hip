@@ -1159,7 +1159,7 @@ constexpr int64_t kXcdSkew = 20;
 // turn, and a SIMD issues the wavefronts it received first ahead of the later
 // ones: splits of earlier quarters get a larger share of their stream's
 // groups (per mille of the average).
-constexpr int64_t kQuarterWeight[4] = {1060, 1020, 980, 940};
+constexpr int64_t kQuarterWeight[4] = {1150, 1050, 950, 850};
 
 __device__ __forceinline__ int64_t quarter_splits(int64_t splits, int r) {
     return (splits + 3 - r) / 4;
