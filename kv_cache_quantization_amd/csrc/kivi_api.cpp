@@ -207,12 +207,13 @@ constexpr int64_t kDeepGroups = 2048;
 
 // Short passes (fewer groups per stream than this) aim at no more than
 // kShortWaves: with ~5 groups per split a wavefront's prologue and memory
-// round trips dominate, and twice the groups per split in half the
-// wavefronts measured faster on the streaming workload (8 KV x 8 batch,
-// 262-272 groups per stream): 21.4 -> 20.4 us per fused warm step, 26.2 ->
-// 24.9 cold; 1024, 1536 and 3072 were slower than 2048.
+// round trips dominate, and fewer, longer splits measured faster on the
+// streaming workload (8 KV x 8 batch, 262-272 groups per stream).  With the
+// split prologue in 32-bit arithmetic, 3072 measured best (fused warm step
+// 19.3-19.5 us; 2048: 19.6-19.7, 2560: 19.55-19.6, 3584: 19.45-19.6, 4096:
+// 20.0-20.1); with the earlier 64-bit prologue 2048 had been best.
 constexpr int64_t kShortGroups = 512;
-constexpr int64_t kShortWaves = 2048;
+constexpr int64_t kShortWaves = 3072;
 
 // Split items aimed for per decode launch: one round of resident wavefronts.
 // A wavefront's LDS (as the decode kernel declares it) is its copy stages
