@@ -1556,7 +1556,7 @@ __device__ void decode_split(const DecodeArgs &a, int stream, int sp, uint8_t *p
     // scalar unit serves its 16 wavefronts' prologues in turn.)
     constexpr int WE = 1000 + (int)kXcdSkew, WO = 1000 - (int)kXcdSkew;
     const int streams32 = a.batch * a.kv_heads;
-    const int tail_blocks = streams32 * a.tail_items;
+    const int tail_blocks = streams32 * (a.tail_items + a.mixed_items);
     auto cum = [&](int k) {                             // weight of splits [0, k)
         int64_t c = 0;
         int k0 = 0;
@@ -1799,6 +1799,11 @@ __device__ __forceinline__ void code_pos(bool is_v, int t, int c, int &dw, int &
 // item's running state like a residual chunk; p.V runs on the vector ALUs,
 // lane l owning channels 2l, 2l+1, with V-hat = code * scale, then + zero,
 // in float32 for tokens below n_vquant and the ring's rows for the others.
+// The items are blocks of decode_kernel's launch (after the residual items,
+// before the splits) and use its LDS: the block, p, and kMixedRowBytes of
+// ring rows, so that the item holds no more registers than a split item.
+constexpr int kMixedRowBytes = 4096;
+
 template <int BITS, int GQ, bool RF32, bool QF32, bool OUT, bool SPLIT = false>
 __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t *lds,
                                uint4 *q_lds) {
@@ -1811,7 +1816,7 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
     const int b = stream / a.kv_heads, hk = stream % a.kv_heads;
     const char *rvb = (const char *)a.ring_v + (int64_t)stream * a.ring_cap * D * (RF32 ? 4 : 2);
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
-    float *p_lds = (float *)(lds + SB);               // [GQ][G]
+    float *p_lds = (float *)(lds + SB);               // [G][GQ]
     // q of the lane's head is loaded here, the unscaled q for LDS after the
     // first group's copies and value-row loads; both are first used after
     // those, so the item waits one memory round trip for all of them (loads
@@ -1838,22 +1843,6 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
             lbase, l, false,
             a.side.kside + ((int64_t)stream * a.side.max_kunits + (g >> a.side.kunit_shift)) * (4 * D),
             32 * a.side.nvs);
-        // the group's value rows from the ring (slots of tokens below
-        // n_vquant may hold other tokens: those rows are not used)
-        // (one modulo per group: the ring holds more than G slots, so the
-        // group's rows wrap around it at most once)
-        const int64_t slot0 = (g * G) % a.ring_cap;
-        float2 vr[G];
-#pragma unroll
-        for (int r = 0; r < G; r++) {
-            const int64_t slot = slot0 + r < a.ring_cap ? slot0 + r : slot0 + r - a.ring_cap;
-            if constexpr (RF32) {
-                vr[r] = *(const float2 *)(rvb + (slot * D + c0) * 4);
-            } else {
-                const h2 hv = *(const h2 *)(rvb + (slot * D + c0) * 2);
-                vr[r] = (float2){(float)hv[0], (float)hv[1]};
-            }
-        }
         if (gi == g_begin) {
             uint4 uq;
             if constexpr (QF32) {
@@ -1955,48 +1944,86 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
             for (int e = 0; e < 4; e++) {
                 const float pv = __builtin_amdgcn_exp2f(S[t][e] - m);
                 ls += pv;
-                if (j < GQ) p_lds[j * G + 16 * t + 4 * Gl + e] = pv;     // [head][token]
+                if (j < GQ) p_lds[(16 * t + 4 * Gl + e) * GQ + j] = pv;  // [token][head]
             }
         ls = xsum_rows(ls);
         lds_sync_wave();
-        // the lane's two channels of every token of the group
-        {
-#pragma clang fp contract(off)
-            const uint32_t *vcode = (const uint32_t *)(stg + PP::CB);
-            const _Float16 *sd = (const _Float16 *)(stg + 2 * PP::CB);
+        // p . V, lane l owning channels c0, c0 + 1: rows below n_vquant from
+        // their codes (V-hat = code * scale, then + zero, in float32), the
+        // others from the ring.  Those are copied into LDS 4 KiB at a time
+        // (16 fp16 or 8 fp32 rows; a group's rows are contiguous in the ring,
+        // whose size and the group's first slot are multiples of G) and read
+        // a row at a time, so that they hold no registers; each head sums its
+        // rows in order.
+        constexpr int RB = RF32 ? 4 : 2;
+        constexpr int CR = kMixedRowBytes / (D * RB);       // rows per copy
+        const uint32_t rows_lds = lbase + (uint32_t)(SB + GQ * G * 4);
+        const uint8_t *rows = lds + SB + GQ * G * 4;
+        const uint8_t *rsrc = (const uint8_t *)rvb + (g * G) % a.ring_cap * D * RB;
+        const int64_t ncv = a.n_vquant - g * G;
+        const int nc = ncv < 0 ? 0 : ncv > G ? G : (int)ncv;  // rows with codes
+        const uint32_t *vcode = (const uint32_t *)(stg + PP::CB);
+        const _Float16 *sd = (const _Float16 *)(stg + 2 * PP::CB);
+        float x0[GQ], x1[GQ];
 #pragma unroll
-            for (int r = 0; r < G; r++) {
-                if (g * G + r < a.n_vquant) {
+        for (int hh = 0; hh < GQ; hh++) x0[hh] = x1[hh] = 0.f;
+        for (int r0 = 0; r0 < G; r0 += CR) {
+            if (r0 + CR > nc) {
+                lds_sync_wave();            // the previous rows' LDS reads are done
+#pragma unroll
+                for (int c = 0; c < kMixedRowBytes / 1024; c++)
+                    dma_1k(rsrc + r0 * D * RB + c * 1024 + 16 * l,
+                           __builtin_amdgcn_readfirstlane(rows_lds + c * 1024));
+                wait_vm<0>();
+            }
+#pragma unroll 2
+            for (int i = 0; i < CR; i++) {
+                const int r = r0 + i;
+                float vx, vy;
+                if (r < nc) {
+#pragma clang fp contract(off)
                     int dv0, bv0, dv1, bv1;
                     code_pos<BITS>(true, r, c0, dv0, bv0);
                     code_pos<BITS>(true, r, c0 + 1, dv1, bv1);
                     const float vs = (float)sd[vsf + r];
                     const float vz = (float)sd[vzf + r];
-                    vr[r].x = (float)((vcode[dv0] >> bv0) & M1) * vs + vz;
-                    vr[r].y = (float)((vcode[dv1] >> bv1) & M1) * vs + vz;
+                    vx = (float)((vcode[dv0] >> bv0) & M1) * vs + vz;
+                    vy = (float)((vcode[dv1] >> bv1) & M1) * vs + vz;
+                } else if constexpr (RF32) {
+                    const float2 f = *(const float2 *)(rows + (i * D + c0) * 4);
+                    vx = f.x;
+                    vy = f.y;
+                } else {
+                    const h2 hv = *(const h2 *)(rows + (i * D + c0) * 2);
+                    vx = (float)hv[0];
+                    vy = (float)hv[1];
+                }
+                float pr[GQ];
+                if constexpr (GQ == 4) {
+                    const float4 p4 = *(const float4 *)&p_lds[4 * r];
+                    pr[0] = p4.x; pr[1] = p4.y; pr[2] = p4.z; pr[3] = p4.w;
+                } else if constexpr (GQ == 2) {
+                    const float2 p2 = *(const float2 *)&p_lds[2 * r];
+                    pr[0] = p2.x; pr[1] = p2.y;
+                } else {
+                    pr[0] = p_lds[r];
+                }
+#pragma unroll
+                for (int hh = 0; hh < GQ; hh++) {
+                    x0[hh] = __builtin_fmaf(pr[hh], vx, x0[hh]);
+                    x1[hh] = __builtin_fmaf(pr[hh], vy, x1[hh]);
                 }
             }
         }
 #pragma unroll
         for (int hh = 0; hh < GQ; hh++) {
-            float x0 = 0.f, x1 = 0.f;
-#pragma unroll
-            for (int r4 = 0; r4 < G / 4; r4++) {
-                const float4 p4 = *(const float4 *)&p_lds[hh * G + 4 * r4];
-                const float pq[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    x0 = __builtin_fmaf(pq[e], vr[4 * r4 + e].x, x0);
-                    x1 = __builtin_fmaf(pq[e], vr[4 * r4 + e].y, x1);
-                }
-            }
             // merge into the running state (head hh's (m, l) sit in lane hh)
             const float mc = readlane_f(m, hh), lc = readlane_f(ls, hh);
             const float mn = fmaxf(Mr[hh], mc);
             const float fo = __builtin_amdgcn_exp2f(Mr[hh] - mn);
             const float fc = __builtin_amdgcn_exp2f(mc - mn);
-            O0[hh] = __builtin_fmaf(O0[hh], fo, x0 * fc);
-            O1[hh] = __builtin_fmaf(O1[hh], fo, x1 * fc);
+            O0[hh] = __builtin_fmaf(O0[hh], fo, x0[hh] * fc);
+            O1[hh] = __builtin_fmaf(O1[hh], fo, x1[hh] * fc);
             Lr[hh] = __builtin_fmaf(Lr[hh], fo, lc * fc);
             Mr[hh] = mn;
         }
@@ -2013,23 +2040,6 @@ __device__ void decode_mixed_t(const DecodeArgs &a, int stream, int mi, uint8_t 
     }
 }
 
-// A kernel of its own (one wavefront per (stream, mixed item)), so that its
-// registers do not count against the occupancy of decode_kernel.
-template <int BITS, int GQ, bool OUT, bool SPLIT = false>
-__global__ __launch_bounds__(64) void decode_mixed_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t blk[stage_bytes<BITS, OUT>() + GQ * G * 4];
-    __shared__ uint4 q_lds[64];
-    const int streams = a.batch * a.kv_heads;
-    const int stream = (int)(blockIdx.x % streams), mi = (int)(blockIdx.x / streams);
-    if (a.ring_is_f32) {
-        if (a.q_is_f32) decode_mixed_t<BITS, GQ, true, true, OUT, SPLIT>(a, stream, mi, blk, q_lds);
-        else decode_mixed_t<BITS, GQ, true, false, OUT, SPLIT>(a, stream, mi, blk, q_lds);
-    } else {
-        if (a.q_is_f32) decode_mixed_t<BITS, GQ, false, true, OUT, SPLIT>(a, stream, mi, blk, q_lds);
-        else decode_mixed_t<BITS, GQ, false, false, OUT, SPLIT>(a, stream, mi, blk, q_lds);
-    }
-}
-
 template <int BITS, int GQ, bool OUT = false, bool DEEP = false, bool SPLIT = false>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t pipe[decode_lds_bytes<BITS, OUT, DEEP>()];
@@ -2043,11 +2053,29 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         else decode_tail_f16<GQ, false>(a, stream, ti, pipe);
         return;
     }
+    // paper policy: the items of the groups with partial value codes
+    // (a.mixed_items per stream, 0 otherwise), staged in the same LDS
+    const int64_t mixed_blocks = streams * a.mixed_items;
+    if (item < streams * a.tail_items + mixed_blocks) {
+        static_assert(stage_bytes<BITS, OUT>() + GQ * G * 4 + kMixedRowBytes <=
+                          decode_lds_bytes<BITS, OUT, DEEP>(),
+                      "mixed items stage a block, p and value rows in the ring's LDS");
+        const int64_t mt = item - streams * a.tail_items;
+        const int stream = (int)(mt % streams), mi = (int)(mt / streams);
+        if (a.ring_is_f32) {
+            if (a.q_is_f32) decode_mixed_t<BITS, GQ, true, true, OUT, SPLIT>(a, stream, mi, pipe, q_lds);
+            else decode_mixed_t<BITS, GQ, true, false, OUT, SPLIT>(a, stream, mi, pipe, q_lds);
+        } else {
+            if (a.q_is_f32) decode_mixed_t<BITS, GQ, false, true, OUT, SPLIT>(a, stream, mi, pipe, q_lds);
+            else decode_mixed_t<BITS, GQ, false, false, OUT, SPLIT>(a, stream, mi, pipe, q_lds);
+        }
+        return;
+    }
     // (q's dtype selects an instantiation: the prologue's loads must not
     // meet at a control-flow join, where the compiler would wait for them)
     // split item it: quarter r, then stream, then split (kQuarterWeight)
     // (in 32 bits: the launch keeps every block number below 2^31)
-    const uint32_t it = (uint32_t)(item - streams * a.tail_items), st = (uint32_t)streams;
+    const uint32_t it = (uint32_t)(item - streams * a.tail_items - mixed_blocks), st = (uint32_t)streams;
     uint32_t k0 = 0;
     int r = 0;
     for (; r < 3 && it >= st * (k0 + (uint32_t)quarter_splits(a.splits, r)); r++)
@@ -2925,28 +2953,14 @@ static void launch_decode_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream
     else hipLaunchKernelGGL((decode_kernel<BITS, 1, OUT, DEEP, SPLIT>), grid, dim3(64), 0, s, a);
 }
 
-template <int BITS, bool OUT, bool SPLIT = false>
-static void launch_mixed_out(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
-    if (gq == 4) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 4, OUT, SPLIT>), grid, dim3(64), 0, s, a);
-    else if (gq == 2) hipLaunchKernelGGL((decode_mixed_kernel<BITS, 2, OUT, SPLIT>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((decode_mixed_kernel<BITS, 1, OUT, SPLIT>), grid, dim3(64), 0, s, a);
-}
-
-template <int BITS>
-static void launch_mixed_bits(const DecodeArgs &a, int gq, dim3 grid, hipStream_t s) {
-    if (a.n_out > 0) launch_mixed_out<BITS, true>(a, gq, grid, s);
-    else if (a.side.split) launch_mixed_out<BITS, false, true>(a, gq, grid, s);
-    else launch_mixed_out<BITS, false>(a, gq, grid, s);
-}
-
-// decode_kernel: a.tail_items + a.splits items per stream (residual, splits)
-// writing partials a.splits .. a.splits + a.tail_items - 1 and 0 .. a.splits
-// - 1; under the paper policy decode_mixed_kernel's a.mixed_items items per
-// stream write the partials after those.
+// decode_kernel: a.tail_items + a.mixed_items + a.splits items per stream
+// (residual, groups with partial value codes under the paper policy,
+// splits), writing partials a.splits .. a.splits + a.tail_items - 1, the
+// a.mixed_items after those, and 0 .. a.splits - 1.
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const int streams = a.batch * a.kv_heads;
     const int gq = a.q_heads / a.kv_heads;
-    const int64_t items = (int64_t)streams * (a.splits + a.tail_items);
+    const int64_t items = (int64_t)streams * (a.splits + a.tail_items + a.mixed_items);
     if (a.items > kMaxItems || items > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (a.tail_items < 1 || a.tail_chunk_step < 1 ||
         (int64_t)a.tail_items * a.tail_chunk_step < a.tail_chunks)
@@ -2956,17 +2970,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     if (a.n_out < 0 || a.n_out > kMaxKeyOutliers || (a.n_out > 0 && !a.outliers))
         return hipErrorInvalidValue;
     if (!side_args_ok(a.side, a.n_out)) return hipErrorInvalidValue;
-    if (a.mixed_groups > 0) {
-        if (a.mixed_items < 1 || a.mixed_step < 1 ||
-            (int64_t)a.mixed_items * a.mixed_step < a.mixed_groups)
-            return hipErrorInvalidValue;
-        const dim3 mgrid((unsigned)(streams * a.mixed_items));
-        if (a.bits == 2) launch_mixed_bits<2>(a, gq, mgrid, s);
-        else if (a.bits == 8) launch_mixed_bits<8>(a, gq, mgrid, s);
-        else launch_mixed_bits<4>(a, gq, mgrid, s);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    if (a.mixed_groups > 0 ? (a.mixed_items < 1 || a.mixed_step < 1 ||
+                              (int64_t)a.mixed_items * a.mixed_step < a.mixed_groups)
+                           : a.mixed_items != 0)
+        return hipErrorInvalidValue;
     dim3 grid((unsigned)items);
     if (a.n_out > 0) {
         if (a.bits == 2) launch_decode_bits<2, true>(a, gq, grid, s);

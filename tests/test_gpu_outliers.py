@@ -152,8 +152,8 @@ PAPER = 1
 def test_outliers_paper_policy(orc):
     """Outlier-aware keys under the paper's flush policy: key groups quantized
     R tokens at a time carry records; the groups whose values continue in the
-    ring take the correction in decode_mixed_kernel and in the attention's
-    mixed pass.  Caches bit-exact, one-shot and streamed across key flushes."""
+    ring take the correction in the decode's mixed items and in the
+    attention's mixed pass.  Caches bit-exact, one-shot and streamed across key flushes."""
     _run(orc, 2, 3, 12, 1000, 2, 128, 2, seed=95, label="out-paper", policy=PAPER)
     _run(orc, 2, 2, 4, 700, 4, 64, 3, seed=96, chunks=[150] + [1] * 140 + [410],
          label="out-paper-stream", policy=PAPER)

@@ -62,6 +62,7 @@ def _run(orc, B, H, Hq, n, bits, R, seed, chunks=None, dtype=np.float16, q_dtype
     (1024, 8, 128, 1),     # n a multiple of R: empty key residual
     (777, 4, 32, 4),       # R = G
     (2049, 2, 128, 2),
+    (4613, 2, 2304, 4),    # Q_K = 4608, Q_V = 2309: 72 mixed groups, two per item
 ])
 def test_oneshot(orc, n, bits, R, gq):
     _run(orc, 2, 3, 3 * gq, n, bits, R, seed=n + 7, label="paper-%d" % n)
