@@ -286,16 +286,16 @@ int64_t max_tail_items(const kivi_config &cfg) {
 // to kMaxTailItems items per stream.
 int64_t max_mixed_items(const kivi_config &cfg) { return max_tail_items(cfg) + 1; }
 
-// Attention of T queries: kAttnBlocks x 16 / GQ queries per wavefront,
-// kAttnWaves wavefronts per workgroup (one query block), and the groups split
-// so that about two workgroups per compute unit are in flight.
+// Attention of T queries: kAttnColBlocks x 16 / GQ queries per workgroup
+// (one query block), and the groups split so that about two workgroups per
+// compute unit are in flight.
 void attn_plan(const kivi_cache *c, int64_t T, int64_t q, int32_t *qblocks, int32_t *splits,
                int32_t *gps) {
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
     const int gq = c->cfg.n_q_heads / c->cfg.n_kv_heads;
     const int64_t qt = 16 / gq;
     const int64_t cbs = (T + qt - 1) / qt;
-    const int64_t qb = (cbs + kAttnWaves * kAttnBlocks - 1) / (kAttnWaves * kAttnBlocks);
+    const int64_t qb = (cbs + kAttnColBlocks - 1) / kAttnColBlocks;
     *qblocks = (int32_t)qb;
     const int64_t ng = q / kGroup;
     int64_t want = 2 * kComputeUnits / (streams * qb);
@@ -311,8 +311,7 @@ int64_t attn_max_splits(const kivi_cache *c, int64_t T) {
     const int64_t streams = (int64_t)c->cfg.batch * c->cfg.n_kv_heads;
     const int gq = c->cfg.n_q_heads / c->cfg.n_kv_heads;
     const int64_t qt = 16 / gq;
-    const int64_t qb = ((T + qt - 1) / qt + kAttnWaves * kAttnBlocks - 1) /
-                       (kAttnWaves * kAttnBlocks);
+    const int64_t qb = ((T + qt - 1) / qt + kAttnColBlocks - 1) / kAttnColBlocks;
     int64_t want = 2 * kComputeUnits / (streams * qb);
     return want < 1 ? 1 : want;
 }

@@ -176,7 +176,12 @@ hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
 
-constexpr int kAttnWaves = 8;   // wavefronts per attention workgroup
-constexpr int kAttnBlocks = 1;  // 16-column blocks per attention wavefront (2 measured no faster)
+// Attention of T queries: a workgroup covers kAttnColBlocks 16-column blocks
+// (one query block, 128 columns) and reads each cache block once.  Its
+// wavefronts take CB column blocks each (kAttnColBlocks / CB wavefronts):
+// CB = 2 unpacks a block's codes once for two column blocks (~220 VGPRs, 2
+// wavefronts per SIMD); CB = 1 (8 wavefronts) serves calls whose first query
+// block is not full, where a second column block would be empty work.
+constexpr int kAttnColBlocks = 8;
 
 }  // namespace kivi

@@ -2240,9 +2240,10 @@ static void launch_combine(const float *part_o, const float *part_ml, float *out
 // The same products as the decode path, with the matrix core's 16 columns
 // holding QT = 16 / GQ queries x GQ heads (column j: query j / GQ of the
 // wavefront's block, head j % GQ): no column is a replica, so each value
-// channel group gets its own B operand.  The kAttnWaves wavefronts of a
-// workgroup share each group's block: wavefront 0 copies it HBM -> LDS and
-// one barrier per group hands it to all.  p is kept as P_s = 2^(s - m - kSlack)
+// channel group gets its own B operand.  The wavefronts of a workgroup
+// (kAttnColBlocks / CB, CB column blocks each) share each group's block:
+// wavefront 0 copies it HBM -> LDS and one barrier per two groups hands it to
+// all.  p is kept as P_s = 2^(s - m - kSlack)
 // in fp16 (<= 1); the sums of p and of p * vzero run on the matrix core, and
 // every accumulator carries the same 2^-kSlack, which cancels in o = acc / l.
 
@@ -2292,9 +2293,10 @@ __device__ __forceinline__ void mask_scores(f4 &S0, f4 &S1, int64_t tok0, int Gl
 }
 
 template <int BITS, int GQ, bool QF32, int CB, bool OUT = false, bool SPLIT = false>
-__global__ __launch_bounds__(64 * kAttnWaves, BITS == 2 ? 4 : 1) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * (kAttnColBlocks / CB), BITS == 2 ? (CB == 1 ? 4 : 2) : 1)
+void attn_kernel(AttnArgs a) {
     using PP = Pipe<BITS>;
-    constexpr int W = kAttnWaves;
+    constexpr int W = kAttnColBlocks / CB;      // wavefronts
     constexpr int QT = 16 / GQ;                 // queries per column block
     constexpr int DPL = 2 * BITS;
     constexpr int VTS = 40;                     // fp16 per transposed value row (80 B)
@@ -2995,14 +2997,24 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int BITS, bool QF32, bool OUT, bool SPLIT, int CB>
+static void launch_attn_cb(const AttnArgs &a, int gq, dim3 grid, hipStream_t s) {
+    const dim3 block(64 * (kAttnColBlocks / CB));
+    if (gq == 4)
+        hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32, CB, OUT, SPLIT>), grid, block, 0, s, a);
+    else if (gq == 2)
+        hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32, CB, OUT, SPLIT>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32, CB, OUT, SPLIT>), grid, block, 0, s, a);
+}
+
+// Two column blocks per wavefront once the first query block is full of
+// queries (T x GQ >= 128 columns): 4-5 % faster at T = 64 to 1024.  With
+// fewer queries a wavefront's second block would be empty (25-33 % slower at
+// T = 4 and 16), so those calls take one block per wavefront.
 template <int BITS, bool QF32, bool OUT, bool SPLIT = false>
 static void launch_attn_out(const AttnArgs &a, int gq, dim3 grid, hipStream_t s) {
-    const dim3 block(64 * kAttnWaves);
-    if (gq == 4)
-        hipLaunchKernelGGL((attn_kernel<BITS, 4, QF32, kAttnBlocks, OUT, SPLIT>), grid, block, 0, s, a);
-    else if (gq == 2)
-        hipLaunchKernelGGL((attn_kernel<BITS, 2, QF32, kAttnBlocks, OUT, SPLIT>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<BITS, 1, QF32, kAttnBlocks, OUT, SPLIT>), grid, block, 0, s, a);
+    if (a.T * gq >= 16 * kAttnColBlocks) launch_attn_cb<BITS, QF32, OUT, SPLIT, 2>(a, gq, grid, s);
+    else launch_attn_cb<BITS, QF32, OUT, SPLIT, 1>(a, gq, grid, s);
 }
 
 template <int BITS, bool QF32>

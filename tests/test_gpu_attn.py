@@ -63,6 +63,12 @@ def _run(orc, B, H, Hq, n, T, bits, R, causal, seed, chunks=None, q_dtype=np.flo
     (96, 7, 2, 128, 2, 0),       # everything in the residual window
     (1000, 100, 8, 128, 4, 1),   # 8-bit codes, causal
     (600, 16, 8, 64, 2, 0),      # 8-bit codes, split ranges
+    # the workgroup layout follows T * GQ: one 16-column block per wavefront
+    # below 128 columns, two from 128 on
+    (900, 31, 2, 64, 4, 1),      # 124 columns: one block per wavefront
+    (900, 32, 2, 64, 4, 1),      # 128 columns: two blocks per wavefront
+    (1200, 70, 4, 128, 2, 0),    # two blocks per wavefront at GQ = 2
+    (700, 130, 2, 32, 1, 1),     # two blocks per wavefront at GQ = 1, padding columns
 ])
 def test_attn_shapes(orc, n, T, bits, R, gq, causal):
     _run(orc, 2, 2, 2 * gq, n, T, bits, R, causal, seed=n + T, label="attn-%d-%d" % (n, T))
